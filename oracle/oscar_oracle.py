@@ -1,0 +1,510 @@
+"""Plain, slow, obviously-correct CPU oracle (NumPy; fp64 unless noted).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the product path.
+It shares no code with the HIP library: the page layout, the quantiser and
+the attention are all written out here again from their definitions.
+
+Pages cited (title, site), with the sections used:
+
+* [gist]    "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV
+            Cache Quantization" (gist.science explainer of arXiv 2605.17757),
+            "Technische Zusammenfassung" sections 2.1 (Theoretische
+            Motivation), 2.2 A (Offline-Kalibrierungsphase), 2.2 B
+            (Online-Betriebsphase), 4 (Experimentelle Ergebnisse).
+* [zingnex] "OSCAR：面向2-bit KV缓存量化的谱协方差感知旋转方法" (zingnex.cn),
+            sections 离线协方差估计, 注意力对齐的量化, 自定义INT2注意力内核,
+            离线优化的优势.
+* [yunpan]  "大模型KV Cache 2bit量化实战：OSCAR让显存暴降90%且智商不掉线"
+            (yunpan.plus), sections 二 (2-bit has four states), 三.1
+            三段式 Token 池, 三.2 在线量化与反量化, 三.3 兼容现有架构.
+
+Readings taken where the pages are silent (each one is also listed in the
+design notes of the repository):
+
+R1  Row vectors: a rotated vector is y = x . R, and the inverse is y . R^T.
+R2  C_Q pools all query heads of a layer; C_S pools all query heads, each
+    attending causally to its GQA key/value head.  One R_K and one R_V per
+    layer, shared by every KV head.
+R3  Eigenvectors in descending eigenvalue order; each column's sign makes
+    its largest-magnitude entry positive (ties: lowest index).
+R4  H_Had is block-diagonal normalised Sylvester Hadamard, block 32 (one
+    quantisation group); P_br is the 7-bit bit-reversal permutation,
+    y_j = x_{bitrev(j)}.
+R5  Clip thresholds: per rotated channel, the 99th percentile (linear
+    interpolation) of |x . R| over all calibration tokens and KV heads,
+    separately for K and V; clipping is to [-tau_j, tau_j] with IEEE
+    minNum/maxNum.  0 < tau <= 65504 is a precondition.
+R6  INT2 codes: groups of 32 rotated channels, asymmetric min-max with an
+    fp16 zero z = fp16 rounded toward -inf of the group minimum, and an fp16
+    scale s = fp16 rounded toward +inf of fp32((max - z) / 3); code
+    c = clamp(rint_even(fp32(fp32(y - z) / s)), 0, 3), c = 0 when s = 0.
+    All of this is IEEE fp32 with no fused multiply-add.  Dequantisation is
+    c * s + z.
+R7  Page = 16 tokens.  One 1536-byte block per (page, KV head); its byte
+    layout is defined by the ``*_offset`` / ``*_bitpos`` functions below.
+R8  Tiers: positions [0, 64) are the BF16 sink, the last 256 positions the
+    BF16 recent ring (position p in slot (p - 64) mod 256), everything in
+    between INT2 history (history index h = p - 64, page h // 16, slot
+    h % 16).  A decode step appends before it attends.
+R9  Softmax scale 1/sqrt(128); GQA head h reads KV head h // (Hq / Hkv);
+    output in fp32 (oracle: fp64).
+"""
+from __future__ import annotations
+
+import math
+import numpy as np
+
+HEAD_DIM = 128
+GROUP = 32
+N_GROUPS = HEAD_DIM // GROUP
+PAGE = 16
+N_SINK = 64
+N_RECENT = 256
+BLOCK_BYTES = 1536
+MAX_TAU = 65504.0
+
+
+# ---------------------------------------------------------------------------
+# small numeric helpers
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> exact float64 values."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def f16_round_down(x: np.ndarray) -> np.ndarray:
+    """Largest float16 <= x (x float32).  Returns float16."""
+    x = np.asarray(x, dtype=np.float32)
+    h = x.astype(np.float16)                       # nearest, ties to even
+    over = h.astype(np.float32) > x
+    return np.where(over, np.nextafter(h, np.float16(-np.inf)), h).astype(np.float16)
+
+
+def f16_round_up(x: np.ndarray) -> np.ndarray:
+    """Smallest float16 >= x (x float32).  Returns float16."""
+    x = np.asarray(x, dtype=np.float32)
+    h = x.astype(np.float16)
+    under = h.astype(np.float32) < x
+    return np.where(under, np.nextafter(h, np.float16(np.inf)), h).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# Offline calibration  ([gist] 2.1 and 2.2 A; [zingnex] 离线协方差估计)
+# ---------------------------------------------------------------------------
+
+def query_covariance(q: np.ndarray) -> np.ndarray:
+    """Query-aware key target C_Q = (1/N) sum_n q_n^T q_n ([gist] 2.2 A).
+
+    q: [N, Hq, d]; every (token, head) row is one sample (reading R2).
+    """
+    x = np.asarray(q, dtype=np.float64).reshape(-1, q.shape[-1])
+    return x.T @ x / x.shape[0]
+
+
+def causal_attention_probs(qh: np.ndarray, kh: np.ndarray) -> np.ndarray:
+    """Row-stochastic causal softmax matrix S for one head: S[n, m] for m <= n."""
+    n, d = qh.shape
+    logits = (qh @ kh.T) / math.sqrt(d)
+    logits[np.triu_indices(n, 1)] = -np.inf
+    logits -= logits.max(axis=1, keepdims=True)
+    e = np.exp(logits)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def score_covariance(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Score-aware value target C_S = (1/N) V^T S^T S V ([gist] 2.1, 2.2 A).
+
+    Written through the identity V^T S^T S V = (S V)^T (S V): the covariance
+    of the attention outputs, pooled over query heads (reading R2).
+    q: [N, Hq, d], k, v: [N, Hkv, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, hq, d = q.shape
+    g = hq // k.shape[1]
+    acc = np.zeros((d, d))
+    for h in range(hq):
+        s = causal_attention_probs(q[:, h, :], k[:, h // g, :])
+        o = s @ v[:, h // g, :]
+        acc += o.T @ o
+    return acc / (n * hq)
+
+
+def eigenbasis(c: np.ndarray) -> np.ndarray:
+    """Eigenvectors of a symmetric matrix as columns, descending eigenvalues,
+    sign fixed per reading R3 ([gist] 2.2 A "Rotationsermittlung")."""
+    w, u = np.linalg.eigh(np.asarray(c, dtype=np.float64))
+    order = np.argsort(-w, kind="stable")
+    u = u[:, order].copy()
+    for col in range(u.shape[1]):
+        i = int(np.argmax(np.abs(u[:, col])))       # first index on ties
+        if u[i, col] < 0:
+            u[:, col] = -u[:, col]
+    return u
+
+
+def sylvester_hadamard(n: int) -> np.ndarray:
+    """Unnormalised Sylvester Hadamard matrix of order n (a power of two)."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_block(d: int = HEAD_DIM, block: int = GROUP) -> np.ndarray:
+    """Block-diagonal orthonormal Hadamard H_Had (reading R4; [gist] 2.2 A)."""
+    hb = sylvester_hadamard(block) / math.sqrt(block)
+    out = np.zeros((d, d))
+    for b0 in range(0, d, block):
+        out[b0:b0 + block, b0:b0 + block] = hb
+    return out
+
+
+def bit_reverse(j: int, bits: int) -> int:
+    r = 0
+    for _ in range(bits):
+        r = (r << 1) | (j & 1)
+        j >>= 1
+    return r
+
+
+def bitrev_permutation(d: int = HEAD_DIM) -> np.ndarray:
+    """P_br as a matrix acting on row vectors: (x P)_j = x_{bitrev(j)}."""
+    bits = d.bit_length() - 1
+    p = np.zeros((d, d))
+    for j in range(d):
+        p[bit_reverse(j, bits), j] = 1.0
+    return p
+
+
+def composite_rotation(u: np.ndarray, block: int = GROUP) -> np.ndarray:
+    """R = U . H_Had . P_br ([gist] 2.2 A "Aufbau der zusammengesetzten Rotation")."""
+    d = u.shape[0]
+    return u @ hadamard_block(d, block) @ bitrev_permutation(d)
+
+
+def clip_thresholds(x: np.ndarray, r: np.ndarray, percentile: float = 99.0) -> np.ndarray:
+    """Per rotated channel percentile of |x . R| (reading R5; [gist] 2.2 A
+    "Clipping-Schwellenwerte"). x: [..., d] values; returns float32 [d]."""
+    y = np.asarray(x, dtype=np.float64).reshape(-1, r.shape[0]) @ np.asarray(r, np.float64)
+    return np.percentile(np.abs(y), percentile, axis=0, method="linear").astype(np.float32)
+
+
+def calibrate(q, k, v, hadamard_block_size: int = GROUP, percentile: float = 99.0):
+    """Offline calibration of one layer: returns (R_K, R_V, tau_K, tau_V),
+    R as float32 [d, d] (y = x . R) and tau as float32 [d]."""
+    c_q = query_covariance(q)
+    c_s = score_covariance(q, k, v)
+    r_k = composite_rotation(eigenbasis(c_q), hadamard_block_size).astype(np.float32)
+    r_v = composite_rotation(eigenbasis(c_s), hadamard_block_size).astype(np.float32)
+    tau_k = clip_thresholds(k, r_k, percentile)
+    tau_v = clip_thresholds(v, r_v, percentile)
+    return r_k, r_v, tau_k, tau_v
+
+
+# ---------------------------------------------------------------------------
+# Demotion: rotate -> clip -> quantise -> pack  ([yunpan] 三.2; [gist] 2.2 B)
+# ---------------------------------------------------------------------------
+
+def rotate_fp32(x: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """y = fp32(x . R) with the product taken in fp64 (reading R1)."""
+    return (np.asarray(x, np.float64) @ np.asarray(r, np.float64)).astype(np.float32)
+
+
+def clip(y: np.ndarray, tau: np.ndarray) -> np.ndarray:
+    """Symmetric per-channel clip to [-tau, tau] (IEEE minNum/maxNum)."""
+    y = np.asarray(y, np.float32)
+    t = np.asarray(tau, np.float32)
+    return np.fmin(np.fmax(y, -t), t)
+
+
+def group_params(yc: np.ndarray):
+    """Per 32-channel group: (scale, zero) as float16, reading R6.
+
+    yc: float32 [..., 128] -> scale, zero: float16 [..., 4].
+    """
+    g = np.asarray(yc, np.float32).reshape(yc.shape[:-1] + (N_GROUPS, GROUP))
+    mn = g.min(axis=-1)
+    mx = g.max(axis=-1)
+    zero = f16_round_down(mn)
+    span = (mx - zero.astype(np.float32)).astype(np.float32)
+    scale = f16_round_up((span / np.float32(3.0)).astype(np.float32))
+    return scale, zero
+
+
+def quant_codes(yc: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
+    """INT2 codes (4 levels; [yunpan] 二) for clipped rotated values, R6."""
+    g = np.asarray(yc, np.float32).reshape(yc.shape[:-1] + (N_GROUPS, GROUP))
+    s = scale.astype(np.float32)[..., None]
+    z = zero.astype(np.float32)[..., None]
+    diff = (g - z).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quot = np.where(s > 0, diff / np.where(s > 0, s, np.float32(1)), np.float32(0))
+    c = np.clip(np.rint(quot.astype(np.float32)), 0, 3).astype(np.uint8)
+    return c.reshape(yc.shape)
+
+
+def dequantize(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
+    """c * s + z in fp64, per group. codes [..., 128], scale/zero [..., 4]."""
+    c = np.asarray(codes, np.float64).reshape(codes.shape[:-1] + (N_GROUPS, GROUP))
+    out = c * scale.astype(np.float64)[..., None] + zero.astype(np.float64)[..., None]
+    return out.reshape(codes.shape)
+
+
+def quantize_rotated(y: np.ndarray, tau: np.ndarray):
+    """Clip + quantise already-rotated fp32 vectors: returns codes, scale, zero."""
+    yc = clip(y, tau)
+    scale, zero = group_params(yc)
+    return quant_codes(yc, scale, zero), scale, zero
+
+
+# ---------------------------------------------------------------------------
+# Page block layout (reading R7).  "Four 2-bit values per byte" is the only
+# thing the pages fix ([yunpan] 三.2); the rest is this format's own choice.
+#
+# Block of one (page, KV head), 1536 bytes:
+#   [   0, 1024)  codes: 64 chunks of 16 bytes; chunk c = 16*a + b holds
+#                 K codes in bytes 0..7 and V codes in bytes 8..15.
+#   [1024, 1152)  K scales  fp16, index [token][group]
+#   [1152, 1280)  K zeros   fp16, index [token][group]
+#   [1280, 1408)  V scales  fp16, index [token // 4][group][token % 4]
+#   [1408, 1536)  V zeros   fp16, same index
+# Codes are 2-bit fields of little-endian 32-bit words; field f occupies
+# bits 2f, 2f+1 of its word.
+# ---------------------------------------------------------------------------
+
+def k_code_bitpos(t: int, j: int) -> int:
+    """Absolute bit index (byte*8 + bit) of K code (token t, channel j)."""
+    a = (j >> 3) & 3                 # which quarter of the group
+    word = j >> 6                    # groups {0,1} -> word 0, {2,3} -> word 1
+    field = 4 * ((j >> 5) & 1) + ((j >> 1) & 3) + 8 * (j & 1)
+    byte = 16 * (16 * a + t) + 4 * word
+    return byte * 8 + 2 * field
+
+
+def v_code_bitpos(t: int, j: int) -> int:
+    """Absolute bit index of V code (token t, channel j)."""
+    x = j & 15
+    blk = j >> 4
+    tq, u = t >> 2, t & 3
+    word = u >> 1
+    field = blk + 8 * (u & 1)
+    byte = 16 * (16 * tq + x) + 8 + 4 * word
+    return byte * 8 + 2 * field
+
+
+def k_scale_offset(t: int, g: int) -> int:
+    return 1024 + 8 * t + 2 * g
+
+
+def k_zero_offset(t: int, g: int) -> int:
+    return 1152 + 8 * t + 2 * g
+
+
+def v_scale_offset(t: int, g: int) -> int:
+    return 1280 + 32 * (t >> 2) + 8 * g + 2 * (t & 3)
+
+
+def v_zero_offset(t: int, g: int) -> int:
+    return 1408 + 32 * (t >> 2) + 8 * g + 2 * (t & 3)
+
+
+def _put_code(block: np.ndarray, bitpos: int, c: int) -> None:
+    byte, bit = divmod(bitpos, 8)
+    block[byte] = (int(block[byte]) & ~(3 << bit) | ((int(c) & 3) << bit)) & 0xFF
+
+
+def _get_code(block: np.ndarray, bitpos: int) -> int:
+    byte, bit = divmod(bitpos, 8)
+    return (int(block[byte]) >> bit) & 3
+
+
+def _put_f16(block: np.ndarray, off: int, val) -> None:
+    b = np.asarray(val, dtype=np.float16).reshape(1).view(np.uint8)
+    block[off] = b[0]
+    block[off + 1] = b[1]
+
+
+def _get_f16(block: np.ndarray, off: int) -> np.float16:
+    return block[off:off + 2].copy().view(np.float16)[0]
+
+
+def write_token(block: np.ndarray, slot: int, kc, ks, kz, vc, vs, vz) -> None:
+    """Store one token's K and V codes [128] and scale/zero [4] into a block."""
+    for j in range(HEAD_DIM):
+        _put_code(block, k_code_bitpos(slot, j), kc[j])
+        _put_code(block, v_code_bitpos(slot, j), vc[j])
+    for g in range(N_GROUPS):
+        _put_f16(block, k_scale_offset(slot, g), ks[g])
+        _put_f16(block, k_zero_offset(slot, g), kz[g])
+        _put_f16(block, v_scale_offset(slot, g), vs[g])
+        _put_f16(block, v_zero_offset(slot, g), vz[g])
+
+
+def read_token(block: np.ndarray, slot: int):
+    """Inverse of write_token: (kc, ks, kz, vc, vs, vz)."""
+    kc = np.array([_get_code(block, k_code_bitpos(slot, j)) for j in range(HEAD_DIM)], np.uint8)
+    vc = np.array([_get_code(block, v_code_bitpos(slot, j)) for j in range(HEAD_DIM)], np.uint8)
+    ks = np.array([_get_f16(block, k_scale_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
+    kz = np.array([_get_f16(block, k_zero_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
+    vs = np.array([_get_f16(block, v_scale_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
+    vz = np.array([_get_f16(block, v_zero_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
+    return kc, ks, kz, vc, vs, vz
+
+
+# ---------------------------------------------------------------------------
+# Three-tier pool ([yunpan] 三.1, 三.2; [gist] 2.2 B "Mixed-Precision-Layout")
+# ---------------------------------------------------------------------------
+
+def tier_of(p: int, n: int) -> str:
+    """Tier of position p in a sequence of n tokens (reading R8)."""
+    if p < N_SINK:
+        return "sink"
+    if p >= max(N_SINK, n - N_RECENT):
+        return "recent"
+    return "history"
+
+
+def ring_slot(p: int) -> int:
+    return (p - N_SINK) % N_RECENT
+
+
+class Pool:
+    """Tiered KV pool state, byte-for-byte in the library's formats.
+
+    sink_k/v, recent_k/v: uint16 bf16 bits [S, Hkv, 64|256, 128]
+    hist: uint8 [num_pages, Hkv, 1536]; page_table: int32 [S, max_pages]
+    """
+
+    def __init__(self, n_slots, n_kv_heads, num_pages, page_table):
+        self.hkv = n_kv_heads
+        self.sink_k = np.zeros((n_slots, n_kv_heads, N_SINK, HEAD_DIM), np.uint16)
+        self.sink_v = np.zeros_like(self.sink_k)
+        self.recent_k = np.zeros((n_slots, n_kv_heads, N_RECENT, HEAD_DIM), np.uint16)
+        self.recent_v = np.zeros_like(self.recent_k)
+        self.hist = np.zeros((num_pages, n_kv_heads, BLOCK_BYTES), np.uint8)
+        self.page_table = np.asarray(page_table, np.int32)
+        self.length = np.zeros(n_slots, np.int64)
+
+    def demote_rotated(self, slot: int, h_index: int, yk, yv, tau_k, tau_v) -> None:
+        """Quantise already-rotated fp32 K/V [Hkv, 128] into history index h."""
+        page = int(self.page_table[slot, h_index // PAGE])
+        ps = h_index % PAGE
+        kc, ks, kz = quantize_rotated(yk, tau_k)
+        vc, vs, vz = quantize_rotated(yv, tau_v)
+        for hd in range(self.hkv):
+            write_token(self.hist[page, hd], ps, kc[hd], ks[hd], kz[hd], vc[hd], vs[hd], vz[hd])
+
+    def demote(self, slot, h_index, k_bits, v_bits, r_k, r_v, tau_k, tau_v) -> None:
+        """Rotate bf16 K/V [Hkv, 128] by R and demote them ([yunpan] 三.2)."""
+        yk = rotate_fp32(bf16_to_f64(k_bits), r_k)
+        yv = rotate_fp32(bf16_to_f64(v_bits), r_v)
+        self.demote_rotated(slot, h_index, yk, yv, tau_k, tau_v)
+
+    def append(self, slot, k_bits, v_bits, r_k, r_v, tau_k, tau_v) -> None:
+        """Route one new token (k, v: bf16 bits [Hkv, 128]) into the tiers.
+
+        When the recent ring is full, its oldest token (position p - 256)
+        is demoted first, then the new token takes its ring slot.
+        """
+        p = int(self.length[slot])
+        if p < N_SINK:
+            self.sink_k[slot, :, p] = k_bits
+            self.sink_v[slot, :, p] = v_bits
+        else:
+            r = ring_slot(p)
+            if p >= N_SINK + N_RECENT:
+                self.demote(slot, p - N_SINK - N_RECENT, self.recent_k[slot, :, r],
+                            self.recent_v[slot, :, r], r_k, r_v, tau_k, tau_v)
+            self.recent_k[slot, :, r] = k_bits
+            self.recent_v[slot, :, r] = v_bits
+        self.length[slot] = p + 1
+
+    def reconstruct(self, slot, n, r_k, r_v):
+        """K~, V~ [Hkv, n, 128] fp64 in the unrotated space (plain definition):
+        BF16 values for sink/recent, dequant(c, s, z) . R^T for history."""
+        kt = np.zeros((self.hkv, n, HEAD_DIM))
+        vt = np.zeros((self.hkv, n, HEAD_DIM))
+        rk = np.asarray(r_k, np.float64)
+        rv = np.asarray(r_v, np.float64)
+        for p in range(n):
+            tier = tier_of(p, n)
+            if tier == "sink":
+                kt[:, p] = bf16_to_f64(self.sink_k[slot, :, p])
+                vt[:, p] = bf16_to_f64(self.sink_v[slot, :, p])
+            elif tier == "recent":
+                r = ring_slot(p)
+                kt[:, p] = bf16_to_f64(self.recent_k[slot, :, r])
+                vt[:, p] = bf16_to_f64(self.recent_v[slot, :, r])
+            else:
+                h = p - N_SINK
+                page = int(self.page_table[slot, h // PAGE])
+                for hd in range(self.hkv):
+                    kc, ks, kz, vc, vs, vz = read_token(self.hist[page, hd], h % PAGE)
+                    kt[hd, p] = dequantize(kc, ks, kz) @ rk.T
+                    vt[hd, p] = dequantize(vc, vs, vz) @ rv.T
+        return kt, vt
+
+
+# ---------------------------------------------------------------------------
+# Attention (the plain definition; [gist] 2.2 B, [zingnex] 自定义INT2注意力内核)
+# ---------------------------------------------------------------------------
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """softmax(q K^T / sqrt(d)) V for one query vector or rows of queries (fp64)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    logits = q @ k.T / math.sqrt(q.shape[-1])
+    logits -= logits.max(axis=-1, keepdims=True)
+    w = np.exp(logits)
+    w /= w.sum(axis=-1, keepdims=True)
+    return w @ v
+
+
+def decode_tiered(q_bits, pool: Pool, seq_slot, seq_len, r_k, r_v) -> np.ndarray:
+    """Single-token decode over the tiered pool: out [B, Hq, 128] fp64.
+
+    q_bits: bf16 bits [B, Hq, 128]; seq_len[b] counts the tokens in the cache
+    after this step's append, so the new token attends to itself (R8).
+    """
+    q = bf16_to_f64(q_bits)
+    b_n, hq, _ = q.shape
+    g = hq // pool.hkv
+    out = np.zeros((b_n, hq, HEAD_DIM))
+    for b in range(b_n):
+        kt, vt = pool.reconstruct(int(seq_slot[b]), int(seq_len[b]), r_k, r_v)
+        for h in range(hq):
+            out[b, h] = attention(q[b, h], kt[h // g], vt[h // g])
+    return out
+
+
+# BF16 baseline pool: [num_pages, Hkv, 2, 16, 128] bf16 (K page, then V page).
+
+def bf16_pool_gather(pool_bits, page_table_row, n):
+    """All n tokens of one sequence from a BF16 paged pool: K, V [Hkv, n, 128]."""
+    hkv = pool_bits.shape[1]
+    k = np.zeros((hkv, n, HEAD_DIM))
+    v = np.zeros((hkv, n, HEAD_DIM))
+    for p in range(n):
+        page = int(page_table_row[p // PAGE])
+        k[:, p] = bf16_to_f64(pool_bits[page, :, 0, p % PAGE])
+        v[:, p] = bf16_to_f64(pool_bits[page, :, 1, p % PAGE])
+    return k, v
+
+
+def decode_bf16(q_bits, pool_bits, page_table, seq_slot, seq_len) -> np.ndarray:
+    """Full-precision decode over a BF16 paged pool (the comparison baseline)."""
+    q = bf16_to_f64(q_bits)
+    b_n, hq, _ = q.shape
+    g = hq // pool_bits.shape[1]
+    out = np.zeros((b_n, hq, HEAD_DIM))
+    for b in range(b_n):
+        k, v = bf16_pool_gather(pool_bits, page_table[int(seq_slot[b])], int(seq_len[b]))
+        for h in range(hq):
+            out[b, h] = attention(q[b, h], k[h // g], v[h // g])
+    return out

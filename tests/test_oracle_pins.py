@@ -1,0 +1,447 @@
+"""Pins for the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types an oracle formula: each checks a closed form, a
+hand-worked fixture, an invariant or a brute-force evaluation.  All run on
+the CPU (no ``gpu`` mark).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from bit_rotated_kv_demote_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- rotation
+
+def test_hadamard_order4_matches_sylvester_fixture():
+    g = _gold("hadamard4.json")
+    h = orc.sylvester_hadamard(4)
+    assert np.array_equal(h, np.array(g["H4_unnormalised"], float))
+
+
+def test_hadamard_popcount_closed_form_and_orthonormal():
+    hb = orc.hadamard_block(128, 32)
+    for i in range(128):
+        for j in range(128):
+            if i // 32 == j // 32:
+                exp = (-1) ** bin((i % 32) & (j % 32)).count("1") / math.sqrt(32)
+            else:
+                exp = 0.0
+            assert hb[i, j] == pytest.approx(exp, abs=1e-15)
+    assert np.allclose(hb @ hb.T, np.eye(128), atol=1e-13)
+
+
+def test_bitrev_fixture_involution_permutation():
+    for j, r in _gold("bitrev7.json")["pairs"]:
+        assert orc.bit_reverse(j, 7) == r
+    p = orc.bitrev_permutation(128)
+    assert np.array_equal(p @ p, np.eye(128))          # involution
+    assert np.array_equal(p.sum(0), np.ones(128)) and np.array_equal(p.sum(1), np.ones(128))
+    x = np.arange(128, dtype=float)
+    y = x @ p
+    assert all(y[j] == orc.bit_reverse(j, 7) for j in range(128))
+
+
+def test_bitrev_interleaves_hadamard_blocks_into_every_group():
+    # Each 32-channel quantisation group must draw 8 channels from each of
+    # the 4 Hadamard blocks (the stated purpose of P_br).
+    p = orc.bitrev_permutation(128)
+    src = np.argmax(p, axis=0)           # output channel j takes input src[j]
+    for g in range(4):
+        blocks = src[32 * g:32 * g + 32] // 32
+        assert sorted(np.bincount(blocks, minlength=4).tolist()) == [8, 8, 8, 8]
+
+
+def test_eigenbasis_planted_closed_form():
+    rng = np.random.default_rng(7)
+    q0 = synth.random_rotation(rng).astype(np.float64)
+    q0, _ = np.linalg.qr(q0)
+    lam = np.linspace(50.0, 1.0, 128)                  # distinct, descending
+    c = q0 @ np.diag(lam) @ q0.T
+    u = orc.eigenbasis(c)
+    # Expected: columns of q0 in the same order, signs per the rule.
+    for col in range(128):
+        v = q0[:, col].copy()
+        i = int(np.argmax(np.abs(v)))
+        if v[i] < 0:
+            v = -v
+        assert np.allclose(u[:, col], v, atol=1e-9)
+    d = u.T @ c @ u
+    assert np.allclose(d, np.diag(np.diag(d)), atol=1e-9)
+    assert np.all(np.diff(np.diag(d)) <= 1e-9)
+
+
+def test_query_covariance_planted_population():
+    # q = z A with z ~ N(0, I): E[q^T q] = A^T A.  With many samples C_Q -> A^T A.
+    rng = np.random.default_rng(3)
+    a = np.diag(np.linspace(3.0, 0.5, 8))
+    z = rng.standard_normal((200000, 2, 8))
+    c = orc.query_covariance(z @ a)
+    assert np.allclose(c, a.T @ a, atol=0.03)
+
+
+def _brute_causal_probs(qh, kh):
+    n, d = qh.shape
+    s = np.zeros((n, n))
+    for i in range(n):
+        logits = [sum(qh[i, t] * kh[j, t] for t in range(d)) / math.sqrt(d) for j in range(i + 1)]
+        mx = max(logits)
+        e = [math.exp(x - mx) for x in logits]
+        tot = sum(e)
+        for j in range(i + 1):
+            s[i, j] = e[j] / tot
+    return s
+
+
+def test_score_covariance_equals_explicit_vtstsv():
+    rng = np.random.default_rng(11)
+    n, hq, hkv, d = 7, 4, 2, 6
+    q = rng.standard_normal((n, hq, d))
+    k = rng.standard_normal((n, hkv, d))
+    v = rng.standard_normal((n, hkv, d))
+    expect = np.zeros((d, d))
+    for h in range(hq):
+        s = _brute_causal_probs(q[:, h], k[:, h // 2])
+        vv = v[:, h // 2]
+        expect += vv.T @ s.T @ s @ vv               # V^T S^T S V, no identity used
+    expect /= n * hq
+    assert np.allclose(orc.score_covariance(q, k, v), expect, atol=1e-12)
+
+
+def test_calibrate_rotation_orthogonal_and_clip_order_statistic():
+    st = synth.streams(0)
+    out = synth.outlier_channels(st["outliers"])
+    n = 256
+    k = synth.bf16_bits_to_f32(synth.kv_tokens(st["k"], st["lognormal"], n, 2, out))
+    v = synth.bf16_bits_to_f32(synth.kv_tokens(st["v"], st["lognormal"], n, 2, out))
+    q = synth.bf16_bits_to_f32(synth.queries(st["q"], (n, 4, 128)))
+    r_k, r_v, t_k, t_v = orc.calibrate(q, k, v)
+    for r in (r_k, r_v):
+        r64 = r.astype(np.float64)
+        assert np.linalg.norm(r64 @ r64.T - np.eye(128)) < 1e-5
+    # tau_j: with N distinct samples the linear 99th percentile leaves exactly
+    # N - 1 - floor(0.99 (N - 1)) samples strictly above it.
+    y = np.abs(k.reshape(-1, 128).astype(np.float64) @ r_k.astype(np.float64))
+    nn = y.shape[0]
+    above = (y > t_k.astype(np.float64)[None, :] * (1 + 1e-6)).sum(0)
+    want = nn - 1 - math.floor(0.99 * (nn - 1))
+    assert np.all(np.abs(above - want) <= 1)
+
+
+def test_percentile_fixture():
+    x = np.arange(1, 101, dtype=float)[:, None] * np.ones((1, 128))
+    tau = orc.clip_thresholds(x, np.eye(128))
+    assert np.allclose(tau, 99.01, atol=1e-5)          # 1 + 0.99 * 99
+
+
+# ---------------------------------------------------------------- quantiser
+
+def test_quant_hand_worked_groups():
+    g = _gold("quant_groups.json")
+    y = np.array([np.float32(s) for s in g["y"]], np.float32)
+    c, s, z = orc.quantize_rotated(y[None], np.full(128, 65504, np.float32))
+    assert [float(v) for v in s[0]] == [float(x) for x in g["scale"]]
+    assert [float(v) for v in z[0]] == [float(x) for x in g["zero"]]
+    assert c[0].tolist() == g["codes"]
+
+
+def _random_rotated(n, seed):
+    st = synth.streams(seed)
+    out = synth.outlier_channels(st["outliers"])
+    x = synth.bf16_bits_to_f32(synth.kv_tokens(st["k"], st["lognormal"], n, 1, out))[:, 0]
+    r = synth.random_rotation(st["rot"])
+    return orc.rotate_fp32(x, r)
+
+
+def test_quant_error_within_half_step_for_unclipped():
+    y = _random_rotated(4000, 0)
+    tau = np.full(128, 65504, np.float32)
+    c, s, z = orc.quantize_rotated(y, tau)
+    assert c.min() >= 0 and c.max() <= 3
+    xh = orc.dequantize(c, s, z)
+    err = np.abs(xh - y.astype(np.float64)).reshape(-1, 4, 32)
+    half = s.astype(np.float64)[..., None] / 2
+    # slack: the one fp32 rounding of (y - z) before the division
+    ulp = np.spacing(np.abs(y).astype(np.float32)).reshape(-1, 4, 32).astype(np.float64)
+    assert np.all(err <= half * (1 + 2 ** -20) + ulp)
+
+
+def test_quant_grid_roundtrip_lossless():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        z = np.float16(rng.integers(-512, 512) / 8.0)
+        s = np.float16(rng.integers(1, 64) / 16.0)
+        codes = rng.integers(0, 4, size=32)
+        codes[0], codes[1] = 0, 3                          # the group spans the grid
+        y = (np.float32(z) + codes.astype(np.float32) * np.float32(s)).astype(np.float32)
+        yy = np.tile(y, 4)[None]
+        c, sc, zc = orc.quantize_rotated(yy, np.full(128, 65504, np.float32))
+        assert np.all(sc == s) and np.all(zc == z)
+        assert np.array_equal(c[0, :32], codes)
+
+
+def test_quant_monotone_and_nearest_level():
+    y = _random_rotated(500, 2)
+    c, s, z = orc.quantize_rotated(y, np.full(128, 65504, np.float32))
+    g = y.reshape(-1, 4, 32).astype(np.float64)
+    cg = c.reshape(-1, 4, 32)
+    for i in range(g.shape[0]):
+        for gg in range(4):
+            order = np.argsort(g[i, gg], kind="stable")
+            assert np.all(np.diff(cg[i, gg][order].astype(int)) >= 0)
+            levels = float(z[i, gg]) + np.arange(4) * float(s[i, gg])
+            d = np.abs(g[i, gg][:, None] - levels[None, :])
+            best = d.argmin(1)
+            tie = np.sort(d, 1)[:, 1] - np.sort(d, 1)[:, 0] < 1e-6 * float(s[i, gg])
+            assert np.all((best == cg[i, gg]) | tie)
+
+
+def test_identity_rotation_no_clip_is_textbook_minmax_int2():
+    # R = I and a clip bound above the data: demotion is plain asymmetric
+    # min-max 2-bit quantisation with step (max - min) / 3.
+    rng = np.random.default_rng(9)
+    x = synth.bf16_bits_to_f32(synth.to_bf16_bits(rng.standard_normal((64, 128)).astype(np.float32)))
+    y = orc.rotate_fp32(x, np.eye(128, dtype=np.float32))
+    assert np.array_equal(y, x)
+    c, s, z = orc.quantize_rotated(y, np.full(128, 65504, np.float32))
+    g = x.reshape(64, 4, 32).astype(np.float64)
+    step = (g.max(-1) - g.min(-1)) / 3
+    assert np.all(s.astype(np.float64) >= step) and np.all(s.astype(np.float64) <= step * (1 + 2 ** -9) + 2 ** -24)
+    assert np.all(z.astype(np.float64) <= g.min(-1)) and np.all(g.min(-1) - z.astype(np.float64) <= np.abs(g.min(-1)) * 2 ** -10 + 2 ** -24)
+    assert c.reshape(64, 4, 32)[np.arange(64)[:, None], np.arange(4)[None], g.argmin(-1)].max() == 0
+
+
+def test_clip_saturates_and_degenerate_group():
+    y = np.zeros((1, 128), np.float32)
+    y[0, :32] = np.linspace(-10, 10, 32)
+    y[0, 32:64] = np.float32(0.75)                          # constant, fp16-exact
+    tau = np.full(128, 2.0, np.float32)
+    c, s, z = orc.quantize_rotated(y, tau)
+    assert float(z[0, 0]) == -2.0 and float(s[0, 0]) == pytest.approx(4 / 3, rel=2e-3)
+    assert c[0, 0] == 0 and c[0, 31] == 3
+    assert float(s[0, 1]) == 0.0 and float(z[0, 1]) == 0.75 and np.all(c[0, 32:64] == 0)
+    assert np.array_equal(orc.clip(np.array([np.inf, -np.inf], np.float32), np.array([3, 3], np.float32)),
+                          np.array([3, -3], np.float32))
+
+
+# ---------------------------------------------------------------- layout
+
+def test_layout_fixture_points():
+    g = _gold("layout_points.json")
+    for t, j, b in g["k_code"]:
+        assert orc.k_code_bitpos(t, j) == b
+    for t, j, b in g["v_code"]:
+        assert orc.v_code_bitpos(t, j) == b
+    for t, gg, o in g["k_scale"]:
+        assert orc.k_scale_offset(t, gg) == o
+    for t, gg, o in g["v_scale"]:
+        assert orc.v_scale_offset(t, gg) == o
+    for t, gg, o in g["v_zero"]:
+        assert orc.v_zero_offset(t, gg) == o
+
+
+def test_layout_is_a_bijection_four_codes_per_byte():
+    kb = {orc.k_code_bitpos(t, j) for t in range(16) for j in range(128)}
+    vb = {orc.v_code_bitpos(t, j) for t in range(16) for j in range(128)}
+    assert len(kb) == 2048 and len(vb) == 2048 and not (kb & vb)
+    assert all(b % 2 == 0 for b in kb | vb)
+    bytes_used = {b // 8 for b in kb | vb}
+    assert bytes_used == set(range(1024))                   # 4 codes per byte, no gaps
+    assert {(b // 8) % 16 < 8 for b in kb} == {True}         # K in bytes 0..7 of a chunk
+    assert {(b // 8) % 16 >= 8 for b in vb} == {True}
+    meta = set()
+    for t in range(16):
+        for gg in range(4):
+            for f in (orc.k_scale_offset, orc.k_zero_offset, orc.v_scale_offset, orc.v_zero_offset):
+                o = f(t, gg)
+                meta |= {o, o + 1}
+    assert meta == set(range(1024, 1536))
+
+
+def test_block_pack_roundtrip_exhaustive():
+    rng = np.random.default_rng(1)
+    block = np.zeros(1536, np.uint8)
+    toks = []
+    for slot in range(16):
+        kc, vc = rng.integers(0, 4, 128).astype(np.uint8), rng.integers(0, 4, 128).astype(np.uint8)
+        ks, kz, vs, vz = (rng.standard_normal(4).astype(np.float16) for _ in range(4))
+        orc.write_token(block, slot, kc, ks, kz, vc, vs, vz)
+        toks.append((kc, ks, kz, vc, vs, vz))
+    for slot in range(16):
+        got = orc.read_token(block, slot)
+        for a, b in zip(got, toks[slot]):
+            assert np.array_equal(a, b)
+    # every byte value survives: exhaustive over the 256 patterns of one byte
+    for val in range(256):
+        blk = np.zeros(1536, np.uint8)
+        blk[0] = val
+        kc = orc.read_token(blk, 0)[0]
+        ref = np.zeros(1536, np.uint8)
+        orc.write_token(ref, 0, kc, *[np.zeros(4, np.float16)] * 2, np.zeros(128, np.uint8),
+                        *[np.zeros(4, np.float16)] * 2)
+        assert ref[0] == val
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_two_token_closed_form():
+    g = _gold("attention_two_tokens.json")
+    q = np.zeros(128)
+    q[0] = math.sqrt(128) * math.log(3)
+    k = np.zeros((2, 128))
+    v = np.zeros((2, 128))
+    for row, (ch, val) in enumerate(g["k"]):
+        k[row, ch] = val
+    for row, (ch, val) in enumerate(g["v"]):
+        v[row, ch] = val
+    o = orc.attention(q, k, v)
+    exp = np.zeros(128)
+    for ch, val in g["expected_nonzero"].items():
+        exp[int(ch)] = val
+    assert np.allclose(o, exp, atol=1e-12)
+
+
+def test_attention_rotation_invariance():
+    rng = np.random.default_rng(4)
+    r = np.linalg.qr(rng.standard_normal((128, 128)))[0]
+    q = rng.standard_normal(128)
+    k = rng.standard_normal((50, 128)) * 3
+    v = rng.standard_normal((50, 128))
+    a = orc.attention(q @ r, k @ r, v @ r) @ r.T
+    assert np.allclose(a, orc.attention(q, k, v), atol=1e-12)
+
+
+def _brute_attention(q, k, v):
+    d = len(q)
+    logits = [sum(q[i] * kk[i] for i in range(d)) / math.sqrt(d) for kk in k]
+    m = max(logits)
+    w = [math.exp(x - m) for x in logits]
+    tot = sum(w)
+    return np.array([sum(w[t] * v[t][i] for t in range(len(k))) / tot for i in range(d)])
+
+
+# ---------------------------------------------------------------- pool
+
+def _run_appends(n, hkv=1, seed=0, num_pages=64):
+    st = synth.streams(seed)
+    out = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out)
+    r = synth.random_rotation(st["rot"])
+    tau = orc.clip_thresholds(synth.bf16_bits_to_f32(k), r)
+    pt = synth.page_permutation(st["perm"], num_pages)[None, :]
+    pool = orc.Pool(1, hkv, num_pages, pt)
+    for p in range(n):
+        pool.append(0, k[p], v[p], r, r, tau, tau)
+    return pool, k, v, r, tau
+
+
+def test_tier_boundaries():
+    for n in (1, 63, 64, 65, 320, 321, 1000):
+        tiers = [orc.tier_of(p, n) for p in range(n)]
+        assert tiers.count("sink") == min(n, 64)
+        assert tiers.count("recent") == min(max(n - 64, 0), 256)
+        assert tiers.count("history") == max(n - 320, 0)
+        if n > 320:
+            assert tiers[64] == "history" and tiers[n - 257] == "history" and tiers[n - 256] == "recent"
+
+
+def test_no_history_decode_equals_brute_force_attention():
+    n = 300
+    pool, k, v, r, tau = _run_appends(n)
+    assert not pool.hist.any()                               # no demotion before p >= 320
+    q = synth.queries(np.random.default_rng(2), (1, 2, 128))
+    out = orc.decode_tiered(q, pool, [0], [n], r, r)
+    kk = synth.bf16_bits_to_f32(k[:, 0]).astype(np.float64)
+    vv = synth.bf16_bits_to_f32(v[:, 0]).astype(np.float64)
+    qq = synth.bf16_bits_to_f32(q).astype(np.float64)
+    for h in range(2):
+        assert np.allclose(out[0, h], _brute_attention(qq[0, h], kk.tolist(), vv.tolist()), atol=1e-10)
+
+
+def test_history_decode_equals_brute_force_over_dequantised_cache():
+    n = 360                                                  # 40 history tokens
+    pool, k, v, r, tau = _run_appends(n)
+    q = synth.queries(np.random.default_rng(3), (1, 2, 128))
+    out = orc.decode_tiered(q, pool, [0], [n], r, r)
+    kk = synth.bf16_bits_to_f32(k[:, 0]).astype(np.float64)
+    vv = synth.bf16_bits_to_f32(v[:, 0]).astype(np.float64)
+    r64 = r.astype(np.float64)
+    # Rebuild history independently: quantise the rotated originals directly.
+    for p in range(64, n - 256):
+        yk = orc.rotate_fp32(kk[p][None], r)[0]
+        yv = orc.rotate_fp32(vv[p][None], r)[0]
+        ck, sk, zk = orc.quantize_rotated(yk[None], tau)
+        cv, sv, zv = orc.quantize_rotated(yv[None], tau)
+        kk[p] = orc.dequantize(ck, sk, zk)[0] @ r64.T
+        vv[p] = orc.dequantize(cv, sv, zv)[0] @ r64.T
+    qq = synth.bf16_bits_to_f32(q).astype(np.float64)
+    for h in range(2):
+        assert np.allclose(out[0, h], _brute_attention(qq[0, h], kk.tolist(), vv.tolist()), atol=1e-9)
+    assert pool.length[0] == n
+
+
+def test_prefill_tiering_equals_per_token_appends():
+    n = 400
+    pool, k, v, r, tau = _run_appends(n)
+    bulk = orc.Pool(1, 1, pool.hist.shape[0], pool.page_table)
+    for h in range(n - 320):
+        bulk.demote(0, h, k[64 + h], v[64 + h], r, r, tau, tau)
+    assert np.array_equal(bulk.hist, pool.hist)
+
+
+def test_tiered_error_shrinks_with_rotation_on_outliers():
+    # Sanity of the method, not a parity pin: with outlier channels, the
+    # rotated INT2 history gives smaller attention error than R = I.
+    n = 420
+    st = synth.streams(0)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, 1, out_ch)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, 1, out_ch)
+    q = synth.queries(st["q"], (1, 2, 128))
+    kk = synth.bf16_bits_to_f32(k[:, 0]).astype(np.float64)
+    vv = synth.bf16_bits_to_f32(v[:, 0]).astype(np.float64)
+    exact = [orc.attention(synth.bf16_bits_to_f32(q[0, h]).astype(np.float64), kk, vv) for h in range(2)]
+    errs = []
+    for r in (np.eye(128, dtype=np.float32), synth.random_rotation(st["rot"])):
+        big = np.full(128, 65504, np.float32)
+        pool = orc.Pool(1, 1, 32, np.arange(32, dtype=np.int32)[None])
+        for p in range(n):
+            pool.append(0, k[p], v[p], r, r, big, big)
+        o = orc.decode_tiered(q, pool, [0], [n], r, r)
+        errs.append(sum(np.linalg.norm(o[0, h] - exact[h]) for h in range(2)))
+    assert errs[1] < errs[0]
+
+
+def test_ring_slot_fixture_and_contents():
+    g = _gold("layout_points.json")
+    for p, s in g["ring_slot"]:
+        assert orc.ring_slot(p) == s
+    n = 1001
+    pool, k, v, r, tau = _run_appends(n, num_pages=64)
+    for p, s in g["ring_slot"]:
+        if p >= n - 256:
+            assert np.array_equal(pool.recent_k[0, :, s], k[p])
+
+
+def test_composite_rotation_spreads_each_eigendirection_over_all_groups():
+    # With U = I, R = H_Had P_br: eigen-direction i (row i of R) must land on
+    # 8 channels of every quantisation group, the purpose the pages give for
+    # interleaving after the Hadamard mix.
+    r = orc.composite_rotation(np.eye(128))
+    for i in range(128):
+        nz = np.abs(r[i]) > 1e-12
+        assert nz.sum() == 32
+        assert nz.reshape(4, 32).sum(1).tolist() == [8, 8, 8, 8]
+    assert np.allclose(np.abs(r[np.abs(r) > 1e-12]), 1 / math.sqrt(32))
