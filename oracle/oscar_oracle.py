@@ -424,30 +424,115 @@ class Pool:
             self.recent_v[slot, :, r] = v_bits
         self.length[slot] = p + 1
 
-    def reconstruct(self, slot, n, r_k, r_v):
-        """K~, V~ [Hkv, n, 128] fp64 in the unrotated space (plain definition):
-        BF16 values for sink/recent, dequant(c, s, z) . R^T for history."""
-        kt = np.zeros((self.hkv, n, HEAD_DIM))
-        vt = np.zeros((self.hkv, n, HEAD_DIM))
-        rk = np.asarray(r_k, np.float64)
-        rv = np.asarray(r_v, np.float64)
-        for p in range(n):
-            tier = tier_of(p, n)
-            if tier == "sink":
-                kt[:, p] = bf16_to_f64(self.sink_k[slot, :, p])
-                vt[:, p] = bf16_to_f64(self.sink_v[slot, :, p])
-            elif tier == "recent":
-                r = ring_slot(p)
-                kt[:, p] = bf16_to_f64(self.recent_k[slot, :, r])
-                vt[:, p] = bf16_to_f64(self.recent_v[slot, :, r])
-            else:
-                h = p - N_SINK
-                page = int(self.page_table[slot, h // PAGE])
-                for hd in range(self.hkv):
-                    kc, ks, kz, vc, vs, vz = read_token(self.hist[page, hd], h % PAGE)
-                    kt[hd, p] = dequantize(kc, ks, kz) @ rk.T
-                    vt[hd, p] = dequantize(vc, vs, vz) @ rv.T
+    def demote_rotated_many(self, slot, h_indices, yk, yv, tau_k, tau_v, kv_heads=None):
+        """Vectorised demote_rotated for many history indices of one slot.
+        yk, yv: float32 [N, H, 128] for the KV heads in `kv_heads` (default all)."""
+        heads = list(range(self.hkv)) if kv_heads is None else list(kv_heads)
+        h = np.asarray(h_indices, np.int64)
+        pages = self.page_table[slot, h // PAGE]
+        kc, ks, kz = quantize_rotated(yk, tau_k)
+        vc, vs, vz = quantize_rotated(yv, tau_v)
+        for i, hd in enumerate(heads):
+            write_tokens(self.hist, hd, pages, h % PAGE, kc[:, i], ks[:, i], kz[:, i], vc[:, i], vs[:, i], vz[:, i])
+
+    def demote_many(self, slot, h_indices, k_bits, v_bits, r_k, r_v, tau_k, tau_v, kv_heads=None):
+        """Rotate (fp64 product rounded to fp32) and demote many bf16 tokens [N, H, 128]."""
+        yk = rotate_fp32(bf16_to_f64(k_bits), r_k)
+        yv = rotate_fp32(bf16_to_f64(v_bits), r_v)
+        self.demote_rotated_many(slot, h_indices, yk, yv, tau_k, tau_v, kv_heads)
+
+    @classmethod
+    def from_state(cls, state, n_kv_heads):
+        """Oracle pool holding given bytes (e.g. copied back from a device)."""
+        pool = cls(state["sink_k"].shape[0], n_kv_heads, state["hist"].shape[0], state["page_table"])
+        for name in ("sink_k", "sink_v", "recent_k", "recent_v", "hist"):
+            setattr(pool, name, np.array(state[name], copy=True))
+        return pool
+
+    def reconstruct(self, slot, n, r_k, r_v, kv_heads=None):
+        """K~, V~ [H, n, 128] fp64 in the unrotated space (plain definition):
+        BF16 values for sink/recent, dequant(c, s, z) . R^T for history.
+        kv_heads selects the KV heads returned (default: all)."""
+        heads = np.arange(self.hkv) if kv_heads is None else np.asarray(kv_heads)
+        kt = np.zeros((len(heads), n, HEAD_DIM))
+        vt = np.zeros((len(heads), n, HEAD_DIM))
+        pos = np.arange(n)
+        sink = pos < N_SINK
+        recent = (pos >= max(N_SINK, n - N_RECENT))
+        hist = ~sink & ~recent
+        kt[:, sink] = bf16_to_f64(self.sink_k[slot][heads][:, pos[sink]])
+        vt[:, sink] = bf16_to_f64(self.sink_v[slot][heads][:, pos[sink]])
+        ring = (pos[recent] - N_SINK) % N_RECENT
+        kt[:, recent] = bf16_to_f64(self.recent_k[slot][heads][:, ring])
+        vt[:, recent] = bf16_to_f64(self.recent_v[slot][heads][:, ring])
+        if hist.any():
+            h = pos[hist] - N_SINK
+            pages = self.page_table[slot, h // PAGE]
+            blocks = self.hist[pages][:, heads]                        # [n_hist, H, 1536]
+            kc, ks, kz, vc, vs, vz = unpack_tokens(blocks, h % PAGE)   # [n_hist, Hkv, ...]
+            kt[:, hist] = np.moveaxis(dequantize(kc, ks, kz) @ np.asarray(r_k, np.float64).T, 1, 0)
+            vt[:, hist] = np.moveaxis(dequantize(vc, vs, vz) @ np.asarray(r_v, np.float64).T, 1, 0)
         return kt, vt
+
+
+_BIT_TABLES = None
+
+
+def _bit_tables():
+    """(byte, bit) of every K and V code of a block, from the *_bitpos definitions."""
+    global _BIT_TABLES
+    if _BIT_TABLES is None:
+        kb = np.array([[k_code_bitpos(t, j) for j in range(HEAD_DIM)] for t in range(PAGE)])
+        vb = np.array([[v_code_bitpos(t, j) for j in range(HEAD_DIM)] for t in range(PAGE)])
+        ks = np.array([[k_scale_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
+        kz = np.array([[k_zero_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
+        vs = np.array([[v_scale_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
+        vz = np.array([[v_zero_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
+        _BIT_TABLES = (kb // 8, kb % 8, vb // 8, vb % 8, ks, kz, vs, vz)
+    return _BIT_TABLES
+
+
+def write_tokens(hist, head, pages, slots, kc, ks, kz, vc, vs, vz):
+    """Vectorised write_token into a pool hist array uint8 [num_pages, Hkv, 1536]:
+    token i goes to block (pages[i], head), slot slots[i]."""
+    kby, kbi, vby, vbi, kso, kzo, vso, vzo = _bit_tables()
+    flat = hist.reshape(-1)
+    assert np.shares_memory(flat, hist), "hist must be contiguous"
+    base = ((np.asarray(pages, np.int64) * hist.shape[1] + head) * BLOCK_BYTES)[:, None]
+    t = np.asarray(slots, np.int64)
+    for byt, bit, codes in ((kby, kbi, kc), (vby, vbi, vc)):
+        idx = (base + byt[t]).ravel()
+        sh = bit[t].ravel().astype(np.uint8)
+        np.bitwise_and.at(flat, idx, (~(np.uint8(3) << sh)).astype(np.uint8))
+        np.bitwise_or.at(flat, idx, ((np.asarray(codes, np.uint8).ravel() & 3) << sh).astype(np.uint8))
+    for off, vals in ((kso, ks), (kzo, kz), (vso, vs), (vzo, vz)):
+        b = np.asarray(vals, np.float16).view(np.uint16)
+        idx = base + off[t]
+        flat[idx] = (b & 0xFF).astype(np.uint8)
+        flat[idx + 1] = (b >> 8).astype(np.uint8)
+
+def unpack_tokens(blocks: np.ndarray, slots: np.ndarray):
+    """Codes and scale/zero of token slot slots[i] of blocks[i, ...] (vectorised
+    read_token).  blocks: uint8 [N, ..., 1536]; slots: [N]."""
+    kby, kbi, vby, vbi, kso, kzo, vso, vzo = _bit_tables()
+    b = np.asarray(blocks)
+    idx = np.asarray(slots)
+    extra = (1,) * (b.ndim - 2)
+
+    def gather(off):                      # off: [16, m] byte offsets -> [N, ..., m] bytes
+        o = off[idx].reshape((len(idx),) + extra + (off.shape[1],))
+        return np.take_along_axis(b, np.broadcast_to(o, b.shape[:-1] + (off.shape[1],)), axis=-1)
+
+    def f16(off):
+        lo = gather(off).astype(np.uint16)
+        hi = gather(off + 1).astype(np.uint16)
+        return (lo | (hi << 8)).view(np.float16)
+
+    sh_k = kbi[idx].reshape((len(idx),) + extra + (HEAD_DIM,))
+    sh_v = vbi[idx].reshape((len(idx),) + extra + (HEAD_DIM,))
+    kc = ((gather(kby) >> sh_k) & 3).astype(np.uint8)
+    vc = ((gather(vby) >> sh_v) & 3).astype(np.uint8)
+    return kc, f16(kso), f16(kzo), vc, f16(vso), f16(vzo)
 
 
 # ---------------------------------------------------------------------------
@@ -466,20 +551,27 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     return w @ v
 
 
-def decode_tiered(q_bits, pool: Pool, seq_slot, seq_len, r_k, r_v) -> np.ndarray:
+def decode_tiered(q_bits, pool: Pool, seq_slot, seq_len, r_k, r_v, heads=None) -> np.ndarray:
     """Single-token decode over the tiered pool: out [B, Hq, 128] fp64.
 
     q_bits: bf16 bits [B, Hq, 128]; seq_len[b] counts the tokens in the cache
     after this step's append, so the new token attends to itself (R8).
+    heads: optional list of (b, h) to evaluate (others are left at zero).
     """
     q = bf16_to_f64(q_bits)
     b_n, hq, _ = q.shape
     g = hq // pool.hkv
     out = np.zeros((b_n, hq, HEAD_DIM))
+    want = None if heads is None else set((int(b), int(h)) for b, h in heads)
     for b in range(b_n):
-        kt, vt = pool.reconstruct(int(seq_slot[b]), int(seq_len[b]), r_k, r_v)
-        for h in range(hq):
-            out[b, h] = attention(q[b, h], kt[h // g], vt[h // g])
+        hs = [h for h in range(hq) if want is None or (b, h) in want]
+        if not hs:
+            continue
+        kvh = sorted(set(h // g for h in hs))
+        kt, vt = pool.reconstruct(int(seq_slot[b]), int(seq_len[b]), r_k, r_v, kvh)
+        for h in hs:
+            i = kvh.index(h // g)
+            out[b, h] = attention(q[b, h], kt[i], vt[i])
     return out
 
 

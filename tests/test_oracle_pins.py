@@ -445,3 +445,47 @@ def test_composite_rotation_spreads_each_eigendirection_over_all_groups():
         assert nz.sum() == 32
         assert nz.reshape(4, 32).sum(1).tolist() == [8, 8, 8, 8]
     assert np.allclose(np.abs(r[np.abs(r) > 1e-12]), 1 / math.sqrt(32))
+
+
+def test_vectorised_block_access_agrees_with_per_token_access():
+    rng = np.random.default_rng(21)
+    hist = np.zeros((5, 3, 1536), np.uint8)               # several KV heads: non-trivial strides
+    ref = np.zeros_like(hist)
+    for head in range(3):
+        pages = rng.integers(0, 5, 40)
+        slots = rng.integers(0, 16, 40)
+        keep = {}
+        for i in range(40):
+            keep[(pages[i], slots[i])] = i                  # last write wins
+        kc = rng.integers(0, 4, (40, 128)).astype(np.uint8)
+        vc = rng.integers(0, 4, (40, 128)).astype(np.uint8)
+        meta = [rng.standard_normal((40, 4)).astype(np.float16) for _ in range(4)]
+        order = sorted(keep.values())
+        orc.write_tokens(hist, head, pages[order], slots[order], kc[order], meta[0][order], meta[1][order],
+                         vc[order], meta[2][order], meta[3][order])
+        for i in order:
+            orc.write_token(ref[pages[i], head], slots[i], kc[i], meta[0][i], meta[1][i], vc[i], meta[2][i],
+                            meta[3][i])
+        got = orc.unpack_tokens(hist[pages[order], head], slots[order])
+        for i, row in enumerate(order):
+            slow = orc.read_token(hist[pages[row], head], slots[row])
+            for a, b in zip(got, slow):
+                assert np.array_equal(a[i], b)
+    assert hist.any() and np.array_equal(hist, ref)
+
+
+def test_many_token_demotion_equals_per_token_demotion_multihead():
+    n, hkv = 120, 3
+    st = synth.streams(6)
+    out = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out)
+    r = synth.random_rotation(st["rot"])
+    tau = orc.clip_thresholds(synth.bf16_bits_to_f32(k), r)
+    pt = synth.page_permutation(st["perm"], 10)[None, :]
+    a = orc.Pool(1, hkv, 10, pt)
+    b = orc.Pool(1, hkv, 10, pt)
+    a.demote_many(0, np.arange(n), k, v, r, r, tau, tau)
+    for h in range(n):
+        b.demote(0, h, k[h], v[h], r, r, tau, tau)
+    assert a.hist.any() and np.array_equal(a.hist, b.hist)
