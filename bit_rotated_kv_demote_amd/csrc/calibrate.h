@@ -1,0 +1,10 @@
+// Host-side offline calibration (internal).
+#pragma once
+#include <stdint.h>
+
+namespace oscar {
+// Returns 0 on success, -1 when an input or a resulting clip threshold is not
+// finite, not positive, or above 65504.
+int calibrate_layer(int hq, int hkv, int hadamard_block, float percentile, const float* q, const float* k,
+                    const float* v, int64_t n, float* rot_k, float* rot_v, float* clip_k, float* clip_v);
+}  // namespace oscar

@@ -1,0 +1,73 @@
+// BF16 paged decode attention: the full-precision cache the INT2 tiers are
+// measured against ("OSCAR：面向2-bit KV缓存量化的谱协方差感知旋转方法" (zingnex.cn),
+// 系统级收益 / 解码加速 compares decode speed with BF16).  Same structure as
+// the INT2 kernel: XCD-aware work items of (sequence, KV head, page range),
+// per-split partials, last-arriving workgroup merges by log-sum-exp.
+#include "attn_common.h"
+#include "launchers.h"
+
+namespace oscar {
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeBf16Args a) {
+  __shared__ SplitSmem<G> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int item = (blockIdx.x & 7) * a.grid_per_xcd + (blockIdx.x >> 3);
+  if (item >= a.n_groups_total * a.n_splits) return;
+  const int grp = item / a.n_splits, split = item % a.n_splits;
+  const int b = grp / a.hkv, hk = grp % a.hkv;
+  const int slot = a.seq_slot ? a.seq_slot[b] : b;
+  const int n = a.seq_len[b];
+  const int npages = (n + kPage - 1) / kPage;
+  const int act = (npages + a.pages_per_split - 1) / a.pages_per_split;
+  if (split >= act) return;
+  const int t0 = split * a.pages_per_split * kPage;
+  const int count = min(a.pages_per_split * kPage, n - t0);
+  const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
+  auto row = [&](int uu, int kv) -> const uint16_t* {
+    const int tok = t0 + uu;
+    const int page = pt_row[tok >> 4];
+    return a.kv + ((((size_t)page * a.hkv + hk) * 2 + kv) * kPage + (tok & 15)) * kD;
+  };
+  bf16_span_wave<G>(a.q + ((size_t)b * a.hkv * G + hk * G) * kD, count, [&](int uu) { return row(uu, 0); },
+                    [&](int uu) { return row(uu, 1); }, sm, wave, lane);
+  float* part_base = a.partials + (size_t)grp * a.n_splits * G * kPartStride;
+  store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
+  if (!finish_ticket<G>(sm, &a.counters[grp], (uint32_t)act, tid)) return;
+  merge_group<G>(sm, part_base, act, act, [](int k) { return k; }, nullptr,
+                 a.out + ((size_t)b * a.hkv * G + hk * G) * kD, tid, wave, lane);
+  if (tid == 0) a.counters[grp] = 0u;
+}
+
+DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len) {
+  DecodePlan p{};
+  const int max_pages = (max_seq_len + kPage - 1) / kPage;
+  const long total_pages = (long)batch * hkv * max_pages;
+  long pps = (total_pages + 479) / 480;
+  pps = ((pps + 1) / 2) * 2;
+  if (pps < 2) pps = 2;
+  while ((max_pages + pps - 1) / pps > kMaxSplits) pps += 2;
+  p.pages_per_split = (int)pps;
+  p.n_hist_splits = (int)((max_pages + pps - 1) / pps);
+  p.n_tile_splits = 0;
+  p.n_splits_total = p.n_hist_splits;
+  p.n_work = batch * hkv * p.n_splits_total;
+  p.grid = ((p.n_work + 7) / 8) * 8;
+  p.partial_floats = (size_t)batch * hkv * p.n_splits_total * group * kPartStride;
+  p.workspace_bytes = p.partial_floats * sizeof(float) + (size_t)batch * hkv * sizeof(uint32_t);
+  return p;
+}
+
+hipError_t launch_decode_bf16(const DecodeBf16Args& a, int group, int grid, hipStream_t st) {
+  switch (group) {
+    case 1: hipLaunchKernelGGL(decode_bf16_kernel<1>, dim3(grid), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL(decode_bf16_kernel<2>, dim3(grid), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(decode_bf16_kernel<4>, dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(decode_bf16_kernel<8>, dim3(grid), dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -1,0 +1,343 @@
+// KV demotion kernels: rotate -> clip -> quantise to INT2 -> pack -> store.
+//
+// The online demotion pipeline of "大模型KV Cache 2bit量化实战：OSCAR让显存暴降90%且
+// 智商不掉线" (yunpan.plus), section 三.2: when the recent BF16 window is full,
+// its oldest token is rotated, clipped, quantised, packed four codes per byte
+// and moved to the INT2 history; the tiers are those of section 三.1 and of
+// "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache
+// Quantization" (gist.science), 2.2 B.  The rotation R and the per-channel
+// clip thresholds are fixed offline (same page, 2.2 A).
+//
+// Three kernels:
+//   append_kernel      one decode step: demote the ring slot about to be
+//                      reused (fp32 VALU rotation, latency-bound), then write
+//                      the new token into sink or ring.
+//   demote_bulk_kernel many tokens: 16-token tiles per wave; the rotation is
+//                      a 128x128x16 product on the matrix cores with R split
+//                      into bf16 hi + lo terms (fp32 accumulation), or the
+//                      input is already-rotated fp32.
+//   prefill_route_kernel  copies of the sink and recent tiers of a prefill.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace oscar {
+
+// ---------------------------------------------------------------------------
+// Quantise + pack one vector held one channel per thread (threads 0..127 of
+// the block; every thread of the block must call it).  `sh` is 32 words of
+// LDS.  Writes token slot `ps` of the block `blk`.
+// ---------------------------------------------------------------------------
+__device__ void quantize_pack_channel_per_thread(float yc, bool is_v, uint8_t* blk, int ps,
+                                                 uint32_t* sh) {
+  const int c = threadIdx.x;
+  const bool act = c < kD;
+  float mn = yc, mx = yc;
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m));
+    mx = fmaxf(mx, __shfl_xor(mx, m));
+  }
+  __half s, z;
+  group_scale_zero(mn, mx, &s, &z);
+  const uint32_t code = quant_code(yc, __half2float(z), __half2float(s));
+  if (c < 32) sh[c] = 0u;
+  __syncthreads();
+  if (act) {
+    if (!is_v)
+      atomicOr(&sh[2 * ((c >> 3) & 3) + (c >> 6)], code << (2 * k_field(c)));
+    else
+      atomicOr(&sh[8 + (c & 15)], code << (2 * v_field_in_half(c)));
+  }
+  __syncthreads();
+  if (!is_v) {
+    if (c < 8) *reinterpret_cast<uint32_t*>(blk + 16 * (16 * (c >> 1) + ps) + 4 * (c & 1)) = sh[c];
+  } else {
+    if (c < 16) *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, c)) = (uint16_t)sh[8 + c];
+  }
+  if (act && (c & 31) == 0) {
+    const int g = c >> 5;
+    const int so = is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g);
+    const int zo = is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g);
+    *reinterpret_cast<uint16_t*>(blk + so) = half_bits(s);
+    *reinterpret_cast<uint16_t*>(blk + zo) = half_bits(z);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// append: grid (batch, Hkv, 2 = {K, V}), 256 threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  __shared__ float xs[kD];
+  __shared__ float part[2][kD];
+  __shared__ uint32_t sh[32];
+  const int b = blockIdx.x, hk = blockIdx.y, is_v = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int slot = a.seq_slot ? a.seq_slot[b] : b;
+  const int p = a.position[b];
+  const uint16_t* src = (is_v ? a.v_new : a.k_new) + ((size_t)b * a.hkv + hk) * kD;
+  if (p < kSink) {
+    uint16_t* dst = (is_v ? a.sink_v : a.sink_k) + (((size_t)slot * a.hkv + hk) * kSink + p) * kD;
+    if (tid < kD / 2) reinterpret_cast<uint32_t*>(dst)[tid] = reinterpret_cast<const uint32_t*>(src)[tid];
+    return;
+  }
+  const int r = (p - kSink) & (kRecent - 1);
+  uint16_t* ring = (is_v ? a.recent_v : a.recent_k) + (((size_t)slot * a.hkv + hk) * kRecent + r) * kD;
+  if (p >= kSink + kRecent) {
+    if (tid < kD / 2) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(ring)[tid];
+      xs[2 * tid] = bf16_bits_to_float(w & 0xFFFFu);
+      xs[2 * tid + 1] = bf16_bits_to_float(w >> 16);
+    }
+    __syncthreads();
+    // y_j = sum_i x_i R[i][j]; thread (j, half) covers i in [64 half, 64 half + 64).
+    const float* R = is_v ? a.rot_v : a.rot_k;
+    const int j = tid & (kD - 1), half = tid >> 7;
+    float acc = 0.0f;
+#pragma unroll 16
+    for (int i = 64 * half; i < 64 * half + 64; ++i) acc = fmaf(xs[i], R[i * kD + j], acc);
+    part[half][j] = acc;
+    __syncthreads();  // also orders the ring read above before the overwrite below
+    const float* tau = is_v ? a.clip_v : a.clip_k;
+    float yc = 0.0f;
+    if (tid < kD) yc = clip_value(part[0][tid] + part[1][tid], tau[tid]);
+    const int h = p - kSink - kRecent;
+    const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
+    uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
+    quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh);
+  }
+  if (tid < kD / 2) reinterpret_cast<uint32_t*>(ring)[tid] = reinterpret_cast<const uint32_t*>(src)[tid];
+}
+
+// ---------------------------------------------------------------------------
+// Bulk demotion.  grid (ceil(T/256), batch*Hkv, 2), 256 threads; each wave
+// handles 4 tiles of 16 tokens.  In a tile, lane l = 16a + t owns token t and
+// channels j = 16 m + 4 a + i (m = 0..7, i = 0..3): the layout of the 16x16
+// result blocks of the rotation product D[j][t] = sum_i R[i][j] x[t][i].
+// ---------------------------------------------------------------------------
+// LDS copy of R^T: row j holds R[:, j] as 16 chunks of 8 bf16; chunk c of row j
+// is stored at chunk position c ^ (j & 15) so that the 16 rows read by one
+// fragment load fall on different banks.
+__device__ __forceinline__ int rt_index(int j, int i) { return j * kD + ((((i >> 3) ^ (j & 15))) << 3) + (i & 7); }
+
+template <bool kRotatedInput>
+__global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
+  __shared__ __bf16 rt_hi[kRotatedInput ? 1 : kD * kD];
+  __shared__ __bf16 rt_lo[kRotatedInput ? 1 : kD * kD];
+  const int bh = blockIdx.y;
+  const int b = bh / a.hkv, hk = bh % a.hkv, is_v = blockIdx.z;
+  const int count = a.length ? max(0, a.length[b] - kSink - kRecent) : a.n_tokens;
+  const int tile0 = blockIdx.x * 256;
+  if (tile0 >= count) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tcol = lane & 15, qa = lane >> 4;
+
+  if constexpr (!kRotatedInput) {
+    // R (row-major fp32) -> LDS R^T split into bf16 hi + lo.
+    const float* R = is_v ? a.rot_v : a.rot_k;
+    for (int idx = tid; idx < kD * kD / 4; idx += 256) {
+      const float4 v4 = reinterpret_cast<const float4*>(R)[idx];
+      const int i = idx / (kD / 4), j0 = (idx % (kD / 4)) * 4;
+      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 hi = (__bf16)vv[e];
+        const __bf16 lo = (__bf16)(vv[e] - (float)hi);
+        rt_hi[rt_index(j0 + e, i)] = hi;
+        rt_lo[rt_index(j0 + e, i)] = lo;
+      }
+    }
+    __syncthreads();
+  }
+  const float* tau_p = is_v ? a.clip_v : a.clip_k;
+  float tau[8][4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tau[m][i] = tau_p[16 * m + 4 * qa + i];
+
+  const int slot = a.seq_slot ? a.seq_slot[b] : b;
+  const int h0 = a.hist_start ? a.hist_start[b] : 0;
+
+  for (int s = 0; s < 4; ++s) {
+    const int tok = tile0 + 64 * wave + 16 * s + tcol;
+    if (tile0 + 64 * wave + 16 * s >= count) break;          // wave-uniform
+    const bool valid = tok < count;
+    const int tl = valid ? tok : count - 1;
+    float y[8][4];
+    if constexpr (kRotatedInput) {
+      const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) +
+                         (((size_t)b * a.src_tokens + a.src_tok0 + tl) * a.hkv + hk) * kD;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float4 v4 = *reinterpret_cast<const float4*>(src + 16 * m + 4 * qa);
+        y[m][0] = v4.x; y[m][1] = v4.y; y[m][2] = v4.z; y[m][3] = v4.w;
+      }
+    } else {
+      const uint16_t* src = (is_v ? a.src_v : a.src_k) +
+                            (((size_t)b * a.src_tokens + a.src_tok0 + tl) * a.hkv + hk) * kD;
+      bf16x8_t xb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) xb[kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * qa);
+      float4_t acc[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[m] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int row = rt_index(16 * m + tcol, 32 * kk + 8 * qa);
+          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&rt_hi[row]);
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&rt_lo[row]);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xb[kk], acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, xb[kk], acc[m], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[m][i] = acc[m][i];
+    }
+    // clip, group min / max over the 32 channels of (token, group)
+    float gmn[4], gmx[4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[m][i] = clip_value(y[m][i], tau[m][i]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float mn = y[2 * g][0], mx = y[2 * g][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) {
+        const float v = y[2 * g + (e >> 2)][e & 3];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      // across the four lanes a = 0..3 that share this token
+      const auto pn = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+      const auto px = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mn = fminf(__uint_as_float(pn[0]), __uint_as_float(pn[1]));
+      mx = fmaxf(__uint_as_float(px[0]), __uint_as_float(px[1]));
+      const auto qn = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+      const auto qx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      gmn[g] = fminf(__uint_as_float(qn[0]), __uint_as_float(qn[1]));
+      gmx[g] = fmaxf(__uint_as_float(qx[0]), __uint_as_float(qx[1]));
+    }
+    __half sc[4], zr[4];
+    float sf[4], zf[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      group_scale_zero(gmn[g], gmx[g], &sc[g], &zr[g]);
+      sf[g] = __half2float(sc[g]);
+      zf[g] = __half2float(zr[g]);
+    }
+    uint32_t code[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) code[m][i] = quant_code(y[m][i], zf[m >> 1], sf[m >> 1]);
+
+    const int h = h0 + tl;
+    const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
+    uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
+    const int ps = h & 15;
+    if (!is_v) {
+      // K: channel j = 16m + 4a + i lands in word (2(m&1) + (a>>1), m>>2) at
+      // field 4((m>>1)&1) + 2(a&1) + (i>>1) + 8(i&1); lanes a and a^1 fill
+      // complementary fields of the same four words.
+      uint32_t wd[2][2];
+#pragma unroll
+      for (int ai = 0; ai < 2; ++ai)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          uint32_t acc = 0u;
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int m = ai + 2 * hb + 4 * w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc |= code[m][i] << (2 * (4 * hb + 2 * (qa & 1) + (i >> 1) + 8 * (i & 1)));
+          }
+          const auto pr = __builtin_amdgcn_permlane16_swap(acc, acc, false, false);
+          wd[ai][w] = pr[0] | pr[1];
+        }
+      if (valid && (qa & 1) == 0) {
+#pragma unroll
+        for (int ai = 0; ai < 2; ++ai) {
+          const int aa = 2 * ai + (qa >> 1);
+          *reinterpret_cast<u32x2_t*>(blk + 16 * (16 * aa + ps)) = (u32x2_t){wd[ai][0], wd[ai][1]};
+        }
+      }
+    } else {
+      // V: the 8 codes of (token, channel 4a + i) form one half-word, code of
+      // channel 16m + 4a + i at bits 2m.
+      if (valid) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t hw = 0u;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) hw |= code[m][i] << (2 * m);
+          *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, 4 * qa + i)) = (uint16_t)hw;
+        }
+      }
+    }
+    if (valid) {
+      // lane a stores group a's scale and zero (selects, not a dynamic index)
+      const int g = qa;
+      const uint32_t s01 = half_bits(sc[0]) | ((uint32_t)half_bits(sc[1]) << 16);
+      const uint32_t s23 = half_bits(sc[2]) | ((uint32_t)half_bits(sc[3]) << 16);
+      const uint32_t z01 = half_bits(zr[0]) | ((uint32_t)half_bits(zr[1]) << 16);
+      const uint32_t z23 = half_bits(zr[2]) | ((uint32_t)half_bits(zr[3]) << 16);
+      const int sh = 16 * (g & 1);
+      const int so = is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g);
+      const int zo = is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g);
+      *reinterpret_cast<uint16_t*>(blk + so) = (uint16_t)(((g < 2) ? s01 : s23) >> sh);
+      *reinterpret_cast<uint16_t*>(blk + zo) = (uint16_t)(((g < 2) ? z01 : z23) >> sh);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill routing of the BF16 tiers.  grid (20, batch*Hkv, 2), 256 threads:
+// 16 tokens x 16 threads of 16 bytes.  Compact index u in [0, 320): u < 64 is
+// sink position u, u >= 64 is position max(64, n-256) + (u-64).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_route_kernel(PrefillArgs a) {
+  const int bh = blockIdx.y;
+  const int b = bh / a.hkv, hk = bh % a.hkv, is_v = blockIdx.z;
+  const int n = a.length[b];
+  const int u = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int part = threadIdx.x & 15;
+  const int p = u < kSink ? u : max(kSink, n - kRecent) + (u - kSink);
+  if (p >= n) return;
+  const int slot = a.seq_slot ? a.seq_slot[b] : b;
+  const uint16_t* src = (is_v ? a.src_v : a.src_k) + (((size_t)b * a.max_len + p) * a.hkv + hk) * kD;
+  uint16_t* dst;
+  if (p < kSink)
+    dst = (is_v ? a.sink_v : a.sink_k) + (((size_t)slot * a.hkv + hk) * kSink + p) * kD;
+  else
+    dst = (is_v ? a.recent_v : a.recent_k) +
+          (((size_t)slot * a.hkv + hk) * kRecent + ((p - kSink) & (kRecent - 1))) * kD;
+  reinterpret_cast<uint4*>(dst)[part] = reinterpret_cast<const uint4*>(src)[part];
+}
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(append_kernel, dim3(batch, a.hkv, 2), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_demote(const DemoteArgs& a, int batch, int max_count, bool rotated, hipStream_t st) {
+  if (max_count <= 0) return hipSuccess;
+  const dim3 grid((max_count + 255) / 256, batch * a.hkv, 2);
+  if (rotated)
+    hipLaunchKernelGGL(demote_bulk_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(demote_bulk_kernel<false>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_route(const PrefillArgs& a, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_route_kernel, dim3((kSink + kRecent) / 16, batch * a.hkv, 2), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

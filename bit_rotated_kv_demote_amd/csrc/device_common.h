@@ -1,0 +1,72 @@
+// Device-side helpers shared by the HIP kernels of libamdoscar (gfx950).
+//
+// Page-block format (one 1536-byte block per (page, KV head)); see
+// include/oscar.h for the full description.  The format is designed around
+// the decode kernel's matrix-core operands: lane l = 16a + b of a wave loads
+// the 16-byte chunk l of the code area, whose low 8 bytes are exactly the
+// 2-bit K codes the lane feeds to the score MFMAs and whose high 8 bytes are
+// the V codes it feeds to the value MFMAs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace oscar {
+
+constexpr int kD = 128;          // head_dim
+constexpr int kPage = 16;        // tokens per page
+constexpr int kSink = 64;        // BF16 sink tokens
+constexpr int kRecent = 256;     // BF16 recent ring
+constexpr int kGroup = 32;       // channels per quantisation group
+constexpr int kGroups = 4;
+constexpr int kBlock = 1536;     // bytes per (page, KV head)
+constexpr int kKScaleOff = 1024;
+constexpr int kKZeroOff = 1152;
+constexpr int kVScaleOff = 1280;
+constexpr int kVZeroOff = 1408;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// ---- position of K code (token t, channel j): byte of its 32-bit word and field
+__device__ __forceinline__ int k_word_byte(int t, int j) { return 16 * (16 * ((j >> 3) & 3) + t) + 4 * (j >> 6); }
+__device__ __forceinline__ int k_field(int j) { return 4 * ((j >> 5) & 1) + ((j >> 1) & 3) + 8 * (j & 1); }
+// ---- V codes: the 16-bit half-word holding the 8 codes of (token t, channel j & 15)
+__device__ __forceinline__ int v_halfword_byte(int t, int j) {
+  return 16 * (16 * (t >> 2) + (j & 15)) + 8 + 4 * ((t & 3) >> 1) + 2 * (t & 1);
+}
+__device__ __forceinline__ int v_field_in_half(int j) { return j >> 4; }
+__device__ __forceinline__ int k_scale_byte(int t, int g) { return kKScaleOff + 8 * t + 2 * g; }
+__device__ __forceinline__ int k_zero_byte(int t, int g) { return kKZeroOff + 8 * t + 2 * g; }
+__device__ __forceinline__ int v_scale_byte(int t, int g) { return kVScaleOff + 32 * (t >> 2) + 8 * g + 2 * (t & 3); }
+__device__ __forceinline__ int v_zero_byte(int t, int g) { return kVZeroOff + 32 * (t >> 2) + 8 * g + 2 * (t & 3); }
+
+// ---- INT2 quantiser of one 32-channel group (asymmetric min-max, four levels).
+// zero = fp16 rounded toward -inf of the group minimum, scale = fp16 rounded
+// toward +inf of (max - zero) / 3, code = clamp(rint((y - zero) / scale), 0, 3)
+// in IEEE fp32 with a correctly rounded division; code 0 when scale == 0.
+__device__ __forceinline__ void group_scale_zero(float mn, float mx, __half* scale, __half* zero) {
+  const __half z = __float2half_rd(mn);
+  const float span = mx - __half2float(z);
+  *zero = z;
+  *scale = __float2half_ru(span / 3.0f);
+}
+
+__device__ __forceinline__ uint32_t quant_code(float yc, float zf, float sf) {
+  if (!(sf > 0.0f)) return 0u;
+  const float q = (yc - zf) / sf;
+  const float c = fminf(fmaxf(rintf(q), 0.0f), 3.0f);
+  return (uint32_t)c;
+}
+
+__device__ __forceinline__ float clip_value(float y, float tau) { return fminf(fmaxf(y, -tau), tau); }
+
+__device__ __forceinline__ uint16_t half_bits(__half h) { return __half_as_ushort(h); }
+
+}  // namespace oscar

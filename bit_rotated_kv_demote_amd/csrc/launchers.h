@@ -1,0 +1,111 @@
+// Internal kernel-argument structs and launchers of libamdoscar (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oscar {
+
+struct AppendArgs {
+  const uint16_t* k_new;   // bf16 [batch][Hkv][128]
+  const uint16_t* v_new;
+  const int32_t* seq_slot; // nullable
+  const int32_t* position; // [batch]
+  uint16_t* sink_k; uint16_t* sink_v;
+  uint16_t* recent_k; uint16_t* recent_v;
+  uint8_t* hist;
+  const int32_t* page_table;
+  const float* rot_k; const float* rot_v;
+  const float* clip_k; const float* clip_v;
+  int hkv;
+  int max_pages;
+};
+
+struct DemoteArgs {
+  const uint16_t* src_k; const uint16_t* src_v;        // bf16 [batch][src_tokens][Hkv][128]
+  const float* src_k_f32; const float* src_v_f32;      // or fp32 rotated, same shape
+  int src_tokens;     // tokens per batch entry in the source
+  int src_tok0;       // source index of the first demoted token
+  int n_tokens;       // tokens to demote per entry (when length == nullptr)
+  const int32_t* length;      // nullable: count = max(0, length[b] - 320)
+  const int32_t* hist_start;  // nullable: 0
+  const int32_t* seq_slot;    // nullable
+  const float* rot_k; const float* rot_v;
+  const float* clip_k; const float* clip_v;
+  uint8_t* hist;
+  const int32_t* page_table;
+  int max_pages;
+  int hkv;
+};
+
+struct PrefillArgs {
+  const uint16_t* src_k; const uint16_t* src_v;   // bf16 [batch][max_len][Hkv][128]
+  const int32_t* length;
+  const int32_t* seq_slot;
+  uint16_t* sink_k; uint16_t* sink_v;
+  uint16_t* recent_k; uint16_t* recent_v;
+  int max_len;
+  int hkv;
+};
+
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [batch][Hq][128]
+  float* out;                 // fp32 [batch][Hq][128]
+  const int32_t* seq_slot;    // nullable
+  const int32_t* seq_len;     // [batch]
+  const uint16_t* sink_k; const uint16_t* sink_v;
+  const uint16_t* recent_k; const uint16_t* recent_v;
+  const uint8_t* hist;
+  const int32_t* page_table;
+  const float* rot_k; const float* rot_v;
+  float* partials;            // workspace: [batch*Hkv][n_splits][G][130]
+  uint32_t* counters;         // workspace: [batch*Hkv]
+  int hkv;
+  int max_pages;
+  int n_hist_splits;          // history splits per (sequence, KV head)
+  int pages_per_split;        // multiple of 8
+  int n_tile_splits;          // BF16 sink/recent splits per (sequence, KV head)
+  int n_groups_total;         // batch * Hkv
+  int grid_per_xcd;
+};
+
+struct DecodeBf16Args {
+  const uint16_t* q;
+  float* out;
+  const int32_t* seq_slot;
+  const int32_t* seq_len;
+  const uint16_t* kv;         // [num_pages][Hkv][2][16][128]
+  const int32_t* page_table;
+  float* partials;
+  uint32_t* counters;
+  int hkv;
+  int max_pages;
+  int n_splits;
+  int pages_per_split;
+  int n_groups_total;
+  int grid_per_xcd;
+};
+
+// Decode split geometry, shared by the workspace-size query and the launch.
+struct DecodePlan {
+  int n_hist_splits;
+  int pages_per_split;
+  int n_tile_splits;
+  int n_splits_total;         // hist + tile
+  int n_work;                 // batch * Hkv * n_splits_total
+  int grid;                   // padded to a multiple of 8 (one slice per XCD)
+  size_t partial_floats;
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len);
+DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len);
+
+hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st);
+hipError_t launch_demote(const DemoteArgs& a, int batch, int max_count, bool rotated, hipStream_t st);
+hipError_t launch_prefill_route(const PrefillArgs& a, int batch, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t st);
+hipError_t launch_decode_bf16(const DecodeBf16Args& a, int group, int grid, hipStream_t st);
+
+}  // namespace oscar

@@ -1,0 +1,252 @@
+// extern "C" entry points of libamdoscar.so (see include/oscar.h): argument
+// validation on the host, then kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/oscar.h"
+#include "calibrate.h"
+#include "launchers.h"
+
+using namespace oscar;
+
+namespace {
+
+oscar_status check_desc(const oscar_layer_desc* d) {
+  if (!d) return OSCAR_ERR_INVALID;
+  if (d->head_dim != 128 || d->page_size != 16 || d->n_sink != 64 || d->n_recent != 256 || d->group_size != 32)
+    return OSCAR_ERR_UNSUPPORTED;
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return OSCAR_ERR_INVALID;
+  if (d->num_q_heads % d->num_kv_heads != 0) return OSCAR_ERR_INVALID;
+  const int g = d->num_q_heads / d->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return OSCAR_ERR_UNSUPPORTED;
+  return OSCAR_OK;
+}
+
+oscar_status check_pool(const oscar_pool* p, bool need_hist_tiers) {
+  if (!p) return OSCAR_ERR_INVALID;
+  if (!p->sink_k || !p->sink_v || !p->recent_k || !p->recent_v) return OSCAR_ERR_INVALID;
+  if (need_hist_tiers && (!p->hist || !p->page_table)) return OSCAR_ERR_INVALID;
+  if (!p->rot_k || !p->rot_v || !p->clip_k || !p->clip_v) return OSCAR_ERR_INVALID;
+  if (p->n_slots <= 0 || p->max_pages_per_seq < 0 || p->num_pages < 0) return OSCAR_ERR_INVALID;
+  return OSCAR_OK;
+}
+
+thread_local char g_hip_error[160] = "";
+
+oscar_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return OSCAR_OK;
+  snprintf(g_hip_error, sizeof(g_hip_error), "HIP runtime error: %s (%s)", hipGetErrorName(e), hipGetErrorString(e));
+  return OSCAR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t oscar_abi_version(void) { return OSCAR_ABI_VERSION; }
+
+const char* oscar_status_string(oscar_status s) {
+  switch (s) {
+    case OSCAR_OK: return "ok";
+    case OSCAR_ERR_INVALID: return "invalid argument";
+    case OSCAR_ERR_UNSUPPORTED: return "unsupported shape";
+    case OSCAR_ERR_CAPACITY: return "workspace or page table too small";
+    case OSCAR_ERR_HIP: return g_hip_error[0] ? g_hip_error : "HIP runtime error";
+    case OSCAR_ERR_NUMERIC: return "non-finite or out-of-range calibration value";
+  }
+  return "unknown status";
+}
+
+oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opts* opts, const float* q,
+                             const float* k, const float* v, int64_t n_tokens, float* rot_k, float* rot_v,
+                             float* clip_k, float* clip_v) {
+  oscar_status st = check_desc(desc);
+  if (st != OSCAR_OK) return st;
+  if (!opts || !q || !k || !v || !rot_k || !rot_v || !clip_k || !clip_v || n_tokens < 2) return OSCAR_ERR_INVALID;
+  if (opts->hadamard_block != 32 && opts->hadamard_block != 128) return OSCAR_ERR_UNSUPPORTED;
+  if (!(opts->clip_percentile > 0.0f && opts->clip_percentile <= 100.0f)) return OSCAR_ERR_INVALID;
+  const int rc = calibrate_layer(desc->num_q_heads, desc->num_kv_heads, opts->hadamard_block, opts->clip_percentile,
+                                 q, k, v, n_tokens, rot_k, rot_v, clip_k, clip_v);
+  return rc == 0 ? OSCAR_OK : OSCAR_ERR_NUMERIC;
+}
+
+oscar_status oscar_append(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                          const int32_t* position, const void* k_new, const void* v_new, int32_t batch,
+                          void* stream) {
+  oscar_status st = check_desc(desc);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_pool(pool, true)) != OSCAR_OK) return st;
+  if (!position || !k_new || !v_new || batch <= 0) return OSCAR_ERR_INVALID;
+  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
+  AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.seq_slot = seq_slot;
+  a.position = position;
+  a.sink_k = static_cast<uint16_t*>(pool->sink_k);
+  a.sink_v = static_cast<uint16_t*>(pool->sink_v);
+  a.recent_k = static_cast<uint16_t*>(pool->recent_k);
+  a.recent_v = static_cast<uint16_t*>(pool->recent_v);
+  a.hist = pool->hist;
+  a.page_table = pool->page_table;
+  a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
+  a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
+  a.hkv = desc->num_kv_heads;
+  a.max_pages = pool->max_pages_per_seq;
+  return hip_status(launch_append(a, batch, static_cast<hipStream_t>(stream)));
+}
+
+static oscar_status demote_common(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                                  const int32_t* hist_start, const int32_t* length, const void* k, const void* v,
+                                  int32_t src_kind, int32_t batch, int32_t src_tokens, int32_t src_tok0,
+                                  int32_t n_tokens, int32_t max_count, void* stream) {
+  DemoteArgs a{};
+  if (src_kind == OSCAR_SRC_BF16) {
+    a.src_k = static_cast<const uint16_t*>(k);
+    a.src_v = static_cast<const uint16_t*>(v);
+  } else if (src_kind == OSCAR_SRC_F32_ROTATED) {
+    a.src_k_f32 = static_cast<const float*>(k);
+    a.src_v_f32 = static_cast<const float*>(v);
+  } else {
+    return OSCAR_ERR_INVALID;
+  }
+  a.src_tokens = src_tokens;
+  a.src_tok0 = src_tok0;
+  a.n_tokens = n_tokens;
+  a.length = length;
+  a.hist_start = hist_start;
+  a.seq_slot = seq_slot;
+  a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
+  a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
+  a.hist = pool->hist;
+  a.page_table = pool->page_table;
+  a.max_pages = pool->max_pages_per_seq;
+  a.hkv = desc->num_kv_heads;
+  return hip_status(launch_demote(a, batch, max_count, src_kind == OSCAR_SRC_F32_ROTATED,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+oscar_status oscar_demote(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                          const int32_t* hist_start, const void* k, const void* v, int32_t src_kind, int32_t batch,
+                          int32_t n_tokens, void* stream) {
+  oscar_status st = check_desc(desc);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_pool(pool, true)) != OSCAR_OK) return st;
+  if (!hist_start || !k || !v || batch <= 0 || n_tokens < 0) return OSCAR_ERR_INVALID;
+  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
+  if (n_tokens == 0) return OSCAR_OK;
+  return demote_common(desc, pool, seq_slot, hist_start, nullptr, k, v, src_kind, batch, n_tokens, 0, n_tokens,
+                       n_tokens, stream);
+}
+
+oscar_status oscar_prefill(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                           const int32_t* length, const void* k, const void* v, int32_t batch, int32_t max_len,
+                           void* stream) {
+  oscar_status st = check_desc(desc);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_pool(pool, max_len > 320)) != OSCAR_OK) return st;
+  if (!length || !k || !v || batch <= 0 || max_len <= 0) return OSCAR_ERR_INVALID;
+  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
+  const int max_hist = max_len - 320;
+  if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
+  PrefillArgs pa{};
+  pa.src_k = static_cast<const uint16_t*>(k);
+  pa.src_v = static_cast<const uint16_t*>(v);
+  pa.length = length;
+  pa.seq_slot = seq_slot;
+  pa.sink_k = static_cast<uint16_t*>(pool->sink_k);
+  pa.sink_v = static_cast<uint16_t*>(pool->sink_v);
+  pa.recent_k = static_cast<uint16_t*>(pool->recent_k);
+  pa.recent_v = static_cast<uint16_t*>(pool->recent_v);
+  pa.max_len = max_len;
+  pa.hkv = desc->num_kv_heads;
+  const oscar_status rs = hip_status(launch_prefill_route(pa, batch, static_cast<hipStream_t>(stream)));
+  if (rs != OSCAR_OK) return rs;
+  if (max_hist <= 0) return OSCAR_OK;
+  return demote_common(desc, pool, seq_slot, nullptr, length, k, v, OSCAR_SRC_BF16, batch, max_len, 64, 0,
+                       max_hist, stream);
+}
+
+size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
+  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0) return 0;
+  const int g = desc->num_q_heads / desc->num_kv_heads;
+  return plan_decode(batch, desc->num_kv_heads, g, max_seq_len).workspace_bytes;
+}
+
+oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                          const int32_t* seq_len, const void* q, float* out, void* workspace, size_t ws_bytes,
+                          int32_t batch, int32_t max_seq_len, void* stream) {
+  oscar_status st = check_desc(desc);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_pool(pool, max_seq_len > 320)) != OSCAR_OK) return st;
+  if (!seq_len || !q || !out || !workspace || batch <= 0 || max_seq_len <= 0) return OSCAR_ERR_INVALID;
+  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
+  const int hkv = desc->num_kv_heads, g = desc->num_q_heads / hkv;
+  const int max_hist = max_seq_len - 320;
+  if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
+  const DecodePlan plan = plan_decode(batch, hkv, g, max_seq_len);
+  if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = out;
+  a.seq_slot = seq_slot;
+  a.seq_len = seq_len;
+  a.sink_k = static_cast<const uint16_t*>(pool->sink_k);
+  a.sink_v = static_cast<const uint16_t*>(pool->sink_v);
+  a.recent_k = static_cast<const uint16_t*>(pool->recent_k);
+  a.recent_v = static_cast<const uint16_t*>(pool->recent_v);
+  a.hist = pool->hist;
+  a.page_table = pool->page_table;
+  a.rot_k = pool->rot_k;
+  a.rot_v = pool->rot_v;
+  a.partials = static_cast<float*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(static_cast<float*>(workspace) + plan.partial_floats);
+  a.hkv = hkv;
+  a.max_pages = pool->max_pages_per_seq;
+  a.n_hist_splits = plan.n_hist_splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.n_tile_splits = plan.n_tile_splits;
+  a.n_groups_total = batch * hkv;
+  a.grid_per_xcd = plan.grid / 8;
+  return hip_status(launch_decode(a, g, plan.grid, static_cast<hipStream_t>(stream)));
+}
+
+size_t oscar_decode_bf16_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
+  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0) return 0;
+  const int g = desc->num_q_heads / desc->num_kv_heads;
+  return plan_decode_bf16(batch, desc->num_kv_heads, g, max_seq_len).workspace_bytes;
+}
+
+oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_pool* pool, const int32_t* seq_slot,
+                               const int32_t* seq_len, const void* q, float* out, void* workspace, size_t ws_bytes,
+                               int32_t batch, int32_t max_seq_len, void* stream) {
+  oscar_status st = check_desc(desc);
+  if (st != OSCAR_OK) return st;
+  if (!pool || !pool->kv || !pool->page_table || pool->n_slots <= 0) return OSCAR_ERR_INVALID;
+  if (!seq_len || !q || !out || !workspace || batch <= 0 || max_seq_len <= 0) return OSCAR_ERR_INVALID;
+  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
+  if ((max_seq_len + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
+  const int hkv = desc->num_kv_heads, g = desc->num_q_heads / hkv;
+  const DecodePlan plan = plan_decode_bf16(batch, hkv, g, max_seq_len);
+  if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
+  DecodeBf16Args a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.out = out;
+  a.seq_slot = seq_slot;
+  a.seq_len = seq_len;
+  a.kv = static_cast<const uint16_t*>(pool->kv);
+  a.page_table = pool->page_table;
+  a.partials = static_cast<float*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(static_cast<float*>(workspace) + plan.partial_floats);
+  a.hkv = hkv;
+  a.max_pages = pool->max_pages_per_seq;
+  a.n_splits = plan.n_splits_total;
+  a.pages_per_split = plan.pages_per_split;
+  a.n_groups_total = batch * hkv;
+  a.grid_per_xcd = plan.grid / 8;
+  return hip_status(launch_decode_bf16(a, g, plan.grid, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

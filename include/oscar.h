@@ -1,0 +1,257 @@
+/*
+ * oscar.h -- C ABI of libamdoscar.so: OSCAR-style 2-bit KV-cache demotion and
+ * tiered single-token decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, site):
+ *   [gist]    "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV
+ *             Cache Quantization" (gist.science), "Technische Zusammenfassung"
+ *             sections 2.1, 2.2 A (Offline-Kalibrierungsphase), 2.2 B
+ *             (Online-Betriebsphase).
+ *   [zingnex] "OSCAR：面向2-bit KV缓存量化的谱协方差感知旋转方法" (zingnex.cn),
+ *             sections 离线协方差估计, 自定义INT2注意力内核, 离线优化的优势.
+ *   [yunpan]  "大模型KV Cache 2bit量化实战：OSCAR让显存暴降90%且智商不掉线"
+ *             (yunpan.plus), sections 三.1 三段式 Token 池, 三.2 在线量化与反量化,
+ *             三.3 兼容现有架构.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - head_dim = 128, page = 16 tokens, sink = 64 tokens, recent ring = 256
+ *   tokens, quantisation group = 32 channels.  Other values return
+ *   OSCAR_ERR_UNSUPPORTED.  num_q_heads / num_kv_heads (the GQA group G) must
+ *   be 1, 2, 4 or 8.
+ * - Rotations act on row vectors: y = x . R, R stored row-major fp32
+ *   [128][128]; the inverse rotation is y . R^T.
+ * - "device" pointers are HIP device memory owned by the caller (for example
+ *   torch tensors); "host" pointers are ordinary host memory.  The library
+ *   never allocates, frees or retains any caller buffer.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Device entry points only enqueue work on it and return; they do not
+ *   synchronise.  Argument checks happen on the host before anything is
+ *   enqueued: a negative status means nothing was enqueued.  A launch failure
+ *   reported by the runtime returns OSCAR_ERR_HIP.  Values inside device
+ *   buffers (page ids, lengths, positions) are not checked on the host: an
+ *   out-of-range value there is undefined behaviour.
+ * - Calls are stateless and reentrant apart from the decode workspace, which
+ *   one call at a time may use.
+ *
+ * Pool layout (device)
+ * --------------------
+ *   sink_k/sink_v     bf16 [n_slots][Hkv][64][128]      positions 0..63
+ *   recent_k/recent_v bf16 [n_slots][Hkv][256][128]     position p >= 64 in
+ *                                                        ring slot (p-64) mod 256
+ *   hist              u8   [num_pages][Hkv][1536]       INT2 history blocks
+ *   page_table        i32  [n_slots][max_pages_per_seq] history index h (= p-64)
+ *                                                        lives in page
+ *                                                        page_table[s][h/16],
+ *                                                        slot h%16
+ * Three tiers as in [yunpan] 三.1 and [gist] 2.2 B: BF16 sink, INT2 history
+ * of rotated and clipped vectors, BF16 recent tokens.
+ *
+ * History block of one (page, KV head), 1536 bytes (this library's format;
+ * the pages fix only "four 2-bit codes per byte", [yunpan] 三.2):
+ *   [0,1024)    64 chunks of 16 bytes.  Chunk c = 16a + b:
+ *               bytes 0..7  = K codes of token b, channels with ((j>>3)&3)==a:
+ *                             32-bit word w = j>>6, 2-bit field
+ *                             4((j>>5)&1) + ((j>>1)&3) + 8(j&1);
+ *               bytes 8..15 = V codes of tokens 4a..4a+3, channels with
+ *                             (j&15)==b: word (t&3)>>1, field (j>>4) + 8(t&1).
+ *   [1024,1152) K scale fp16 [token][group]
+ *   [1152,1280) K zero  fp16 [token][group]
+ *   [1280,1408) V scale fp16 [token/4][group][token%4]
+ *   [1408,1536) V zero  fp16 [token/4][group][token%4]
+ * A code c of group g dequantises to c * scale + zero in the rotated space.
+ */
+#ifndef OSCAR_H
+#define OSCAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OSCAR_ABI_VERSION 1
+
+typedef enum {
+  OSCAR_OK = 0,
+  OSCAR_ERR_INVALID = -1,     /* null pointer, bad count, inconsistent sizes   */
+  OSCAR_ERR_UNSUPPORTED = -2, /* shape outside the supported set (see above)   */
+  OSCAR_ERR_CAPACITY = -3,    /* workspace or page table too small            */
+  OSCAR_ERR_HIP = -4,         /* the HIP runtime reported a launch failure     */
+  OSCAR_ERR_NUMERIC = -5      /* calibration produced a non-finite or too large
+                                 value (clip threshold > 65504)               */
+} oscar_status;
+
+typedef struct {
+  int32_t num_q_heads;  /* Hq                                 */
+  int32_t num_kv_heads; /* Hkv; Hq % Hkv == 0, Hq/Hkv in {1,2,4,8} */
+  int32_t head_dim;     /* must be 128                        */
+  int32_t page_size;    /* must be 16                         */
+  int32_t n_sink;       /* must be 64                         */
+  int32_t n_recent;     /* must be 256                        */
+  int32_t group_size;   /* must be 32                         */
+} oscar_layer_desc;
+
+typedef struct {
+  void* sink_k;                /* device bf16, layout above                  */
+  void* sink_v;
+  void* recent_k;              /* device bf16, layout above                  */
+  void* recent_v;
+  uint8_t* hist;               /* device, [num_pages][Hkv][1536]             */
+  const int32_t* page_table;   /* device, [n_slots][max_pages_per_seq]       */
+  int32_t n_slots;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  const float* rot_k;          /* device fp32 [128][128]: R_K, y = x . R_K   */
+  const float* rot_v;          /* device fp32 [128][128]: R_V                */
+  const float* clip_k;         /* device fp32 [128]: per rotated channel     */
+  const float* clip_v;         /*   clip thresholds, 0 < tau <= 65504        */
+} oscar_pool;
+
+typedef struct {
+  int32_t hadamard_block;      /* 32 (one quantisation group) or 128         */
+  float clip_percentile;       /* e.g. 99.0                                   */
+} oscar_calib_opts;
+
+/* Source formats accepted by oscar_demote. */
+enum {
+  OSCAR_SRC_BF16 = 0,          /* unrotated bf16 K/V: rotate, clip, quantise */
+  OSCAR_SRC_F32_ROTATED = 1    /* already-rotated fp32 K/V: clip, quantise   */
+};
+
+/* ABI version of the loaded library (OSCAR_ABI_VERSION). */
+int32_t oscar_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* oscar_status_string(oscar_status s);
+
+/*
+ * oscar_calibrate -- offline calibration of one layer, on the host.
+ * [gist] 2.1 and 2.2 A; [zingnex] 离线协方差估计 and 离线优化的优势 (fixed
+ * rotation computed offline).
+ *   C_Q = (1/(N Hq)) sum_{n,h} q_{n,h}^T q_{n,h}                 (key target)
+ *   C_S = (1/(N Hq)) sum_h (S_h V_{h/G})^T (S_h V_{h/G}),  S_h the causal
+ *         softmax of Q_h K_{h/G}^T / sqrt(128)                    (value target)
+ *   U_Q, U_S = eigenvectors, descending eigenvalues, each column's largest
+ *         entry made positive;  R = U . H_Had . P_br with H_Had block-diagonal
+ *         normalised Sylvester Hadamard and P_br the 7-bit bit reversal;
+ *   tau = per rotated channel percentile of |x . R| over all tokens and KV
+ *         heads, separately for K and V.
+ * In:  q host fp32 [n_tokens][Hq][128]; k, v host fp32 [n_tokens][Hkv][128]
+ *      (token-major, one calibration sequence, causal).
+ * Out: rot_k, rot_v host fp32 [128][128]; clip_k, clip_v host fp32 [128].
+ * Synchronous, CPU only, uses up to the machine's cores.  Errors:
+ * OSCAR_ERR_INVALID (null pointer, n_tokens < 2), OSCAR_ERR_UNSUPPORTED,
+ * OSCAR_ERR_NUMERIC (non-finite input or tau > 65504).
+ */
+oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opts* opts,
+                             const float* q, const float* k, const float* v, int64_t n_tokens,
+                             float* rot_k, float* rot_v, float* clip_k, float* clip_v);
+
+/*
+ * oscar_append -- route one new token per sequence into the tiered pool
+ * ([yunpan] 三.1 and 三.2; [gist] 2.2 B).  For batch entry b with slot
+ * s = seq_slot[b] (seq_slot may be NULL: s = b) and new position
+ * p = position[b] (the number of tokens already cached):
+ *   p < 64:   write the token to sink[s][:, p];
+ *   p >= 64:  ring slot r = (p-64) mod 256; if p >= 320 the token at ring
+ *             slot r (position p-256) is first demoted -- rotated by R,
+ *             clipped, quantised to INT2 and packed -- into history index
+ *             p-320; then the new token overwrites ring slot r.
+ * k_new, v_new: device bf16 [batch][Hkv][128].  position, seq_slot: device
+ * int32 [batch].  The caller guarantees page_table[s][(p-320)/16] is a valid
+ * page when p >= 320, and that no two batch entries name the same slot.
+ * Positions are not advanced by the call.
+ */
+oscar_status oscar_append(const oscar_layer_desc* desc, const oscar_pool* pool,
+                          const int32_t* seq_slot, const int32_t* position,
+                          const void* k_new, const void* v_new, int32_t batch, void* stream);
+
+/*
+ * oscar_demote -- bulk demotion of n_tokens consecutive history tokens per
+ * sequence (rotate -> clip -> quantise -> pack, [yunpan] 三.2), written to
+ * history indices hist_start[b] .. hist_start[b]+n_tokens-1 of slot
+ * seq_slot[b].  Source k, v: device [batch][n_tokens][Hkv][128], bf16
+ * unrotated (OSCAR_SRC_BF16; the rotation uses the matrix cores) or fp32
+ * already rotated (OSCAR_SRC_F32_ROTATED; only clip, quantise, pack -- the
+ * bit-exact reference entry).  hist_start, seq_slot: device int32 [batch]
+ * (seq_slot may be NULL).  Pages touched must be valid in page_table; tokens
+ * outside the written range keep their bytes.
+ */
+oscar_status oscar_demote(const oscar_layer_desc* desc, const oscar_pool* pool,
+                          const int32_t* seq_slot, const int32_t* hist_start,
+                          const void* k, const void* v, int32_t src_kind,
+                          int32_t batch, int32_t n_tokens, void* stream);
+
+/*
+ * oscar_prefill -- place whole fresh sequences into the tiers, with the
+ * same result as appending their tokens one at a time: positions [0, 64)
+ * to the sink, [64, n-256) demoted to history, the last min(n-64, 256)
+ * positions to the recent ring.  k, v: device bf16
+ * [batch][max_len][Hkv][128]; length: device int32 [batch], n = length[b]
+ * <= max_len.  seq_slot as above.
+ */
+oscar_status oscar_prefill(const oscar_layer_desc* desc, const oscar_pool* pool,
+                           const int32_t* seq_slot, const int32_t* length,
+                           const void* k, const void* v, int32_t batch, int32_t max_len,
+                           void* stream);
+
+/*
+ * oscar_decode -- single-token decode attention over the tiered pool
+ * ([gist] 2.2 B "Kernel-Integration": unpack, dequantise, inverse rotation and
+ * attention fused; [zingnex] 自定义INT2注意力内核).  For batch entry b with
+ * slot s and n = seq_len[b] cached tokens (counting the token appended this
+ * step) and each query head h (KV head h / G):
+ *   out[b][h] = softmax(q[b][h] . K~^T / sqrt(128)) . V~
+ * where K~, V~ hold the BF16 sink and recent tokens and, for history,
+ * dequant(codes) . R^T.  History is scored in the rotated space (q . R_K),
+ * accumulated there, and rotated back once (. R_V^T) after the split-K
+ * partial results are merged by log-sum-exp.
+ * q: device bf16 [batch][Hq][128].  out: device fp32 [batch][Hq][128].
+ * seq_len, seq_slot: device int32 [batch]; every seq_len[b] must be in
+ * [1, max_seq_len].  workspace: device, at least
+ * oscar_decode_workspace_bytes(desc, batch, max_seq_len) bytes, zero-filled
+ * once by the caller before its first use; each call leaves it zero-filled
+ * again.  Errors: OSCAR_ERR_CAPACITY if ws_bytes is too small or
+ * max_seq_len needs more pages than max_pages_per_seq.
+ */
+oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool,
+                          const int32_t* seq_slot, const int32_t* seq_len, const void* q,
+                          float* out, void* workspace, size_t ws_bytes, int32_t batch,
+                          int32_t max_seq_len, void* stream);
+
+size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
+                                    int32_t max_seq_len);
+
+/*
+ * BF16 paged baseline (the full-precision cache INT2 is compared against;
+ * [zingnex] 系统级收益 / 解码加速 report speed-ups over BF16).
+ *   kv: device bf16 [num_pages][Hkv][2][16][128] (K page then V page);
+ *   page_table: device int32 [n_slots][max_pages_per_seq]; token p of slot s
+ *   lives in page page_table[s][p/16], row p%16.
+ * oscar_decode_bf16 computes out[b][h] = softmax(q . K^T / sqrt(128)) . V over
+ * all seq_len[b] tokens, with the same split-K / log-sum-exp structure as
+ * oscar_decode.  Workspace rules as for oscar_decode.
+ */
+typedef struct {
+  const void* kv;
+  const int32_t* page_table;
+  int32_t n_slots;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+} oscar_bf16_pool;
+
+oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_pool* pool,
+                               const int32_t* seq_slot, const int32_t* seq_len, const void* q,
+                               float* out, void* workspace, size_t ws_bytes, int32_t batch,
+                               int32_t max_seq_len, void* stream);
+
+size_t oscar_decode_bf16_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
+                                         int32_t max_seq_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OSCAR_H */

@@ -1,0 +1,159 @@
+"""GPU parity of tiered decode attention (and the BF16 baseline).
+
+Decode parity runs on identical pool bytes: the oracle builds the pool from
+the seeded inputs, the bytes are uploaded to the device, and the device
+decode is compared with the oracle's decode of the same bytes.  Tolerance:
+relative L2 over the compared heads <= 2e-3 (fp32 accumulation)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from bit_rotated_kv_demote_amd import synth
+from bit_rotated_kv_demote_amd.pool import PagedBF16, bf16_tensor
+
+from _gpu_util import Layer, i32, rel_l2, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _decode_vs_oracle(layer, lengths, kv_heads=None, max_seq_len=None, q_index=0, prefill_device=False):
+    opool = layer.oracle_pool(lengths, kv_heads)
+    dev = layer.device_pool()
+    if prefill_device:
+        dev.prefill(i32(lengths), bf16_tensor(layer.k), bf16_tensor(layer.v))
+    upload(dev, opool, kv_heads)
+    q = np.ascontiguousarray(layer.q[q_index])
+    out = dev.decode(bf16_tensor(q), i32(lengths), max_seq_len or max(lengths)).cpu().numpy()
+    g = layer.hq // layer.hkv
+    heads = None
+    if kv_heads is not None:
+        heads = [(b, h) for b in range(layer.batch) for h in range(layer.hq) if h // g in kv_heads]
+    ref = orc.decode_tiered(q, opool, list(range(layer.batch)), lengths, layer.rot, layer.rot, heads=heads)
+    if heads is None:
+        return out, ref
+    idx = tuple(np.array(heads).T)
+    return out[idx], ref[idx]
+
+
+def test_decode_tiny_config_32_steps():
+    # 1 layer, batch 1, 2 q heads / 1 KV head, context 1024 (64 sink + 704 INT2
+    # + 256 recent), then 32 steps, each appending one token before decoding.
+    n0, steps = 1024, 32
+    layer = Layer(seed=1000, batch=1, hq=2, hkv=1, max_len=n0 + steps, n_q=steps)
+    opool = layer.oracle_pool([n0])
+    dev = layer.device_pool()
+    for s in range(steps):
+        p = n0 + s
+        opool.append(0, layer.k[0, p], layer.v[0, p], layer.rot, layer.rot, layer.tau_k, layer.tau_v)
+        upload(dev, opool)
+        q = np.ascontiguousarray(layer.q[s])
+        out = dev.decode(bf16_tensor(q), i32([p + 1]), n0 + steps).cpu().numpy()
+        ref = orc.decode_tiered(q, opool, [0], [p + 1], layer.rot, layer.rot)
+        err = rel_l2(out, ref)
+        assert err <= TOL, (s, err)
+
+
+def test_decode_end_to_end_with_device_appends():
+    # Device append + device decode against oracle append + oracle decode.  The
+    # two pools differ by the fused rotation's rare code flips, so this uses
+    # the end-to-end bound 5e-3 rather than the identical-bytes bound.
+    n0, steps = 700, 24
+    layer = Layer(seed=1001, batch=1, hq=4, hkv=1, max_len=n0 + steps, n_q=steps)
+    opool = layer.oracle_pool([n0])
+    dev = layer.device_pool()
+    upload(dev, opool)
+    for s in range(steps):
+        p = n0 + s
+        opool.append(0, layer.k[0, p], layer.v[0, p], layer.rot, layer.rot, layer.tau_k, layer.tau_v)
+        dev.append(i32([p]), bf16_tensor(np.ascontiguousarray(layer.k[:, p])),
+                   bf16_tensor(np.ascontiguousarray(layer.v[:, p])))
+        q = np.ascontiguousarray(layer.q[s])
+        out = dev.decode(bf16_tensor(q), i32([p + 1]), n0 + steps).cpu().numpy()
+        ref = orc.decode_tiered(q, opool, [0], [p + 1], layer.rot, layer.rot)
+        assert rel_l2(out, ref) <= 5e-3, s
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_edge_lengths_all_groups(group):
+    lengths = [1, 17, 63, 64, 65, 200, 320, 321, 336, 337, 1000, 1531]
+    layer = Layer(seed=1100 + group, batch=len(lengths), hq=2 * group, hkv=2, max_len=max(lengths))
+    out, ref = _decode_vs_oracle(layer, lengths)
+    for b in range(len(lengths)):
+        assert rel_l2(out[b], ref[b]) <= TOL, (group, lengths[b])
+
+
+def test_decode_invariant_to_split_count_and_page_order():
+    lengths = [3000, 1200]
+    layer = Layer(seed=1200, batch=2, hq=8, hkv=2, max_len=max(lengths), extra_pages=200)
+    opool = layer.oracle_pool(lengths)
+    dev = layer.device_pool()
+    upload(dev, opool)
+    q = bf16_tensor(np.ascontiguousarray(layer.q[0]))
+    a = dev.decode(q, i32(lengths), 3000).cpu().numpy()
+    b = dev.decode(q, i32(lengths), 3000 + 16 * 200).cpu().numpy()   # larger split size
+    c = dev.decode(q, i32(lengths), 3000).cpu().numpy()              # workspace reuse
+    assert rel_l2(b, a) <= 1e-5 and np.array_equal(a, c)
+    # same tokens under a different page permutation
+    perm_layer = Layer(seed=1200, batch=2, hq=8, hkv=2, max_len=max(lengths), extra_pages=200)
+    perm_layer.page_table = np.ascontiguousarray(perm_layer.page_table[:, ::-1])
+    opool2 = perm_layer.oracle_pool(lengths)
+    dev2 = perm_layer.device_pool()
+    upload(dev2, opool2)
+    d = dev2.decode(q, i32(lengths), 3000).cpu().numpy()
+    assert rel_l2(d, a) <= 1e-5
+    ref = orc.decode_tiered(layer.q[0], opool, [0, 1], lengths, layer.rot, layer.rot)
+    assert rel_l2(a, ref) <= TOL
+
+
+def test_decode_ragged_batch_gqa8_shuffled_pages():
+    # Qwen3-32B-shaped heads (64 q / 8 KV) on a ragged batch of 16 with
+    # shuffled page tables; context lengths scaled down 10x for the oracle.
+    rng = synth.streams(4)["lengths"]
+    lengths = synth.ragged_lengths(rng, 16, 820, 6554).tolist()
+    layer = Layer(seed=1004, batch=16, hq=64, hkv=8, max_len=max(lengths))
+    out, ref = _decode_vs_oracle(layer, lengths, kv_heads=[2, 7], prefill_device=True)
+    assert rel_l2(out, ref) <= TOL
+
+
+def test_decode_qwen3_4b_32k_sampled_heads():
+    # Full size of the 32K workload, in the bench's launch configuration:
+    # 32 q / 8 KV heads, 32768 cached tokens + the appended one.
+    n = 32768 + 1
+    layer = Layer(seed=1001, batch=1, hq=32, hkv=8, max_len=n)
+    out, ref = _decode_vs_oracle(layer, [n], kv_heads=[0, 5], max_seq_len=n, prefill_device=True)
+    assert rel_l2(out, ref) <= TOL
+
+
+def test_decode_qwen3_8b_128k_sampled_head():
+    n = 131072 + 1
+    layer = Layer(seed=1002, batch=1, hq=32, hkv=8, max_len=n)
+    out, ref = _decode_vs_oracle(layer, [n], kv_heads=[3], max_seq_len=n, prefill_device=True)
+    assert rel_l2(out, ref) <= TOL
+
+
+def test_bf16_baseline_matches_oracle():
+    lengths = [1, 500, 2000]
+    hq, hkv = 8, 2
+    st = synth.streams(77)
+    out_ch = synth.outlier_channels(st["outliers"])
+    max_pages = math.ceil(max(lengths) / 16)
+    num_pages = len(lengths) * max_pages
+    pt = synth.page_permutation(st["perm"], num_pages).reshape(len(lengths), max_pages)
+    kv = np.zeros((num_pages, hkv, 2, 16, 128), np.uint16)
+    for b, n in enumerate(lengths):
+        k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out_ch)
+        v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out_ch)
+        for p in range(n):
+            kv[pt[b, p // 16], :, 0, p % 16] = k[p]
+            kv[pt[b, p // 16], :, 1, p % 16] = v[p]
+    q = synth.queries(st["q"], (len(lengths), hq, 128))
+    pool = PagedBF16(hq, hkv, kv, pt)
+    out = pool.decode(bf16_tensor(q), i32(lengths), max(lengths)).cpu().numpy()
+    ref = orc.decode_bf16(q, kv, pt, [0, 1, 2], lengths)
+    for b in range(len(lengths)):
+        assert rel_l2(out[b], ref[b]) <= TOL, lengths[b]

@@ -1,0 +1,122 @@
+"""GPU parity of the demotion path (rotate -> clip -> quantise -> pack)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from bit_rotated_kv_demote_amd import binding, synth
+from bit_rotated_kv_demote_amd.pool import bf16_bits, bf16_tensor
+
+pytestmark = pytest.mark.gpu
+
+from _gpu_util import Layer, code_diff_stats, i32  # noqa: E402
+
+# fused-path budget: at most 0.1% of codes differ from the oracle, each by 1,
+# scales / zeros within 2 fp16 ulp
+FLIP_RATE = 1e-3
+
+
+def _rotated_inputs(layer, batch, n_tokens, starts):
+    yk = np.zeros((batch, n_tokens, layer.hkv, 128), np.float32)
+    yv = np.zeros_like(yk)
+    for b in range(batch):
+        src = slice(64 + starts[b], 64 + starts[b] + n_tokens)
+        yk[b] = orc.rotate_fp32(synth.bf16_bits_to_f32(layer.k[b, src]), layer.rot)
+        yv[b] = orc.rotate_fp32(synth.bf16_bits_to_f32(layer.v[b, src]), layer.rot)
+    # edge cases in the first tokens of sequence 0: a constant group, a group at
+    # the clip bound, exact half-step ties, values far beyond the clip
+    yk[0, 0, 0, :32] = np.float32(0.75)
+    yk[0, 1, 0, 32:64] = layer.tau_k[32:64]
+    z, s = np.float16(-1.0), np.float16(0.5)
+    yk[0, 2, 0, :32] = (np.float32(z) + (np.arange(32) % 4 + 0.5).astype(np.float32) * np.float32(s)).clip(-1, 0.5)
+    yk[0, 2, 0, 0], yk[0, 2, 0, 1] = np.float32(-1.0), np.float32(0.5)
+    yv[0, 3, 0, 64:96] = np.float32(1e4)
+    yv[0, 3, 0, 96:] = np.float32(-3e4)
+    return yk, yv
+
+
+def test_demote_from_rotated_fp32_is_bit_exact():
+    batch, n_tokens = 3, 70
+    layer = Layer(seed=11, batch=batch, hq=8, hkv=4, max_len=64 + 48 + n_tokens + 256 + 16)
+    starts = [0, 5, 37]                                   # mid-page starts
+    yk, yv = _rotated_inputs(layer, batch, n_tokens, starts)
+    dev = layer.device_pool()
+    dev.demote(i32(starts), torch.from_numpy(yk).cuda(), torch.from_numpy(yv).cuda(),
+               src_kind=binding.OSCAR_SRC_F32_ROTATED)
+    torch.cuda.synchronize()
+    ref = orc.Pool(batch, layer.hkv, layer.num_pages, layer.page_table)
+    for b in range(batch):
+        ref.demote_rotated_many(b, np.arange(starts[b], starts[b] + n_tokens), yk[b], yv[b], layer.tau_k, layer.tau_v)
+    got = dev.hist.cpu().numpy()
+    assert np.array_equal(got, ref.hist), f"{np.count_nonzero(got != ref.hist)} bytes differ"
+
+
+def test_demote_bf16_fused_rotation_within_flip_budget():
+    batch, n_tokens = 2, 600
+    layer = Layer(seed=12, batch=batch, hq=16, hkv=8, max_len=64 + n_tokens + 256 + 32)
+    starts = [0, 9]
+    k = np.ascontiguousarray(np.stack([layer.k[b, 64 + starts[b]:64 + starts[b] + n_tokens] for b in range(batch)]))
+    v = np.ascontiguousarray(np.stack([layer.v[b, 64 + starts[b]:64 + starts[b] + n_tokens] for b in range(batch)]))
+    dev = layer.device_pool()
+    dev.demote(i32(starts), bf16_tensor(k), bf16_tensor(v))
+    torch.cuda.synchronize()
+    ref = orc.Pool(batch, layer.hkv, layer.num_pages, layer.page_table)
+    for b in range(batch):
+        ref.demote_many(b, np.arange(starts[b], starts[b] + n_tokens), k[b], v[b], layer.rot, layer.rot,
+                        layer.tau_k, layer.tau_v)
+    got = dev.hist.cpu().numpy()
+    pages = np.concatenate([layer.page_table[b, (starts[b] + np.arange(n_tokens)) // 16] for b in range(batch)])
+    slots = np.concatenate([(starts[b] + np.arange(n_tokens)) % 16 for b in range(batch)])
+    rate, maxd, meta_ulp = code_diff_stats(got, ref.hist, pages, slots)
+    assert rate <= FLIP_RATE and maxd <= 1 and meta_ulp <= 2, (rate, maxd, meta_ulp)
+    # bytes outside the demoted tokens stay untouched (zero)
+    untouched = np.ones(got.shape[0], bool)
+    untouched[np.unique(pages)] = False
+    assert not got[untouched].any()
+
+
+def test_append_sequence_matches_oracle_state_machine():
+    # Two sequences in swapped slots, appended token by token from empty
+    # through several demotions; new tokens attend to nothing here.
+    n_steps = 420
+    layer = Layer(seed=13, batch=2, hq=4, hkv=2, max_len=n_steps)
+    dev = layer.device_pool()
+    slots = [1, 0]
+    ref = orc.Pool(2, layer.hkv, layer.num_pages, layer.page_table)
+    slot_t = i32(slots)
+    for p in range(n_steps):
+        kn = np.ascontiguousarray(layer.k[:, p])
+        vn = np.ascontiguousarray(layer.v[:, p])
+        dev.append(i32([p, p]), bf16_tensor(kn), bf16_tensor(vn), seq_slot=slot_t)
+        for b in range(2):
+            ref.append(slots[b], kn[b], vn[b], layer.rot, layer.rot, layer.tau_k, layer.tau_v)
+    torch.cuda.synchronize()
+    st = dev.host_state()
+    for name in ("sink_k", "sink_v", "recent_k", "recent_v"):
+        assert np.array_equal(st[name], getattr(ref, name)), name
+    n_hist = n_steps - 320
+    pages, sl = [], []
+    for s in range(2):
+        pages.append(layer.page_table[s, np.arange(n_hist) // 16])
+        sl.append(np.arange(n_hist) % 16)
+    rate, maxd, meta_ulp = code_diff_stats(st["hist"], ref.hist, np.concatenate(pages), np.concatenate(sl))
+    assert rate <= FLIP_RATE and maxd <= 1 and meta_ulp <= 2, (rate, maxd, meta_ulp)
+
+
+def test_prefill_ragged_matches_oracle():
+    lengths = [50, 320, 333, 1000]
+    layer = Layer(seed=14, batch=4, hq=8, hkv=2, max_len=max(lengths))
+    dev = layer.device_pool()
+    dev.prefill(i32(lengths), bf16_tensor(layer.k), bf16_tensor(layer.v))
+    torch.cuda.synchronize()
+    ref = layer.oracle_pool(lengths)
+    st = dev.host_state()
+    for name in ("sink_k", "sink_v", "recent_k", "recent_v"):
+        assert np.array_equal(st[name], getattr(ref, name)), name
+    pages, sl = [], []
+    for b, n in enumerate(lengths):
+        h = np.arange(max(0, n - 320))
+        pages.append(layer.page_table[b, h // 16])
+        sl.append(h % 16)
+    rate, maxd, meta_ulp = code_diff_stats(st["hist"], ref.hist, np.concatenate(pages), np.concatenate(sl))
+    assert rate <= FLIP_RATE and maxd <= 1 and meta_ulp <= 2, (rate, maxd, meta_ulp)
