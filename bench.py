@@ -1,0 +1,373 @@
+"""Benchmark of the OSCAR-style INT2 tiered decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: oscar_append (route
+the new token; demote the ring slot it reuses: rotate, clip, quantise, pack)
+followed by oscar_decode (tiered decode attention).  The default workload is
+the Qwen3-4B-shaped layer: 32 q / 8 KV heads, head_dim 128, batch 1, 32768
+cached tokens (64 BF16 sink + INT2 history + 256 BF16 recent, 16-token pages),
+seeded synthetic K/V/q, R and clip thresholds from oscar_calibrate on 4096
+seeded calibration tokens.  Steps cycle through distinct per-layer pools
+totalling more than 512 MB so that repeated steps are served from HBM, not
+from the 256 MB last-level cache.
+
+Prints one JSON line.  Also reported: the 128K-context decode (Qwen3-8B
+shape), the BF16 paged baseline at both contexts, bulk demotion tok/s
+(16 sequences x 4096-token chunks, 8 KV heads) and the CPU oracle timed on
+a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "INT2 decode-attn µs/step + HBM GB/s (% roofline) at 32K–128K ctx; demote tok/s"
+
+
+def decode_bytes(lengths, hq, hkv):
+    """Algorithmic HBM bytes of one oscar_decode call (see the design notes)."""
+    total = 0
+    for n in lengths:
+        hist = max(0, n - 320)
+        total += hist * hkv * 96 + min(n, 320) * hkv * 512 + 4 * math.ceil(hist / 16)
+    total += len(lengths) * hq * 128 * (2 + 4) + 2 * 128 * 128 * 4
+    return total
+
+
+def bf16_decode_bytes(lengths, hq, hkv):
+    total = 0
+    for n in lengths:
+        total += n * hkv * 512 + 4 * math.ceil(n / 16)
+    return total + len(lengths) * hq * 128 * (2 + 4)
+
+
+_HOLD_CYCLES_PER_MS = None
+
+
+def gpu_hold(torch, ms):
+    """Enqueue a bounded spin kernel of about `ms` milliseconds on the current
+    stream, so that the host can queue the timed launches ahead of the GPU
+    (the timed region then measures back-to-back GPU execution, not the
+    Python launch loop)."""
+    global _HOLD_CYCLES_PER_MS
+    if _HOLD_CYCLES_PER_MS is None:
+        n = 1_000_000
+        torch.cuda._sleep(n)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(n)
+        b.record()
+        torch.cuda.synchronize()
+        _HOLD_CYCLES_PER_MS = n / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_HOLD_CYCLES_PER_MS * ms))
+
+
+class Timer:
+    """HIP events on the current stream around each launch of one kernel."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_us(self):
+        return 1000.0 * sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
+
+
+def build_layers(torch, hq, hkv, n0, n_layers, steps_per_layer, seed, calib_tokens=4096, calib=None):
+    """n_layers distinct pools holding the same seeded context of n0 tokens.
+    calib: (rot_k, rot_v, tau_k, tau_v) to reuse; default: oscar_calibrate."""
+    from bit_rotated_kv_demote_amd import binding, synth
+    from bit_rotated_kv_demote_amd.pool import TieredKV, bf16_tensor
+
+    st = synth.streams(seed)
+    out = synth.outlier_channels(st["outliers"])
+    n_tot = n0 + steps_per_layer
+    k = synth.kv_tokens(st["k"], st["lognormal"], n_tot, hkv, out)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n_tot, hkv, out)
+    calib_s = 0.0
+    if calib is None:
+        # offline calibration on seeded calibration tokens (host C++ in the library)
+        cq = synth.bf16_bits_to_f32(synth.queries(st["calib"], (calib_tokens, hq, 128)))
+        ck = synth.bf16_bits_to_f32(synth.kv_tokens(st["calib"], st["lognormal"], calib_tokens, hkv, out))
+        cv = synth.bf16_bits_to_f32(synth.kv_tokens(st["calib"], st["lognormal"], calib_tokens, hkv, out))
+        rot_k = torch.zeros((128, 128), dtype=torch.float32)
+        rot_v = torch.zeros((128, 128), dtype=torch.float32)
+        tau_k = torch.zeros(128, dtype=torch.float32)
+        tau_v = torch.zeros(128, dtype=torch.float32)
+        t0 = time.time()
+        binding.oscar_calibrate(binding.layer_desc(hq, hkv), torch.from_numpy(cq), torch.from_numpy(ck),
+                                torch.from_numpy(cv), rot_k, rot_v, tau_k, tau_v)
+        calib_s = time.time() - t0
+        calib = (rot_k.numpy(), rot_v.numpy(), tau_k.numpy(), tau_v.numpy())
+    max_pages = math.ceil((n_tot - 320) / 16)
+    layers = []
+    kd = bf16_tensor(k[None, :n0])
+    vd = bf16_tensor(v[None, :n0])
+    for li in range(n_layers):
+        pt = synth.page_permutation(np.random.default_rng(seed * 100 + li), max_pages)[None, :]
+        pool = TieredKV(hq, hkv, 1, max_pages, max_pages, *calib, page_table=pt)
+        pool.prefill(torch.tensor([n0], dtype=torch.int32, device="cuda"), kd, vd)
+        layers.append(pool)
+    new_k = bf16_tensor(np.ascontiguousarray(k[n0:]))    # [steps, Hkv, 128]
+    new_v = bf16_tensor(np.ascontiguousarray(v[n0:]))
+    q = bf16_tensor(synth.queries(st["q"], (steps_per_layer, 1, hq, 128)))
+    torch.cuda.synchronize()
+    del kd, vd
+    return layers, new_k, new_v, q, calib_s, (k, v) + tuple(calib)
+
+
+def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None):
+    """Time exactly `steps` append+decode steps cycling through n_layers pools,
+    then as many again with HIP events around every launch (kernel durations)."""
+    rounds = math.ceil((warmup + 2 * steps) / n_layers)
+    layers, new_k, new_v, q, calib_s, host = build_layers(torch, hq, hkv, n0, n_layers, rounds, seed, calib=calib)
+    positions = torch.arange(n0, n0 + rounds, dtype=torch.int32, device="cuda")
+    lens = positions + 1
+    max_len = n0 + rounds
+    outs = [torch.empty((1, hq, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
+    for pool in layers:
+        pool.workspace(1, max_len)
+
+    def step(i, t_dec=None, t_app=None):
+        li, r = i % n_layers, i // n_layers
+        pool = layers[li]
+        s = t_app.start() if t_app else None
+        pool.append(positions[r:r + 1], new_k[r:r + 1], new_v[r:r + 1])
+        if t_app:
+            t_app.stop(s)
+        s = t_dec.start() if t_dec else None
+        pool.decode(q[r], lens[r:r + 1], max_len, out=outs[i & 1])
+        if t_dec:
+            t_dec.stop(s)
+
+    for i in range(warmup):
+        step(i)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gpu_hold(torch, 20 + 0.1 * steps)
+    e0.record()
+    for i in range(warmup, warmup + steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    t_dec, t_app = Timer(torch), Timer(torch)
+    gpu_hold(torch, 20 + 0.2 * steps)
+    for i in range(warmup + steps, warmup + 2 * steps):
+        step(i, t_dec, t_app)
+    torch.cuda.synchronize()
+    pool_bytes = sum(p.hist.numel() + 4 * p.sink_k.numel() + 4 * p.recent_k.numel() for p in layers)
+    mid_len = n0 + (warmup + steps) // n_layers + 1
+    return dict(total_ms=total_ms, us_per_step=1000.0 * total_ms / steps, decode_us=t_dec.mean_us(),
+                append_us=t_app.mean_us(), decode_bytes=decode_bytes([mid_len], hq, hkv), layers=n_layers,
+                pool_mb=pool_bytes / 1e6, calib_s=calib_s, host=host, n_mid=mid_len, max_len=max_len)
+
+
+def run_bf16(torch, hq, hkv, n, n_layers, steps, seed, k_bits, v_bits):
+    from bit_rotated_kv_demote_amd import synth
+    from bit_rotated_kv_demote_amd.pool import PagedBF16, bf16_tensor
+
+    pages = math.ceil(n / 16)
+    kv = np.zeros((pages, hkv, 2, 16, 128), np.uint16)
+    kp = np.zeros((pages * 16, hkv, 128), np.uint16)
+    vp = np.zeros((pages * 16, hkv, 128), np.uint16)
+    kp[:n] = k_bits[:n]
+    vp[:n] = v_bits[:n]
+    kv[:, :, 0] = kp.reshape(pages, 16, hkv, 128).transpose(0, 2, 1, 3)
+    kv[:, :, 1] = vp.reshape(pages, 16, hkv, 128).transpose(0, 2, 1, 3)
+    q = bf16_tensor(synth.queries(synth.streams(seed)["q"], (1, hq, 128)))
+    pools = []
+    for li in range(n_layers):
+        perm = synth.page_permutation(np.random.default_rng(7000 + li), pages)
+        phys = np.empty_like(kv)
+        phys[perm] = kv
+        pools.append(PagedBF16(hq, hkv, phys, perm[None, :]))
+    lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+    out = torch.empty((1, hq, 128), dtype=torch.float32, device="cuda")
+    for p in pools:
+        p.decode(q, lens, n, out=out)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    gpu_hold(torch, 20 + 0.2 * steps)
+    for i in range(steps):
+        s = t.start()
+        pools[i % n_layers].decode(q, lens, n, out=out)
+        t.stop(s)
+    torch.cuda.synchronize()
+    return dict(decode_us=t.mean_us(), decode_bytes=bf16_decode_bytes([n], hq, hkv), layers=n_layers,
+                pool_mb=n_layers * kv.nbytes / 1e6)
+
+
+def run_demote(torch, reps, seed):
+    """Bulk demotion of a 4096-token chunk for 16 sequences x 8 KV heads."""
+    from bit_rotated_kv_demote_amd import synth
+    from bit_rotated_kv_demote_amd.pool import TieredKV, bf16_tensor
+
+    batch, chunk, hkv, hq = 16, 4096, 8, 64
+    st = synth.streams(seed)
+    out = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], batch * chunk, hkv, out).reshape(batch, chunk, hkv, 128)
+    v = synth.kv_tokens(st["v"], st["lognormal"], batch * chunk, hkv, out).reshape(batch, chunk, hkv, 128)
+    rot = synth.random_rotation(st["rot"])
+    tau = np.full(128, 64.0, np.float32)
+    max_pages = 4096 // 16 + 2
+    pt = synth.page_permutation(st["perm"], batch * max_pages).reshape(batch, max_pages)
+    pool = TieredKV(hq, hkv, batch, max_pages, batch * max_pages, rot, rot, tau, tau, page_table=pt)
+    starts = torch.tensor(synth.ragged_lengths(st["lengths"], batch, 0, 15), dtype=torch.int32, device="cuda")
+    kd, vd = bf16_tensor(k), bf16_tensor(v)
+    pool.demote(starts, kd, vd)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    gpu_hold(torch, 20)
+    for _ in range(reps):
+        s = t.start()
+        pool.demote(starts, kd, vd)
+        t.stop(s)
+    torch.cuda.synchronize()
+    us = t.mean_us()
+    tokens = batch * chunk
+    nbytes = tokens * hkv * (2 * 256 + 96)
+    return dict(us=us, tok_per_s=tokens / (us * 1e-6), gbps=nbytes / (us * 1e3), tokens=tokens, bytes=nbytes)
+
+
+def cpu_baseline(hq, hkv, n0, host, seed, kv_sample=8):
+    """The oracle, as it stands, on a bounded sample of the same step."""
+    import oracle as orc
+    from bit_rotated_kv_demote_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    k, v, rot_k, rot_v, tau_k, tau_v = host
+    heads = list(range(kv_sample))
+    max_pages = math.ceil((n0 + 1 - 320) / 16)
+    pt = np.arange(max_pages, dtype=np.int32)[None, :]
+    pool = orc.Pool(1, hkv, max_pages, pt)
+    ns = 64
+    pool.sink_k[0][:, :ns] = k[:ns].transpose(1, 0, 2)
+    pool.sink_v[0][:, :ns] = v[:ns].transpose(1, 0, 2)
+    pos = np.arange(n0 - 256, n0)
+    pool.recent_k[0][:, (pos - 64) % 256] = k[pos].transpose(1, 0, 2)
+    pool.recent_v[0][:, (pos - 64) % 256] = v[pos].transpose(1, 0, 2)
+    h = np.arange(n0 - 320)
+    pool.demote_many(0, h, k[64 + h][:, heads], v[64 + h][:, heads], rot_k, rot_v, tau_k, tau_v, kv_heads=heads)
+    pool.length[0] = n0
+    q = synth.queries(synth.streams(seed)["q"], (1, hq, 128))
+    g = hq // hkv
+    t0 = time.time()
+    pool.append(0, k[n0], v[n0], rot_k, rot_v, tau_k, tau_v)
+    orc.decode_tiered(q, pool, [0], [n0 + 1], rot_k, rot_v, heads=[(0, hh) for hh in range(kv_sample * g)])
+    secs = time.time() - t0
+    scaled_us = secs * 1e6 * hkv / kv_sample
+    return {"value": round(scaled_us, 1), "unit": "us/step", "cores": int(blas), "kind": "oracle",
+            "sample": f"one append (all {hkv} KV heads) + decode of {kv_sample} of {hkv} KV heads "
+                      f"({kv_sample * g} q heads) at {n0 + 1} tokens, {secs:.2f} s, scaled x{hkv // kv_sample}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--layers", type=int, default=24, help="distinct pools cycled (>512 MB total)")
+    ap.add_argument("--no-extra", action="store_true", help="only the 32K tiered step")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="append one plain device copy of this many MB (counter calibration runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from bit_rotated_kv_demote_amd import binding
+    binding.load()
+
+    hq, hkv, n0 = 32, 8, 32768
+    res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001)
+    dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
+    extra = {"decode_kernel_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),
+             "decode_algorithmic_bytes": res["decode_bytes"], "decode_GBps": round(dec_gbps, 1),
+             "pools": res["layers"], "pool_MB_total": round(res["pool_mb"], 1),
+             "calibrate_host_s": round(res["calib_s"], 2)}
+    if not args.no_extra:
+        b = run_bf16(torch, hq, hkv, res["n_mid"], 8, min(args.steps, 200), 1001, res["host"][0], res["host"][1])
+        extra["bf16_decode_us"] = round(b["decode_us"], 3)
+        extra["bf16_decode_GBps"] = round(b["decode_bytes"] / (b["decode_us"] * 1e3), 1)
+        extra["int2_vs_bf16_decode_speedup"] = round(b["decode_us"] / res["decode_us"], 3)
+        del b
+        r128 = run_tiered(torch, hq, hkv, 131072, 8, min(args.steps, 160), 8, seed=1002, calib=res["host"][2:])
+        g128 = r128["decode_bytes"] / (r128["decode_us"] * 1e3)
+        extra["ctx128k"] = {"us_per_step": round(r128["us_per_step"], 3), "decode_kernel_us": round(r128["decode_us"], 3),
+                            "append_kernel_us": round(r128["append_us"], 3), "decode_GBps": round(g128, 1),
+                            "decode_frac_of_8TBps": round(g128 / HBM_PEAK_GBPS, 4),
+                            "decode_algorithmic_bytes": r128["decode_bytes"], "pools": r128["layers"],
+                            "pool_MB_total": round(r128["pool_mb"], 1)}
+        b128 = run_bf16(torch, hq, hkv, r128["n_mid"], 4, 60, 1002, r128["host"][0], r128["host"][1])
+        extra["ctx128k"]["bf16_decode_us"] = round(b128["decode_us"], 3)
+        extra["ctx128k"]["bf16_decode_GBps"] = round(b128["decode_bytes"] / (b128["decode_us"] * 1e3), 1)
+        extra["ctx128k"]["int2_vs_bf16_decode_speedup"] = round(b128["decode_us"] / r128["decode_us"], 3)
+        del r128, b128
+        d = run_demote(torch, 20, 1004)
+        extra["demote_tok_per_s"] = round(d["tok_per_s"], 0)
+        extra["demote_us_per_chunk"] = round(d["us"], 2)
+        extra["demote_GBps"] = round(d["gbps"], 1)
+        extra["demote_workload"] = "16 sequences x 4096-token chunk, 8 KV heads, K+V, bf16 in, MFMA rotation"
+    if args.copy_probe_mb:
+        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(hq, hkv, n0, res["host"], 1001)
+    line = {
+        "metric": METRIC,
+        "value": round(res["us_per_step"], 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["us_per_step"] / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2-kv/fp32-acc",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-4b-shaped tiered decode step (append + decode): 32 q / 8 KV heads, "
+                               "head_dim 128, batch 1, 32768 cached tokens + 1 appended per step, "
+                               "64 bf16 sink / int2 history / 256 bf16 recent, 16-token pages",
+                   "global_batch": 1, "seq_len": n0, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,10 @@ DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
                 # never emit packed-fp32 VALU instructions
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 # LDS use stays exactly what the kernels declare
-                "-mllvm", "-disable-promote-alloca-to-lds"]
+                "-mllvm", "-disable-promote-alloca-to-lds",
+                # matrix-core accumulators in VGPRs: no AGPR <-> VGPR copies in
+                # loops whose accumulators are also touched by vector code
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 HIP_SOURCES = ["demote.hip", "decode.hip", "decode_bf16.hip"]
 HOST_HIP_SOURCES = ["oscar_api.cpp"]      # host code that needs the HIP runtime headers
 HOST_SOURCES = ["calibrate.cpp"]          # plain C++

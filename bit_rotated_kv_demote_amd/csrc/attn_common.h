@@ -44,6 +44,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Split records cross workgroups (and XCDs, each with its own L2): they are
+// written and read only with device-scope relaxed atomic accesses, which the
+// hardware keeps coherent across L2s without whole-cache writeback or
+// invalidation.  A workgroup's record is complete once every thread has
+// waited for its stores (s_waitcnt), which precedes the ticket below.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4 ld_dev4(const float* p) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float*>(p));
+  const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                     __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+}
+
 template <int G>
 struct alignas(16) SplitSmem {
   float pt[4][32][G];        // probabilities of a 32-token BF16 chunk, per wave
@@ -52,6 +71,7 @@ struct alignas(16) SplitSmem {
   float wo[4][G][kD];        // per-wave unnormalised outputs
   float mw[G][kMaxSplits];   // merge: per-split weights
   float ohist[G][kD];        // merge: rotated part
+  float mred[2048];          // merge: per-part sums [parts][2][G*128] (parts * G * 128 == 1024)
   float lsum[G];
   int last;
 };
@@ -81,17 +101,24 @@ __device__ void bf16_span_wave(const uint16_t* qg, int count, RowK rowk, RowV ro
   for (int c = wave; 32 * c < count; c += 4) {
     const int cbase = 32 * c;
     const int cn = min(32, count - cbase);
+    // issue every load of the chunk first: 2 x 4 K fragments and 32 V words per lane
+    bf16x8_t ka[2][4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint16_t* kr = rowk(cbase + min(16 * blk + x, cn - 1));
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ka[blk][kk] = *reinterpret_cast<const bf16x8_t*>(kr + 32 * kk + 8 * qa);
+    }
+    uint32_t vw[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t)
+      vw[t] = *reinterpret_cast<const uint32_t*>(rowv(cbase + min(t, cn - 1)) + 2 * lane);
     float sc[2][4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int ut = min(16 * blk + x, cn - 1);
-      const uint16_t* kr = rowk(cbase + ut);
       float4_t d = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kr + 32 * kk + 8 * qa);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, bq[kk], d, 0, 0, 0);
-      }
+      for (int kk = 0; kk < 4; ++kk) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[blk][kk], bq[kk], d, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * blk + 4 * qa + r;
@@ -124,12 +151,12 @@ __device__ void bf16_span_wave(const uint16_t* qg, int count, RowK rowk, RowV ro
       o[h][0] *= alpha;
       o[h][1] *= alpha;
     }
-    for (int t = 0; t < cn; ++t) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(rowv(cbase + t) + 2 * lane);
-      const float v0 = bf16_bits_to_float(vv & 0xFFFFu), v1 = bf16_bits_to_float(vv >> 16);
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const float v0 = bf16_bits_to_float(vw[t] & 0xFFFFu), v1 = bf16_bits_to_float(vw[t] >> 16);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float pw = sm.pt[wave][t][h];
+        const float pw = sm.pt[wave][t][h];     // 0 for t >= cn
         o[h][0] = fmaf(pw, v0, o[h][0]);
         o[h][1] = fmaf(pw, v1, o[h][1]);
       }
@@ -162,92 +189,158 @@ __device__ void store_split(SplitSmem<G>& sm, float* rec, int tid) {
     float acc = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) acc = fmaf(__builtin_amdgcn_exp2f(sm.wm[w][h] - mm), sm.wo[w][h][j], acc);
-    rec[h * kPartStride + j] = acc;
+    st_dev(&rec[h * kPartStride + j], acc);
     if (j == 0) {
       float ll = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) ll = fmaf(__builtin_amdgcn_exp2f(sm.wm[w][h] - mm), sm.wl[w][h], ll);
-      rec[h * kPartStride + kD] = mm;
-      rec[h * kPartStride + kD + 1] = ll;
+      st_dev(&rec[h * kPartStride + kD], mm);
+      st_dev(&rec[h * kPartStride + kD + 1], ll);
     }
   }
 }
 
-// Release this workgroup's record and take a ticket; true for the last
+// Publish this workgroup's record and take a ticket; true for the last
 // workgroup of the group (which then owns the merge and resets the counter).
 template <int G>
 __device__ bool finish_ticket(SplitSmem<G>& sm, uint32_t* counter, uint32_t target, int tid) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's record stores are complete
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = atomicAdd(counter, 1u);
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.last = (prev == target - 1u) ? 1 : 0;
   }
   __syncthreads();
-  if (!sm.last) return false;
-  __threadfence();
-  return true;
+  return sm.last != 0;
 }
 
 // LSE merge of n_act split records of one group.  Records k < n_plain are in
 // the output space; the others are in the rotated space and are summed, then
 // rotated back with R^T ((y R^T)_i = sum_j y_j R[i][j]).  out: [G][128] fp32.
+// Each phase issues its loads together: the merge runs after the rest of the
+// grid has drained, so its latency is the kernel's tail.
 template <int G, class SplitId>
 __device__ void merge_group(SplitSmem<G>& sm, const float* part_base, int n_act, int n_plain, SplitId split_id,
                             const float* rot, float* out, int tid, int wave, int lane) {
+  const bool any_rot = n_act > n_plain;
+  // this thread's slice of R for phase D: row ri, columns [64 jh, 64 jh + 64)
+  const int ri = tid & (kD - 1), jh = tid >> 7;
+  float4 rrow[16];
+  if (any_rot) {
+    const float4* rp = reinterpret_cast<const float4*>(rot + (size_t)ri * kD + 64 * jh);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
+  }
+  // B0: this thread's record loads (float4 column of one head, split residue
+  // class), issued before the weights are known
+  constexpr int kCols = G * kD / 4;
+  constexpr int kParts = 256 / kCols;
+  constexpr int kBatch = 16;
+  const int col = tid % kCols, part = tid / kCols;
+  const int ch = col / (kD / 4), j4 = col % (kD / 4);
+  float4 v[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int k = part + u * kParts;
+    v[u] = k < n_act ? ld_dev4(&part_base[((size_t)split_id(k) * G + ch) * kPartStride + 4 * j4])
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // A: per-head global max, split weights and the total sum
   for (int h = wave; h < G; h += 4) {
+    float mk[(kMaxSplits + 63) / 64], lk[(kMaxSplits + 63) / 64];
     float mm = kMInit;
-    for (int k = lane; k < n_act; k += 64)
-      mm = fmaxf(mm, __builtin_nontemporal_load(&part_base[((size_t)split_id(k) * G + h) * kPartStride + kD]));
+#pragma unroll
+    for (int r = 0; r < (kMaxSplits + 63) / 64; ++r) {
+      const int k = lane + 64 * r;
+      mk[r] = kMInit;
+      lk[r] = 0.0f;
+      if (k < n_act) {
+        const float* rp = &part_base[((size_t)split_id(k) * G + h) * kPartStride + kD];
+        mk[r] = ld_dev(rp);
+        lk[r] = ld_dev(rp + 1);
+      }
+      mm = fmaxf(mm, mk[r]);
+    }
     mm = wave_max(mm);
     float ll = 0.0f;
-    for (int k = lane; k < n_act; k += 64) {
-      const float* r = &part_base[((size_t)split_id(k) * G + h) * kPartStride];
-      const float wk = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(&r[kD]) - mm);
-      sm.mw[h][k] = wk;
-      ll = fmaf(wk, __builtin_nontemporal_load(&r[kD + 1]), ll);
+#pragma unroll
+    for (int r = 0; r < (kMaxSplits + 63) / 64; ++r) {
+      const int k = lane + 64 * r;
+      if (k < n_act) {
+        const float wk = __builtin_amdgcn_exp2f(mk[r] - mm);
+        sm.mw[h][k] = wk;
+        ll = fmaf(wk, lk[r], ll);
+      }
     }
     ll = wave_sum(ll);
     if (lane == 0) sm.lsum[h] = ll;
   }
   __syncthreads();
-  constexpr int kPer = (G * kD + 255) / 256;
-  float oplain[kPer];
+  // B: weighted sums
+  {
+    float4 ap = make_float4(0.f, 0.f, 0.f, 0.f), ar = ap;
+    auto acc_into = [&](int kk, const float4& x) {
+      const float w = sm.mw[ch][kk];
+      float4& acc = kk < n_plain ? ap : ar;
+      acc.x = fmaf(w, x.x, acc.x); acc.y = fmaf(w, x.y, acc.y);
+      acc.z = fmaf(w, x.z, acc.z); acc.w = fmaf(w, x.w, acc.w);
+    };
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int idx = tid + 256 * e;
-    oplain[e] = 0.0f;
-    if (idx >= G * kD) continue;
-    const int h = idx / kD, j = idx % kD;
-    float ar = 0.0f, ap = 0.0f;
-    for (int k = 0; k < n_act; ++k) {
-      const float v = __builtin_nontemporal_load(&part_base[((size_t)split_id(k) * G + h) * kPartStride + j]);
-      if (k < n_plain) ap = fmaf(sm.mw[h][k], v, ap);
-      else ar = fmaf(sm.mw[h][k], v, ar);
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = part + u * kParts;
+      if (k < n_act) acc_into(k, v[u]);
     }
-    sm.ohist[h][j] = ar;
-    oplain[e] = ap;
-  }
-  __syncthreads();
-  const bool any_rot = n_act > n_plain;
+    for (int k0 = part + kBatch * kParts; k0 < n_act; k0 += kBatch * kParts) {
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int idx = tid + 256 * e;
-    if (idx >= G * kD) continue;
-    const int h = idx / kD, i = idx % kD;
-    float acc = oplain[e];
-    if (any_rot) {
-      const float4* rrow = reinterpret_cast<const float4*>(rot + (size_t)i * kD);
-#pragma unroll 4
-      for (int j4 = 0; j4 < kD / 4; ++j4) {
-        const float4 r4 = rrow[j4];
-        acc = fmaf(sm.ohist[h][4 * j4], r4.x, acc);
-        acc = fmaf(sm.ohist[h][4 * j4 + 1], r4.y, acc);
-        acc = fmaf(sm.ohist[h][4 * j4 + 2], r4.z, acc);
-        acc = fmaf(sm.ohist[h][4 * j4 + 3], r4.w, acc);
+      for (int u = 0; u < kBatch; ++u) {
+        const int k = k0 + u * kParts;
+        v[u] = k < n_act ? ld_dev4(&part_base[((size_t)split_id(k) * G + ch) * kPartStride + 4 * j4])
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int k = k0 + u * kParts;
+        if (k < n_act) acc_into(k, v[u]);
       }
     }
-    out[(size_t)h * kD + i] = acc / sm.lsum[h];
+    reinterpret_cast<float4*>(&sm.mred[(part * 2 + 0) * G * kD])[col] = ap;
+    reinterpret_cast<float4*>(&sm.mred[(part * 2 + 1) * G * kD])[col] = ar;
+  }
+  __syncthreads();
+  // C: reduce the residue classes; plain part -> wo[0], rotated part -> ohist
+  float* plain = &sm.wo[0][0][0];
+  for (int idx = tid; idx < G * kD; idx += 256) {
+    float ap = 0.f, ar = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < kParts; ++pp) {
+      ap += sm.mred[(pp * 2 + 0) * G * kD + idx];
+      ar += sm.mred[(pp * 2 + 1) * G * kD + idx];
+    }
+    plain[idx] = ap;
+    sm.ohist[idx / kD][idx % kD] = ar;
+  }
+  __syncthreads();
+  // D: half of (ohist . R^T) per thread, into wo[1 + jh]
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.0f;
+    if (any_rot) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float* oh = &sm.ohist[h][64 * jh + 4 * e];
+        acc = fmaf(oh[0], rrow[e].x, acc);
+        acc = fmaf(oh[1], rrow[e].y, acc);
+        acc = fmaf(oh[2], rrow[e].z, acc);
+        acc = fmaf(oh[3], rrow[e].w, acc);
+      }
+    }
+    sm.wo[1 + jh][h][ri] = acc;
+  }
+  __syncthreads();
+  // E: normalise and store
+  for (int idx = tid; idx < G * kD; idx += 256) {
+    const int h = idx / kD, i = idx % kD;
+    out[(size_t)h * kD + i] = (plain[idx] + sm.wo[1][h][i] + sm.wo[2][h][i]) / sm.lsum[h];
   }
 }
 

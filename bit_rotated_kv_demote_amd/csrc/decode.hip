@@ -52,9 +52,24 @@ struct alignas(16) DecodeSmem : SplitSmem<G> {
 // Per-wave partial of a history split: pages [pg_begin, pg_end) of the
 // sequence's history (hist_len valid tokens).
 // ---------------------------------------------------------------------------
+// Loads of one page pair for a wave: codes (16 B per lane per page) and
+// scale/zero metadata (8 B per lane per page).
+__device__ __forceinline__ void issue_pair(const DecodeArgs& a, const int32_t* pt_row, int hk, int pg_begin,
+                                           int pg_end, int pr, int lane, u32x4_t* c, u32x2_t* md) {
+  const int pg0 = pg_begin + 2 * pr;
+  const int pg1 = (pg0 + 1 < pg_end) ? pg0 + 1 : pg0;
+  const uint8_t* b0 = a.hist + ((size_t)pt_row[pg0] * a.hkv + hk) * kBlock;
+  const uint8_t* b1 = a.hist + ((size_t)pt_row[pg1] * a.hkv + hk) * kBlock;
+  c[0] = *reinterpret_cast<const u32x4_t*>(b0 + 16 * lane);
+  c[1] = *reinterpret_cast<const u32x4_t*>(b1 + 16 * lane);
+  md[0] = *reinterpret_cast<const u32x2_t*>(b0 + 1024 + 8 * lane);
+  md[1] = *reinterpret_cast<const u32x2_t*>(b1 + 1024 + 8 * lane);
+}
+
 template <int G>
 __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int slot, int hk, int hist_len,
-                          int pg_begin, int pg_end, int wave, int lane) {
+                          int pg_begin, int pg_end, int wave, int lane, const u32x4_t* c_first,
+                          const u32x2_t* m_first, const u32x4_t* c_second, const u32x2_t* m_second) {
   const int x = lane & 15, qa = lane >> 4;
   const int col_head = x < G ? x : (x < 2 * G ? x - G : -1);
   // ---- score operands: q' in fp16 hi (columns 0..G-1) and lo (G..2G-1)
@@ -89,32 +104,19 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int slot, int 
   const int npairs = (pg_end - pg_begin + 1) >> 1;
   uint8_t* mbuf = &sm.meta[wave][0][0];
 
-  auto block_ptr = [&](int pg) -> const uint8_t* {
-    const int page = pt_row[pg];
-    return a.hist + ((size_t)page * a.hkv + hk) * kBlock;
-  };
-  // prefetch ring: codes (16 B per lane per page) and metadata (8 B per lane per page)
-  u32x4_t c_cur[2], c_nxt[2];
-  u32x2_t m_cur[2], m_nxt[2];
-  auto issue = [&](int pr, u32x4_t* c, u32x2_t* md) {
-    const int pg0 = pg_begin + 2 * pr;
-    const int pg1 = (pg0 + 1 < pg_end) ? pg0 + 1 : pg0;
-    const uint8_t* b0 = block_ptr(pg0);
-    const uint8_t* b1 = block_ptr(pg1);
-    c[0] = *reinterpret_cast<const u32x4_t*>(b0 + 16 * lane);
-    c[1] = *reinterpret_cast<const u32x4_t*>(b1 + 16 * lane);
-    md[0] = *reinterpret_cast<const u32x2_t*>(b0 + 1024 + 8 * lane);
-    md[1] = *reinterpret_cast<const u32x2_t*>(b1 + 1024 + 8 * lane);
-  };
+  // three-stage prefetch ring: while pair pr is processed, pairs pr + 4 and
+  // pr + 8 of this wave are in flight (the first two were issued before the
+  // prologue)
+  u32x4_t cA[2] = {c_first[0], c_first[1]}, cB[2] = {c_second[0], c_second[1]}, cC[2];
+  u32x2_t mA[2] = {m_first[0], m_first[1]}, mB[2] = {m_second[0], m_second[1]}, mC[2];
+  auto issue = [&](int pr_, u32x4_t* c, u32x2_t* md) { issue_pair(a, pt_row, hk, pg_begin, pg_end, pr_, lane, c, md); };
   int pr = wave;
-  if (pr < npairs) issue(pr, c_cur, m_cur);
-  for (; pr < npairs; pr += 4) {
+  auto body = [&](const u32x4_t* c_cur, const u32x2_t* m_cur) __attribute__((always_inline)) {
     const int pg0 = pg_begin + 2 * pr;
     const bool has1 = pg0 + 1 < pg_end;
     // stage this pair's metadata in LDS (wave-private)
     *reinterpret_cast<u32x2_t*>(mbuf + 8 * lane) = m_cur[0];
     *reinterpret_cast<u32x2_t*>(mbuf + 512 + 8 * lane) = m_cur[1];
-    if (pr + 4 < npairs) issue(pr + 4, c_nxt, m_nxt);
     __builtin_amdgcn_wave_barrier();
 
     // valid tokens of the pair: token t of page p is history index 16 (pg0 + p) + t
@@ -264,8 +266,23 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int slot, int 
       bz32[0] = pp[0]; bz32[1] = pp[1]; bz32[2] = pp[2]; bz32[3] = pp[3];
       acc_z = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, acc_z, 0, 0, 0);
     }
-    c_cur[0] = c_nxt[0]; c_cur[1] = c_nxt[1];
-    m_cur[0] = m_nxt[0]; m_cur[1] = m_nxt[1];
+  };
+  // The prefetch is issued unconditionally (past the end it re-reads this
+  // wave's last pair, an L2 hit) so that every body sees the same number of
+  // loads in flight and waits only for its own pair's.
+  const int last_pr = npairs > wave ? wave + ((npairs - 1 - wave) / 4) * 4 : wave;
+  while (pr < npairs) {
+    issue(min(pr + 8, last_pr), cC, mC);
+    body(cA, mA);
+    pr += 4;
+    if (pr >= npairs) break;
+    issue(min(pr + 8, last_pr), cA, mA);
+    body(cB, mB);
+    pr += 4;
+    if (pr >= npairs) break;
+    issue(min(pr + 8, last_pr), cB, mB);
+    body(cC, mC);
+    pr += 4;
   }
   // ---- wave epilogue: true-unit rotated outputs to LDS
   l_run = rows_sum(l_run);
@@ -328,49 +345,70 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
                       [&](int uu) { return row(a.sink_k, a.recent_k, uu); },
                       [&](int uu) { return row(a.sink_v, a.recent_v, uu); }, sm, wave, lane);
   } else {
-    // q -> LDS, q' = q . R_K, scale exponents and group sums
-    const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
-    for (int idx = tid; idx < G * kD; idx += 256) sm.q[idx / kD][idx % kD] = bf16_bits_to_float(qg[idx]);
-    __syncthreads();
-    {
-      const int j = tid & (kD - 1), hh = tid >> 7;
-      float acc[(G + 1) / 2];
-#pragma unroll
-      for (int e = 0; e < (G + 1) / 2; ++e) acc[e] = 0.0f;
-#pragma unroll 8
-      for (int i = 0; i < kD; ++i) {
-        const float r = a.rot_k[i * kD + j];
-#pragma unroll
-        for (int e = 0; e < (G + 1) / 2; ++e) {
-          const int h = hh + 2 * e;
-          if (h < G) acc[e] = fmaf(sm.q[h][i], r, acc[e]);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < (G + 1) / 2; ++e) {
-        const int h = hh + 2 * e;
-        if (h < G) sm.qr[h][j] = acc[e];
-      }
-    }
-    __syncthreads();
-    {
-      for (int h = wave; h < G; h += 4) {
-        const float v0 = sm.qr[h][lane], v1 = sm.qr[h][lane + 64];
-        const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1))) * kC0;
-        int e2 = 0;
-        frexpf(amax, &e2);
-        const int s_exp = amax > 0.0f ? min(15 - e2, 100) : 0;
-        // group sums: lanes 0..31 hold channels of groups 0 (v0) and 2 (v1), lanes 32..63 groups 1 and 3
-        float g0 = v0, g1 = v1;
-        for (int m = 16; m >= 1; m >>= 1) { g0 += __shfl_xor(g0, m); g1 += __shfl_xor(g1, m); }
-        if (lane == 0) { sm.sexp[h] = (float)s_exp; sm.qs[h][0] = g0; sm.qs[h][2] = g1; }
-        if (lane == 32) { sm.qs[h][1] = g0; sm.qs[h][3] = g1; }
-      }
-    }
-    __syncthreads();
     const int pg_begin = hs * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);
-    hist_wave<G>(a, sm, slot, hk, hist_len, pg_begin, pg_end, wave, lane);
+    const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
+    // q . R_K operands first (thread (j, hh) takes rows [64 hh, 64 hh + 64) of
+    // column j), then this wave's first two page pairs: the prologue waits
+    // only for the older loads, so the loop is entered with exactly the page
+    // loads in flight that every later iteration also has.
+    const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
+    const int j = tid & (kD - 1), hh = tid >> 7;
+    float rcol[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) rcol[e] = a.rot_k[(64 * hh + e) * kD + j];
+    constexpr int kQPer = (G * kD + 255) / 256;
+    uint16_t qv[kQPer];
+#pragma unroll
+    for (int e = 0; e < kQPer; ++e) qv[e] = (tid + 256 * e < G * kD) ? qg[tid + 256 * e] : (uint16_t)0;
+    u32x4_t c_first[2] = {}, c_second[2] = {};
+    u32x2_t m_first[2] = {}, m_second[2] = {};
+    const int npairs = (pg_end - pg_begin + 1) / 2;
+    // unconditional, clamped to a valid pair of this split (npairs >= 1): the
+    // same loads are in flight on every path into the loop
+    // (kept in the loop's per-pair issue order, so the wait counts the loop
+    // computes for its first iteration are exact)
+    issue_pair(a, pt_row, hk, pg_begin, pg_end, min(wave, npairs - 1), lane, c_first, m_first);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_pair(a, pt_row, hk, pg_begin, pg_end, min(wave + 4, npairs - 1), lane, c_second, m_second);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < kQPer; ++e) {
+      const int idx = tid + 256 * e;
+      if (idx < G * kD) sm.q[idx / kD][idx % kD] = bf16_bits_to_float(qv[e]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e4 = 0; e4 < 16; ++e4) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&sm.q[h][64 * hh + 4 * e4]);
+        acc = fmaf(q4.x, rcol[4 * e4], acc);
+        acc = fmaf(q4.y, rcol[4 * e4 + 1], acc);
+        acc = fmaf(q4.z, rcol[4 * e4 + 2], acc);
+        acc = fmaf(q4.w, rcol[4 * e4 + 3], acc);
+      }
+      sm.wo[hh][h][j] = acc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * kD; idx += 256)
+      sm.qr[idx / kD][idx % kD] = sm.wo[0][idx / kD][idx % kD] + sm.wo[1][idx / kD][idx % kD];
+    __syncthreads();
+    for (int h = wave; h < G; h += 4) {
+      const float v0 = sm.qr[h][lane], v1 = sm.qr[h][lane + 64];
+      const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1))) * kC0;
+      int e2 = 0;
+      frexpf(amax, &e2);
+      const int s_exp = amax > 0.0f ? min(15 - e2, 100) : 0;
+      // group sums: lanes 0..31 hold groups 0 (v0) and 2 (v1), lanes 32..63 groups 1 and 3
+      float g0 = v0, g1 = v1;
+      for (int m = 16; m >= 1; m >>= 1) { g0 += __shfl_xor(g0, m); g1 += __shfl_xor(g1, m); }
+      if (lane == 0) { sm.sexp[h] = (float)s_exp; sm.qs[h][0] = g0; sm.qs[h][2] = g1; }
+      if (lane == 32) { sm.qs[h][1] = g0; sm.qs[h][3] = g1; }
+    }
+    __syncthreads();
+    hist_wave<G>(a, sm, slot, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first, c_second, m_second);
   }
   float* rec = part_base + (size_t)split * G * kPartStride;
   store_split<G>(sm, rec, tid);

@@ -83,18 +83,22 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int r = (p - kSink) & (kRecent - 1);
   uint16_t* ring = (is_v ? a.recent_v : a.recent_k) + (((size_t)slot * a.hkv + hk) * kRecent + r) * kD;
   if (p >= kSink + kRecent) {
+    // y_j = sum_i x_i R[i][j]; thread (j, half) covers i in [64 half, 64 half + 64).
+    // Its 64 R values are requested together with the ring slot.
+    const float* R = is_v ? a.rot_v : a.rot_k;
+    const int j = tid & (kD - 1), half = tid >> 7;
+    float rc[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) rc[e] = R[(64 * half + e) * kD + j];
     if (tid < kD / 2) {
       const uint32_t w = reinterpret_cast<const uint32_t*>(ring)[tid];
       xs[2 * tid] = bf16_bits_to_float(w & 0xFFFFu);
       xs[2 * tid + 1] = bf16_bits_to_float(w >> 16);
     }
     __syncthreads();
-    // y_j = sum_i x_i R[i][j]; thread (j, half) covers i in [64 half, 64 half + 64).
-    const float* R = is_v ? a.rot_v : a.rot_k;
-    const int j = tid & (kD - 1), half = tid >> 7;
     float acc = 0.0f;
-#pragma unroll 16
-    for (int i = 64 * half; i < 64 * half + 64; ++i) acc = fmaf(xs[i], R[i * kD + j], acc);
+#pragma unroll
+    for (int e = 0; e < 64; ++e) acc = fmaf(xs[64 * half + e], rc[e], acc);
     part[half][j] = acc;
     __syncthreads();  // also orders the ring read above before the overwrite below
     const float* tau = is_v ? a.clip_v : a.clip_k;
