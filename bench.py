@@ -252,7 +252,43 @@ def run_demote(torch, reps, seed):
     return dict(us=us, tok_per_s=tokens / (us * 1e-6), gbps=nbytes / (us * 1e3), tokens=tokens, bytes=nbytes)
 
 
-def cpu_baseline(hq, hkv, n0, host, seed, kv_sample=8):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int2_qwen3-4b_32k_traffic.md")
+
+
+def kernel_source_digest():
+    """Digest of the device sources and build flags of the library; a counter
+    summary taken on other sources no longer describes the kernel."""
+    import hashlib
+    from bit_rotated_kv_demote_amd import build
+    h = hashlib.sha256(" ".join(build.DEVICE_FLAGS).encode())
+    csrc = os.path.join(ROOT, "bit_rotated_kv_demote_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary (FETCH_SIZE
+    + WRITE_SIZE, scaled by the copy-kernel calibration), or None when the
+    summary is missing or was taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    block = text.split("```json", 1)[-1].split("```", 1)[0] if "```json" in text else ""
+    try:
+        rec = json.loads(block)
+    except ValueError:
+        return None
+    if rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(hq, hkv, n0, host, seed, kv_sample=8, min_seconds=10.0):
     """The oracle, as it stands, on a bounded sample of the same step."""
     import oracle as orc
     from bit_rotated_kv_demote_amd import synth
@@ -277,14 +313,21 @@ def cpu_baseline(hq, hkv, n0, host, seed, kv_sample=8):
     pool.length[0] = n0
     q = synth.queries(synth.streams(seed)["q"], (1, hq, 128))
     g = hq // hkv
+    # successive steps (append token n, decode at length n + 1) until about
+    # min_seconds of CPU work, at most len(k) - n0 steps
     t0 = time.time()
-    pool.append(0, k[n0], v[n0], rot_k, rot_v, tau_k, tau_v)
-    orc.decode_tiered(q, pool, [0], [n0 + 1], rot_k, rot_v, heads=[(0, hh) for hh in range(kv_sample * g)])
+    n_steps = 0
+    while n_steps < len(k) - n0 and (n_steps == 0 or time.time() - t0 < min_seconds):
+        n = n0 + n_steps
+        pool.append(0, k[n], v[n], rot_k, rot_v, tau_k, tau_v)
+        orc.decode_tiered(q, pool, [0], [n + 1], rot_k, rot_v, heads=[(0, hh) for hh in range(kv_sample * g)])
+        n_steps += 1
     secs = time.time() - t0
-    scaled_us = secs * 1e6 * hkv / kv_sample
+    scaled_us = secs * 1e6 / n_steps * hkv / kv_sample
     return {"value": round(scaled_us, 1), "unit": "us/step", "cores": int(blas), "kind": "oracle",
-            "sample": f"one append (all {hkv} KV heads) + decode of {kv_sample} of {hkv} KV heads "
-                      f"({kv_sample * g} q heads) at {n0 + 1} tokens, {secs:.2f} s, scaled x{hkv // kv_sample}"}
+            "sample": f"{n_steps} successive steps, each one append (all {hkv} KV heads) + decode of {kv_sample} of "
+                      f"{hkv} KV heads ({kv_sample * g} q heads) from {n0 + 1} tokens, {secs:.1f} s in total"
+                      + (f", scaled x{hkv / kv_sample:g}" if kv_sample != hkv else "")}
 
 
 def main():
@@ -337,9 +380,12 @@ def main():
         extra["demote_GBps"] = round(d["gbps"], 1)
         extra["demote_workload"] = "16 sequences x 4096-token chunk, 8 KV heads, K+V, bf16 in, MFMA rotation"
     if args.copy_probe_mb:
-        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
+        # a plain streaming kernel of known size (reads and writes n bytes once):
+        # the counter calibration for the traffic figure
+        src = torch.ones((args.copy_probe_mb << 20) // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu:
@@ -362,10 +408,11 @@ def main():
                                "64 bf16 sink / int2 history / 256 bf16 recent, 16-token pages",
                    "global_batch": 1, "seq_len": n0, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "extra": extra,
     }
+    extra["source_digest"] = kernel_source_digest()
     print(json.dumps(line))
 
 
