@@ -35,6 +35,11 @@ __device__ __forceinline__ float rows_sum(float v) {
   const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
+// v(lane) + v(lane ^ 32)
+__device__ __forceinline__ float half_swap_sum(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
 __device__ __forceinline__ float wave_max(float v) {
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
@@ -44,24 +49,34 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Split records cross workgroups (and XCDs, each with its own L2): they are
-// written and read only with device-scope relaxed atomic accesses, which the
-// hardware keeps coherent across L2s without whole-cache writeback or
-// invalidation.  A workgroup's record is complete once every thread has
-// waited for its stores (s_waitcnt), which precedes the ticket below.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Split records cross workgroups (and XCDs, each with its own L2).  They are
+// written and read through buffer instructions with the device-scope cache
+// policy (sc1), which the hardware keeps coherent across L2s without
+// whole-cache writeback or invalidation.  A workgroup's record is complete
+// once every thread has waited for its stores (s_waitcnt), which precedes the
+// ticket below.  Buffer accesses outside the resource's byte range read 0 and
+// write nothing.
+constexpr int kCachePolicyDevice = 16;          // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
+  const u32x4_t w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, kCachePolicyDevice);
 }
-__device__ __forceinline__ float4 ld_dev4(const float* p) {
-  unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float*>(p));
-  const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return make_float4(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
-                     __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32)));
+__device__ __forceinline__ void st_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b) {
+  const u32x2_t w = {__float_as_uint(a), __float_as_uint(b)};
+  __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, kCachePolicyDevice);
 }
+__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyDevice);
+  return make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3]));
+}
+__device__ __forceinline__ float2 ld_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCachePolicyDevice);
+  return make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;   // a byte offset past every resource: reads 0
 
 template <int G>
 struct alignas(16) SplitSmem {
@@ -71,7 +86,8 @@ struct alignas(16) SplitSmem {
   float wo[4][G][kD];        // per-wave unnormalised outputs
   float mw[G][kMaxSplits];   // merge: per-split weights
   float ohist[G][kD];        // merge: rotated part
-  float mred[2048];          // merge: per-part sums [parts][2][G*128] (parts * G * 128 == 1024)
+  // merge: split sums l [G][kMaxSplits], then per-part sums [parts][2][G*128] (parts * G * 128 == 1024)
+  float mred[G * kMaxSplits > 2048 ? G * kMaxSplits : 2048];
   float lsum[G];
   int last;
 };
@@ -177,26 +193,28 @@ __device__ void bf16_span_wave(const uint16_t* qg, int count, RowK rowk, RowV ro
 }
 
 // Combine the four waves' partials of a workgroup into its split record
-// rec[h * kPartStride + (0..127 acc, 128 m, 129 l)].
+// rec[h * kPartStride + (0..127 acc, 128 m, 129 l)] (16-byte stores).
 template <int G>
 __device__ void store_split(SplitSmem<G>& sm, float* rec, int tid) {
   __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += 256) {
-    const int h = idx / kD, j = idx % kD;
+  const auto r = dev_rsrc(rec, G * kPartStride * 4);
+  for (int c = tid; c < G * kD / 4; c += 256) {
+    const int h = c / (kD / 4), j4 = c % (kD / 4);
     float mm = kMInit;
 #pragma unroll
     for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sm.wm[w][h]);
-    float acc = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float ll = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) acc = fmaf(__builtin_amdgcn_exp2f(sm.wm[w][h] - mm), sm.wo[w][h][j], acc);
-    st_dev(&rec[h * kPartStride + j], acc);
-    if (j == 0) {
-      float ll = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) ll = fmaf(__builtin_amdgcn_exp2f(sm.wm[w][h] - mm), sm.wl[w][h], ll);
-      st_dev(&rec[h * kPartStride + kD], mm);
-      st_dev(&rec[h * kPartStride + kD + 1], ll);
+    for (int w = 0; w < 4; ++w) {
+      const float f = __builtin_amdgcn_exp2f(sm.wm[w][h] - mm);
+      const float4 o = *reinterpret_cast<const float4*>(&sm.wo[w][h][4 * j4]);
+      acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);
+      acc.z = fmaf(f, o.z, acc.z); acc.w = fmaf(f, o.w, acc.w);
+      ll = fmaf(f, sm.wl[w][h], ll);
     }
+    st_dev4(r, 4u * (h * kPartStride + 4 * j4), acc);
+    if (j4 == 0) st_dev2(r, 4u * (h * kPartStride + kD), mm, ll);
   }
 }
 
@@ -214,16 +232,41 @@ __device__ bool finish_ticket(SplitSmem<G>& sm, uint32_t* counter, uint32_t targ
   return sm.last != 0;
 }
 
-// LSE merge of n_act split records of one group.  Records k < n_plain are in
-// the output space; the others are in the rotated space and are summed, then
-// rotated back with R^T ((y R^T)_i = sum_j y_j R[i][j]).  out: [G][128] fp32.
-// Each phase issues its loads together: the merge runs after the rest of the
-// grid has drained, so its latency is the kernel's tail.
+// LSE merge of n_act split records of one group (part_bytes: the group's
+// record area).  Records k < n_plain are in the output space; the others are
+// in the rotated space and are summed, then rotated back with R^T
+// ((y R^T)_i = sum_j y_j R[i][j]).  out: [G][128] fp32.
+// The merge runs after the rest of the grid has drained, so its latency is
+// the kernel's tail: every load is issued up front, in the order the phases
+// consume them ((m, l) pairs, record columns, rows of R), and out-of-range
+// slots read 0 instead of branching.
 template <int G, class SplitId>
-__device__ void merge_group(SplitSmem<G>& sm, const float* part_base, int n_act, int n_plain, SplitId split_id,
-                            const float* rot, float* out, int tid, int wave, int lane) {
+__device__ void merge_group(SplitSmem<G>& sm, const float* part_base, uint32_t part_bytes, int n_act, int n_plain,
+                            SplitId split_id, const float* rot, float* out, int tid, int wave, int lane) {
   const bool any_rot = n_act > n_plain;
-  // this thread's slice of R for phase D: row ri, columns [64 jh, 64 jh + 64)
+  const auto rsrc = dev_rsrc(part_base, part_bytes);
+  // (m, l) of every (split, head): slot idx = k * G + h
+  constexpr int kMl = (kMaxSplits * G + 255) / 256;
+  float2 ml[kMl];
+#pragma unroll
+  for (int r = 0; r < kMl; ++r) {
+    const int idx = tid + 256 * r, k = idx / G, h = idx % G;
+    ml[r] = ld_dev2(rsrc, idx < n_act * G ? 4u * ((split_id(k) * G + h) * kPartStride + kD) : kOutOfRange);
+  }
+  // record columns: thread (col, part) takes the float4 column col of splits
+  // k = part, part + kParts, ...
+  constexpr int kCols = G * kD / 4;
+  constexpr int kParts = 256 / kCols;
+  constexpr int kBatch = 16;
+  const int col = tid % kCols, part = tid / kCols;
+  const int ch = col / (kD / 4), j4 = col % (kD / 4);
+  auto rec_off = [&](int k) -> uint32_t {
+    return k < n_act ? 4u * ((split_id(k) * G + ch) * kPartStride + 4 * j4) : kOutOfRange;
+  };
+  float4 v[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) v[u] = ld_dev4(rsrc, rec_off(part + u * kParts));
+  // this thread's slice of R for the inverse rotation: row ri, columns [64 jh, 64 jh + 64)
   const int ri = tid & (kD - 1), jh = tid >> 7;
   float4 rrow[16];
   if (any_rot) {
@@ -231,46 +274,26 @@ __device__ void merge_group(SplitSmem<G>& sm, const float* part_base, int n_act,
 #pragma unroll
     for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
   }
-  // B0: this thread's record loads (float4 column of one head, split residue
-  // class), issued before the weights are known
-  constexpr int kCols = G * kD / 4;
-  constexpr int kParts = 256 / kCols;
-  constexpr int kBatch = 16;
-  const int col = tid % kCols, part = tid / kCols;
-  const int ch = col / (kD / 4), j4 = col % (kD / 4);
-  float4 v[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int k = part + u * kParts;
-    v[u] = k < n_act ? ld_dev4(&part_base[((size_t)split_id(k) * G + ch) * kPartStride + 4 * j4])
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   // A: per-head global max, split weights and the total sum
-  for (int h = wave; h < G; h += 4) {
-    float mk[(kMaxSplits + 63) / 64], lk[(kMaxSplits + 63) / 64];
-    float mm = kMInit;
+  float* lbuf = sm.mred;     // l values [G][kMaxSplits], consumed before phase B reuses mred
 #pragma unroll
-    for (int r = 0; r < (kMaxSplits + 63) / 64; ++r) {
-      const int k = lane + 64 * r;
-      mk[r] = kMInit;
-      lk[r] = 0.0f;
-      if (k < n_act) {
-        const float* rp = &part_base[((size_t)split_id(k) * G + h) * kPartStride + kD];
-        mk[r] = ld_dev(rp);
-        lk[r] = ld_dev(rp + 1);
-      }
-      mm = fmaxf(mm, mk[r]);
+  for (int r = 0; r < kMl; ++r) {
+    const int idx = tid + 256 * r, k = idx / G, h = idx % G;
+    if (idx < n_act * G) {
+      sm.mw[h][k] = ml[r].x;
+      lbuf[h * kMaxSplits + k] = ml[r].y;
     }
+  }
+  __syncthreads();
+  for (int h = wave; h < G; h += 4) {
+    float mm = kMInit;
+    for (int k = lane; k < n_act; k += 64) mm = fmaxf(mm, sm.mw[h][k]);
     mm = wave_max(mm);
     float ll = 0.0f;
-#pragma unroll
-    for (int r = 0; r < (kMaxSplits + 63) / 64; ++r) {
-      const int k = lane + 64 * r;
-      if (k < n_act) {
-        const float wk = __builtin_amdgcn_exp2f(mk[r] - mm);
-        sm.mw[h][k] = wk;
-        ll = fmaf(wk, lk[r], ll);
-      }
+    for (int k = lane; k < n_act; k += 64) {
+      const float wk = __builtin_amdgcn_exp2f(sm.mw[h][k] - mm);
+      sm.mw[h][k] = wk;
+      ll = fmaf(wk, lbuf[h * kMaxSplits + k], ll);
     }
     ll = wave_sum(ll);
     if (lane == 0) sm.lsum[h] = ll;
@@ -292,17 +315,14 @@ __device__ void merge_group(SplitSmem<G>& sm, const float* part_base, int n_act,
     }
     for (int k0 = part + kBatch * kParts; k0 < n_act; k0 += kBatch * kParts) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int k = k0 + u * kParts;
-        v[u] = k < n_act ? ld_dev4(&part_base[((size_t)split_id(k) * G + ch) * kPartStride + 4 * j4])
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int u = 0; u < kBatch; ++u) v[u] = ld_dev4(rsrc, rec_off(k0 + u * kParts));
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int k = k0 + u * kParts;
         if (k < n_act) acc_into(k, v[u]);
       }
     }
+    __syncthreads();   // every l value has been read before mred is reused
     reinterpret_cast<float4*>(&sm.mred[(part * 2 + 0) * G * kD])[col] = ap;
     reinterpret_cast<float4*>(&sm.mred[(part * 2 + 1) * G * kD])[col] = ar;
   }
@@ -327,11 +347,11 @@ __device__ void merge_group(SplitSmem<G>& sm, const float* part_base, int n_act,
     if (any_rot) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float* oh = &sm.ohist[h][64 * jh + 4 * e];
-        acc = fmaf(oh[0], rrow[e].x, acc);
-        acc = fmaf(oh[1], rrow[e].y, acc);
-        acc = fmaf(oh[2], rrow[e].z, acc);
-        acc = fmaf(oh[3], rrow[e].w, acc);
+        const float4 oh = *reinterpret_cast<const float4*>(&sm.ohist[h][64 * jh + 4 * e]);
+        acc = fmaf(oh.x, rrow[e].x, acc);
+        acc = fmaf(oh.y, rrow[e].y, acc);
+        acc = fmaf(oh.z, rrow[e].z, acc);
+        acc = fmaf(oh.w, rrow[e].w, acc);
       }
     }
     sm.wo[1 + jh][h][ri] = acc;

@@ -53,13 +53,16 @@ struct alignas(16) DecodeSmem : SplitSmem<G> {
 // sequence's history (hist_len valid tokens).
 // ---------------------------------------------------------------------------
 // Loads of one page pair for a wave: codes (16 B per lane per page) and
-// scale/zero metadata (8 B per lane per page).
-__device__ __forceinline__ void issue_pair(const DecodeArgs& a, const int32_t* pt_row, int hk, int pg_begin,
-                                           int pg_end, int pr, int lane, u32x4_t* c, u32x2_t* md) {
-  const int pg0 = pg_begin + 2 * pr;
-  const int pg1 = (pg0 + 1 < pg_end) ? pg0 + 1 : pg0;
-  const uint8_t* b0 = a.hist + ((size_t)pt_row[pg0] * a.hkv + hk) * kBlock;
-  const uint8_t* b1 = a.hist + ((size_t)pt_row[pg1] * a.hkv + hk) * kBlock;
+// scale/zero metadata (8 B per lane per page).  ids: this wave's page ids,
+// lane 2k + i holding page 2 (wave + 4k) + i of the split (clamped to its
+// last page), so the k-th pair of the wave needs no memory access for its
+// page ids.
+__device__ __forceinline__ void issue_pair(const DecodeArgs& a, int32_t ids, int hk, int k, int lane,
+                                           u32x4_t* c, u32x2_t* md) {
+  const int p0 = __builtin_amdgcn_readlane(ids, 2 * k);
+  const int p1 = __builtin_amdgcn_readlane(ids, 2 * k + 1);
+  const uint8_t* b0 = a.hist + ((size_t)p0 * a.hkv + hk) * kBlock;
+  const uint8_t* b1 = a.hist + ((size_t)p1 * a.hkv + hk) * kBlock;
   c[0] = *reinterpret_cast<const u32x4_t*>(b0 + 16 * lane);
   c[1] = *reinterpret_cast<const u32x4_t*>(b1 + 16 * lane);
   md[0] = *reinterpret_cast<const u32x2_t*>(b0 + 1024 + 8 * lane);
@@ -67,7 +70,7 @@ __device__ __forceinline__ void issue_pair(const DecodeArgs& a, const int32_t* p
 }
 
 template <int G>
-__device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int slot, int hk, int hist_len,
+__device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, int hk, int hist_len,
                           int pg_begin, int pg_end, int wave, int lane, const u32x4_t* c_first,
                           const u32x2_t* m_first, const u32x4_t* c_second, const u32x2_t* m_second) {
   const int x = lane & 15, qa = lane >> 4;
@@ -100,7 +103,6 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int slot, int 
   float4_t acc_z = (float4_t){0.f, 0.f, 0.f, 0.f};
   float m_run = kMInit, l_run = 0.0f;
 
-  const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
   const int npairs = (pg_end - pg_begin + 1) >> 1;
   uint8_t* mbuf = &sm.meta[wave][0][0];
 
@@ -109,7 +111,7 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int slot, int 
   // prologue)
   u32x4_t cA[2] = {c_first[0], c_first[1]}, cB[2] = {c_second[0], c_second[1]}, cC[2];
   u32x2_t mA[2] = {m_first[0], m_first[1]}, mB[2] = {m_second[0], m_second[1]}, mC[2];
-  auto issue = [&](int pr_, u32x4_t* c, u32x2_t* md) { issue_pair(a, pt_row, hk, pg_begin, pg_end, pr_, lane, c, md); };
+  auto issue = [&](int pr_, u32x4_t* c, u32x2_t* md) { issue_pair(a, ids, hk, (pr_ - wave) >> 2, lane, c, md); };
   int pr = wave;
   auto body = [&](const u32x4_t* c_cur, const u32x2_t* m_cur) __attribute__((always_inline)) {
     const int pg0 = pg_begin + 2 * pr;
@@ -348,29 +350,31 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
     const int pg_begin = hs * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);
     const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
-    // q . R_K operands first (thread (j, hh) takes rows [64 hh, 64 hh + 64) of
-    // column j), then this wave's first two page pairs: the prologue waits
-    // only for the older loads, so the loop is entered with exactly the page
-    // loads in flight that every later iteration also has.
+    // page ids of this wave's pairs (pairs wave, wave + 4, ...): one load per lane
+    const int32_t ids = pt_row[pg_begin + min(2 * (wave + 4 * (lane >> 1)) + (lane & 1), pg_end - pg_begin - 1)];
+    // q . R_K operands first (thread (c4, rs) takes output columns
+    // [4 c4, 4 c4 + 4) and rows [16 rs, 16 rs + 16) of R_K: 16 float4 loads),
+    // then this wave's first two page pairs: the prologue waits only for the
+    // older loads, so the loop is entered with exactly the page loads in
+    // flight that every later iteration also has.
     const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
-    const int j = tid & (kD - 1), hh = tid >> 7;
-    float rcol[64];
+    const int c4 = tid & 31, rs = tid >> 5;
+    float4 rq[16];
 #pragma unroll
-    for (int e = 0; e < 64; ++e) rcol[e] = a.rot_k[(64 * hh + e) * kD + j];
+    for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(a.rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
     constexpr int kQPer = (G * kD + 255) / 256;
     uint16_t qv[kQPer];
 #pragma unroll
-    for (int e = 0; e < kQPer; ++e) qv[e] = (tid + 256 * e < G * kD) ? qg[tid + 256 * e] : (uint16_t)0;
+    for (int e = 0; e < kQPer; ++e) qv[e] = qg[min(tid + 256 * e, G * kD - 1)];   // unconditional
     u32x4_t c_first[2] = {}, c_second[2] = {};
     u32x2_t m_first[2] = {}, m_second[2] = {};
-    const int npairs = (pg_end - pg_begin + 1) / 2;
-    // unconditional, clamped to a valid pair of this split (npairs >= 1): the
-    // same loads are in flight on every path into the loop
+    // unconditional (the ids are clamped to pages of this split): the same
+    // loads are in flight on every path into the loop
     // (kept in the loop's per-pair issue order, so the wait counts the loop
     // computes for its first iteration are exact)
-    issue_pair(a, pt_row, hk, pg_begin, pg_end, min(wave, npairs - 1), lane, c_first, m_first);
+    issue_pair(a, ids, hk, 0, lane, c_first, m_first);
     __builtin_amdgcn_sched_barrier(0);
-    issue_pair(a, pt_row, hk, pg_begin, pg_end, min(wave + 4, npairs - 1), lane, c_second, m_second);
+    issue_pair(a, ids, hk, 1, lane, c_second, m_second);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {
@@ -378,22 +382,35 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
       if (idx < G * kD) sm.q[idx / kD][idx % kD] = bf16_bits_to_float(qv[e]);
     }
     __syncthreads();
+    // lanes l and l + 32 of a wave hold row slices 2 wave and 2 wave + 1 of
+    // the same columns: add them with one lane swap, then sum the four waves
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float acc = 0.0f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int e4 = 0; e4 < 16; ++e4) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&sm.q[h][64 * hh + 4 * e4]);
-        acc = fmaf(q4.x, rcol[4 * e4], acc);
-        acc = fmaf(q4.y, rcol[4 * e4 + 1], acc);
-        acc = fmaf(q4.z, rcol[4 * e4 + 2], acc);
-        acc = fmaf(q4.w, rcol[4 * e4 + 3], acc);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&sm.q[h][16 * rs + 4 * e4]);
+        const float qe[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 r = rq[4 * e4 + i];
+          acc.x = fmaf(qe[i], r.x, acc.x);
+          acc.y = fmaf(qe[i], r.y, acc.y);
+          acc.z = fmaf(qe[i], r.z, acc.z);
+          acc.w = fmaf(qe[i], r.w, acc.w);
+        }
       }
-      sm.wo[hh][h][j] = acc;
+      acc.x = half_swap_sum(acc.x);
+      acc.y = half_swap_sum(acc.y);
+      acc.z = half_swap_sum(acc.z);
+      acc.w = half_swap_sum(acc.w);
+      if (lane < 32) *reinterpret_cast<float4*>(&sm.wo[wave][h][4 * c4]) = acc;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * kD; idx += 256)
-      sm.qr[idx / kD][idx % kD] = sm.wo[0][idx / kD][idx % kD] + sm.wo[1][idx / kD][idx % kD];
+    for (int idx = tid; idx < G * kD; idx += 256) {
+      const int h = idx / kD, jj = idx % kD;
+      sm.qr[h][jj] = (sm.wo[0][h][jj] + sm.wo[1][h][jj]) + (sm.wo[2][h][jj] + sm.wo[3][h][jj]);
+    }
     __syncthreads();
     for (int h = wave; h < G; h += 4) {
       const float v0 = sm.qr[h][lane], v1 = sm.qr[h][lane + 64];
@@ -408,7 +425,7 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
       if (lane == 32) { sm.qs[h][1] = g0; sm.qs[h][3] = g1; }
     }
     __syncthreads();
-    hist_wave<G>(a, sm, slot, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first, c_second, m_second);
+    hist_wave<G>(a, sm, ids, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first, c_second, m_second);
   }
   float* rec = part_base + (size_t)split * G * kPartStride;
   store_split<G>(sm, rec, tid);
@@ -416,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
   // ---- completion ticket: the last workgroup of the group merges
   if (!finish_ticket<G>(sm, &a.counters[grp], (uint32_t)(act_tile + act_hist), tid)) return;
   // active splits: tile 0..act_tile-1 (unrotated), history n_tile_splits + 0..act_hist-1 (rotated)
-  merge_group<G>(sm, part_base, act_tile + act_hist, act_tile,
+  merge_group<G>(sm, part_base, (uint32_t)(n_split_total * G * kPartStride * 4), act_tile + act_hist, act_tile,
                  [&](int k) { return k < act_tile ? k : a.n_tile_splits + (k - act_tile); }, a.rot_v,
                  a.out + ((size_t)b * a.hkv * G + hk * G) * kD, tid, wave, lane);
   if (tid == 0) a.counters[grp] = 0u;
@@ -431,7 +448,9 @@ DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len) {
   long pps = (total_pages + 479) / 480;
   pps = ((pps + 7) / 8) * 8;
   if (pps < 8) pps = 8;
-  while (max_pages > 0 && (max_pages + pps - 1) / pps > kMaxSplits - 4) pps += 8;
+  if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
+  while (max_pages > 0 && (max_pages + pps - 1) / pps > kMaxSplits - 4 && pps < kMaxPagesPerSplit) pps += 8;
+  p.ok = max_pages == 0 || (max_pages + pps - 1) / pps <= kMaxSplits - 4;
   p.pages_per_split = (int)pps;
   p.n_hist_splits = max_pages > 0 ? (int)((max_pages + pps - 1) / pps) : 0;
   const int max_tile = min(max_seq_len, kSink + kRecent);

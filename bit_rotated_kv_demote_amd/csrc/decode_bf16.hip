@@ -35,13 +35,14 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeBf16Args a) {
   float* part_base = a.partials + (size_t)grp * a.n_splits * G * kPartStride;
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
   if (!finish_ticket<G>(sm, &a.counters[grp], (uint32_t)act, tid)) return;
-  merge_group<G>(sm, part_base, act, act, [](int k) { return k; }, nullptr,
+  merge_group<G>(sm, part_base, (uint32_t)(a.n_splits * G * kPartStride * 4), act, act, [](int k) { return k; }, nullptr,
                  a.out + ((size_t)b * a.hkv * G + hk * G) * kD, tid, wave, lane);
   if (tid == 0) a.counters[grp] = 0u;
 }
 
 DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len) {
   DecodePlan p{};
+  p.ok = true;
   const int max_pages = (max_seq_len + kPage - 1) / kPage;
   const long total_pages = (long)batch * hkv * max_pages;
   long pps = (total_pages + 479) / 480;

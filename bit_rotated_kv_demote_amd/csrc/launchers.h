@@ -97,7 +97,12 @@ struct DecodePlan {
   int grid;                   // padded to a multiple of 8 (one slice per XCD)
   size_t partial_floats;
   size_t workspace_bytes;
+  bool ok;                    // false: the context needs more splits than the merge holds
 };
+
+// INT2 decode: a history split covers at most this many pages (each wave
+// keeps the page ids of its pairs in one register: 32 pairs x 2 pages)
+constexpr int kMaxPagesPerSplit = 256;
 
 DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len);
 DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len);

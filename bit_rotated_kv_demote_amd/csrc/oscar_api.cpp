@@ -187,6 +187,7 @@ oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, 
   const int max_hist = max_seq_len - 320;
   if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
   const DecodePlan plan = plan_decode(batch, hkv, g, max_seq_len);
+  if (!plan.ok) return OSCAR_ERR_UNSUPPORTED;
   if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
