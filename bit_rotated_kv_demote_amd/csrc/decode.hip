@@ -37,6 +37,11 @@ __device__ __forceinline__ uint32_t field_pair(uint32_t w, uint32_t w6) {
 }
 __host__ __device__ constexpr int field_shift(int f) { return f <= 4 ? f : f - 3; }
 
+// A wave walks its share of a split in steps of kStepPages pages: wave w
+// takes steps w, w + 4, ...  While one step is processed the next one is in
+// flight.
+constexpr int kStepPages = 2;
+
 // Shared memory of one workgroup (256 threads = 4 waves).
 template <int G>
 struct alignas(16) DecodeSmem : SplitSmem<G> {
@@ -44,7 +49,7 @@ struct alignas(16) DecodeSmem : SplitSmem<G> {
   float qr[G][kD];           // q' = q . R_K
   float sexp[G];             // S_h: q' operands are scaled by 2^S_h
   float qs[G][kGroups];      // per-group sums of q'
-  uint8_t meta[4][2][512];   // per wave, two pages of scale/zero metadata
+  uint8_t meta[4][kStepPages][512];   // per wave, one step's scale/zero metadata
   float zs[4][kGroups][16];  // per-wave V zero-point accumulators
 };
 
@@ -52,30 +57,36 @@ struct alignas(16) DecodeSmem : SplitSmem<G> {
 // Per-wave partial of a history split: pages [pg_begin, pg_end) of the
 // sequence's history (hist_len valid tokens).
 // ---------------------------------------------------------------------------
-// Loads of one page pair for a wave: codes (16 B per lane per page) and
-// scale/zero metadata (8 B per lane per page).  ids: this wave's page ids,
-// lane 2k + i holding page 2 (wave + 4k) + i of the split (clamped to its
-// last page), so the k-th pair of the wave needs no memory access for its
-// page ids.
-__device__ __forceinline__ void issue_pair(const DecodeArgs& a, int32_t ids, int hk, int k, int lane,
+// Loads of one step for a wave: codes (16 B per lane per page) and
+// scale/zero metadata (8 B per lane per page), as buffer loads whose base is
+// the page block (scalar address arithmetic only).  ids: this wave's page
+// ids, lane kStepPages k + i holding page kStepPages (wave + 4k) + i of the
+// split (clamped to its last page), so the k-th step of the wave needs no
+// memory access for its page ids.
+__device__ __forceinline__ void issue_step(const DecodeArgs& a, int32_t ids, int hk, int k, int lane,
                                            u32x4_t* c, u32x2_t* md) {
-  const int p0 = __builtin_amdgcn_readlane(ids, 2 * k);
-  const int p1 = __builtin_amdgcn_readlane(ids, 2 * k + 1);
-  const uint8_t* b0 = a.hist + ((size_t)p0 * a.hkv + hk) * kBlock;
-  const uint8_t* b1 = a.hist + ((size_t)p1 * a.hkv + hk) * kBlock;
-  c[0] = *reinterpret_cast<const u32x4_t*>(b0 + 16 * lane);
-  c[1] = *reinterpret_cast<const u32x4_t*>(b1 + 16 * lane);
-  md[0] = *reinterpret_cast<const u32x2_t*>(b0 + 1024 + 8 * lane);
-  md[1] = *reinterpret_cast<const u32x2_t*>(b1 + 1024 + 8 * lane);
+#pragma unroll
+  for (int i = 0; i < kStepPages; ++i) {
+    const int pid = __builtin_amdgcn_readlane(ids, kStepPages * k + i);
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.hist) + ((size_t)pid * a.hkv + hk) * kBlock,
+                                                     (short)0, kBlock, 0x00020000);
+    c[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 0);
+    md[i] = __builtin_amdgcn_raw_buffer_load_b64(r, 1024 + 8 * lane, 0, 0);
+  }
 }
+
+// masked score (finite, so that a zero weight times it stays 0)
+constexpr float kMasked = -1.0e30f;
 
 template <int G>
 __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, int hk, int hist_len,
                           int pg_begin, int pg_end, int wave, int lane, const u32x4_t* c_first,
-                          const u32x2_t* m_first, const u32x4_t* c_second, const u32x2_t* m_second) {
+                          const u32x2_t* m_first) {
   const int x = lane & 15, qa = lane >> 4;
-  const int col_head = x < G ? x : (x < 2 * G ? x - G : -1);
   // ---- score operands: q' in fp16 hi (columns 0..G-1) and lo (G..2G-1)
+  const int col_head = x < G ? x : (x < 2 * G ? x - G : 0);
+  const bool col_used = x < 2 * G;
+  const float col_scale = ldexpf(kC0, (int)sm.sexp[col_head]);
   half8_t bq[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
@@ -84,51 +95,62 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int j = 32 * g + 8 * qa + 2 * i + hf;
-        const int s = field_shift(4 * (g & 1) + i);
-        _Float16 e = (_Float16)0.0f;
-        if (col_head >= 0) {
-          const float v = ldexpf(sm.qr[col_head][j] * kC0, (int)sm.sexp[col_head] - 2 * s);
-          const _Float16 hi = (_Float16)v;
-          e = (x < G) ? hi : (_Float16)(v - (float)hi);
-        }
-        bq[g][2 * i + hf] = e;
+        const int sh = field_shift(4 * (g & 1) + i);
+        const float v = ldexpf(sm.qr[col_head][j] * col_scale, -2 * sh);
+        const _Float16 hi = (_Float16)v;
+        const _Float16 e = (x < G) ? hi : (_Float16)(v - (float)hi);
+        bq[g][2 * i + hf] = col_used ? e : (_Float16)0.0f;
       }
   // zero-point term operand (fp32 product, 4 groups = K of 4)
   const float be = (x < G) ? ldexpf(sm.qs[x][qa] * kC0, (int)sm.sexp[x] - 24) : 0.0f;
-  const float mult = (x < G) ? ldexpf(1.0f, 24 - (int)sm.sexp[x]) : 1.0f;
+  // matrix-core units -> log2 units; 0 for the columns that hold no head, so
+  // that their (unused) scores stay at 0 and never move the running maximum
+  const float mult = (x < G) ? ldexpf(1.0f, 24 - (int)sm.sexp[x]) : 0.0f;
+  // row 4 of the value zero-point operand is all ones: that product row
+  // accumulates sum_t p_t, the softmax denominator
+  const uint32_t ones_row = (x == 4) ? 0x3C003C00u : 0u;
 
   float4_t acc_o[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) acc_o[m] = (float4_t){0.f, 0.f, 0.f, 0.f};
   float4_t acc_z = (float4_t){0.f, 0.f, 0.f, 0.f};
-  float m_run = kMInit, l_run = 0.0f;
+  float m_run = kMInit;
 
-  const int npairs = (pg_end - pg_begin + 1) >> 1;
+  const int nsteps = (pg_end - pg_begin + kStepPages - 1) / kStepPages;
   uint8_t* mbuf = &sm.meta[wave][0][0];
 
-  // three-stage prefetch ring: while pair pr is processed, pairs pr + 4 and
-  // pr + 8 of this wave are in flight (the first two were issued before the
-  // prologue)
-  u32x4_t cA[2] = {c_first[0], c_first[1]}, cB[2] = {c_second[0], c_second[1]}, cC[2];
-  u32x2_t mA[2] = {m_first[0], m_first[1]}, mB[2] = {m_second[0], m_second[1]}, mC[2];
-  auto issue = [&](int pr_, u32x4_t* c, u32x2_t* md) { issue_pair(a, ids, hk, (pr_ - wave) >> 2, lane, c, md); };
-  int pr = wave;
+  // two-stage prefetch ring: while step st is processed, step st + 4 of this
+  // wave is in flight (the first step was issued before the prologue)
+  u32x4_t cA[kStepPages], cB[kStepPages];
+  u32x2_t mA[kStepPages], mB[kStepPages];
+#pragma unroll
+  for (int i = 0; i < kStepPages; ++i) { cA[i] = c_first[i]; mA[i] = m_first[i]; }
+  auto issue = [&](int st_, u32x4_t* c, u32x2_t* md) { issue_step(a, ids, hk, (st_ - wave) >> 2, lane, c, md); };
+  int st = wave;
+  // A partial step (only the last step of a sequence) has tokens past the end
+  // of the history: their scores are masked, so their weights are exactly 0.
+  // Their slots hold either zeros or bytes an earlier demotion wrote (finite
+  // scales and zeros), so 0 times them stays 0.
   auto body = [&](const u32x4_t* c_cur, const u32x2_t* m_cur) __attribute__((always_inline)) {
-    const int pg0 = pg_begin + 2 * pr;
-    const bool has1 = pg0 + 1 < pg_end;
-    // stage this pair's metadata in LDS (wave-private)
-    *reinterpret_cast<u32x2_t*>(mbuf + 8 * lane) = m_cur[0];
-    *reinterpret_cast<u32x2_t*>(mbuf + 512 + 8 * lane) = m_cur[1];
+    const int pg0 = pg_begin + kStepPages * st;
+    const int n_valid = min(kStepPages, pg_end - pg0);
+    // valid tokens of the step: token t of page p is history index 16 (pg0 + p) + t
+    const int base_tok = 16 * pg0;
+    const int lim = min(hist_len - base_tok, 16 * n_valid);
+    const bool partial = lim < 16 * kStepPages;
+    // stage this step's metadata in LDS (wave-private)
+#pragma unroll
+    for (int p = 0; p < kStepPages; ++p) *reinterpret_cast<u32x2_t*>(mbuf + 512 * p + 8 * lane) = m_cur[p];
     __builtin_amdgcn_wave_barrier();
 
-    // valid tokens of the pair: token t of page p is history index 16 (pg0 + p) + t
-    const int base_tok = 16 * pg0;
-    const bool full = has1 && (base_tok + 32 <= hist_len);
-
     // ---------------- scores
-    float sc[2][4];
+    float sc[kStepPages][4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < kStepPages; ++p) {
+      const uint8_t* mp = mbuf + 512 * p;
+      // sum_g zero[t][g] * (scaled group sums of q'), t = lane's row token
+      const _Float16 zk = *reinterpret_cast<const _Float16*>(mp + 128 + 8 * x + 2 * qa);
+      float4_t cacc = __builtin_amdgcn_mfma_f32_16x16x4f32((float)zk, be, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       const uint32_t w0 = c_cur[p][0], w1 = c_cur[p][1];
       const uint32_t w0s = w0 >> 6, w1s = w1 >> 6;
       half8_t ak[4];
@@ -146,38 +168,35 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
       for (int g = 0; g < 4; ++g)
         d[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[g], bq[g], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       // scales of tokens 4qa..4qa+3 (K scale area [token][group])
-      const uint8_t* mp = mbuf + 512 * p;
       const u32x4_t s01 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa);
       const u32x4_t s23 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa + 16);
       const _Float16* sh0 = reinterpret_cast<const _Float16*>(&s01);
       const _Float16* sh1 = reinterpret_cast<const _Float16*>(&s23);
-      float4_t cacc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const _Float16* sr = (r < 2) ? sh0 + 4 * r : sh1 + 4 * (r - 2);
-        float v = (float)sr[0] * d[0][r];
-        v = fmaf((float)sr[1], d[1][r], v);
-        v = fmaf((float)sr[2], d[2][r], v);
-        v = fmaf((float)sr[3], d[3][r], v);
-        cacc[r] = v;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) cacc[r] = fmaf((float)sr[g], d[g][r], cacc[r]);
       }
-      // + sum_g zero[t][g] * (scaled group sums of q'), t = lane's row token
-      const _Float16 zk = *reinterpret_cast<const _Float16*>(mp + 128 + 8 * x + 2 * qa);
-      cacc = __builtin_amdgcn_mfma_f32_16x16x4f32((float)zk, be, cacc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        // hi + lo halves of the same head
         const float other = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
             0u, __float_as_uint(cacc[r]), 0x120 + (16 - G), 0xF, 0xF, false));
-        float l = cacc[r] + other;
-        const int tok = base_tok + 16 * p + 4 * qa + r;
-        const bool ok = (x < G) && (p == 0 || has1) && (full || tok < hist_len);
-        sc[p][r] = ok ? l : -INFINITY;
+        sc[p][r] = cacc[r] + other;
       }
     }
-    // ---------------- online softmax over the 32 tokens of the pair
+    if (partial) {
+#pragma unroll
+      for (int p = 0; p < kStepPages; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * p + 4 * qa + r >= lim) sc[p][r] = kMasked;
+    }
+    // ---------------- online softmax over the step's tokens
     float mx = sc[0][0];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < kStepPages; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[p][r]);
     mx = rows_max(mx);
@@ -187,127 +206,107 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
 #pragma unroll
       for (int m = 0; m < 8; ++m) acc_o[m] *= alpha;
       acc_z *= alpha;
-      l_run *= alpha;
       m_run = m_new;
     }
-    float pv[2][4];
+    // ---------------- values, one page pair (32 tokens = one k block) at a time
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int j = 0; j < kStepPages / 2; ++j) {
+      float pv[2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[p][r] = __builtin_amdgcn_exp2f(fmaf(sc[p][r], mult, -m_run));
-        l_run += pv[p][r];
-      }
-    // ---------------- values
-    uint32_t pp[4];                 // fp16 p pairs: (page i>>1, tokens 2(i&1), +1)
-    pp[0] = pack_h2(pv[0][0], pv[0][1]);
-    pp[1] = pack_h2(pv[0][2], pv[0][3]);
-    pp[2] = pack_h2(pv[1][0], pv[1][1]);
-    pp[3] = pack_h2(pv[1][2], pv[1][3]);
-    // V scales [token/4][group][token%4]: lane reads its token quad of both pages
-    u32x4_t vs[2][2];
+      for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      vs[p][0] = *reinterpret_cast<const u32x4_t*>(mbuf + 512 * p + 256 + 32 * qa);
-      vs[p][1] = *reinterpret_cast<const u32x4_t*>(mbuf + 512 * p + 256 + 32 * qa + 16);
-    }
-    u32x2_t vz[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      vz[p] = (x < 4) ? *reinterpret_cast<const u32x2_t*>(mbuf + 512 * p + 384 + 32 * qa + 8 * x)
-                      : (u32x2_t){0u, 0u};
-    if (!full) {
-      // tokens past the end may hold stale bytes: zero their scales and zeros
+        for (int r = 0; r < 4; ++r) pv[p][r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * j + p][r], mult, -m_run));
+      uint32_t pp[4];                 // fp16 p pairs: (page i>>1, tokens 2(i&1), +1)
+      pp[0] = pack_h2(pv[0][0], pv[0][1]);
+      pp[1] = pack_h2(pv[0][2], pv[0][3]);
+      pp[2] = pack_h2(pv[1][0], pv[1][1]);
+      pp[3] = pack_h2(pv[1][2], pv[1][3]);
+      const uint8_t* mq = mbuf + 512 * (2 * j);
+      // V scales [token/4][group][token%4]: lane reads its token quad of both pages
+      u32x4_t vs[2][2];
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        uint32_t keep[2];
+        vs[p][0] = *reinterpret_cast<const u32x4_t*>(mq + 512 * p + 256 + 32 * qa);
+        vs[p][1] = *reinterpret_cast<const u32x4_t*>(mq + 512 * p + 256 + 32 * qa + 16);
+      }
+      u32x2_t vz[2];
 #pragma unroll
-        for (int hw = 0; hw < 2; ++hw) {
-          const int t0 = base_tok + 16 * p + 4 * qa + 2 * hw;
-          const bool pg_ok = (p == 0) || has1;
-          keep[hw] = (pg_ok && t0 < hist_len ? 0x0000FFFFu : 0u) | (pg_ok && t0 + 1 < hist_len ? 0xFFFF0000u : 0u);
+      for (int p = 0; p < 2; ++p)
+        vz[p] = (x < 4) ? *reinterpret_cast<const u32x2_t*>(mq + 512 * p + 384 + 32 * qa + 8 * x)
+                        : (u32x2_t){ones_row, ones_row};
+      // B operands per group: p * scale (fp16)
+      half8_t bv[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint32_t* b32 = reinterpret_cast<uint32_t*>(&bv[g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = i >> 1, hw = i & 1;
+          // group g's scale pair (tokens 2hw, 2hw+1 of the quad) is word 2g + hw of the 32 bytes
+          const uint32_t sw = (g < 2) ? vs[p][0][2 * g + hw] : vs[p][1][2 * (g - 2) + hw];
+          b32[i] = mul_h2(pp[i], sw);
         }
-        vs[p][0][0] &= keep[0]; vs[p][0][1] &= keep[1]; vs[p][0][2] &= keep[0]; vs[p][0][3] &= keep[1];
-        vs[p][1][0] &= keep[0]; vs[p][1][1] &= keep[1]; vs[p][1][2] &= keep[0]; vs[p][1][3] &= keep[1];
-        vz[p][0] &= keep[0]; vz[p][1] &= keep[1];
       }
-    }
-    // B operands per group: p * scale (fp16)
-    half8_t bv[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t* b32 = reinterpret_cast<uint32_t*>(&bv[g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = i >> 1, hw = i & 1;
-        // group g's scale pair (tokens 2hw, 2hw+1 of the quad) is word 2g + hw of the 32 bytes
-        const uint32_t sw = (g < 2) ? vs[p][0][2 * g + hw] : vs[p][1][2 * (g - 2) + hw];
-        b32[i] = mul_h2(pp[i], sw);
-      }
-    }
-    const uint32_t v00 = c_cur[0][2], v01 = c_cur[0][3], v10 = c_cur[1][2], v11 = c_cur[1][3];
-    const uint32_t v00s = v00 >> 6, v01s = v01 >> 6, v10s = v10 >> 6, v11s = v11 >> 6;
+      const uint32_t v00 = c_cur[2 * j][2], v01 = c_cur[2 * j][3], v10 = c_cur[2 * j + 1][2], v11 = c_cur[2 * j + 1][3];
+      const uint32_t v00s = v00 >> 6, v01s = v01 >> 6, v10s = v10 >> 6, v11s = v11 >> 6;
 #define OSCAR_VBLOCK(M)                                                                   \
-    {                                                                                     \
-      half8_t av;                                                                         \
-      uint32_t* a32 = reinterpret_cast<uint32_t*>(&av);                                   \
-      a32[0] = field_pair<M>(v00, v00s);                                                  \
-      a32[1] = field_pair<M>(v01, v01s);                                                  \
-      a32[2] = field_pair<M>(v10, v10s);                                                  \
-      a32[3] = field_pair<M>(v11, v11s);                                                  \
-      acc_o[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[(M) >> 1], acc_o[M], 0, 0, 0); \
-    }
-    OSCAR_VBLOCK(0) OSCAR_VBLOCK(1) OSCAR_VBLOCK(2) OSCAR_VBLOCK(3)
-    OSCAR_VBLOCK(4) OSCAR_VBLOCK(5) OSCAR_VBLOCK(6) OSCAR_VBLOCK(7)
+      {                                                                                   \
+        half8_t av;                                                                       \
+        uint32_t* a32 = reinterpret_cast<uint32_t*>(&av);                                 \
+        a32[0] = field_pair<M>(v00, v00s);                                                \
+        a32[1] = field_pair<M>(v01, v01s);                                                \
+        a32[2] = field_pair<M>(v10, v10s);                                                \
+        a32[3] = field_pair<M>(v11, v11s);                                                \
+        acc_o[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[(M) >> 1], acc_o[M], 0, 0, 0); \
+      }
+      OSCAR_VBLOCK(0) OSCAR_VBLOCK(1) OSCAR_VBLOCK(2) OSCAR_VBLOCK(3)
+      OSCAR_VBLOCK(4) OSCAR_VBLOCK(5) OSCAR_VBLOCK(6) OSCAR_VBLOCK(7)
 #undef OSCAR_VBLOCK
-    {
-      half8_t az, bz;
-      uint32_t* az32 = reinterpret_cast<uint32_t*>(&az);
-      uint32_t* bz32 = reinterpret_cast<uint32_t*>(&bz);
-      az32[0] = vz[0][0]; az32[1] = vz[0][1]; az32[2] = vz[1][0]; az32[3] = vz[1][1];
-      bz32[0] = pp[0]; bz32[1] = pp[1]; bz32[2] = pp[2]; bz32[3] = pp[3];
-      acc_z = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, acc_z, 0, 0, 0);
+      {
+        // rows 0..3: sum_t p_t zero[t][g]; row 4: sum_t p_t
+        half8_t az, bz;
+        uint32_t* az32 = reinterpret_cast<uint32_t*>(&az);
+        uint32_t* bz32 = reinterpret_cast<uint32_t*>(&bz);
+        az32[0] = vz[0][0]; az32[1] = vz[0][1]; az32[2] = vz[1][0]; az32[3] = vz[1][1];
+        bz32[0] = pp[0]; bz32[1] = pp[1]; bz32[2] = pp[2]; bz32[3] = pp[3];
+        acc_z = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, acc_z, 0, 0, 0);
+      }
     }
   };
   // The prefetch is issued unconditionally (past the end it re-reads this
-  // wave's last pair, an L2 hit) so that every body sees the same number of
-  // loads in flight and waits only for its own pair's.
-  const int last_pr = npairs > wave ? wave + ((npairs - 1 - wave) / 4) * 4 : wave;
-  while (pr < npairs) {
-    issue(min(pr + 8, last_pr), cC, mC);
+  // wave's last step, an L2 hit) so that every body sees the same number of
+  // loads in flight and waits only for its own step's.
+  const int last_st = nsteps > wave ? wave + ((nsteps - 1 - wave) / 4) * 4 : wave;
+  while (st < nsteps) {
+    issue(min(st + 4, last_st), cB, mB);
     body(cA, mA);
-    pr += 4;
-    if (pr >= npairs) break;
-    issue(min(pr + 8, last_pr), cA, mA);
+    st += 4;
+    if (st >= nsteps) break;
+    issue(min(st + 4, last_st), cA, mA);
     body(cB, mB);
-    pr += 4;
-    if (pr >= npairs) break;
-    issue(min(pr + 8, last_pr), cB, mB);
-    body(cC, mC);
-    pr += 4;
+    st += 4;
   }
   // ---- wave epilogue: true-unit rotated outputs to LDS
-  l_run = rows_sum(l_run);
   if (qa == 0) {
     sm.wm[wave][x] = m_run;
-    sm.wl[wave][x] = l_run;
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.zs[wave][r][x] = acc_z[r];
   }
+  if (qa == 1) sm.wl[wave][x] = acc_z[0];
   __builtin_amdgcn_wave_barrier();
   if (x < G) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float sc = ldexpf(1.0f, 24 - 2 * field_shift(m));
+      const float scl = ldexpf(1.0f, 24 - 2 * field_shift(m));
       const float zg = sm.zs[wave][m >> 1][x];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.wo[wave][x][16 * m + 4 * qa + r] = fmaf(acc_o[m][r], sc, zg);
+      for (int r = 0; r < 4; ++r) sm.wo[wave][x][16 * m + 4 * qa + r] = fmaf(acc_o[m][r], scl, zg);
     }
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 3) void decode_int2_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -350,11 +349,12 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
     const int pg_begin = hs * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);
     const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
-    // page ids of this wave's pairs (pairs wave, wave + 4, ...): one load per lane
-    const int32_t ids = pt_row[pg_begin + min(2 * (wave + 4 * (lane >> 1)) + (lane & 1), pg_end - pg_begin - 1)];
+    // page ids of this wave's steps (steps wave, wave + 4, ...): one load per lane
+    const int32_t ids = pt_row[pg_begin + min(kStepPages * (wave + 4 * (lane / kStepPages)) + lane % kStepPages,
+                                              pg_end - pg_begin - 1)];
     // q . R_K operands first (thread (c4, rs) takes output columns
     // [4 c4, 4 c4 + 4) and rows [16 rs, 16 rs + 16) of R_K: 16 float4 loads),
-    // then this wave's first two page pairs: the prologue waits only for the
+    // then this wave's first step: the prologue waits only for the
     // older loads, so the loop is entered with exactly the page loads in
     // flight that every later iteration also has.
     const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
@@ -366,15 +366,13 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
     uint16_t qv[kQPer];
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) qv[e] = qg[min(tid + 256 * e, G * kD - 1)];   // unconditional
-    u32x4_t c_first[2] = {}, c_second[2] = {};
-    u32x2_t m_first[2] = {}, m_second[2] = {};
+    u32x4_t c_first[kStepPages];
+    u32x2_t m_first[kStepPages];
     // unconditional (the ids are clamped to pages of this split): the same
     // loads are in flight on every path into the loop
-    // (kept in the loop's per-pair issue order, so the wait counts the loop
-    // computes for its first iteration are exact)
-    issue_pair(a, ids, hk, 0, lane, c_first, m_first);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_pair(a, ids, hk, 1, lane, c_second, m_second);
+    // (kept in the loop's issue order, so the wait counts the loop computes
+    // for its first iteration are exact)
+    issue_step(a, ids, hk, 0, lane, c_first, m_first);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {
@@ -425,7 +423,7 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(DecodeArgs a) {
       if (lane == 32) { sm.qs[h][1] = g0; sm.qs[h][3] = g1; }
     }
     __syncthreads();
-    hist_wave<G>(a, sm, ids, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first, c_second, m_second);
+    hist_wave<G>(a, sm, ids, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first);
   }
   float* rec = part_base + (size_t)split * G * kPartStride;
   store_split<G>(sm, rec, tid);

@@ -100,8 +100,8 @@ struct DecodePlan {
   bool ok;                    // false: the context needs more splits than the merge holds
 };
 
-// INT2 decode: a history split covers at most this many pages (each wave
-// keeps the page ids of its pairs in one register: 32 pairs x 2 pages)
+// INT2 decode: a history split covers at most this many pages (each of the
+// four waves keeps the page ids of its share in one 64-lane register)
 constexpr int kMaxPagesPerSplit = 256;
 
 DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len);
