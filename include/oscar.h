@@ -60,6 +60,9 @@
  *   [1280,1408) V scale fp16 [token/4][group][token%4]
  *   [1408,1536) V zero  fp16 [token/4][group][token%4]
  * A code c of group g dequantises to c * scale + zero in the rotated space.
+ * The caller zero-fills hist when it allocates it; afterwards every byte of
+ * a block is either zero or written by this library.  (Decode reads whole
+ * pages and relies on the metadata of not-yet-written slots being finite.)
  */
 #ifndef OSCAR_H
 #define OSCAR_H
