@@ -12,11 +12,13 @@
 //   append_kernel      one decode step: demote the ring slot about to be
 //                      reused (fp32 VALU rotation, latency-bound), then write
 //                      the new token into sink or ring.
-//   demote_bulk_kernel many tokens: 16-token tiles per wave; the rotation is
-//                      a 128x128x16 product on the matrix cores with R split
+//   demote_bulk_kernel many tokens: 64-token units per wave; the rotation is
+//                      a 128x128x64 product on the matrix cores with R split
 //                      into bf16 hi + lo terms (fp32 accumulation), or the
 //                      input is already-rotated fp32.
 //   prefill_route_kernel  copies of the sink and recent tiers of a prefill.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -113,26 +115,131 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Bulk demotion.  grid (ceil(T/256), batch*Hkv, 2), 256 threads; each wave
-// handles 4 tiles of 16 tokens.  In a tile, lane l = 16a + t owns token t and
-// channels j = 16 m + 4 a + i (m = 0..7, i = 0..3): the layout of the 16x16
-// result blocks of the rotation product D[j][t] = sum_i R[i][j] x[t][i].
+// Bulk demotion.  grid (nwg, 2): blockIdx.y picks K or V, 256 threads.  The
+// workgroup stages R^T once (bf16 hi + lo) and its four waves then take work
+// units of 64 tokens of one (sequence, KV head) in turn: unit u goes to wave
+// u mod (4 nwg).  A unit is four 16-token tiles; every R^T fragment read
+// from LDS feeds the four tiles' products.  In a tile, lane l = 16a + t owns
+// token t and channels j = 16 m + 4 a + i (m = 0..7, i = 0..3): the layout
+// of the 16x16 result blocks of the rotation product
+// D[j][t] = sum_i R[i][j] x[t][i].
 // ---------------------------------------------------------------------------
 // LDS copy of R^T: row j holds R[:, j] as 16 chunks of 8 bf16; chunk c of row j
 // is stored at chunk position c ^ (j & 15) so that the 16 rows read by one
 // fragment load fall on different banks.
 __device__ __forceinline__ int rt_index(int j, int i) { return j * kD + ((((i >> 3) ^ (j & 15))) << 3) + (i & 7); }
 
+// Clip, quantise, pack and store one token's vector held as y[m][i] =
+// channel 16 m + 4 qa + i (the lanes qa = 0..3 with the same token hold the
+// rest).  tau: LDS [128].  Every lane of the wave must call it (lane swaps).
+__device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float* tau, bool is_v, bool valid,
+                                                  uint8_t* blk, int ps, int qa) {
+  float gmn[4], gmx[4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float4 t4 = *reinterpret_cast<const float4*>(&tau[16 * m + 4 * qa]);
+    y[m][0] = clip_med3(y[m][0], t4.x);
+    y[m][1] = clip_med3(y[m][1], t4.y);
+    y[m][2] = clip_med3(y[m][2], t4.z);
+    y[m][3] = clip_med3(y[m][3], t4.w);
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float mn = y[2 * g][0], mx = y[2 * g][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      const float v = y[2 * g + (e >> 2)][e & 3];
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+    // across the four lanes a = 0..3 that share this token
+    const auto pn = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+    const auto px = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mn = fminf(__uint_as_float(pn[0]), __uint_as_float(pn[1]));
+    mx = fmaxf(__uint_as_float(px[0]), __uint_as_float(px[1]));
+    const auto qn = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+    const auto qx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    gmn[g] = fminf(__uint_as_float(qn[0]), __uint_as_float(qn[1]));
+    gmx[g] = fmaxf(__uint_as_float(qx[0]), __uint_as_float(qx[1]));
+  }
+  __half sc[4], zr[4];
+  float zf[4];
+  CodeCut cut[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    group_scale_zero(gmn[g], gmx[g], &sc[g], &zr[g]);
+    zf[g] = __half2float(zr[g]);
+    cut[g] = code_cut(__half2float(sc[g]));
+  }
+  uint32_t code[8][4];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) code[m][i] = quant_code_cut(y[m][i] - zf[m >> 1], cut[m >> 1]);
+
+  if (!is_v) {
+    // K: channel j = 16m + 4a + i lands in word (2(m&1) + (a>>1), m>>2) at
+    // field 4((m>>1)&1) + 2(a&1) + (i>>1) + 8(i&1); lanes a and a^1 fill
+    // complementary fields of the same four words.
+    uint32_t wd[2][2];
+#pragma unroll
+    for (int ai = 0; ai < 2; ++ai)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int m = ai + 2 * hb + 4 * w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc |= code[m][i] << (2 * (4 * hb + 2 * (qa & 1) + (i >> 1) + 8 * (i & 1)));
+        }
+        const auto pr = __builtin_amdgcn_permlane16_swap(acc, acc, false, false);
+        wd[ai][w] = pr[0] | pr[1];
+      }
+    if (valid && (qa & 1) == 0) {
+#pragma unroll
+      for (int ai = 0; ai < 2; ++ai) {
+        const int aa = 2 * ai + (qa >> 1);
+        *reinterpret_cast<u32x2_t*>(blk + 16 * (16 * aa + ps)) = (u32x2_t){wd[ai][0], wd[ai][1]};
+      }
+    }
+  } else {
+    // V: the 8 codes of (token, channel 4a + i) form one half-word, code of
+    // channel 16m + 4a + i at bits 2m.
+    if (valid) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t hw = 0u;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) hw |= code[m][i] << (2 * m);
+        *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, 4 * qa + i)) = (uint16_t)hw;
+      }
+    }
+  }
+  if (valid) {
+    // lane a stores group a's scale and zero (selects, not a dynamic index)
+    const int g = qa;
+    const uint32_t s01 = half_bits(sc[0]) | ((uint32_t)half_bits(sc[1]) << 16);
+    const uint32_t s23 = half_bits(sc[2]) | ((uint32_t)half_bits(sc[3]) << 16);
+    const uint32_t z01 = half_bits(zr[0]) | ((uint32_t)half_bits(zr[1]) << 16);
+    const uint32_t z23 = half_bits(zr[2]) | ((uint32_t)half_bits(zr[3]) << 16);
+    const int sh = 16 * (g & 1);
+    const int so = is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g);
+    const int zo = is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g);
+    *reinterpret_cast<uint16_t*>(blk + so) = (uint16_t)(((g < 2) ? s01 : s23) >> sh);
+    *reinterpret_cast<uint16_t*>(blk + zo) = (uint16_t)(((g < 2) ? z01 : z23) >> sh);
+  }
+}
+
 template <bool kRotatedInput>
 __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
   __shared__ __bf16 rt_hi[kRotatedInput ? 1 : kD * kD];
   __shared__ __bf16 rt_lo[kRotatedInput ? 1 : kD * kD];
-  const int bh = blockIdx.y;
-  const int b = bh / a.hkv, hk = bh % a.hkv, is_v = blockIdx.z;
-  const int count = a.length ? max(0, a.length[b] - kSink - kRecent) : a.n_tokens;
-  const int tile0 = blockIdx.x * 256;
-  if (tile0 >= count) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float tau_s[kD];
+  const int is_v = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tcol = lane & 15, qa = lane >> 4;
 
   if constexpr (!kRotatedInput) {
@@ -150,41 +257,56 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
         rt_lo[rt_index(j0 + e, i)] = lo;
       }
     }
-    __syncthreads();
   }
-  const float* tau_p = is_v ? a.clip_v : a.clip_k;
-  float tau[8][4];
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tau[m][i] = tau_p[16 * m + 4 * qa + i];
+  if (tid < kD) tau_s[tid] = (is_v ? a.clip_v : a.clip_k)[tid];
+  __syncthreads();
 
-  const int slot = a.seq_slot ? a.seq_slot[b] : b;
-  const int h0 = a.hist_start ? a.hist_start[b] : 0;
-
-  for (int s = 0; s < 4; ++s) {
-    const int tok = tile0 + 64 * wave + 16 * s + tcol;
-    if (tile0 + 64 * wave + 16 * s >= count) break;          // wave-uniform
-    const bool valid = tok < count;
-    const int tl = valid ? tok : count - 1;
-    float y[8][4];
+  const int ups = a.unit_tiles;                       // units per (sequence, KV head)
+  const int n_units = a.batch * a.hkv * ups;
+  for (int u = blockIdx.x * 4 + wave; u < n_units; u += gridDim.x * 4) {
+    const int b = u / (a.hkv * ups), rem = u % (a.hkv * ups);
+    const int hk = rem / ups, tok0 = kUnitTokens * (rem % ups);
+    const int count = a.length ? max(0, a.length[b] - kSink - kRecent) : a.n_tokens;
+    if (tok0 >= count) continue;                       // wave-uniform
+    const int slot = a.seq_slot ? a.seq_slot[b] : b;
+    const int h0 = a.hist_start ? a.hist_start[b] : 0;
+    // token of tile t for this lane (clamped to the last valid token)
+    auto src_token = [&](int t) { return min(tok0 + 16 * t + tcol, count - 1); };
+    auto store = [&](float (&y)[8][4], int t) {
+      const int tok = tok0 + 16 * t + tcol;
+      const int h = h0 + min(tok, count - 1);
+      const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
+      uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
+      quant_store_token(y, tau_s, is_v != 0, tok < count, blk, h & 15, qa);
+    };
     if constexpr (kRotatedInput) {
-      const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) +
-                         (((size_t)b * a.src_tokens + a.src_tok0 + tl) * a.hkv + hk) * kD;
+      for (int t = 0; t < kUnitTokens / 16; ++t) {
+        if (tok0 + 16 * t >= count) break;             // wave-uniform
+        const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) +
+                           (((size_t)b * a.src_tokens + a.src_tok0 + src_token(t)) * a.hkv + hk) * kD;
+        float y[8][4];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4 v4 = *reinterpret_cast<const float4*>(src + 16 * m + 4 * qa);
-        y[m][0] = v4.x; y[m][1] = v4.y; y[m][2] = v4.z; y[m][3] = v4.w;
+        for (int m = 0; m < 8; ++m) {
+          const float4 v4 = *reinterpret_cast<const float4*>(src + 16 * m + 4 * qa);
+          y[m][0] = v4.x; y[m][1] = v4.y; y[m][2] = v4.z; y[m][3] = v4.w;
+        }
+        store(y, t);
       }
     } else {
-      const uint16_t* src = (is_v ? a.src_v : a.src_k) +
-                            (((size_t)b * a.src_tokens + a.src_tok0 + tl) * a.hkv + hk) * kD;
-      bf16x8_t xb[4];
+      constexpr int kT = kUnitTokens / 16;
+      bf16x8_t xb[kT][4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) xb[kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * qa);
-      float4_t acc[8];
+      for (int t = 0; t < kT; ++t) {
+        const uint16_t* src = (is_v ? a.src_v : a.src_k) +
+                              (((size_t)b * a.src_tokens + a.src_tok0 + src_token(t)) * a.hkv + hk) * kD;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) acc[m] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < 4; ++kk) xb[t][kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * qa);
+      }
+      float4_t acc[kT][8];
+#pragma unroll
+      for (int t = 0; t < kT; ++t)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[t][m] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -192,110 +314,22 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
           const int row = rt_index(16 * m + tcol, 32 * kk + 8 * qa);
           const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&rt_hi[row]);
           const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&rt_lo[row]);
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xb[kk], acc[m], 0, 0, 0);
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, xb[kk], acc[m], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < kT; ++t) acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xb[t][kk], acc[t][m], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < kT; ++t) acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, xb[t][kk], acc[t][m], 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int m = 0; m < 8; ++m)
+      for (int t = 0; t < kT; ++t) {
+        if (tok0 + 16 * t >= count) break;             // wave-uniform
+        float y[8][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[m][i] = acc[m][i];
-    }
-    // clip, group min / max over the 32 channels of (token, group)
-    float gmn[4], gmx[4];
+        for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[m][i] = clip_value(y[m][i], tau[m][i]);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float mn = y[2 * g][0], mx = y[2 * g][0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) {
-        const float v = y[2 * g + (e >> 2)][e & 3];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+          for (int i = 0; i < 4; ++i) y[m][i] = acc[t][m][i];
+        store(y, t);
       }
-      // across the four lanes a = 0..3 that share this token
-      const auto pn = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-      const auto px = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mn = fminf(__uint_as_float(pn[0]), __uint_as_float(pn[1]));
-      mx = fmaxf(__uint_as_float(px[0]), __uint_as_float(px[1]));
-      const auto qn = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-      const auto qx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      gmn[g] = fminf(__uint_as_float(qn[0]), __uint_as_float(qn[1]));
-      gmx[g] = fmaxf(__uint_as_float(qx[0]), __uint_as_float(qx[1]));
-    }
-    __half sc[4], zr[4];
-    float sf[4], zf[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      group_scale_zero(gmn[g], gmx[g], &sc[g], &zr[g]);
-      sf[g] = __half2float(sc[g]);
-      zf[g] = __half2float(zr[g]);
-    }
-    uint32_t code[8][4];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) code[m][i] = quant_code(y[m][i], zf[m >> 1], sf[m >> 1]);
-
-    const int h = h0 + tl;
-    const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
-    uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
-    const int ps = h & 15;
-    if (!is_v) {
-      // K: channel j = 16m + 4a + i lands in word (2(m&1) + (a>>1), m>>2) at
-      // field 4((m>>1)&1) + 2(a&1) + (i>>1) + 8(i&1); lanes a and a^1 fill
-      // complementary fields of the same four words.
-      uint32_t wd[2][2];
-#pragma unroll
-      for (int ai = 0; ai < 2; ++ai)
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          uint32_t acc = 0u;
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const int m = ai + 2 * hb + 4 * w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc |= code[m][i] << (2 * (4 * hb + 2 * (qa & 1) + (i >> 1) + 8 * (i & 1)));
-          }
-          const auto pr = __builtin_amdgcn_permlane16_swap(acc, acc, false, false);
-          wd[ai][w] = pr[0] | pr[1];
-        }
-      if (valid && (qa & 1) == 0) {
-#pragma unroll
-        for (int ai = 0; ai < 2; ++ai) {
-          const int aa = 2 * ai + (qa >> 1);
-          *reinterpret_cast<u32x2_t*>(blk + 16 * (16 * aa + ps)) = (u32x2_t){wd[ai][0], wd[ai][1]};
-        }
-      }
-    } else {
-      // V: the 8 codes of (token, channel 4a + i) form one half-word, code of
-      // channel 16m + 4a + i at bits 2m.
-      if (valid) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t hw = 0u;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) hw |= code[m][i] << (2 * m);
-          *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, 4 * qa + i)) = (uint16_t)hw;
-        }
-      }
-    }
-    if (valid) {
-      // lane a stores group a's scale and zero (selects, not a dynamic index)
-      const int g = qa;
-      const uint32_t s01 = half_bits(sc[0]) | ((uint32_t)half_bits(sc[1]) << 16);
-      const uint32_t s23 = half_bits(sc[2]) | ((uint32_t)half_bits(sc[3]) << 16);
-      const uint32_t z01 = half_bits(zr[0]) | ((uint32_t)half_bits(zr[1]) << 16);
-      const uint32_t z23 = half_bits(zr[2]) | ((uint32_t)half_bits(zr[3]) << 16);
-      const int sh = 16 * (g & 1);
-      const int so = is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g);
-      const int zo = is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g);
-      *reinterpret_cast<uint16_t*>(blk + so) = (uint16_t)(((g < 2) ? s01 : s23) >> sh);
-      *reinterpret_cast<uint16_t*>(blk + zo) = (uint16_t)(((g < 2) ? z01 : z23) >> sh);
     }
   }
 }
@@ -329,9 +363,15 @@ hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_demote(const DemoteArgs& a, int batch, int max_count, bool rotated, hipStream_t st) {
+hipError_t launch_demote(const DemoteArgs& a_in, int batch, int max_count, bool rotated, hipStream_t st) {
   if (max_count <= 0) return hipSuccess;
-  const dim3 grid((max_count + 255) / 256, batch * a.hkv, 2);
+  DemoteArgs a = a_in;
+  a.batch = batch;
+  a.unit_tiles = (max_count + kUnitTokens - 1) / kUnitTokens;
+  const long units = (long)batch * a.hkv * a.unit_tiles;
+  // two workgroups per compute unit per tensor at most (each stages R once)
+  const int nwg = (int)std::min<long>((units + 3) / 4, 256);
+  const dim3 grid(nwg, 2);
   if (rotated)
     hipLaunchKernelGGL(demote_bulk_kernel<true>, grid, dim3(256), 0, st, a);
   else

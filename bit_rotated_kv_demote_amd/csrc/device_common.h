@@ -65,7 +65,30 @@ __device__ __forceinline__ uint32_t quant_code(float yc, float zf, float sf) {
   return (uint32_t)c;
 }
 
+// The same code without a division, for x = fl(y - zero) >= 0 and a group
+// scale s (an fp16 value): the correctly rounded quotient q = fl(x / s) gives
+// rint(q) >= 1 iff q > 0.5, >= 2 iff q >= 1.5 and 3 iff q > 2.5 (ties to even
+// round 0.5 and 2.5 down and 1.5 up), and over the exact quotient these are
+// x/s > 0.5 + 2^-25, x/s >= 1.5 - 2^-24 and x/s > 2.5 + 2^-23 (half an fp32
+// spacing past each midpoint).  Near each midpoint x - k s is exact (the two
+// terms are within a factor of two), so a fused multiply-add decides each
+// test exactly; far from it the margin is far larger than any rounding.
+// For s == 0 (then x == 0) every test fails: code 0.
+struct CodeCut {
+  float s, e0, e1, e2;
+};
+__device__ __forceinline__ CodeCut code_cut(float sf) {
+  return {sf, ldexpf(sf, -25), sf > 0.0f ? -ldexpf(sf, -24) : 1.0f, ldexpf(sf, -23)};
+}
+__device__ __forceinline__ uint32_t quant_code_cut(float x, const CodeCut& c) {
+  return (uint32_t)(fmaf(-0.5f, c.s, x) > c.e0) + (uint32_t)(fmaf(-1.5f, c.s, x) >= c.e1) +
+         (uint32_t)(fmaf(-2.5f, c.s, x) > c.e2);
+}
+
 __device__ __forceinline__ float clip_value(float y, float tau) { return fminf(fmaxf(y, -tau), tau); }
+// The same clip in one instruction (median of three; a NaN y gives -tau, as
+// the IEEE minNum / maxNum form does).
+__device__ __forceinline__ float clip_med3(float y, float tau) { return __builtin_amdgcn_fmed3f(y, -tau, tau); }
 
 __device__ __forceinline__ uint16_t half_bits(__half h) { return __half_as_ushort(h); }
 

@@ -32,6 +32,20 @@ def _rotated_inputs(layer, batch, n_tokens, starts):
     yk[0, 2, 0, 0], yk[0, 2, 0, 1] = np.float32(-1.0), np.float32(0.5)
     yv[0, 3, 0, 64:96] = np.float32(1e4)
     yv[0, 3, 0, 96:] = np.float32(-3e4)
+    # one fp32 step either side of each half-step tie (zero -1, scale 0.5):
+    # the code decision must follow the correctly rounded quotient exactly
+    t = np.array([-0.75, -0.25, 0.25], np.float32)
+    near = np.concatenate([np.nextafter(t, np.float32(-np.inf)), np.nextafter(t, np.float32(np.inf)), t])
+    for arr, hd in ((yk, 1), (yv, 2)):
+        row = np.zeros(32, np.float32)
+        row[:9] = near
+        row[9], row[10] = np.float32(-1.0), np.float32(0.5)
+        arr[0, 4, hd, 32:64] = row
+    # non-finite inputs clip to the bounds (NaN to -tau)
+    yk[0, 5, 2, 7] = np.float32(np.nan)
+    yk[0, 5, 2, 40] = np.float32(np.inf)
+    yv[0, 5, 3, 100] = np.float32(-np.inf)
+    yv[0, 6, 1, 3] = np.float32(np.nan)
     return yk, yv
 
 
