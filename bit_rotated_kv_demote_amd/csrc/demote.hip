@@ -176,24 +176,29 @@ __device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float*
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) code[m][i] = quant_code_cut(y[m][i] - zf[m >> 1], cut[m >> 1]);
+  auto push = [&](uint32_t acc, int sh, int m, int i) { return (acc << sh) + code[m][i]; };
 
   if (!is_v) {
     // K: channel j = 16m + 4a + i lands in word (2(m&1) + (a>>1), m>>2) at
     // field 4((m>>1)&1) + 2(a&1) + (i>>1) + 8(i&1); lanes a and a^1 fill
-    // complementary fields of the same four words.
+    // complementary fields of the same four words.  A lane builds its eight
+    // fields at 4hb + (i>>1) + 8(i&1) from the highest down, then moves them
+    // up by 2(a&1) fields.
     uint32_t wd[2][2];
 #pragma unroll
     for (int ai = 0; ai < 2; ++ai)
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        uint32_t acc = 0u;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int m = ai + 2 * hb + 4 * w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc |= code[m][i] << (2 * (4 * hb + 2 * (qa & 1) + (i >> 1) + 8 * (i & 1)));
-        }
+        const int m0 = ai + 4 * w, m1 = ai + 2 + 4 * w;   // hb = 0, 1
+        uint32_t acc = push(0u, 0, m1, 3);               // field 13
+        acc = push(acc, 2, m1, 1);                       // 12
+        acc = push(acc, 6, m0, 3);                       // 9
+        acc = push(acc, 2, m0, 1);                       // 8
+        acc = push(acc, 6, m1, 2);                       // 5
+        acc = push(acc, 2, m1, 0);                       // 4
+        acc = push(acc, 6, m0, 2);                       // 1
+        acc = push(acc, 2, m0, 0);                       // 0
+        acc <<= 4 * (qa & 1);
         const auto pr = __builtin_amdgcn_permlane16_swap(acc, acc, false, false);
         wd[ai][w] = pr[0] | pr[1];
       }
@@ -207,14 +212,12 @@ __device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float*
   } else {
     // V: the 8 codes of (token, channel 4a + i) form one half-word, code of
     // channel 16m + 4a + i at bits 2m.
-    if (valid) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t hw = 0u;
+    for (int i = 0; i < 4; ++i) {
+      uint32_t hw = push(0u, 0, 7, i);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) hw |= code[m][i] << (2 * m);
-        *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, 4 * qa + i)) = (uint16_t)hw;
-      }
+      for (int m = 6; m >= 0; --m) hw = push(hw, 2, m, i);
+      if (valid) *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, 4 * qa + i)) = (uint16_t)hw;
     }
   }
   if (valid) {
@@ -272,12 +275,11 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
     const int h0 = a.hist_start ? a.hist_start[b] : 0;
     // token of tile t for this lane (clamped to the last valid token)
     auto src_token = [&](int t) { return min(tok0 + 16 * t + tcol, count - 1); };
-    auto store = [&](float (&y)[8][4], int t) {
+    auto page_of = [&](int t) { return a.page_table[(size_t)slot * a.max_pages + ((h0 + src_token(t)) >> 4)]; };
+    auto store = [&](float (&y)[8][4], int t, int page) {
       const int tok = tok0 + 16 * t + tcol;
-      const int h = h0 + min(tok, count - 1);
-      const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
       uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
-      quant_store_token(y, tau_s, is_v != 0, tok < count, blk, h & 15, qa);
+      quant_store_token(y, tau_s, is_v != 0, tok < count, blk, (h0 + src_token(t)) & 15, qa);
     };
     if constexpr (kRotatedInput) {
       for (int t = 0; t < kUnitTokens / 16; ++t) {
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
           const float4 v4 = *reinterpret_cast<const float4*>(src + 16 * m + 4 * qa);
           y[m][0] = v4.x; y[m][1] = v4.y; y[m][2] = v4.z; y[m][3] = v4.w;
         }
-        store(y, t);
+        store(y, t, page_of(t));
       }
     } else {
       constexpr int kT = kUnitTokens / 16;
@@ -302,6 +304,10 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) xb[t][kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * qa);
       }
+      // page ids travel with the inputs, so the stores never wait for them
+      int pg[kT];
+#pragma unroll
+      for (int t = 0; t < kT; ++t) pg[t] = page_of(t);
       float4_t acc[kT][8];
 #pragma unroll
       for (int t = 0; t < kT; ++t)
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
         for (int m = 0; m < 8; ++m)
 #pragma unroll
           for (int i = 0; i < 4; ++i) y[m][i] = acc[t][m][i];
-        store(y, t);
+        store(y, t, pg[t]);
       }
     }
   }

@@ -65,24 +65,24 @@ __device__ __forceinline__ uint32_t quant_code(float yc, float zf, float sf) {
   return (uint32_t)c;
 }
 
-// The same code without a division, for x = fl(y - zero) >= 0 and a group
-// scale s (an fp16 value): the correctly rounded quotient q = fl(x / s) gives
-// rint(q) >= 1 iff q > 0.5, >= 2 iff q >= 1.5 and 3 iff q > 2.5 (ties to even
-// round 0.5 and 2.5 down and 1.5 up), and over the exact quotient these are
-// x/s > 0.5 + 2^-25, x/s >= 1.5 - 2^-24 and x/s > 2.5 + 2^-23 (half an fp32
-// spacing past each midpoint).  Near each midpoint x - k s is exact (the two
-// terms are within a factor of two), so a fused multiply-add decides each
-// test exactly; far from it the margin is far larger than any rounding.
-// For s == 0 (then x == 0) every test fails: code 0.
+// The same code without a division, for x = fl(y - zero) >= 0 and an fp16
+// group scale s > 0.  With q = fl(x / s) correctly rounded: rint(q) >= 1 iff
+// q > 0.5, >= 2 iff q >= 1.5 and 3 iff q > 2.5 (ties to even send 0.5 and 2.5
+// down and 1.5 up); over the exact quotient these are x/s > 0.5 + 2^-25,
+// x/s >= 1.5 - 2^-24 and x/s > 2.5 + 2^-23 (half an fp32 spacing past each
+// midpoint).  k s is exact in fp32 for k = 0.5, 1.5, 2.5 (s has 11
+// significant bits), and the fp32 spacing next to k s exceeds s 2^-25,
+// s 2^-24 and s 2^-23 respectively, so for fp32 x the three tests are exactly
+// x > 0.5 s, x >= 1.5 s and x > 2.5 s.  For s == 0 (then x == 0) the middle
+// cut is moved above 0 so that the code is 0.
 struct CodeCut {
-  float s, e0, e1, e2;
+  float c0, c1, c2;
 };
 __device__ __forceinline__ CodeCut code_cut(float sf) {
-  return {sf, ldexpf(sf, -25), sf > 0.0f ? -ldexpf(sf, -24) : 1.0f, ldexpf(sf, -23)};
+  return {0.5f * sf, sf > 0.0f ? 1.5f * sf : 1.0f, 2.5f * sf};
 }
 __device__ __forceinline__ uint32_t quant_code_cut(float x, const CodeCut& c) {
-  return (uint32_t)(fmaf(-0.5f, c.s, x) > c.e0) + (uint32_t)(fmaf(-1.5f, c.s, x) >= c.e1) +
-         (uint32_t)(fmaf(-2.5f, c.s, x) > c.e2);
+  return (uint32_t)(x > c.c0) + (uint32_t)(x >= c.c1) + (uint32_t)(x > c.c2);
 }
 
 __device__ __forceinline__ float clip_value(float y, float tau) { return fminf(fmaxf(y, -tau), tau); }
