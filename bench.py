@@ -220,6 +220,137 @@ def run_bf16(torch, hq, hkv, n, n_layers, steps, seed, k_bits, v_bits):
                 pool_mb=n_layers * kv.nbytes / 1e6)
 
 
+def _seq_kv(hkv, n, seed):
+    """One seeded sequence of n tokens (bf16 bits [n, Hkv, 128]) for K and V."""
+    from bit_rotated_kv_demote_amd import synth
+    st = synth.streams(seed)
+    out = synth.outlier_channels(st["outliers"])
+    return (synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out),
+            synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out))
+
+
+def _int2_pool(torch, hq, hkv, lengths, k1, v1, calib, seed, chunk=4):
+    """INT2 tiered pool holding len(lengths) sequences; sequence b holds the first
+    lengths[b] tokens of the seeded sequence (k1, v1); shuffled page table."""
+    from bit_rotated_kv_demote_amd import synth
+    from bit_rotated_kv_demote_amd.pool import TieredKV, bf16_tensor
+    B = len(lengths)
+    max_pages = max(1, math.ceil((max(lengths) + 1 - 320) / 16))
+    perm = synth.page_permutation(np.random.default_rng(seed), B * max_pages).reshape(B, max_pages)
+    pool = TieredKV(hq, hkv, B, max_pages, B * max_pages, *calib, page_table=perm)
+    kd, vd = bf16_tensor(k1), bf16_tensor(v1)
+    for b0 in range(0, B, chunk):
+        bs = list(range(b0, min(B, b0 + chunk)))
+        n = max(lengths[b] for b in bs)
+        kk = kd[None, :n].expand(len(bs), -1, -1, -1).contiguous()
+        vv = vd[None, :n].expand(len(bs), -1, -1, -1).contiguous()
+        pool.prefill(torch.tensor([lengths[b] for b in bs], dtype=torch.int32, device="cuda"), kk, vv,
+                     seq_slot=torch.tensor(bs, dtype=torch.int32, device="cuda"))
+        del kk, vv
+    torch.cuda.synchronize()
+    return pool
+
+
+def _bf16_pool(torch, hq, hkv, B, n, k1, v1, seed):
+    """BF16 paged pool of B copies of the first n tokens of (k1, v1), built on the device."""
+    from bit_rotated_kv_demote_amd import synth
+    from bit_rotated_kv_demote_amd.pool import PagedBF16, bf16_tensor
+    P = math.ceil(n / 16)
+    base = torch.zeros((P, hkv, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    for c, src in ((0, k1), (1, v1)):
+        t = torch.zeros((P * 16, hkv, 128), dtype=torch.bfloat16, device="cuda")
+        t[:n] = bf16_tensor(src[:n])
+        base[:, :, c] = t.view(P, 16, hkv, 128).permute(0, 2, 1, 3)
+    perm = synth.page_permutation(np.random.default_rng(seed), B * P)
+    phys = torch.empty((B * P, hkv, 2, 16, 128), dtype=torch.bfloat16, device="cuda")
+    phys[torch.as_tensor(perm, device="cuda").long()] = base.repeat(B, 1, 1, 1, 1)
+    del base
+    return PagedBF16(hq, hkv, phys, perm.reshape(B, P))
+
+
+def _time_decode(torch, pool, q, lens, max_len, steps, seq_slot=None):
+    out = torch.empty((q.shape[0], q.shape[1], 128), dtype=torch.float32, device="cuda")
+    pool.decode(q, lens, max_len, out=out, seq_slot=seq_slot)
+    torch.cuda.synchronize()
+    t = Timer(torch)
+    gpu_hold(torch, 5 + 0.5 * steps)
+    for _ in range(steps):
+        s0 = t.start()
+        pool.decode(q, lens, max_len, out=out, seq_slot=seq_slot)
+        t.stop(s0)
+    torch.cuda.synchronize()
+    return t.mean_us()
+
+
+def run_ragged_gqa8(torch, steps, calib, seed=1005):
+    """Qwen3-32B-shaped ragged batch: 64 q / 8 KV heads (G = 8), batch 16,
+    contexts uniform in [8192, 65536], shuffled page tables; INT2 decode and the
+    BF16 baseline on the same batch."""
+    from bit_rotated_kv_demote_amd import synth
+    from bit_rotated_kv_demote_amd.pool import bf16_tensor
+    hq, hkv, B = 64, 8, 16
+    st = synth.streams(seed)
+    lengths = [int(x) for x in synth.ragged_lengths(st["lengths"], B, 8192, 65536)]
+    n_max = max(lengths)
+    k1, v1 = _seq_kv(hkv, n_max, seed)
+    pool = _int2_pool(torch, hq, hkv, lengths, k1, v1, calib, seed)
+    q = bf16_tensor(synth.queries(st["q"], (B, hq, 128)))
+    lens = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    us = _time_decode(torch, pool, q, lens, n_max, steps)
+    nbytes = decode_bytes(lengths, hq, hkv)
+    del pool
+    torch.cuda.empty_cache()
+    # BF16 baseline: one shared page layout with the longest context, per-sequence lengths
+    bpool = _bf16_pool(torch, hq, hkv, B, n_max, k1, v1, seed + 1)
+    bus = _time_decode(torch, bpool, q, lens, n_max, steps)
+    bbytes = bf16_decode_bytes(lengths, hq, hkv)
+    del bpool
+    torch.cuda.empty_cache()
+    return {"workload": "64 q / 8 KV heads, batch 16, contexts U[8192, 65536] (seeded), shuffled pages",
+            "total_tokens": int(sum(lengths)), "decode_us": round(us, 3), "decode_GBps": round(nbytes / (us * 1e3), 1),
+            "decode_algorithmic_bytes": nbytes, "bf16_decode_us": round(bus, 3),
+            "bf16_decode_GBps": round(bbytes / (bus * 1e3), 1), "int2_vs_bf16_decode_speedup": round(bus / us, 3)}
+
+
+def run_fixed_memory(torch, steps, calib, seed=1004, layers=36, budget_gb=64.0):
+    """Fixed-memory batch sweep: 32 q / 8 KV heads at 16384 tokens; the INT2
+    pool and the BF16 cache each get the same per-layer share of a 64 GB budget
+    (over an assumed 36 layers); decode tokens/s (batch / step time) per batch."""
+    from bit_rotated_kv_demote_amd import synth
+    from bit_rotated_kv_demote_amd.pool import bf16_tensor
+    hq, hkv, n = 32, 8, 16384
+    per_layer = budget_gb * 1e9 / layers
+    int2_seq = (n - 320) * hkv * 96 + 320 * hkv * 512
+    bf16_seq = n * hkv * 512
+    max_int2, max_bf16 = int(per_layer // int2_seq), int(per_layer // bf16_seq)
+    st = synth.streams(seed)
+    k1, v1 = _seq_kv(hkv, n, seed)
+    q_all = bf16_tensor(synth.queries(st["q"], (max_int2, hq, 128)))
+    batches = sorted({b for b in (1, 2, 4, 8, 16, 32, 64, 128) if b <= max_int2} | {max_int2, max_bf16})
+    res = {"workload": f"32 q / 8 KV heads, {n} tokens per sequence, {budget_gb:g} GB over {layers} layers "
+                       f"= {per_layer / 1e9:.3f} GB per layer",
+           "max_batch_int2": max_int2, "max_batch_bf16": max_bf16, "int2_tok_per_s": {}, "bf16_tok_per_s": {}}
+    pool = _int2_pool(torch, hq, hkv, [n] * max_int2, k1, v1, calib, seed)
+    for b in batches:
+        lens = torch.full((b,), n, dtype=torch.int32, device="cuda")
+        us = _time_decode(torch, pool, q_all[:b], lens, n, steps)
+        res["int2_tok_per_s"][str(b)] = round(b / (us * 1e-6), 1)
+    del pool
+    torch.cuda.empty_cache()
+    bpool = _bf16_pool(torch, hq, hkv, max_bf16, n, k1, v1, seed + 1)
+    for b in batches:
+        if b > max_bf16:
+            continue
+        lens = torch.full((b,), n, dtype=torch.int32, device="cuda")
+        us = _time_decode(torch, bpool, q_all[:b], lens, n, steps)
+        res["bf16_tok_per_s"][str(b)] = round(b / (us * 1e-6), 1)
+    del bpool
+    torch.cuda.empty_cache()
+    res["throughput_ratio_at_max_batch"] = round(res["int2_tok_per_s"][str(max_int2)] /
+                                                 res["bf16_tok_per_s"][str(max_bf16)], 3)
+    return res
+
+
 def run_demote(torch, reps, seed):
     """Bulk demotion of a 4096-token chunk for 16 sequences x 8 KV heads."""
     from bit_rotated_kv_demote_amd import synth
@@ -374,6 +505,8 @@ def main():
         extra["ctx128k"]["bf16_decode_GBps"] = round(b128["decode_bytes"] / (b128["decode_us"] * 1e3), 1)
         extra["ctx128k"]["int2_vs_bf16_decode_speedup"] = round(b128["decode_us"] / r128["decode_us"], 3)
         del r128, b128
+        extra["ragged_gqa8"] = run_ragged_gqa8(torch, min(args.steps, 50), res["host"][2:])
+        extra["fixed_memory_16k"] = run_fixed_memory(torch, min(args.steps, 20), res["host"][2:])
         d = run_demote(torch, 20, 1004)
         extra["demote_tok_per_s"] = round(d["tok_per_s"], 0)
         extra["demote_us_per_chunk"] = round(d["us"], 2)

@@ -306,7 +306,7 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
 }
 
 template <int G>
-__global__ __launch_bounds__(256, 3) void decode_int2_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

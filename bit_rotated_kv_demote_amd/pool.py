@@ -82,9 +82,10 @@ class TieredKV:
 class PagedBF16:
     """BF16 paged cache [num_pages, Hkv, 2, 16, 128] for the baseline decode."""
 
-    def __init__(self, num_q_heads, num_kv_heads, kv_bits: np.ndarray, page_table, device="cuda"):
+    def __init__(self, num_q_heads, num_kv_heads, kv_bits, page_table, device="cuda"):
+        """kv_bits: bf16 bit patterns (host uint16 array) or a device bf16 tensor, used as is."""
         self.hq, self.hkv, self.device = num_q_heads, num_kv_heads, device
-        self.kv = bf16_tensor(kv_bits, device)
+        self.kv = kv_bits.contiguous() if isinstance(kv_bits, torch.Tensor) else bf16_tensor(kv_bits, device)
         self.page_table = torch.as_tensor(np.asarray(page_table, np.int32), device=device).contiguous()
         self.desc = binding.layer_desc(num_q_heads, num_kv_heads)
         self.pool = binding.make_bf16_pool(self.kv, self.page_table)
