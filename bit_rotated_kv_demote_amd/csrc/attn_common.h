@@ -1,6 +1,6 @@
 // Pieces shared by the decode kernels: BF16 span attention on the matrix
-// cores, per-workgroup partial records, the completion ticket and the
-// log-sum-exp merge of split partials (flash-decoding style split-K).
+// cores and the per-workgroup partial records that the log-sum-exp merge
+// kernel combines (flash-decoding style split-K).
 #pragma once
 
 #include "device_common.h"
@@ -49,47 +49,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Split records cross workgroups (and XCDs, each with its own L2).  They are
-// written and read through buffer instructions with the device-scope cache
-// policy (sc1), which the hardware keeps coherent across L2s without
-// whole-cache writeback or invalidation.  A workgroup's record is complete
-// once every thread has waited for its stores (s_waitcnt), which precedes the
-// ticket below.  Buffer accesses outside the resource's byte range read 0 and
-// write nothing.
-constexpr int kCachePolicyDevice = 16;          // sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v) {
-  const u32x4_t w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
-  __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ void st_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b) {
-  const u32x2_t w = {__float_as_uint(a), __float_as_uint(b)};
-  __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)off, 0, kCachePolicyDevice);
-}
-__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t w = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyDevice);
-  return make_float4(__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3]));
-}
-__device__ __forceinline__ float2 ld_dev2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kCachePolicyDevice);
-  return make_float2(__uint_as_float(w[0]), __uint_as_float(w[1]));
-}
-constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;   // a byte offset past every resource: reads 0
-
 template <int G>
 struct alignas(16) SplitSmem {
   float pt[4][32][G];        // probabilities of a 32-token BF16 chunk, per wave
   float wm[4][16];           // per-wave running max per column (head)
   float wl[4][16];           // per-wave running sum per column
   float wo[4][G][kD];        // per-wave unnormalised outputs
-  float mw[G][kMaxSplits];   // merge: per-split weights
-  float ohist[G][kD];        // merge: rotated part
-  // merge: split sums l [G][kMaxSplits], then per-part sums [parts][2][G*128] (parts * G * 128 == 1024)
-  float mred[G * kMaxSplits > 2048 ? G * kMaxSplits : 2048];
-  float lsum[G];
-  int last;
 };
 
 // ---------------------------------------------------------------------------
@@ -193,11 +158,11 @@ __device__ void bf16_span_wave(const uint16_t* qg, int count, RowK rowk, RowV ro
 }
 
 // Combine the four waves' partials of a workgroup into its split record
-// rec[h * kPartStride + (0..127 acc, 128 m, 129 l)] (16-byte stores).
+// rec[h * kPartStride + (0..127 acc, 128 m, 129 l)] (16-byte stores; the
+// merge kernel, next on the stream, reads them).
 template <int G>
 __device__ void store_split(SplitSmem<G>& sm, float* rec, int tid) {
   __syncthreads();
-  const auto r = dev_rsrc(rec, G * kPartStride * 4);
   for (int c = tid; c < G * kD / 4; c += 256) {
     const int h = c / (kD / 4), j4 = c % (kD / 4);
     float mm = kMInit;
@@ -213,154 +178,8 @@ __device__ void store_split(SplitSmem<G>& sm, float* rec, int tid) {
       acc.z = fmaf(f, o.z, acc.z); acc.w = fmaf(f, o.w, acc.w);
       ll = fmaf(f, sm.wl[w][h], ll);
     }
-    st_dev4(r, 4u * (h * kPartStride + 4 * j4), acc);
-    if (j4 == 0) st_dev2(r, 4u * (h * kPartStride + kD), mm, ll);
-  }
-}
-
-// Publish this workgroup's record and take a ticket; true for the last
-// workgroup of the group (which then owns the merge and resets the counter).
-template <int G>
-__device__ bool finish_ticket(SplitSmem<G>& sm, uint32_t* counter, uint32_t target, int tid) {
-  __builtin_amdgcn_s_waitcnt(0);     // this thread's record stores are complete
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = (prev == target - 1u) ? 1 : 0;
-  }
-  __syncthreads();
-  return sm.last != 0;
-}
-
-// LSE merge of n_act split records of one group (part_bytes: the group's
-// record area).  Records k < n_plain are in the output space; the others are
-// in the rotated space and are summed, then rotated back with R^T
-// ((y R^T)_i = sum_j y_j R[i][j]).  out: [G][128] fp32.
-// The merge runs after the rest of the grid has drained, so its latency is
-// the kernel's tail: every load is issued up front, in the order the phases
-// consume them ((m, l) pairs, record columns, rows of R), and out-of-range
-// slots read 0 instead of branching.
-template <int G, class SplitId>
-__device__ void merge_group(SplitSmem<G>& sm, const float* part_base, uint32_t part_bytes, int n_act, int n_plain,
-                            SplitId split_id, const float* rot, float* out, int tid, int wave, int lane) {
-  const bool any_rot = n_act > n_plain;
-  const auto rsrc = dev_rsrc(part_base, part_bytes);
-  // (m, l) of every (split, head): slot idx = k * G + h
-  constexpr int kMl = (kMaxSplits * G + 255) / 256;
-  float2 ml[kMl];
-#pragma unroll
-  for (int r = 0; r < kMl; ++r) {
-    const int idx = tid + 256 * r, k = idx / G, h = idx % G;
-    ml[r] = ld_dev2(rsrc, idx < n_act * G ? 4u * ((split_id(k) * G + h) * kPartStride + kD) : kOutOfRange);
-  }
-  // record columns: thread (col, part) takes the float4 column col of splits
-  // k = part, part + kParts, ...
-  constexpr int kCols = G * kD / 4;
-  constexpr int kParts = 256 / kCols;
-  constexpr int kBatch = 16;
-  const int col = tid % kCols, part = tid / kCols;
-  const int ch = col / (kD / 4), j4 = col % (kD / 4);
-  auto rec_off = [&](int k) -> uint32_t {
-    return k < n_act ? 4u * ((split_id(k) * G + ch) * kPartStride + 4 * j4) : kOutOfRange;
-  };
-  float4 v[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) v[u] = ld_dev4(rsrc, rec_off(part + u * kParts));
-  // this thread's slice of R for the inverse rotation: row ri, columns [64 jh, 64 jh + 64)
-  const int ri = tid & (kD - 1), jh = tid >> 7;
-  float4 rrow[16];
-  if (any_rot) {
-    const float4* rp = reinterpret_cast<const float4*>(rot + (size_t)ri * kD + 64 * jh);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
-  }
-  // A: per-head global max, split weights and the total sum
-  float* lbuf = sm.mred;     // l values [G][kMaxSplits], consumed before phase B reuses mred
-#pragma unroll
-  for (int r = 0; r < kMl; ++r) {
-    const int idx = tid + 256 * r, k = idx / G, h = idx % G;
-    if (idx < n_act * G) {
-      sm.mw[h][k] = ml[r].x;
-      lbuf[h * kMaxSplits + k] = ml[r].y;
-    }
-  }
-  __syncthreads();
-  for (int h = wave; h < G; h += 4) {
-    float mm = kMInit;
-    for (int k = lane; k < n_act; k += 64) mm = fmaxf(mm, sm.mw[h][k]);
-    mm = wave_max(mm);
-    float ll = 0.0f;
-    for (int k = lane; k < n_act; k += 64) {
-      const float wk = __builtin_amdgcn_exp2f(sm.mw[h][k] - mm);
-      sm.mw[h][k] = wk;
-      ll = fmaf(wk, lbuf[h * kMaxSplits + k], ll);
-    }
-    ll = wave_sum(ll);
-    if (lane == 0) sm.lsum[h] = ll;
-  }
-  __syncthreads();
-  // B: weighted sums
-  {
-    float4 ap = make_float4(0.f, 0.f, 0.f, 0.f), ar = ap;
-    auto acc_into = [&](int kk, const float4& x) {
-      const float w = sm.mw[ch][kk];
-      float4& acc = kk < n_plain ? ap : ar;
-      acc.x = fmaf(w, x.x, acc.x); acc.y = fmaf(w, x.y, acc.y);
-      acc.z = fmaf(w, x.z, acc.z); acc.w = fmaf(w, x.w, acc.w);
-    };
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int k = part + u * kParts;
-      if (k < n_act) acc_into(k, v[u]);
-    }
-    for (int k0 = part + kBatch * kParts; k0 < n_act; k0 += kBatch * kParts) {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[u] = ld_dev4(rsrc, rec_off(k0 + u * kParts));
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int k = k0 + u * kParts;
-        if (k < n_act) acc_into(k, v[u]);
-      }
-    }
-    __syncthreads();   // every l value has been read before mred is reused
-    reinterpret_cast<float4*>(&sm.mred[(part * 2 + 0) * G * kD])[col] = ap;
-    reinterpret_cast<float4*>(&sm.mred[(part * 2 + 1) * G * kD])[col] = ar;
-  }
-  __syncthreads();
-  // C: reduce the residue classes; plain part -> wo[0], rotated part -> ohist
-  float* plain = &sm.wo[0][0][0];
-  for (int idx = tid; idx < G * kD; idx += 256) {
-    float ap = 0.f, ar = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < kParts; ++pp) {
-      ap += sm.mred[(pp * 2 + 0) * G * kD + idx];
-      ar += sm.mred[(pp * 2 + 1) * G * kD + idx];
-    }
-    plain[idx] = ap;
-    sm.ohist[idx / kD][idx % kD] = ar;
-  }
-  __syncthreads();
-  // D: half of (ohist . R^T) per thread, into wo[1 + jh]
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float acc = 0.0f;
-    if (any_rot) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float4 oh = *reinterpret_cast<const float4*>(&sm.ohist[h][64 * jh + 4 * e]);
-        acc = fmaf(oh.x, rrow[e].x, acc);
-        acc = fmaf(oh.y, rrow[e].y, acc);
-        acc = fmaf(oh.z, rrow[e].z, acc);
-        acc = fmaf(oh.w, rrow[e].w, acc);
-      }
-    }
-    sm.wo[1 + jh][h][ri] = acc;
-  }
-  __syncthreads();
-  // E: normalise and store
-  for (int idx = tid; idx < G * kD; idx += 256) {
-    const int h = idx / kD, i = idx % kD;
-    out[(size_t)h * kD + i] = (plain[idx] + sm.wo[1][h][i] + sm.wo[2][h][i]) / sm.lsum[h];
+    *reinterpret_cast<float4*>(rec + h * kPartStride + 4 * j4) = acc;
+    if (j4 == 0) *reinterpret_cast<float2*>(rec + h * kPartStride + kD) = make_float2(mm, ll);
   }
 }
 

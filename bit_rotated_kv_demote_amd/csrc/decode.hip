@@ -6,13 +6,12 @@
 // "OSCAR：面向2-bit KV缓存量化的谱协方差感知旋转方法" (zingnex.cn), section
 // 自定义INT2注意力内核.  Tiers: "大模型KV Cache 2bit量化实战" (yunpan.plus), 三.1.
 //
-// One launch per call.  Workgroups are "work items" of one (sequence, KV
-// head) group: BF16 tile splits (sink + recent tokens) and history splits
-// (runs of INT2 pages).  Each writes a partial (running max m, sum l and
-// unnormalised output, all G query heads of the group) to the workspace; the
-// last workgroup of the group to finish (atomic ticket) merges the partials
-// by log-sum-exp, rotates the history part back with R_V^T, and writes the
-// fp32 output.
+// Two launches per call.  Workgroups of the first are "work items" of one
+// (sequence, KV head) group: BF16 tile splits (sink + recent tokens) and
+// history splits (runs of INT2 pages).  Each writes a partial (running max m,
+// sum l and unnormalised output, all G query heads of the group) to the
+// workspace; the merge kernel then combines them by log-sum-exp, rotates the
+// history part back with R_V^T, and writes the fp32 output.
 //
 // History scoring works in the rotated space: with q' = q . R_K and the
 // dequantised key k'_t = s_{t,g} c_{t,j} + z_{t,g},
@@ -425,16 +424,7 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
     __syncthreads();
     hist_wave<G>(a, sm, ids, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first);
   }
-  float* rec = part_base + (size_t)split * G * kPartStride;
-  store_split<G>(sm, rec, tid);
-
-  // ---- completion ticket: the last workgroup of the group merges
-  if (!finish_ticket<G>(sm, &a.counters[grp], (uint32_t)(act_tile + act_hist), tid)) return;
-  // active splits: tile 0..act_tile-1 (unrotated), history n_tile_splits + 0..act_hist-1 (rotated)
-  merge_group<G>(sm, part_base, (uint32_t)(n_split_total * G * kPartStride * 4), act_tile + act_hist, act_tile,
-                 [&](int k) { return k < act_tile ? k : a.n_tile_splits + (k - act_tile); }, a.rot_v,
-                 a.out + ((size_t)b * a.hkv * G + hk * G) * kD, tid, wave, lane);
-  if (tid == 0) a.counters[grp] = 0u;
+  store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
 }
 
 DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len) {
@@ -457,8 +447,7 @@ DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len) {
   p.n_work = batch * hkv * p.n_splits_total;
   p.grid = ((p.n_work + 7) / 8) * 8;
   p.partial_floats = (size_t)batch * hkv * p.n_splits_total * group * kPartStride;
-  p.workspace_bytes = p.partial_floats * sizeof(float) + (size_t)batch * hkv * sizeof(uint32_t);
-  (void)group;
+  p.workspace_bytes = p.partial_floats * sizeof(float);
   return p;
 }
 

@@ -2,7 +2,7 @@
 // measured against ("OSCAR：面向2-bit KV缓存量化的谱协方差感知旋转方法" (zingnex.cn),
 // 系统级收益 / 解码加速 compares decode speed with BF16).  Same structure as
 // the INT2 kernel: XCD-aware work items of (sequence, KV head, page range),
-// per-split partials, last-arriving workgroup merges by log-sum-exp.
+// per-split partials, then the same log-sum-exp merge kernel.
 #include "attn_common.h"
 #include "launchers.h"
 
@@ -34,10 +34,6 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeBf16Args a) {
                     [&](int uu) { return row(uu, 1); }, sm, wave, lane);
   float* part_base = a.partials + (size_t)grp * a.n_splits * G * kPartStride;
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
-  if (!finish_ticket<G>(sm, &a.counters[grp], (uint32_t)act, tid)) return;
-  merge_group<G>(sm, part_base, (uint32_t)(a.n_splits * G * kPartStride * 4), act, act, [](int k) { return k; }, nullptr,
-                 a.out + ((size_t)b * a.hkv * G + hk * G) * kD, tid, wave, lane);
-  if (tid == 0) a.counters[grp] = 0u;
 }
 
 DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len) {
@@ -56,7 +52,7 @@ DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len) {
   p.n_work = batch * hkv * p.n_splits_total;
   p.grid = ((p.n_work + 7) / 8) * 8;
   p.partial_floats = (size_t)batch * hkv * p.n_splits_total * group * kPartStride;
-  p.workspace_bytes = p.partial_floats * sizeof(float) + (size_t)batch * hkv * sizeof(uint32_t);
+  p.workspace_bytes = p.partial_floats * sizeof(float);
   return p;
 }
 

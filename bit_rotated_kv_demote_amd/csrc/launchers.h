@@ -64,8 +64,7 @@ struct DecodeArgs {
   const uint8_t* hist;
   const int32_t* page_table;
   const float* rot_k; const float* rot_v;
-  float* partials;            // workspace: [batch*Hkv][n_splits][G][130]
-  uint32_t* counters;         // workspace: [batch*Hkv]
+  float* partials;            // workspace: [batch*Hkv][n_splits][G][132]
   int hkv;
   int max_pages;
   int n_hist_splits;          // history splits per (sequence, KV head)
@@ -83,13 +82,26 @@ struct DecodeBf16Args {
   const uint16_t* kv;         // [num_pages][Hkv][2][16][128]
   const int32_t* page_table;
   float* partials;
-  uint32_t* counters;
   int hkv;
   int max_pages;
   int n_splits;
   int pages_per_split;
   int n_groups_total;
   int grid_per_xcd;
+};
+
+// Log-sum-exp merge of the decode partials, one workgroup per query head.
+struct MergeArgs {
+  const float* partials;      // [batch*Hkv][n_splits_total][group][132]
+  const int32_t* seq_len;     // [batch]
+  const float* rot;           // R_V for the rotated (history) records; unused when tiered == 0
+  float* out;                 // fp32 [batch][Hq][128]
+  int hkv;
+  int group;
+  int n_splits_total;         // record slots per (sequence, KV head)
+  int n_plain_slots;          // slots before the first rotated record (INT2: tile splits; BF16: 0)
+  int pages_per_split;
+  int tiered;                 // 1: INT2 tiers (plain tile splits + rotated history); 0: BF16 pages
 };
 
 // Decode split geometry, shared by the workspace-size query and the launch.
@@ -117,5 +129,6 @@ hipError_t launch_demote(const DemoteArgs& a, int batch, int max_count, bool rot
 hipError_t launch_prefill_route(const PrefillArgs& a, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeBf16Args& a, int group, int grid, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, int n_heads, hipStream_t st);
 
 }  // namespace oscar

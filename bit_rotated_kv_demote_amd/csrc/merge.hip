@@ -1,0 +1,162 @@
+// Log-sum-exp merge of the split partials that the decode kernels leave in
+// the workspace (flash-decoding split-K).  The history tier is attended in the
+// rotated space, so its merged output is turned back with the inverse
+// rotation before it joins the sink/recent part ("OSCAR: Offline Spectral
+// Covariance-Aware Rotation for 2-bit KV Cache Quantization" (gist.science),
+// 2.2 B "Kernel-Integration": inverse rotation inside the attention kernel).
+//
+// A second kernel on the same stream, one workgroup per (sequence, query
+// head): the kernel boundary publishes every record, so no ticket or
+// device-scope fence is needed, and all of a head's loads - its (m, l) pairs,
+// its record columns and its rows of R - are issued together, which makes the
+// merge one memory round trip instead of a chain of them in a single
+// workgroup per KV head.
+#include "attn_common.h"
+#include "launchers.h"
+
+namespace oscar {
+
+namespace {
+
+constexpr int kParts = 8;          // record rows handled side by side (256 threads / 32 float4 columns)
+constexpr int kMergeBatch = 8;     // record loads in flight per thread: 64 splits per round
+
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  __shared__ float w[kMaxSplits];
+  __shared__ float4 red[kParts][2][kD / 4];
+  __shared__ float oh[2][kD];      // weighted sums: plain part, rotated part
+  __shared__ float rr[2][kD];      // the two halves of (rotated part . R^T)
+  __shared__ float wred[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.group;
+  const int head = blockIdx.x;                       // b * Hq + (hk * G + h)
+  const int grp = head / G, h = head % G;
+  const int b = grp / a.hkv;
+  const int n = a.seq_len[b];
+  // the splits the first kernel filled for this sequence (clamped to the
+  // record slots, so that a length outside [1, max_seq_len] stays in bounds)
+  int n_plain, n_act;
+  if (a.tiered) {
+    const int hist_len = max(0, n - kSink - kRecent);
+    const int n_hist_pages = (hist_len + kPage - 1) / kPage;
+    const int n_tile = min(n, kSink) + min(max(n - kSink, 0), kRecent);
+    n_plain = min((n_tile + kTileTokens - 1) / kTileTokens, a.n_plain_slots);
+    n_act = n_plain + min((n_hist_pages + a.pages_per_split - 1) / a.pages_per_split,
+                          a.n_splits_total - a.n_plain_slots);
+  } else {
+    const int npages = (max(n, 0) + kPage - 1) / kPage;
+    n_plain = n_act = min((npages + a.pages_per_split - 1) / a.pages_per_split, a.n_splits_total);
+  }
+  if (n_act <= 0) {                 // no tokens: nothing to attend
+    if (tid < kD) a.out[(size_t)head * kD + tid] = 0.0f;
+    return;
+  }
+  // active split k: plain splits 0..n_plain-1, then the rotated ones, which
+  // sit after all n_plain_slots plain slots of the group's record area
+  const float* base = a.partials + (size_t)grp * a.n_splits_total * G * kPartStride + (size_t)h * kPartStride;
+  auto rec = [&](int k) {
+    const int s = k < n_plain ? k : a.n_plain_slots + (k - n_plain);
+    return base + (size_t)s * G * kPartStride;
+  };
+  const bool any_rot = n_act > n_plain;
+
+  // every load first: (m, l) pairs, the first round of record columns, R rows
+  const float2 ml0 = *reinterpret_cast<const float2*>(rec(min(tid, n_act - 1)) + kD);
+  const float2 ml1 = *reinterpret_cast<const float2*>(rec(min(tid + 256, n_act - 1)) + kD);
+  const int c4 = tid & 31, part = tid >> 5;
+  float4 v[kMergeBatch];
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u)
+    v[u] = *reinterpret_cast<const float4*>(rec(min(part + kParts * u, n_act - 1)) + 4 * c4);
+  // this thread's slice of R: row ri, columns [64 jh, 64 jh + 64)
+  const int ri = tid & (kD - 1), jh = tid >> 7;
+  float4 rrow[16];
+  if (any_rot) {
+    const float4* rp = reinterpret_cast<const float4*>(a.rot + (size_t)ri * kD + 64 * jh);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
+  }
+
+  // global max over the head's splits, weights, total sum
+  float mm = fmaxf(tid < n_act ? ml0.x : kMInit, tid + 256 < n_act ? ml1.x : kMInit);
+  mm = wave_max(mm);
+  if (lane == 0) wred[0][wave] = mm;
+  __syncthreads();
+  const float m_all = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  float ll = 0.0f;
+  if (tid < n_act) {
+    const float wk = __builtin_amdgcn_exp2f(ml0.x - m_all);
+    w[tid] = wk;
+    ll = wk * ml0.y;
+  }
+  if (tid + 256 < n_act) {
+    const float wk = __builtin_amdgcn_exp2f(ml1.x - m_all);
+    w[tid + 256] = wk;
+    ll = fmaf(wk, ml1.y, ll);
+  }
+  ll = wave_sum(ll);
+  if (lane == 0) wred[1][wave] = ll;
+  __syncthreads();
+  const float l_all = (wred[1][0] + wred[1][1]) + (wred[1][2] + wred[1][3]);
+
+  // weighted sums of the record columns, plain and rotated kept apart
+  float4 ap = make_float4(0.f, 0.f, 0.f, 0.f), ar = ap;
+  auto acc_into = [&](int k, const float4& x) {
+    const float wk = w[k];
+    float4& acc = k < n_plain ? ap : ar;
+    acc.x = fmaf(wk, x.x, acc.x); acc.y = fmaf(wk, x.y, acc.y);
+    acc.z = fmaf(wk, x.z, acc.z); acc.w = fmaf(wk, x.w, acc.w);
+  };
+#pragma unroll
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const int k = part + kParts * u;
+    if (k < n_act) acc_into(k, v[u]);
+  }
+  for (int k0 = part + kParts * kMergeBatch; k0 < n_act; k0 += kParts * kMergeBatch) {
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u)
+      v[u] = *reinterpret_cast<const float4*>(rec(min(k0 + kParts * u, n_act - 1)) + 4 * c4);
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int k = k0 + kParts * u;
+      if (k < n_act) acc_into(k, v[u]);
+    }
+  }
+  red[part][0][c4] = ap;
+  red[part][1][c4] = ar;
+  __syncthreads();
+  {
+    const int which = tid >> 7, j = tid & (kD - 1);
+    const float* rp = reinterpret_cast<const float*>(&red[0][which][0]) + j;
+    float s = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kParts; ++p) s += rp[p * 2 * kD];
+    oh[which][j] = s;
+  }
+  __syncthreads();
+  // inverse rotation of the history part: (y R^T)_i = sum_j y_j R[i][j]
+  float acc = 0.0f;
+  if (any_rot) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float4 y = *reinterpret_cast<const float4*>(&oh[1][64 * jh + 4 * e]);
+      acc = fmaf(y.x, rrow[e].x, acc);
+      acc = fmaf(y.y, rrow[e].y, acc);
+      acc = fmaf(y.z, rrow[e].z, acc);
+      acc = fmaf(y.w, rrow[e].w, acc);
+    }
+  }
+  rr[jh][ri] = acc;
+  __syncthreads();
+  if (tid < kD) a.out[(size_t)head * kD + tid] = (oh[0][tid] + (rr[0][tid] + rr[1][tid])) / l_all;
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int n_heads, hipStream_t st) {
+  if (n_heads <= 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3(n_heads), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace oscar

@@ -203,7 +203,6 @@ oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, 
   a.rot_k = pool->rot_k;
   a.rot_v = pool->rot_v;
   a.partials = static_cast<float*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<float*>(workspace) + plan.partial_floats);
   a.hkv = hkv;
   a.max_pages = pool->max_pages_per_seq;
   a.n_hist_splits = plan.n_hist_splits;
@@ -211,7 +210,20 @@ oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, 
   a.n_tile_splits = plan.n_tile_splits;
   a.n_groups_total = batch * hkv;
   a.grid_per_xcd = plan.grid / 8;
-  return hip_status(launch_decode(a, g, plan.grid, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(launch_decode(a, g, plan.grid, hs))) != OSCAR_OK) return st;
+  MergeArgs m{};
+  m.partials = a.partials;
+  m.seq_len = seq_len;
+  m.rot = pool->rot_v;
+  m.out = out;
+  m.hkv = hkv;
+  m.group = g;
+  m.n_splits_total = plan.n_splits_total;
+  m.n_plain_slots = plan.n_tile_splits;
+  m.pages_per_split = plan.pages_per_split;
+  m.tiered = 1;
+  return hip_status(launch_merge(m, batch * desc->num_q_heads, hs));
 }
 
 size_t oscar_decode_bf16_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
@@ -240,14 +252,26 @@ oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_po
   a.kv = static_cast<const uint16_t*>(pool->kv);
   a.page_table = pool->page_table;
   a.partials = static_cast<float*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(static_cast<float*>(workspace) + plan.partial_floats);
   a.hkv = hkv;
   a.max_pages = pool->max_pages_per_seq;
   a.n_splits = plan.n_splits_total;
   a.pages_per_split = plan.pages_per_split;
   a.n_groups_total = batch * hkv;
   a.grid_per_xcd = plan.grid / 8;
-  return hip_status(launch_decode_bf16(a, g, plan.grid, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(launch_decode_bf16(a, g, plan.grid, hs))) != OSCAR_OK) return st;
+  MergeArgs m{};
+  m.partials = a.partials;
+  m.seq_len = seq_len;
+  m.rot = nullptr;
+  m.out = out;
+  m.hkv = hkv;
+  m.group = g;
+  m.n_splits_total = plan.n_splits_total;
+  m.n_plain_slots = 0;
+  m.pages_per_split = plan.pages_per_split;
+  m.tiered = 0;
+  return hip_status(launch_merge(m, batch * desc->num_q_heads, hs));
 }
 
 }  // extern "C"

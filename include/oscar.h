@@ -214,10 +214,12 @@ oscar_status oscar_prefill(const oscar_layer_desc* desc, const oscar_pool* pool,
  * q: device bf16 [batch][Hq][128].  out: device fp32 [batch][Hq][128].
  * seq_len, seq_slot: device int32 [batch]; every seq_len[b] must be in
  * [1, max_seq_len].  workspace: device, at least
- * oscar_decode_workspace_bytes(desc, batch, max_seq_len) bytes, zero-filled
- * once by the caller before its first use; each call leaves it zero-filled
- * again.  Errors: OSCAR_ERR_CAPACITY if ws_bytes is too small or
- * max_seq_len needs more pages than max_pages_per_seq.
+ * oscar_decode_workspace_bytes(desc, batch, max_seq_len) bytes, needing no
+ * initialisation: the call runs as two kernels on `stream` (the split
+ * partials, then their merge) that pass the partials through it, so calls
+ * sharing one workspace must be ordered (one stream).  Errors:
+ * OSCAR_ERR_CAPACITY if ws_bytes is too small or max_seq_len needs more pages
+ * than max_pages_per_seq.
  */
 oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool,
                           const int32_t* seq_slot, const int32_t* seq_len, const void* q,
