@@ -316,6 +316,24 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
   if (item >= a.n_groups_total * n_split_total) return;
   const int grp = item / n_split_total, split = item % n_split_total;
   const int b = grp / a.hkv, hk = grp % a.hkv;
+  const bool is_tile = split < a.n_tile_splits;
+  // History splits need q . R_K, whose operands do not depend on the
+  // sequence's length: their loads go out before the lengths are read.
+  // (Thread (c4, rs) takes output columns [4 c4, 4 c4 + 4) and rows
+  // [16 rs, 16 rs + 16) of R_K: 16 float4 loads.)
+  const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
+  const int c4 = tid & 31, rs = tid >> 5;
+  constexpr int kQWords = G * kD / 2;               // q as 32-bit words (two bf16 each)
+  constexpr int kQPer = (kQWords + 255) / 256;
+  const uint32_t* qg32 = reinterpret_cast<const uint32_t*>(qg);
+  float4 rq[16];
+  uint32_t qv[kQPer];
+  if (!is_tile) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(a.rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
+#pragma unroll
+    for (int e = 0; e < kQPer; ++e) qv[e] = qg32[min(tid + 256 * e, kQWords - 1)];   // unconditional
+  }
   const int slot = a.seq_slot ? a.seq_slot[b] : b;
   const int n = a.seq_len[b];
   const int hist_len = max(0, n - kSink - kRecent);
@@ -325,7 +343,6 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
   const int n_recent_used = min(max(n - kSink, 0), kRecent);
   const int n_tile = n_sink_used + n_recent_used;
   const int act_tile = (n_tile + kTileTokens - 1) / kTileTokens;
-  const bool is_tile = split < a.n_tile_splits;
   const int hs = split - a.n_tile_splits;
   if (is_tile ? (split >= act_tile) : (hs >= act_hist)) return;
 
@@ -341,30 +358,19 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
       const int pos = recent_first + (u - n_sink_used);
       return ring + (ring_base + ((pos - kSink) & (kRecent - 1))) * kD;
     };
-    bf16_span_wave<G>(a.q + ((size_t)b * a.hkv * G + hk * G) * kD, min(kTileTokens, n_tile - u0),
+    bf16_span_wave<G>(qg, min(kTileTokens, n_tile - u0),
                       [&](int uu) { return row(a.sink_k, a.recent_k, uu); },
                       [&](int uu) { return row(a.sink_v, a.recent_v, uu); }, sm, wave, lane);
   } else {
     const int pg_begin = hs * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);
     const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
-    // page ids of this wave's steps (steps wave, wave + 4, ...): one load per lane
+    // page ids of this wave's steps (steps wave, wave + 4, ...): one load
+    // per lane, then this wave's first step: the prologue below waits only
+    // for the older loads, so the loop is entered with exactly the page
+    // loads in flight that every later iteration also has.
     const int32_t ids = pt_row[pg_begin + min(kStepPages * (wave + 4 * (lane / kStepPages)) + lane % kStepPages,
                                               pg_end - pg_begin - 1)];
-    // q . R_K operands first (thread (c4, rs) takes output columns
-    // [4 c4, 4 c4 + 4) and rows [16 rs, 16 rs + 16) of R_K: 16 float4 loads),
-    // then this wave's first step: the prologue waits only for the
-    // older loads, so the loop is entered with exactly the page loads in
-    // flight that every later iteration also has.
-    const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
-    const int c4 = tid & 31, rs = tid >> 5;
-    float4 rq[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(a.rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
-    constexpr int kQPer = (G * kD + 255) / 256;
-    uint16_t qv[kQPer];
-#pragma unroll
-    for (int e = 0; e < kQPer; ++e) qv[e] = qg[min(tid + 256 * e, G * kD - 1)];   // unconditional
     u32x4_t c_first[kStepPages];
     u32x2_t m_first[kStepPages];
     // unconditional (the ids are clamped to pages of this split): the same
@@ -376,7 +382,10 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {
       const int idx = tid + 256 * e;
-      if (idx < G * kD) sm.q[idx / kD][idx % kD] = bf16_bits_to_float(qv[e]);
+      if (idx < kQWords) {
+        sm.q[(2 * idx) / kD][(2 * idx) % kD] = bf16_bits_to_float(qv[e] & 0xFFFFu);
+        sm.q[(2 * idx) / kD][(2 * idx) % kD + 1] = bf16_bits_to_float(qv[e] >> 16);
+      }
     }
     __syncthreads();
     // lanes l and l + 32 of a wave hold row slices 2 wave and 2 wave + 1 of

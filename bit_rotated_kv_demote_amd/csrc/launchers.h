@@ -99,7 +99,7 @@ struct MergeArgs {
   int hkv;
   int group;
   int n_splits_total;         // record slots per (sequence, KV head)
-  int n_plain_slots;          // slots before the first rotated record (INT2: tile splits; BF16: 0)
+  int n_plain_slots;          // slots before the first rotated record (INT2: tile splits; BF16: all)
   int pages_per_split;
   int tiered;                 // 1: INT2 tiers (plain tile splits + rotated history); 0: BF16 pages
 };

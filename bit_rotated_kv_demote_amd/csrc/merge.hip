@@ -32,64 +32,65 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int head = blockIdx.x;                       // b * Hq + (hk * G + h)
   const int grp = head / G, h = head % G;
   const int b = grp / a.hkv;
-  const int n = a.seq_len[b];
-  // the splits the first kernel filled for this sequence (clamped to the
-  // record slots, so that a length outside [1, max_seq_len] stays in bounds)
-  int n_plain, n_act;
-  if (a.tiered) {
-    const int hist_len = max(0, n - kSink - kRecent);
-    const int n_hist_pages = (hist_len + kPage - 1) / kPage;
-    const int n_tile = min(n, kSink) + min(max(n - kSink, 0), kRecent);
-    n_plain = min((n_tile + kTileTokens - 1) / kTileTokens, a.n_plain_slots);
-    n_act = n_plain + min((n_hist_pages + a.pages_per_split - 1) / a.pages_per_split,
-                          a.n_splits_total - a.n_plain_slots);
-  } else {
-    const int npages = (max(n, 0) + kPage - 1) / kPage;
-    n_plain = n_act = min((npages + a.pages_per_split - 1) / a.pages_per_split, a.n_splits_total);
-  }
-  if (n_act <= 0) {                 // no tokens: nothing to attend
-    if (tid < kD) a.out[(size_t)head * kD + tid] = 0.0f;
-    return;
-  }
-  // active split k: plain splits 0..n_plain-1, then the rotated ones, which
-  // sit after all n_plain_slots plain slots of the group's record area
-  const float* base = a.partials + (size_t)grp * a.n_splits_total * G * kPartStride + (size_t)h * kPartStride;
-  auto rec = [&](int k) {
-    const int s = k < n_plain ? k : a.n_plain_slots + (k - n_plain);
-    return base + (size_t)s * G * kPartStride;
-  };
-  const bool any_rot = n_act > n_plain;
+  const int n_slots = a.n_splits_total;
+  // record slot s of this head: slots [0, n_plain_slots) hold output-space
+  // partials, the rest rotated-space ones (history)
+  const float* base = a.partials + (size_t)grp * n_slots * G * kPartStride + (size_t)h * kPartStride;
+  auto rec = [&](int s) { return base + (size_t)min(s, n_slots - 1) * G * kPartStride; };
 
-  // every load first: (m, l) pairs, the first round of record columns, R rows
-  const float2 ml0 = *reinterpret_cast<const float2*>(rec(min(tid, n_act - 1)) + kD);
-  const float2 ml1 = *reinterpret_cast<const float2*>(rec(min(tid + 256, n_act - 1)) + kD);
+  // Every load first, before the sequence length is known: (m, l) of every
+  // slot, the first round of record columns and this thread's slice of R
+  // (row ri, columns [64 jh, 64 jh + 64)).  Slots the first kernel left
+  // untouched for this length are masked below, never multiplied in.
+  const float2 ml0 = *reinterpret_cast<const float2*>(rec(tid) + kD);
+  const float2 ml1 = *reinterpret_cast<const float2*>(rec(tid + 256) + kD);
   const int c4 = tid & 31, part = tid >> 5;
   float4 v[kMergeBatch];
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u)
-    v[u] = *reinterpret_cast<const float4*>(rec(min(part + kParts * u, n_act - 1)) + 4 * c4);
-  // this thread's slice of R: row ri, columns [64 jh, 64 jh + 64)
+  for (int u = 0; u < kMergeBatch; ++u) v[u] = *reinterpret_cast<const float4*>(rec(part + kParts * u) + 4 * c4);
   const int ri = tid & (kD - 1), jh = tid >> 7;
   float4 rrow[16];
-  if (any_rot) {
+  if (a.tiered) {
     const float4* rp = reinterpret_cast<const float4*>(a.rot + (size_t)ri * kD + 64 * jh);
 #pragma unroll
     for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
   }
 
-  // global max over the head's splits, weights, total sum
-  float mm = fmaxf(tid < n_act ? ml0.x : kMInit, tid + 256 < n_act ? ml1.x : kMInit);
+  // the splits the first kernel filled for this sequence (clamped to the
+  // slots, so that a length outside [1, max_seq_len] stays in bounds)
+  const int n = a.seq_len[b];
+  int n_plain, n_rot;
+  if (a.tiered) {
+    const int hist_len = max(0, n - kSink - kRecent);
+    const int n_hist_pages = (hist_len + kPage - 1) / kPage;
+    const int n_tile = min(n, kSink) + min(max(n - kSink, 0), kRecent);
+    n_plain = min((n_tile + kTileTokens - 1) / kTileTokens, a.n_plain_slots);
+    n_rot = min((n_hist_pages + a.pages_per_split - 1) / a.pages_per_split, n_slots - a.n_plain_slots);
+  } else {
+    const int npages = (max(n, 0) + kPage - 1) / kPage;
+    n_plain = min((npages + a.pages_per_split - 1) / a.pages_per_split, a.n_plain_slots);
+    n_rot = 0;
+  }
+  if (n_plain + n_rot <= 0) {       // no tokens: nothing to attend
+    if (tid < kD) a.out[(size_t)head * kD + tid] = 0.0f;
+    return;
+  }
+  auto active = [&](int s) { return s < a.n_plain_slots ? s < n_plain : s - a.n_plain_slots < n_rot; };
+
+  // global max over the head's active splits, weights, total sum
+  const bool act0 = tid < n_slots && active(tid), act1 = tid + 256 < n_slots && active(tid + 256);
+  float mm = fmaxf(act0 ? ml0.x : kMInit, act1 ? ml1.x : kMInit);
   mm = wave_max(mm);
   if (lane == 0) wred[0][wave] = mm;
   __syncthreads();
   const float m_all = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
   float ll = 0.0f;
-  if (tid < n_act) {
+  if (act0) {
     const float wk = __builtin_amdgcn_exp2f(ml0.x - m_all);
     w[tid] = wk;
     ll = wk * ml0.y;
   }
-  if (tid + 256 < n_act) {
+  if (act1) {
     const float wk = __builtin_amdgcn_exp2f(ml1.x - m_all);
     w[tid + 256] = wk;
     ll = fmaf(wk, ml1.y, ll);
@@ -101,26 +102,20 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
   // weighted sums of the record columns, plain and rotated kept apart
   float4 ap = make_float4(0.f, 0.f, 0.f, 0.f), ar = ap;
-  auto acc_into = [&](int k, const float4& x) {
-    const float wk = w[k];
-    float4& acc = k < n_plain ? ap : ar;
+  auto acc_into = [&](int s, const float4& x) {
+    if (s >= n_slots || !active(s)) return;
+    const float wk = w[s];
+    float4& acc = s < a.n_plain_slots ? ap : ar;
     acc.x = fmaf(wk, x.x, acc.x); acc.y = fmaf(wk, x.y, acc.y);
     acc.z = fmaf(wk, x.z, acc.z); acc.w = fmaf(wk, x.w, acc.w);
   };
 #pragma unroll
-  for (int u = 0; u < kMergeBatch; ++u) {
-    const int k = part + kParts * u;
-    if (k < n_act) acc_into(k, v[u]);
-  }
-  for (int k0 = part + kParts * kMergeBatch; k0 < n_act; k0 += kParts * kMergeBatch) {
+  for (int u = 0; u < kMergeBatch; ++u) acc_into(part + kParts * u, v[u]);
+  for (int s0 = part + kParts * kMergeBatch; s0 < n_slots; s0 += kParts * kMergeBatch) {
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u)
-      v[u] = *reinterpret_cast<const float4*>(rec(min(k0 + kParts * u, n_act - 1)) + 4 * c4);
+    for (int u = 0; u < kMergeBatch; ++u) v[u] = *reinterpret_cast<const float4*>(rec(s0 + kParts * u) + 4 * c4);
 #pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int k = k0 + kParts * u;
-      if (k < n_act) acc_into(k, v[u]);
-    }
+    for (int u = 0; u < kMergeBatch; ++u) acc_into(s0 + kParts * u, v[u]);
   }
   red[part][0][c4] = ap;
   red[part][1][c4] = ar;
@@ -136,7 +131,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   __syncthreads();
   // inverse rotation of the history part: (y R^T)_i = sum_j y_j R[i][j]
   float acc = 0.0f;
-  if (any_rot) {
+  if (n_rot > 0) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float4 y = *reinterpret_cast<const float4*>(&oh[1][64 * jh + 4 * e]);

@@ -268,7 +268,7 @@ oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_po
   m.hkv = hkv;
   m.group = g;
   m.n_splits_total = plan.n_splits_total;
-  m.n_plain_slots = 0;
+  m.n_plain_slots = plan.n_splits_total;
   m.pages_per_split = plan.pages_per_split;
   m.tiered = 0;
   return hip_status(launch_merge(m, batch * desc->num_q_heads, hs));
