@@ -483,7 +483,7 @@ def main():
     hq, hkv, n0 = 32, 8, 32768
     res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001)
     dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
-    extra = {"decode_kernel_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),
+    extra = {"decode_call_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),
              "decode_algorithmic_bytes": res["decode_bytes"], "decode_GBps": round(dec_gbps, 1),
              "pools": res["layers"], "pool_MB_total": round(res["pool_mb"], 1),
              "calibrate_host_s": round(res["calib_s"], 2)}
@@ -495,7 +495,7 @@ def main():
         del b
         r128 = run_tiered(torch, hq, hkv, 131072, 8, min(args.steps, 160), 8, seed=1002, calib=res["host"][2:])
         g128 = r128["decode_bytes"] / (r128["decode_us"] * 1e3)
-        extra["ctx128k"] = {"us_per_step": round(r128["us_per_step"], 3), "decode_kernel_us": round(r128["decode_us"], 3),
+        extra["ctx128k"] = {"us_per_step": round(r128["us_per_step"], 3), "decode_call_us": round(r128["decode_us"], 3),
                             "append_kernel_us": round(r128["append_us"], 3), "decode_GBps": round(g128, 1),
                             "decode_frac_of_8TBps": round(g128 / HBM_PEAK_GBPS, 4),
                             "decode_algorithmic_bytes": r128["decode_bytes"], "pools": r128["layers"],
