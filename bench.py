@@ -351,6 +351,52 @@ def run_fixed_memory(torch, steps, calib, seed=1004, layers=36, budget_gb=64.0):
     return res
 
 
+def run_rotation_study(torch, seed=1006, hq=32, hkv=8, n_calib=1024, n_ctx=8192):
+    """Rotation variants on a layer with planted covariance structure (Qwen3-4B
+    attention shape): host calibration with each rotation on n_calib tokens,
+    device prefill of an n_ctx-token sequence (bulk demotion) and one device
+    decode; error = relative L2 of the output against fp64 attention over the
+    BF16 keys and values (the tiers' quantisation error only).  The exact
+    reference is plain attention, computed in NumPy here."""
+    from bit_rotated_kv_demote_amd import binding, synth
+    from bit_rotated_kv_demote_amd.pool import TieredKV, bf16_tensor
+    qc, kc, vc = synth.planted_layer(np.random.default_rng(seed), n_calib, hq, hkv)
+    qt, kt, vt = synth.planted_layer(np.random.default_rng(seed + 1), n_ctx, hq, hkv)
+    kc, vc = synth.bf16_bits_to_f32(kc), synth.bf16_bits_to_f32(vc)
+    q = np.ascontiguousarray(synth.to_bf16_bits(qt[-1:]))
+    qf = synth.bf16_bits_to_f32(q)[0].astype(np.float64)
+    kf = synth.bf16_bits_to_f32(kt).astype(np.float64)
+    vf = synth.bf16_bits_to_f32(vt).astype(np.float64)
+    g = hq // hkv
+    exact = np.empty((hq, 128))
+    for h in range(hq):
+        lg = kf[:, h // g] @ qf[h] / math.sqrt(128.0)
+        w = np.exp(lg - lg.max())
+        exact[h] = (w / w.sum()) @ vf[:, h // g]
+    max_pages = math.ceil((n_ctx - 320) / 16)
+    pt = synth.page_permutation(np.random.default_rng(seed + 2), max_pages)[None, :].astype(np.int32)
+    lens = torch.tensor([n_ctx], dtype=torch.int32, device="cuda")
+    errs, calib_s = {}, {}
+    for name, code in (("spectral", binding.ROT_SPECTRAL), ("key_attn", binding.ROT_KEY_ATTN),
+                       ("hadamard", binding.ROT_HADAMARD), ("identity", binding.ROT_IDENTITY)):
+        outs = [torch.zeros((128, 128), dtype=torch.float32), torch.zeros((128, 128), dtype=torch.float32),
+                torch.zeros(128, dtype=torch.float32), torch.zeros(128, dtype=torch.float32)]
+        t0 = time.perf_counter()
+        binding.oscar_calibrate(binding.layer_desc(hq, hkv), torch.from_numpy(qc), torch.from_numpy(kc),
+                                torch.from_numpy(vc), *outs, rotation=code)
+        calib_s[name] = round(time.perf_counter() - t0, 2)
+        r_k, r_v, t_k, t_v = [o.numpy() for o in outs]
+        pool = TieredKV(hq, hkv, 1, max_pages, max_pages, r_k, r_v, t_k, t_v, page_table=pt)
+        pool.prefill(lens, bf16_tensor(kt[None]), bf16_tensor(vt[None]))
+        out = pool.decode(bf16_tensor(q), lens, n_ctx).cpu().numpy()[0].astype(np.float64)
+        errs[name] = round(float(np.linalg.norm(out - exact) / np.linalg.norm(exact)), 4)
+        del pool
+    torch.cuda.empty_cache()
+    return {"workload": f"planted covariance layer, {hq} q / {hkv} KV heads, calibration {n_calib} tokens, "
+                        f"context {n_ctx} tokens (64 sink / {n_ctx - 320} INT2 / 256 recent), one decode query per head",
+            "rel_l2_vs_bf16_attention": errs, "calibrate_host_s": calib_s}
+
+
 def run_demote(torch, reps, seed):
     """Bulk demotion of a 4096-token chunk for 16 sequences x 8 KV heads."""
     from bit_rotated_kv_demote_amd import synth
@@ -507,6 +553,7 @@ def main():
         del r128, b128
         extra["ragged_gqa8"] = run_ragged_gqa8(torch, min(args.steps, 50), res["host"][2:])
         extra["fixed_memory_16k"] = run_fixed_memory(torch, min(args.steps, 20), res["host"][2:])
+        extra["rotation_study"] = run_rotation_study(torch)
         d = run_demote(torch, 20, 1004)
         extra["demote_tok_per_s"] = round(d["tok_per_s"], 0)
         extra["demote_us_per_chunk"] = round(d["us"], 2)

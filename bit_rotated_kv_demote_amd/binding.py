@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libamdoscar.so")
 
 OSCAR_SRC_BF16 = 0
 OSCAR_SRC_F32_ROTATED = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_append", "oscar_demote",
             "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_bf16",
@@ -49,7 +49,11 @@ class Bf16Pool(ctypes.Structure):
 
 
 class CalibOpts(ctypes.Structure):
-    _fields_ = [("hadamard_block", ctypes.c_int32), ("clip_percentile", ctypes.c_float)]
+    _fields_ = [("hadamard_block", ctypes.c_int32), ("clip_percentile", ctypes.c_float), ("rotation", ctypes.c_int32)]
+
+
+# oscar_calib_opts.rotation
+ROT_SPECTRAL, ROT_KEY_ATTN, ROT_HADAMARD, ROT_IDENTITY = 0, 1, 2, 3
 
 
 _lib = None
@@ -123,9 +127,10 @@ def make_bf16_pool(kv, page_table) -> Bf16Pool:
     return Bf16Pool(kv.data_ptr(), page_table.data_ptr(), page_table.shape[0], page_table.shape[1], kv.shape[0])
 
 
-def oscar_calibrate(desc, q, k, v, rot_k, rot_v, clip_k, clip_v, hadamard_block=32, clip_percentile=99.0):
+def oscar_calibrate(desc, q, k, v, rot_k, rot_v, clip_k, clip_v, hadamard_block=32, clip_percentile=99.0,
+                    rotation=ROT_SPECTRAL):
     """Host tensors: q [N,Hq,128], k/v [N,Hkv,128] fp32; outputs fp32 [128,128] / [128]."""
-    opts = CalibOpts(hadamard_block, clip_percentile)
+    opts = CalibOpts(hadamard_block, clip_percentile, rotation)
     _check("oscar_calibrate", load().oscar_calibrate(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(k),
                                                       _ptr(v), q.shape[0], _ptr(rot_k), _ptr(rot_v),
                                                       _ptr(clip_k), _ptr(clip_v)))

@@ -1,4 +1,5 @@
-// Offline calibration of one layer on the host (fp64).
+// Offline calibration of one layer on the host (fp64), with the method's
+// rotation or one of the baselines the pages compare it against.
 //
 // "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV Cache
 // Quantization" (gist.science), 2.1 and 2.2 A: the key target is the query
@@ -48,6 +49,8 @@ void query_covariance(const float* q, int64_t n, int hq, double* c) {
 }
 
 // C_S = (1/(N Hq)) sum_h sum_n o_{h,n}^T o_{h,n}, o_{h,n} = sum_{m<=n} softmax_m(q_n . k_m / sqrt(d)) v_m.
+// With the keys passed as v this is the attention-weighted key covariance
+// C_SK = (1/(N Hq)) sum_h (S_h K)^T (S_h K).
 void score_covariance(const float* q, const float* k, const float* v, int64_t n, int hq, int hkv, double* c) {
   std::fill(c, c + D * D, 0.0);
   const int g = hq / hkv;
@@ -192,20 +195,39 @@ void clip_thresholds(const float* x, int64_t rows, const float* r, double pct, f
 
 }  // namespace
 
-int calibrate_layer(int hq, int hkv, int hadamard_block, float percentile, const float* q, const float* k,
-                    const float* v, int64_t n, float* rot_k, float* rot_v, float* clip_k, float* clip_v) {
+int calibrate_layer(int hq, int hkv, int hadamard_block, float percentile, int rotation, const float* q,
+                    const float* k, const float* v, int64_t n, float* rot_k, float* rot_v, float* clip_k,
+                    float* clip_v) {
   for (const float* p : {q, k, v}) {
     const int64_t cnt = n * (p == q ? hq : hkv) * D;
     for (int64_t i = 0; i < cnt; ++i)
       if (!std::isfinite(p[i])) return -1;
   }
-  std::vector<double> cq(D * D), cs(D * D), uq(D * D), us(D * D);
-  query_covariance(q, n, hq, cq.data());
-  score_covariance(q, k, v, n, hq, hkv, cs.data());
-  eigenbasis(cq.data(), uq.data());
-  eigenbasis(cs.data(), us.data());
-  compose_rotation(uq.data(), hadamard_block, rot_k);
-  compose_rotation(us.data(), hadamard_block, rot_v);
+  std::vector<double> ck(D * D), cs(D * D), uk(D * D, 0.0), us(D * D, 0.0);
+  switch (rotation) {
+    case kRotSpectral:                 // key target C_Q, value target C_S
+    case kRotKeyAttn:                  // key target C_SK, value target C_S
+      if (rotation == kRotSpectral)
+        query_covariance(q, n, hq, ck.data());
+      else
+        score_covariance(q, k, k, n, hq, hkv, ck.data());
+      score_covariance(q, k, v, n, hq, hkv, cs.data());
+      eigenbasis(ck.data(), uk.data());
+      eigenbasis(cs.data(), us.data());
+      compose_rotation(uk.data(), hadamard_block, rot_k);
+      compose_rotation(us.data(), hadamard_block, rot_v);
+      break;
+    case kRotHadamard:                 // U = I: R = H P_br
+      for (int i = 0; i < D; ++i) uk[i * D + i] = 1.0;
+      compose_rotation(uk.data(), hadamard_block, rot_k);
+      std::copy(rot_k, rot_k + D * D, rot_v);
+      break;
+    case kRotIdentity:                 // R = I
+      for (int i = 0; i < D * D; ++i) rot_k[i] = rot_v[i] = (i % (D + 1) == 0) ? 1.0f : 0.0f;
+      break;
+    default:
+      return -2;
+  }
   clip_thresholds(k, n * hkv, rot_k, percentile, clip_k);
   clip_thresholds(v, n * hkv, rot_v, percentile, clip_v);
   for (int j = 0; j < D; ++j)

@@ -67,9 +67,10 @@ oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opt
   if (!opts || !q || !k || !v || !rot_k || !rot_v || !clip_k || !clip_v || n_tokens < 2) return OSCAR_ERR_INVALID;
   if (opts->hadamard_block != 32 && opts->hadamard_block != 128) return OSCAR_ERR_UNSUPPORTED;
   if (!(opts->clip_percentile > 0.0f && opts->clip_percentile <= 100.0f)) return OSCAR_ERR_INVALID;
+  if (opts->rotation < OSCAR_ROT_SPECTRAL || opts->rotation > OSCAR_ROT_IDENTITY) return OSCAR_ERR_INVALID;
   const int rc = calibrate_layer(desc->num_q_heads, desc->num_kv_heads, opts->hadamard_block, opts->clip_percentile,
-                                 q, k, v, n_tokens, rot_k, rot_v, clip_k, clip_v);
-  return rc == 0 ? OSCAR_OK : OSCAR_ERR_NUMERIC;
+                                 opts->rotation, q, k, v, n_tokens, rot_k, rot_v, clip_k, clip_v);
+  return rc == 0 ? OSCAR_OK : (rc == -2 ? OSCAR_ERR_INVALID : OSCAR_ERR_NUMERIC);
 }
 
 oscar_status oscar_append(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,

@@ -112,3 +112,34 @@ CONFIGS = {
     3: LayerShape("qwen3-fixedmem-16k", 32, 8, 1, 16384, 1),
     4: LayerShape("qwen3-32b-ragged", 64, 8, 16, 65536, 1),
 }
+
+
+def planted_layer(rng: np.random.Generator, n: int, hq: int, hkv: int, n_query_dirs: int = 16,
+                  key_side_scale: float = 8.0, n_key_side_dirs: int = 8):
+    """A layer with planted covariance structure, for comparing rotations.
+
+    One seeded orthonormal basis B: queries have energy 1 in its first
+    ``n_query_dirs`` directions and 0.05 elsewhere; keys have standard
+    deviation ``key_side_scale`` in the next ``n_key_side_dirs`` directions
+    (energy the queries never look at) and 1 elsewhere; values have standard
+    deviation 3 in the first 8 directions of a second basis and 1 elsewhere.
+    Four seeded raw channels of K are scaled by 6 and two of V by 4.
+    Returns q as float32 [n, hq, 128] (bf16-representable) and K, V as bf16
+    bits [n, hkv, 128].  Random draws and casts only.
+    """
+    d = HEAD_DIM
+    b_qk = random_rotation(rng, d).astype(np.float64)
+    b_v = random_rotation(rng, d).astype(np.float64)
+    sq = np.full(d, 0.05)
+    sq[:n_query_dirs] = 1.0
+    sk = np.ones(d)
+    sk[n_query_dirs:n_query_dirs + n_key_side_dirs] = key_side_scale
+    sv = np.ones(d)
+    sv[:8] = 3.0
+    q = (rng.standard_normal((n, hq, d)) * sq) @ b_qk.T
+    k = (rng.standard_normal((n, hkv, d)) * sk) @ b_qk.T
+    v = (rng.standard_normal((n, hkv, d)) * sv) @ b_v.T
+    oc = np.sort(rng.choice(d, 4, replace=False))
+    k[..., oc] *= 6.0
+    v[..., oc[:2]] *= 4.0
+    return (bf16_bits_to_f32(to_bf16_bits(q)), to_bf16_bits(k), to_bf16_bits(v))

@@ -74,7 +74,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 1
+#define OSCAR_ABI_VERSION 2
 
 typedef enum {
   OSCAR_OK = 0,
@@ -112,9 +112,24 @@ typedef struct {
   const float* clip_v;         /*   clip thresholds, 0 < tau <= 65504        */
 } oscar_pool;
 
+/* Rotation that oscar_calibrate builds (oscar_calib_opts.rotation). */
+enum {
+  OSCAR_ROT_SPECTRAL = 0,      /* the method: R_K = U_Q H P_br, R_V = U_S H P_br
+                                  ([gist] 2.2 A)                               */
+  OSCAR_ROT_KEY_ATTN = 1,      /* R_K from the eigenbasis of the attention-
+                                  weighted key covariance
+                                  C_SK = (1/(N Hq)) sum_h (S_h K)^T (S_h K),
+                                  the value target with keys in place of
+                                  values; R_V as in OSCAR_ROT_SPECTRAL        */
+  OSCAR_ROT_HADAMARD = 2,      /* R_K = R_V = H P_br: the data-blind rotation
+                                  the pages compare against ([gist] 3 and 4) */
+  OSCAR_ROT_IDENTITY = 3       /* R_K = R_V = I: plain INT2 ([gist] 4)        */
+};
+
 typedef struct {
   int32_t hadamard_block;      /* 32 (one quantisation group) or 128         */
   float clip_percentile;       /* e.g. 99.0                                   */
+  int32_t rotation;            /* OSCAR_ROT_*                                 */
 } oscar_calib_opts;
 
 /* Source formats accepted by oscar_demote. */
@@ -143,10 +158,13 @@ const char* oscar_status_string(oscar_status s);
  *         heads, separately for K and V.
  * In:  q host fp32 [n_tokens][Hq][128]; k, v host fp32 [n_tokens][Hkv][128]
  *      (token-major, one calibration sequence, causal).
+ * opts->rotation picks the rotation (OSCAR_ROT_SPECTRAL is the method; the
+ * others are the baselines and the alternative key target above); the clip
+ * thresholds are always the percentiles of the chosen rotation's outputs.
  * Out: rot_k, rot_v host fp32 [128][128]; clip_k, clip_v host fp32 [128].
  * Synchronous, CPU only, uses up to the machine's cores.  Errors:
- * OSCAR_ERR_INVALID (null pointer, n_tokens < 2), OSCAR_ERR_UNSUPPORTED,
- * OSCAR_ERR_NUMERIC (non-finite input or tau > 65504).
+ * OSCAR_ERR_INVALID (null pointer, n_tokens < 2, unknown rotation),
+ * OSCAR_ERR_UNSUPPORTED, OSCAR_ERR_NUMERIC (non-finite input or tau > 65504).
  */
 oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opts* opts,
                              const float* q, const float* k, const float* v, int64_t n_tokens,

@@ -49,6 +49,11 @@ R8  Tiers: positions [0, 64) are the BF16 sink, the last 256 positions the
     h % 16).  A decode step appends before it attends.
 R9  Softmax scale 1/sqrt(128); GQA head h reads KV head h // (Hq / Hkv);
     output in fp32 (oracle: fp64).
+R10 Rotation variants for comparison: besides the method's R, the key
+    eigenbasis may come from the attention-weighted key covariance
+    (1/N) K^T S^T S K (pooled like C_S), and the baselines are R = H P_br
+    (data-blind Hadamard) and R = I (plain INT2); the clip thresholds are
+    always taken after the chosen rotation.
 """
 from __future__ import annotations
 
@@ -194,13 +199,39 @@ def clip_thresholds(x: np.ndarray, r: np.ndarray, percentile: float = 99.0) -> n
     return np.percentile(np.abs(y), percentile, axis=0, method="linear").astype(np.float32)
 
 
-def calibrate(q, k, v, hadamard_block_size: int = GROUP, percentile: float = 99.0):
+def key_attention_covariance(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """Attention-weighted key covariance C_SK = (1/N) K^T S^T S K: the value
+    target of [gist] 2.2 A with the keys in the place of the values (the
+    alternative key target, reading R10)."""
+    return score_covariance(q, k, k)
+
+
+# rotations calibrate() can build (reading R10): the method and the baselines
+ROTATIONS = ("spectral", "key_attn", "hadamard", "identity")
+
+
+def calibrate(q, k, v, hadamard_block_size: int = GROUP, percentile: float = 99.0, rotation: str = "spectral"):
     """Offline calibration of one layer: returns (R_K, R_V, tau_K, tau_V),
-    R as float32 [d, d] (y = x . R) and tau as float32 [d]."""
-    c_q = query_covariance(q)
-    c_s = score_covariance(q, k, v)
-    r_k = composite_rotation(eigenbasis(c_q), hadamard_block_size).astype(np.float32)
-    r_v = composite_rotation(eigenbasis(c_s), hadamard_block_size).astype(np.float32)
+    R as float32 [d, d] (y = x . R) and tau as float32 [d].
+
+    rotation "spectral" is the method ([gist] 2.2 A: R_K = U_Q H P_br,
+    R_V = U_S H P_br); "key_attn" takes the key eigenbasis from C_SK instead
+    of C_Q; "hadamard" (R = H P_br, data-blind) and "identity" (R = I, plain
+    INT2) are the baselines of [gist] 3 and 4."""
+    d = HEAD_DIM
+    if rotation in ("spectral", "key_attn"):
+        c_k = query_covariance(q) if rotation == "spectral" else key_attention_covariance(q, k)
+        c_s = score_covariance(q, k, v)
+        r_k = composite_rotation(eigenbasis(c_k), hadamard_block_size)
+        r_v = composite_rotation(eigenbasis(c_s), hadamard_block_size)
+    elif rotation == "hadamard":
+        r_k = r_v = composite_rotation(np.eye(d), hadamard_block_size)
+    elif rotation == "identity":
+        r_k = r_v = np.eye(d)
+    else:
+        raise ValueError(rotation)
+    r_k = np.asarray(r_k, np.float32)
+    r_v = np.asarray(r_v, np.float32)
     tau_k = clip_thresholds(k, r_k, percentile)
     tau_v = clip_thresholds(v, r_v, percentile)
     return r_k, r_v, tau_k, tau_v

@@ -97,13 +97,13 @@ def _calib_inputs(n=192, hq=4, hkv=2, seed=0):
     return q, k, v
 
 
-def _host_calibrate(q, k, v, hq, hkv, block=32, pct=99.0):
+def _host_calibrate(q, k, v, hq, hkv, block=32, pct=99.0, rotation=0):
     import torch
     outs = [torch.zeros((128, 128), dtype=torch.float32), torch.zeros((128, 128), dtype=torch.float32),
             torch.zeros(128, dtype=torch.float32), torch.zeros(128, dtype=torch.float32)]
     binding.oscar_calibrate(binding.layer_desc(hq, hkv), torch.from_numpy(np.ascontiguousarray(q)),
                             torch.from_numpy(np.ascontiguousarray(k)), torch.from_numpy(np.ascontiguousarray(v)),
-                            *outs, hadamard_block=block, clip_percentile=pct)
+                            *outs, hadamard_block=block, clip_percentile=pct, rotation=rotation)
     return [o.numpy() for o in outs]
 
 
@@ -167,3 +167,35 @@ def test_host_calibrate_rejects_non_finite():
     with pytest.raises(binding.OscarError) as e:
         _host_calibrate(q, k, v, 4, 2)
     assert e.value.status == -5
+
+
+@pytest.mark.parametrize("rotation", ["hadamard", "identity"])
+def test_host_calibrate_baselines_equal_oracle(rotation):
+    q, k, v = _calib_inputs(64)
+    code = {"hadamard": binding.ROT_HADAMARD, "identity": binding.ROT_IDENTITY}[rotation]
+    r_k, r_v, t_k, t_v = _host_calibrate(q, k, v, 4, 2, rotation=code)
+    o_rk, o_rv, o_tk, o_tv = orc.calibrate(q, k, v, rotation=rotation)
+    assert np.allclose(r_k, o_rk, atol=1e-7) and np.allclose(r_v, o_rv, atol=1e-7)
+    assert np.allclose(t_k, o_tk, rtol=1e-5) and np.allclose(t_v, o_tv, rtol=1e-5)
+
+
+def test_host_calibrate_key_attention_target_matches_oracle():
+    q, k, v = _calib_inputs()
+    r_k, r_v, t_k, _ = _host_calibrate(q, k, v, 4, 2, rotation=binding.ROT_KEY_ATTN)
+    _, r_v_s, _, _ = _host_calibrate(q, k, v, 4, 2, rotation=binding.ROT_SPECTRAL)
+    assert np.array_equal(r_v, r_v_s)                 # the value rotation is the method's
+    c = orc.key_attention_covariance(q, k)
+    hp = orc.hadamard_block() @ orc.bitrev_permutation()
+    u = r_k.astype(np.float64) @ hp.T
+    d = u.T @ c @ u
+    w = np.sort(np.linalg.eigvalsh(c))[::-1]
+    assert np.allclose(np.diag(d), w, rtol=1e-5, atol=1e-7 * w[0])
+    assert np.abs(d - np.diag(np.diag(d))).max() < 1e-5 * w[0]
+    assert np.allclose(t_k, orc.clip_thresholds(k, r_k), rtol=1e-5)
+
+
+def test_host_calibrate_rejects_unknown_rotation():
+    q, k, v = _calib_inputs(16)
+    with pytest.raises(binding.OscarError) as e:
+        _host_calibrate(q, k, v, 4, 2, rotation=7)
+    assert e.value.status == -1

@@ -489,3 +489,71 @@ def test_many_token_demotion_equals_per_token_demotion_multihead():
     for h in range(n):
         b.demote(0, h, k[h], v[h], r, r, tau, tau)
     assert a.hist.any() and np.array_equal(a.hist, b.hist)
+
+
+# ---------------------------------------------------------------------------
+# Rotation variants (reading R10): the baselines and the alternative key target
+# ---------------------------------------------------------------------------
+
+def _tiny_layer(n, hq, hkv, seed):
+    st = synth.streams(seed)
+    out = synth.outlier_channels(st["outliers"])
+    k = synth.bf16_bits_to_f32(synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out))
+    v = synth.bf16_bits_to_f32(synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out))
+    q = synth.bf16_bits_to_f32(synth.queries(st["q"], (n, hq, 128)))
+    return q, k, v
+
+
+def test_hadamard_baseline_rows_closed_form():
+    # R = H P_br with H block-diagonal (block 32): (e_i R)_j = H[i][bitrev(j)].
+    # Row 0: H[0][m] = 1/sqrt(32) for m < 32, and bitrev(j) < 32 exactly when
+    # the two low bits of j are 0.  Row 1: the sign (-1)^(m & 1) of H[1][m]
+    # is the top bit of j (bitrev moves bit 0 to bit 6).
+    q, k, v = _tiny_layer(24, 2, 1, 5)
+    r_k, r_v, _, _ = orc.calibrate(q, k, v, rotation="hadamard")
+    assert np.array_equal(r_k, r_v)
+    c = np.float32(1.0 / math.sqrt(32.0))
+    row0 = np.array([c if j % 4 == 0 else 0.0 for j in range(128)], np.float32)
+    row1 = np.array([(c if j < 64 else -c) if j % 4 == 0 else 0.0 for j in range(128)], np.float32)
+    assert np.allclose(r_k[0], row0, atol=1e-7)
+    assert np.allclose(r_k[1], row1, atol=1e-7)
+    assert np.allclose(r_k.astype(np.float64) @ r_k.T, np.eye(128), atol=1e-6)
+
+
+def test_identity_baseline_and_its_clip_order_statistic():
+    # R = I: the rotated values are the inputs, so tau_j is the percentile of
+    # |k_j| itself; checked on a column whose order statistics are hand-set.
+    q, k, v = _tiny_layer(101, 2, 1, 6)
+    k = k.copy()
+    k[:, 0, 7] = np.arange(101, dtype=np.float32) * -0.5        # |k| = 0, 0.5, ..., 50
+    r_k, r_v, t_k, _ = orc.calibrate(q, k, v, rotation="identity")
+    assert np.array_equal(r_k, np.eye(128, dtype=np.float32)) and np.array_equal(r_v, r_k)
+    # 99th percentile of 0, 0.5, ..., 50 (101 values): position 99 -> 49.5
+    assert t_k[7] == np.float32(49.5)
+
+
+def test_key_attention_covariance_special_cases():
+    # One token: S = [1], so C_SK = k k^T for the single KV head.
+    q, k, v = _tiny_layer(1, 2, 1, 7)
+    kk = k[0, 0].astype(np.float64)
+    assert np.allclose(orc.key_attention_covariance(q, k), np.outer(kk, kk), rtol=1e-12, atol=1e-12)
+    # Identical keys at every position: each softmax row sums to one, so every
+    # S K row is that key whatever the queries are.
+    q, k, v = _tiny_layer(9, 4, 2, 8)
+    k = np.repeat(k[:1], 9, axis=0)
+    c = orc.key_attention_covariance(q, k)
+    k0 = k[0].astype(np.float64)
+    want = 0.5 * (np.outer(k0[0], k0[0]) + np.outer(k0[1], k0[1]))
+    assert np.allclose(c, want, rtol=1e-10, atol=1e-10)
+
+
+def test_key_attn_variant_keeps_value_rotation_and_diagonalises_its_target():
+    q, k, v = _tiny_layer(40, 2, 1, 9)
+    rk_s, rv_s, _, _ = orc.calibrate(q, k, v, rotation="spectral")
+    rk_a, rv_a, _, _ = orc.calibrate(q, k, v, rotation="key_attn")
+    assert np.array_equal(rv_a, rv_s)
+    hp = orc.hadamard_block() @ orc.bitrev_permutation()
+    u = rk_a.astype(np.float64) @ hp.T
+    d = u.T @ orc.key_attention_covariance(q, k) @ u
+    w = np.sort(np.linalg.eigvalsh(orc.key_attention_covariance(q, k)))[::-1]
+    assert np.allclose(np.diag(d), w, rtol=1e-5, atol=1e-7 * w[0])
