@@ -437,12 +437,23 @@ def kernel_source_digest():
     summary taken on other sources no longer describes the kernel."""
     import hashlib
     from bit_rotated_kv_demote_amd import build
+    import re
     h = hashlib.sha256(" ".join(build.DEVICE_FLAGS).encode())
     csrc = os.path.join(ROOT, "bit_rotated_kv_demote_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+    # the device translation units and the local headers they include (host
+    # code such as the calibration does not change what the kernels do)
+    todo, seen = list(build.HIP_SOURCES), set()
+    while todo:
+        name = todo.pop()
+        if name in seen or not os.path.exists(os.path.join(csrc, name)):
+            continue
+        seen.add(name)
+        with open(os.path.join(csrc, name), "rb") as f:
+            text = f.read()
+        todo += re.findall(r'#include "([^"/]+)"', text.decode())
+    for name in sorted(seen):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
