@@ -54,6 +54,11 @@ R10 Rotation variants for comparison: besides the method's R, the key
     (1/N) K^T S^T S K (pooled like C_S), and the baselines are R = H P_br
     (data-blind Hadamard) and R = I (plain INT2); the clip thresholds are
     always taken after the chosen rotation.
+R11 Several query tokens per sequence: the T queries of a step are the last
+    T positions n - T, ..., n - 1 of a cache that already holds all n tokens,
+    and query t attends causally to positions [0, n - T + t].  With
+    T <= 256 every INT2 history token precedes every query, so the causal
+    limit only ever falls inside the BF16 tiers.
 """
 from __future__ import annotations
 
@@ -603,6 +608,35 @@ def decode_tiered(q_bits, pool: Pool, seq_slot, seq_len, r_k, r_v, heads=None) -
         for h in hs:
             i = kvh.index(h // g)
             out[b, h] = attention(q[b, h], kt[i], vt[i])
+    return out
+
+
+def attend_tail_tiered(q_bits, pool: Pool, seq_slot, seq_len, r_k, r_v, heads=None) -> np.ndarray:
+    """Attention of the last T positions of each sequence over the tiered pool
+    (several query tokens per step: speculative verification, chunked
+    prefill), reading R11: out [B, T, Hq, 128] fp64.
+
+    q_bits: bf16 bits [B, T, Hq, 128]; query t of sequence b sits at position
+    p = n_b - T + t and attends causally to positions [0, p] of the cache
+    (which already holds all n_b tokens).  heads: optional list of (b, h).
+    """
+    q = bf16_to_f64(q_bits)
+    b_n, t_n, hq, _ = q.shape
+    g = hq // pool.hkv
+    out = np.zeros((b_n, t_n, hq, HEAD_DIM))
+    want = None if heads is None else set((int(b), int(h)) for b, h in heads)
+    for b in range(b_n):
+        hs = [h for h in range(hq) if want is None or (b, h) in want]
+        if not hs:
+            continue
+        n = int(seq_len[b])
+        kvh = sorted(set(h // g for h in hs))
+        kt, vt = pool.reconstruct(int(seq_slot[b]), n, r_k, r_v, kvh)
+        for t in range(t_n):
+            p = n - t_n + t
+            for h in hs:
+                i = kvh.index(h // g)
+                out[b, t, h] = attention(q[b, t, h], kt[i, :p + 1], vt[i, :p + 1])
     return out
 
 

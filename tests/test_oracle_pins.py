@@ -557,3 +557,42 @@ def test_key_attn_variant_keeps_value_rotation_and_diagonalises_its_target():
     d = u.T @ orc.key_attention_covariance(q, k) @ u
     w = np.sort(np.linalg.eigvalsh(orc.key_attention_covariance(q, k)))[::-1]
     assert np.allclose(np.diag(d), w, rtol=1e-5, atol=1e-7 * w[0])
+
+
+# ---------------------------------------------------------------------------
+# Several query tokens per sequence (reading R11)
+# ---------------------------------------------------------------------------
+
+def test_tail_attention_first_of_two_tokens_sees_only_itself():
+    # n = 2, T = 2: query 0 sits at position 0 and sees token 0 alone, so its
+    # output is v_0 exactly whatever the query is.
+    pool, k, v, r, tau = _run_appends(2)
+    q = synth.queries(np.random.default_rng(3), (1, 2, 2, 128))
+    out = orc.attend_tail_tiered(q, pool, [0], [2], r, r)
+    v0 = synth.bf16_bits_to_f32(v[0, 0]).astype(np.float64)
+    assert np.array_equal(out[0, 0, 0], v0) and np.array_equal(out[0, 0, 1], v0)
+
+
+def test_tail_attention_causal_limit_by_perturbation():
+    # Changing the newest token's key and value moves only the last query.
+    n, t_n = 40, 5
+    pool, k, v, r, tau = _run_appends(n)
+    q = synth.queries(np.random.default_rng(4), (1, t_n, 2, 128))
+    base = orc.attend_tail_tiered(q, pool, [0], [n], r, r)
+    slot = n - 1                                   # still in the sink (n <= 64)
+    for name in ("sink_k", "sink_v"):
+        row = getattr(pool, name)[0][0, slot]
+        row[:] = synth.to_bf16_bits(synth.bf16_bits_to_f32(row) + np.float32(0.75))
+    moved = orc.attend_tail_tiered(q, pool, [0], [n], r, r)
+    assert np.array_equal(moved[0, :t_n - 1], base[0, :t_n - 1])
+    assert not np.allclose(moved[0, t_n - 1], base[0, t_n - 1])
+
+
+def test_tail_attention_last_query_equals_single_token_decode():
+    # With history (n = 700, 380 INT2 tokens) the last query sees everything.
+    n, t_n = 700, 4
+    pool, k, v, r, tau = _run_appends(n)
+    q = synth.queries(np.random.default_rng(5), (1, t_n, 2, 128))
+    out = orc.attend_tail_tiered(q, pool, [0], [n], r, r)
+    one = orc.decode_tiered(np.ascontiguousarray(q[:, -1]), pool, [0], [n], r, r)
+    assert np.allclose(out[0, -1], one[0], rtol=0, atol=1e-12)
