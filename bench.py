@@ -351,6 +351,44 @@ def run_fixed_memory(torch, steps, calib, seed=1004, layers=36, budget_gb=64.0):
     return res
 
 
+def run_multi_query(torch, steps, calib, seed=1007, hq=32, hkv=8, n=32768, n_pools=12,
+                    counts=(1, 2, 4, 8, 16, 64)):
+    """Several query tokens per sequence (oscar_decode_multi) on the
+    Qwen3-4B-shaped layer at a 32K context: the last T positions attend
+    causally (speculative verification, chunked prefill).  Pools are cycled
+    so the history comes from HBM; HIP events around every call."""
+    from bit_rotated_kv_demote_amd import synth
+    from bit_rotated_kv_demote_amd.pool import bf16_tensor
+    k1, v1 = _seq_kv(hkv, n, seed)
+    pools = [_int2_pool(torch, hq, hkv, [n], k1, v1, calib, seed + 10 + i) for i in range(n_pools)]
+    lens = torch.tensor([n], dtype=torch.int32, device="cuda")
+    res = {}
+    t_one = None
+    for t_n in counts:
+        q = bf16_tensor(synth.queries(np.random.default_rng(seed + t_n), (1, t_n, hq, 128)))
+        out = torch.empty((1, t_n, hq, 128), dtype=torch.float32, device="cuda")
+        for i in range(n_pools):
+            pools[i].decode_multi(q, lens, n, out=out)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        gpu_hold(torch, 5 + 0.5 * steps)
+        for i in range(steps):
+            s0 = tm.start()
+            pools[i % n_pools].decode_multi(q, lens, n, out=out)
+            tm.stop(s0)
+        torch.cuda.synchronize()
+        us = tm.mean_us()
+        nbytes = decode_bytes([n], hq, hkv) + (t_n - 1) * hq * 128 * (2 + 4)
+        t_one = us if t_n == 1 else t_one
+        res[str(t_n)] = {"us_per_call": round(us, 3), "us_per_query_token": round(us / t_n, 3),
+                         "GBps": round(nbytes / (us * 1e3), 1),
+                         "speedup_vs_single_token_calls": round(t_n * t_one / us, 2)}
+    del pools
+    torch.cuda.empty_cache()
+    return {"workload": f"{hq} q / {hkv} KV heads, one sequence of {n} tokens, the last T positions as queries "
+                        f"(causal among them), {n_pools} pools cycled", "by_query_tokens": res}
+
+
 def run_rotation_study(torch, seed=1006, hq=32, hkv=8, n_calib=1024, n_ctx=8192):
     """Rotation variants on a layer with planted covariance structure (Qwen3-4B
     attention shape): host calibration with each rotation on n_calib tokens,
@@ -564,6 +602,7 @@ def main():
         del r128, b128
         extra["ragged_gqa8"] = run_ragged_gqa8(torch, min(args.steps, 50), res["host"][2:])
         extra["fixed_memory_16k"] = run_fixed_memory(torch, min(args.steps, 20), res["host"][2:])
+        extra["multi_query_32k"] = run_multi_query(torch, min(args.steps, 100), res["host"][2:])
         extra["rotation_study"] = run_rotation_study(torch)
         d = run_demote(torch, 20, 1004)
         extra["demote_tok_per_s"] = round(d["tok_per_s"], 0)

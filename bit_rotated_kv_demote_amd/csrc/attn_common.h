@@ -63,12 +63,15 @@ struct alignas(16) SplitSmem {
 // fp32 accumulation); p . V runs on the vector unit with each lane owning two
 // channels.  rowk(u), rowv(u) give the bf16 rows of token u.
 // ---------------------------------------------------------------------------
-template <int G, class RowK, class RowV>
-__device__ void bf16_span_wave(const uint16_t* qg, int count, RowK rowk, RowV rowv, SplitSmem<G>& sm,
+// qrow(x): the bf16 query row of column x.  Causal limit (several query
+// tokens per sequence): column x sees token uu only if pos(uu) <= lim(x).
+template <int G, class QRow, class RowK, class RowV, class Pos, class Lim>
+__device__ void bf16_span_wave(QRow qrow_of, int count, RowK rowk, RowV rowv, Pos pos, Lim lim, SplitSmem<G>& sm,
                                int wave, int lane) {
   const int x = lane & 15, qa = lane >> 4;
   bf16x8_t bq[4];
-  const uint16_t* qrow = qg + (size_t)(x < G ? x : 0) * kD;
+  const uint16_t* qrow = qrow_of(x < G ? x : 0);
+  const int lim_x = lim(x < G ? x : 0);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * kk + 8 * qa);
@@ -103,7 +106,7 @@ __device__ void bf16_span_wave(const uint16_t* qg, int count, RowK rowk, RowV ro
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * blk + 4 * qa + r;
-        sc[blk][r] = (x < G && t < cn) ? d[r] * kC0 : -INFINITY;
+        sc[blk][r] = (x < G && t < cn && pos(cbase + t) <= lim_x) ? d[r] * kC0 : -INFINITY;
       }
     }
     float mx = sc[0][0];

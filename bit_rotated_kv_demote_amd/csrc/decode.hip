@@ -315,24 +315,33 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
   const int n_split_total = a.n_tile_splits + a.n_hist_splits;
   if (item >= a.n_groups_total * n_split_total) return;
   const int grp = item / n_split_total, split = item % n_split_total;
-  const int b = grp / a.hkv, hk = grp % a.hkv;
+  // group = (sequence b, KV head hk, column group cg); column x of the group
+  // is virtual head cg * G + x = (query token t, head h of the KV head)
+  const int cg = grp % a.n_colgroups;
+  const int b = grp / (a.hkv * a.n_colgroups), hk = (grp / a.n_colgroups) % a.hkv;
+  const int hq_total = a.hkv * a.g_model;
+  auto q_row = [&](int x) -> const uint16_t* {
+    const int vh = cg * G + x, t = vh / a.g_model, h = vh - t * a.g_model;
+    return a.q + (((size_t)b * a.q_tokens + t) * hq_total + hk * a.g_model + h) * kD;
+  };
   const bool is_tile = split < a.n_tile_splits;
   // History splits need q . R_K, whose operands do not depend on the
   // sequence's length: their loads go out before the lengths are read.
   // (Thread (c4, rs) takes output columns [4 c4, 4 c4 + 4) and rows
   // [16 rs, 16 rs + 16) of R_K: 16 float4 loads.)
-  const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
   const int c4 = tid & 31, rs = tid >> 5;
   constexpr int kQWords = G * kD / 2;               // q as 32-bit words (two bf16 each)
   constexpr int kQPer = (kQWords + 255) / 256;
-  const uint32_t* qg32 = reinterpret_cast<const uint32_t*>(qg);
   float4 rq[16];
   uint32_t qv[kQPer];
   if (!is_tile) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(a.rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
 #pragma unroll
-    for (int e = 0; e < kQPer; ++e) qv[e] = qg32[min(tid + 256 * e, kQWords - 1)];   // unconditional
+    for (int e = 0; e < kQPer; ++e) {                 // unconditional
+      const int w = min(tid + 256 * e, kQWords - 1);
+      qv[e] = reinterpret_cast<const uint32_t*>(q_row(w >> 6))[w & 63];
+    }
   }
   const int slot = a.seq_slot ? a.seq_slot[b] : b;
   const int n = a.seq_len[b];
@@ -358,9 +367,12 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
       const int pos = recent_first + (u - n_sink_used);
       return ring + (ring_base + ((pos - kSink) & (kRecent - 1))) * kD;
     };
-    bf16_span_wave<G>(qg, min(kTileTokens, n_tile - u0),
+    // causal limit of column x: its query's position n - q_tokens + t
+    bf16_span_wave<G>(q_row, min(kTileTokens, n_tile - u0),
                       [&](int uu) { return row(a.sink_k, a.recent_k, uu); },
-                      [&](int uu) { return row(a.sink_v, a.recent_v, uu); }, sm, wave, lane);
+                      [&](int uu) { return row(a.sink_v, a.recent_v, uu); },
+                      [&](int uu) { const int u = u0 + uu; return u < n_sink_used ? u : recent_first + (u - n_sink_used); },
+                      [&](int x) { return n - a.q_tokens + (cg * G + x) / a.g_model; }, sm, wave, lane);
   } else {
     const int pg_begin = hs * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);
@@ -436,11 +448,12 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
 }
 
-DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len) {
+DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len) {
   DecodePlan p{};
   const int max_hist = max(0, max_seq_len - kSink - kRecent);
   const int max_pages = (max_hist + kPage - 1) / kPage;
-  const long total_pages = (long)batch * hkv * max_pages;
+  const long n_groups = (long)batch * hkv * n_colgroups;
+  const long total_pages = n_groups * max_pages;
   // aim at roughly two workgroups per compute unit (256 CUs)
   long pps = (total_pages + 479) / 480;
   pps = ((pps + 7) / 8) * 8;
@@ -453,9 +466,9 @@ DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len) {
   const int max_tile = min(max_seq_len, kSink + kRecent);
   p.n_tile_splits = (max_tile + kTileTokens - 1) / kTileTokens;
   p.n_splits_total = p.n_hist_splits + p.n_tile_splits;
-  p.n_work = batch * hkv * p.n_splits_total;
+  p.n_work = (int)(n_groups * p.n_splits_total);
   p.grid = ((p.n_work + 7) / 8) * 8;
-  p.partial_floats = (size_t)batch * hkv * p.n_splits_total * group * kPartStride;
+  p.partial_floats = (size_t)n_groups * p.n_splits_total * group * kPartStride;
   p.workspace_bytes = p.partial_floats * sizeof(float);
   return p;
 }

@@ -30,8 +30,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeBf16Args a) {
     const int page = pt_row[tok >> 4];
     return a.kv + ((((size_t)page * a.hkv + hk) * 2 + kv) * kPage + (tok & 15)) * kD;
   };
-  bf16_span_wave<G>(a.q + ((size_t)b * a.hkv * G + hk * G) * kD, count, [&](int uu) { return row(uu, 0); },
-                    [&](int uu) { return row(uu, 1); }, sm, wave, lane);
+  const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
+  bf16_span_wave<G>([&](int x) { return qg + (size_t)x * kD; }, count, [&](int uu) { return row(uu, 0); },
+                    [&](int uu) { return row(uu, 1); }, [](int) { return 0; }, [](int) { return 0; }, sm, wave,
+                    lane);
   float* part_base = a.partials + (size_t)grp * a.n_splits * G * kPartStride;
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
 }

@@ -55,8 +55,8 @@ struct PrefillArgs {
 };
 
 struct DecodeArgs {
-  const uint16_t* q;          // bf16 [batch][Hq][128]
-  float* out;                 // fp32 [batch][Hq][128]
+  const uint16_t* q;          // bf16 [batch][q_tokens][Hq][128]
+  float* out;                 // fp32 [batch][q_tokens][Hq][128]
   const int32_t* seq_slot;    // nullable
   const int32_t* seq_len;     // [batch]
   const uint16_t* sink_k; const uint16_t* sink_v;
@@ -70,8 +70,15 @@ struct DecodeArgs {
   int n_hist_splits;          // history splits per (sequence, KV head)
   int pages_per_split;        // multiple of 8
   int n_tile_splits;          // BF16 sink/recent splits per (sequence, KV head)
-  int n_groups_total;         // batch * Hkv
+  int n_groups_total;         // batch * Hkv * n_colgroups
   int grid_per_xcd;
+  // Query columns.  A sequence has q_tokens queries (its last q_tokens
+  // positions) and a KV head g_model query heads: q_tokens * g_model
+  // "virtual heads" (t, h), numbered t * g_model + h, in n_colgroups groups
+  // of G (the kernel's template parameter) columns each.
+  int q_tokens;
+  int g_model;
+  int n_colgroups;
 };
 
 struct DecodeBf16Args {
@@ -92,12 +99,15 @@ struct DecodeBf16Args {
 
 // Log-sum-exp merge of the decode partials, one workgroup per query head.
 struct MergeArgs {
-  const float* partials;      // [batch*Hkv][n_splits_total][group][132]
+  const float* partials;      // [batch*Hkv*n_colgroups][n_splits_total][group][132]
   const int32_t* seq_len;     // [batch]
   const float* rot;           // R_V for the rotated (history) records; unused when tiered == 0
-  float* out;                 // fp32 [batch][Hq][128]
+  float* out;                 // fp32 [batch][q_tokens][Hq][128]
   int hkv;
-  int group;
+  int group;                  // columns per record group
+  int q_tokens;               // queries per sequence (virtual heads as in DecodeArgs)
+  int g_model;                // query heads per KV head
+  int n_colgroups;
   int n_splits_total;         // record slots per (sequence, KV head)
   int n_plain_slots;          // slots before the first rotated record (INT2: tile splits; BF16: all)
   int pages_per_split;
@@ -121,7 +131,9 @@ struct DecodePlan {
 // four waves keeps the page ids of its share in one 64-lane register)
 constexpr int kMaxPagesPerSplit = 256;
 
-DecodePlan plan_decode(int batch, int hkv, int group, int max_seq_len);
+// group: columns per work item (1, 2, 4 or 8); n_colgroups column groups per
+// (sequence, KV head)
+DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len);
 DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len);
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st);

@@ -29,9 +29,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   __shared__ float wred[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
-  const int head = blockIdx.x;                       // b * Hq + (hk * G + h)
-  const int grp = head / G, h = head % G;
-  const int b = grp / a.hkv;
+  // output row head = (b * q_tokens + t) * Hq + hq; its records: work-item
+  // group (b, hk, cg) and column x, with virtual head t * g_model + h = cg * G + x
+  const int head = blockIdx.x;
+  const int hq_total = a.hkv * a.g_model;
+  const int b = head / (a.q_tokens * hq_total);
+  const int t = (head / hq_total) % a.q_tokens, hq = head % hq_total;
+  const int vh = t * a.g_model + hq % a.g_model;
+  const int grp = (b * a.hkv + hq / a.g_model) * a.n_colgroups + vh / G, h = vh % G;
   const int n_slots = a.n_splits_total;
   // record slot s of this head: slots [0, n_plain_slots) hold output-space
   // partials, the rest rotated-space ones (history)
@@ -143,7 +148,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
   rr[jh][ri] = acc;
   __syncthreads();
-  if (tid < kD) a.out[(size_t)head * kD + tid] = (oh[0][tid] + (rr[0][tid] + rr[1][tid])) / l_all;
+  // (l_all is 0 only if every token was masked for this query, a length
+  // shorter than the query count)
+  if (tid < kD) a.out[(size_t)head * kD + tid] = l_all > 0.0f ? (oh[0][tid] + (rr[0][tid] + rr[1][tid])) / l_all : 0.0f;
 }
 
 }  // namespace

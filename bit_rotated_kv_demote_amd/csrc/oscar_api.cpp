@@ -43,6 +43,23 @@ oscar_status hip_status(hipError_t e) {
 
 }  // namespace
 
+namespace {
+// Several query tokens per sequence: the query heads' virtual heads (t, h)
+// of one KV head are split into work-item column groups of `group` columns,
+// the largest power of two (at most 8) that divides n_query * G.
+constexpr int kMaxQueryTokens = 256;
+struct QueryColumns {
+  int group;
+  int n_colgroups;
+};
+QueryColumns query_columns(const oscar_layer_desc* d, int n_query) {
+  const int v = n_query * (d->num_q_heads / d->num_kv_heads);
+  int group = 8;
+  while (v % group != 0) group >>= 1;
+  return QueryColumns{group, v / group};
+}
+}  // namespace
+
 extern "C" {
 
 int32_t oscar_abi_version(void) { return OSCAR_ABI_VERSION; }
@@ -171,23 +188,38 @@ oscar_status oscar_prefill(const oscar_layer_desc* desc, const oscar_pool* pool,
 }
 
 size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
-  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0) return 0;
-  const int g = desc->num_q_heads / desc->num_kv_heads;
-  return plan_decode(batch, desc->num_kv_heads, g, max_seq_len).workspace_bytes;
+  return oscar_decode_multi_workspace_bytes(desc, batch, 1, max_seq_len);
+}
+
+size_t oscar_decode_multi_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_query,
+                                          int32_t max_seq_len) {
+  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0 || n_query < 1 || n_query > kMaxQueryTokens)
+    return 0;
+  const QueryColumns c = query_columns(desc, n_query);
+  return plan_decode(batch, desc->num_kv_heads, c.group, c.n_colgroups, max_seq_len).workspace_bytes;
 }
 
 oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                           const int32_t* seq_len, const void* q, float* out, void* workspace, size_t ws_bytes,
                           int32_t batch, int32_t max_seq_len, void* stream) {
+  return oscar_decode_multi(desc, pool, seq_slot, seq_len, q, 1, out, workspace, ws_bytes, batch, max_seq_len, stream);
+}
+
+oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                                const int32_t* seq_len, const void* q, int32_t n_query, float* out, void* workspace,
+                                size_t ws_bytes, int32_t batch, int32_t max_seq_len, void* stream) {
   oscar_status st = check_desc(desc);
   if (st != OSCAR_OK) return st;
   if ((st = check_pool(pool, max_seq_len > 320)) != OSCAR_OK) return st;
   if (!seq_len || !q || !out || !workspace || batch <= 0 || max_seq_len <= 0) return OSCAR_ERR_INVALID;
+  if (n_query < 1 || max_seq_len < n_query) return OSCAR_ERR_INVALID;
+  if (n_query > kMaxQueryTokens) return OSCAR_ERR_UNSUPPORTED;
   if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
   const int hkv = desc->num_kv_heads, g = desc->num_q_heads / hkv;
   const int max_hist = max_seq_len - 320;
   if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
-  const DecodePlan plan = plan_decode(batch, hkv, g, max_seq_len);
+  const QueryColumns c = query_columns(desc, n_query);
+  const DecodePlan plan = plan_decode(batch, hkv, c.group, c.n_colgroups, max_seq_len);
   if (!plan.ok) return OSCAR_ERR_UNSUPPORTED;
   if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
   DecodeArgs a{};
@@ -209,22 +241,28 @@ oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, 
   a.n_hist_splits = plan.n_hist_splits;
   a.pages_per_split = plan.pages_per_split;
   a.n_tile_splits = plan.n_tile_splits;
-  a.n_groups_total = batch * hkv;
+  a.n_groups_total = batch * hkv * c.n_colgroups;
   a.grid_per_xcd = plan.grid / 8;
+  a.q_tokens = n_query;
+  a.g_model = g;
+  a.n_colgroups = c.n_colgroups;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(launch_decode(a, g, plan.grid, hs))) != OSCAR_OK) return st;
+  if ((st = hip_status(launch_decode(a, c.group, plan.grid, hs))) != OSCAR_OK) return st;
   MergeArgs m{};
   m.partials = a.partials;
   m.seq_len = seq_len;
   m.rot = pool->rot_v;
   m.out = out;
   m.hkv = hkv;
-  m.group = g;
+  m.group = c.group;
+  m.q_tokens = n_query;
+  m.g_model = g;
+  m.n_colgroups = c.n_colgroups;
   m.n_splits_total = plan.n_splits_total;
   m.n_plain_slots = plan.n_tile_splits;
   m.pages_per_split = plan.pages_per_split;
   m.tiered = 1;
-  return hip_status(launch_merge(m, batch * desc->num_q_heads, hs));
+  return hip_status(launch_merge(m, batch * n_query * desc->num_q_heads, hs));
 }
 
 size_t oscar_decode_bf16_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
@@ -268,6 +306,9 @@ oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_po
   m.out = out;
   m.hkv = hkv;
   m.group = g;
+  m.q_tokens = 1;
+  m.g_model = g;
+  m.n_colgroups = 1;
   m.n_splits_total = plan.n_splits_total;
   m.n_plain_slots = plan.n_splits_total;
   m.pages_per_split = plan.pages_per_split;

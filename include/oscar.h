@@ -248,6 +248,36 @@ size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
                                     int32_t max_seq_len);
 
 /*
+ * oscar_decode_multi -- several query tokens per sequence over the tiered
+ * pool (speculative verification of draft tokens, chunked prefill), the
+ * same attention as oscar_decode ([gist] 2.2 B; [zingnex] 自定义INT2注意力内核)
+ * with a causal limit.  The n_query queries of batch entry b are its last
+ * n_query positions: with n = seq_len[b] cached tokens (the queries' own
+ * tokens already appended), query t (0 <= t < n_query) sits at position
+ * p = n - n_query + t and, for each query head h,
+ *   out[b][t][h] = softmax(q[b][t][h] . K~[0..p]^T / sqrt(128)) . V~[0..p].
+ * n_query <= 256 keeps every query inside the BF16 recent tier, so every
+ * INT2 history token is visible to every query and the causal limit only
+ * cuts the BF16 tiers.
+ * q: device bf16 [batch][n_query][Hq][128]; out: device fp32
+ * [batch][n_query][Hq][128]; seq_len[b] must be in [n_query, max_seq_len]
+ * (a shorter length leaves queries that see no token, whose output is 0).
+ * The work is split as for oscar_decode, with the (query token, head) pairs
+ * of a KV head as the columns of the matrix-core products; n_query = 1 is
+ * exactly oscar_decode.  Workspace: oscar_decode_multi_workspace_bytes(desc,
+ * batch, n_query, max_seq_len) bytes, rules as for oscar_decode.  Errors as
+ * for oscar_decode, plus OSCAR_ERR_INVALID for n_query < 1 or
+ * n_query > max_seq_len and OSCAR_ERR_UNSUPPORTED for n_query > 256.
+ */
+oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* pool,
+                                const int32_t* seq_slot, const int32_t* seq_len, const void* q,
+                                int32_t n_query, float* out, void* workspace, size_t ws_bytes,
+                                int32_t batch, int32_t max_seq_len, void* stream);
+
+size_t oscar_decode_multi_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
+                                          int32_t n_query, int32_t max_seq_len);
+
+/*
  * BF16 paged baseline (the full-precision cache INT2 is compared against;
  * [zingnex] 系统级收益 / 解码加速 report speed-ups over BF16).
  *   kv: device bf16 [num_pages][Hkv][2][16][128] (K page then V page);

@@ -199,3 +199,18 @@ def test_host_calibrate_rejects_unknown_rotation():
     with pytest.raises(binding.OscarError) as e:
         _host_calibrate(q, k, v, 4, 2, rotation=7)
     assert e.value.status == -1
+
+
+def test_multi_query_validation_and_workspace(lib):
+    d = binding.layer_desc(32, 8)
+    pool = _null_pool(max_pages=4096)
+    args = (None, 256, 256)
+    # n_query outside [1, 256] or above max_seq_len: rejected before any launch
+    for nq, max_len, want in ((0, 100, -1), (257, 4096, -2), (8, 4, -1)):
+        assert lib.oscar_decode_multi(ctypes.byref(d), ctypes.byref(pool), *args, nq, 256, 256, 1 << 30, 1, max_len,
+                                      None) == want, (nq, max_len)
+    # one query is exactly the single-token decode's workspace; more queries need more records
+    one = binding.oscar_decode_multi_workspace_bytes(d, 2, 1, 32768)
+    assert one == binding.oscar_decode_workspace_bytes(d, 2, 32768)
+    assert binding.oscar_decode_multi_workspace_bytes(d, 2, 4, 32768) > one
+    assert binding.oscar_decode_multi_workspace_bytes(d, 2, 0, 32768) == 0
