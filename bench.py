@@ -312,13 +312,14 @@ def run_ragged_gqa8(torch, steps, calib, seed=1005):
             "bf16_decode_GBps": round(bbytes / (bus * 1e3), 1), "int2_vs_bf16_decode_speedup": round(bus / us, 3)}
 
 
-def run_fixed_memory(torch, steps, calib, seed=1004, layers=36, budget_gb=64.0):
-    """Fixed-memory batch sweep: 32 q / 8 KV heads at 16384 tokens; the INT2
-    pool and the BF16 cache each get the same per-layer share of a 64 GB budget
-    (over an assumed 36 layers); decode tokens/s (batch / step time) per batch."""
+def run_fixed_memory(torch, steps, calib, seed=1004, layers=36, budget_gb=64.0, n=16384):
+    """Fixed-memory batch sweep: 32 q / 8 KV heads at n tokens per sequence;
+    the INT2 pool and the BF16 cache each get the same per-layer share of a
+    64 GB budget (over an assumed 36 layers); decode tokens/s (batch / step
+    time) per batch, and the largest batch each format fits."""
     from bit_rotated_kv_demote_amd import synth
     from bit_rotated_kv_demote_amd.pool import bf16_tensor
-    hq, hkv, n = 32, 8, 16384
+    hq, hkv = 32, 8
     per_layer = budget_gb * 1e9 / layers
     int2_seq = (n - 320) * hkv * 96 + 320 * hkv * 512
     bf16_seq = n * hkv * 512
@@ -602,6 +603,7 @@ def main():
         del r128, b128
         extra["ragged_gqa8"] = run_ragged_gqa8(torch, min(args.steps, 50), res["host"][2:])
         extra["fixed_memory_16k"] = run_fixed_memory(torch, min(args.steps, 20), res["host"][2:])
+        extra["fixed_memory_100k"] = run_fixed_memory(torch, min(args.steps, 20), res["host"][2:], n=100000)
         extra["multi_query_32k"] = run_multi_query(torch, min(args.steps, 100), res["host"][2:])
         extra["rotation_study"] = run_rotation_study(torch)
         d = run_demote(torch, 20, 1004)
