@@ -386,6 +386,26 @@ def run_multi_query(torch, steps, calib, seed=1007, hq=32, hkv=8, n=32768, n_poo
                          "speedup_vs_single_token_calls": round(t_n * t_one / us, 2)}
     del pools
     torch.cuda.empty_cache()
+    # the BF16 baseline on the same tokens (4 cycled copies, 537 MB)
+    bpools = [_bf16_pool(torch, hq, hkv, 1, n, k1, v1, seed + 30 + i) for i in range(4)]
+    for t_n in counts:
+        q = bf16_tensor(synth.queries(np.random.default_rng(seed + t_n), (1, t_n, hq, 128)))
+        out = torch.empty((1, t_n, hq, 128), dtype=torch.float32, device="cuda")
+        for bp in bpools:
+            bp.decode_multi(q, lens, n, out=out)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        gpu_hold(torch, 5 + 0.5 * steps)
+        for i in range(steps):
+            s0 = tm.start()
+            bpools[i % 4].decode_multi(q, lens, n, out=out)
+            tm.stop(s0)
+        torch.cuda.synchronize()
+        bus = tm.mean_us()
+        res[str(t_n)]["bf16_us_per_call"] = round(bus, 3)
+        res[str(t_n)]["int2_vs_bf16_speedup"] = round(bus / res[str(t_n)]["us_per_call"], 2)
+    del bpools
+    torch.cuda.empty_cache()
     return {"workload": f"{hq} q / {hkv} KV heads, one sequence of {n} tokens, the last T positions as queries "
                         f"(causal among them), {n_pools} pools cycled", "by_query_tokens": res}
 

@@ -20,7 +20,8 @@ ABI_VERSION = 2
 
 EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_append", "oscar_demote",
             "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_multi",
-            "oscar_decode_multi_workspace_bytes", "oscar_decode_bf16", "oscar_decode_bf16_workspace_bytes")
+            "oscar_decode_multi_workspace_bytes", "oscar_decode_bf16", "oscar_decode_bf16_workspace_bytes",
+            "oscar_decode_bf16_multi", "oscar_decode_bf16_multi_workspace_bytes")
 
 
 class OscarError(RuntimeError):
@@ -91,6 +92,10 @@ def load():
     lib.oscar_decode_bf16.argtypes = [P, P, P, P, P, P, P, SZ, I32, I32, P]
     lib.oscar_decode_bf16_workspace_bytes.restype = SZ
     lib.oscar_decode_bf16_workspace_bytes.argtypes = [P, I32, I32]
+    lib.oscar_decode_bf16_multi.restype = ctypes.c_int
+    lib.oscar_decode_bf16_multi.argtypes = [P, P, P, P, P, I32, P, P, SZ, I32, I32, P]
+    lib.oscar_decode_bf16_multi_workspace_bytes.restype = SZ
+    lib.oscar_decode_bf16_multi_workspace_bytes.argtypes = [P, I32, I32, I32]
     if lib.oscar_abi_version() != ABI_VERSION:
         raise OSError("libamdoscar ABI version mismatch")
     _lib = lib
@@ -188,3 +193,16 @@ def oscar_decode_bf16(desc, pool, seq_slot, seq_len, q, out, workspace, batch, m
     _check("oscar_decode_bf16", load().oscar_decode_bf16(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_slot),
                                                           _ptr(seq_len), _ptr(q), _ptr(out), _ptr(workspace),
                                                           ws_bytes, batch, max_seq_len, _stream(stream)))
+
+
+def oscar_decode_bf16_multi_workspace_bytes(desc, batch, n_query, max_seq_len) -> int:
+    return int(load().oscar_decode_bf16_multi_workspace_bytes(ctypes.byref(desc), batch, n_query, max_seq_len))
+
+
+def oscar_decode_bf16_multi(desc, pool, seq_slot, seq_len, q, n_query, out, workspace, batch, max_seq_len,
+                            stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("oscar_decode_bf16_multi",
+           load().oscar_decode_bf16_multi(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_slot), _ptr(seq_len),
+                                          _ptr(q), n_query, _ptr(out), _ptr(workspace), ws_bytes, batch,
+                                          max_seq_len, _stream(stream)))

@@ -65,9 +65,11 @@ struct alignas(16) SplitSmem {
 // ---------------------------------------------------------------------------
 // qrow(x): the bf16 query row of column x.  Causal limit (several query
 // tokens per sequence): column x sees token uu only if pos(uu) <= lim(x).
+// pos is increasing in uu and every lim(x) >= lim_min, so a 32-token chunk
+// that ends at or before lim_min needs no per-token test.
 template <int G, class QRow, class RowK, class RowV, class Pos, class Lim>
-__device__ void bf16_span_wave(QRow qrow_of, int count, RowK rowk, RowV rowv, Pos pos, Lim lim, SplitSmem<G>& sm,
-                               int wave, int lane) {
+__device__ void bf16_span_wave(QRow qrow_of, int count, RowK rowk, RowV rowv, Pos pos, Lim lim, int lim_min,
+                               SplitSmem<G>& sm, int wave, int lane) {
   const int x = lane & 15, qa = lane >> 4;
   bf16x8_t bq[4];
   const uint16_t* qrow = qrow_of(x < G ? x : 0);
@@ -85,6 +87,7 @@ __device__ void bf16_span_wave(QRow qrow_of, int count, RowK rowk, RowV rowv, Po
   for (int c = wave; 32 * c < count; c += 4) {
     const int cbase = 32 * c;
     const int cn = min(32, count - cbase);
+    const bool partial = pos(cbase + cn - 1) > lim_min;     // some token may be past a query
     // issue every load of the chunk first: 2 x 4 K fragments and 32 V words per lane
     bf16x8_t ka[2][4];
 #pragma unroll
@@ -106,8 +109,15 @@ __device__ void bf16_span_wave(QRow qrow_of, int count, RowK rowk, RowV rowv, Po
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * blk + 4 * qa + r;
-        sc[blk][r] = (x < G && t < cn && pos(cbase + t) <= lim_x) ? d[r] * kC0 : -INFINITY;
+        sc[blk][r] = (x < G && t < cn) ? d[r] * kC0 : -INFINITY;
       }
+    }
+    if (partial) {                       // uniform: only chunks that reach past a query
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (pos(cbase + 16 * blk + 4 * qa + r) > lim_x) sc[blk][r] = -INFINITY;
     }
     float mx = sc[0][0];
 #pragma unroll

@@ -372,7 +372,8 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
                       [&](int uu) { return row(a.sink_k, a.recent_k, uu); },
                       [&](int uu) { return row(a.sink_v, a.recent_v, uu); },
                       [&](int uu) { const int u = u0 + uu; return u < n_sink_used ? u : recent_first + (u - n_sink_used); },
-                      [&](int x) { return n - a.q_tokens + (cg * G + x) / a.g_model; }, sm, wave, lane);
+                      [&](int x) { return n - a.q_tokens + (cg * G + x) / a.g_model; }, n - a.q_tokens, sm, wave,
+                      lane);
   } else {
     const int pg_begin = hs * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);

@@ -16,7 +16,10 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeBf16Args a) {
   const int item = (blockIdx.x & 7) * a.grid_per_xcd + (blockIdx.x >> 3);
   if (item >= a.n_groups_total * a.n_splits) return;
   const int grp = item / a.n_splits, split = item % a.n_splits;
-  const int b = grp / a.hkv, hk = grp % a.hkv;
+  // group = (sequence b, KV head hk, column group cg); column x is virtual
+  // head cg * G + x = (query token t, head h), as in the INT2 kernel
+  const int cg = grp % a.n_colgroups;
+  const int b = grp / (a.hkv * a.n_colgroups), hk = (grp / a.n_colgroups) % a.hkv;
   const int slot = a.seq_slot ? a.seq_slot[b] : b;
   const int n = a.seq_len[b];
   const int npages = (n + kPage - 1) / kPage;
@@ -30,19 +33,26 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeBf16Args a) {
     const int page = pt_row[tok >> 4];
     return a.kv + ((((size_t)page * a.hkv + hk) * 2 + kv) * kPage + (tok & 15)) * kD;
   };
-  const uint16_t* qg = a.q + ((size_t)b * a.hkv * G + hk * G) * kD;
-  bf16_span_wave<G>([&](int x) { return qg + (size_t)x * kD; }, count, [&](int uu) { return row(uu, 0); },
-                    [&](int uu) { return row(uu, 1); }, [](int) { return 0; }, [](int) { return 0; }, sm, wave,
+  const int hq_total = a.hkv * a.g_model;
+  auto q_row = [&](int x) -> const uint16_t* {
+    const int vh = cg * G + x, t = vh / a.g_model, h = vh - t * a.g_model;
+    return a.q + (((size_t)b * a.q_tokens + t) * hq_total + hk * a.g_model + h) * kD;
+  };
+  // causal limit of column x: its query's position n - q_tokens + t
+  bf16_span_wave<G>(q_row, count, [&](int uu) { return row(uu, 0); }, [&](int uu) { return row(uu, 1); },
+                    [&](int uu) { return t0 + uu; },
+                    [&](int x) { return n - a.q_tokens + (cg * G + x) / a.g_model; }, n - a.q_tokens, sm, wave,
                     lane);
   float* part_base = a.partials + (size_t)grp * a.n_splits * G * kPartStride;
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
 }
 
-DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len) {
+DecodePlan plan_decode_bf16(int batch, int hkv, int group, int n_colgroups, int max_seq_len) {
   DecodePlan p{};
   p.ok = true;
   const int max_pages = (max_seq_len + kPage - 1) / kPage;
-  const long total_pages = (long)batch * hkv * max_pages;
+  const long n_groups = (long)batch * hkv * n_colgroups;
+  const long total_pages = n_groups * max_pages;
   long pps = (total_pages + 479) / 480;
   pps = ((pps + 1) / 2) * 2;
   if (pps < 2) pps = 2;
@@ -51,9 +61,9 @@ DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len) {
   p.n_hist_splits = (int)((max_pages + pps - 1) / pps);
   p.n_tile_splits = 0;
   p.n_splits_total = p.n_hist_splits;
-  p.n_work = batch * hkv * p.n_splits_total;
+  p.n_work = (int)(n_groups * p.n_splits_total);
   p.grid = ((p.n_work + 7) / 8) * 8;
-  p.partial_floats = (size_t)batch * hkv * p.n_splits_total * group * kPartStride;
+  p.partial_floats = (size_t)n_groups * p.n_splits_total * group * kPartStride;
   p.workspace_bytes = p.partial_floats * sizeof(float);
   return p;
 }
@@ -64,6 +74,7 @@ hipError_t launch_decode_bf16(const DecodeBf16Args& a, int group, int grid, hipS
     case 2: hipLaunchKernelGGL(decode_bf16_kernel<2>, dim3(grid), dim3(256), 0, st, a); break;
     case 4: hipLaunchKernelGGL(decode_bf16_kernel<4>, dim3(grid), dim3(256), 0, st, a); break;
     case 8: hipLaunchKernelGGL(decode_bf16_kernel<8>, dim3(grid), dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(decode_bf16_kernel<16>, dim3(grid), dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -93,7 +93,10 @@ struct DecodeBf16Args {
   int max_pages;
   int n_splits;
   int pages_per_split;
-  int n_groups_total;
+  int n_groups_total;         // batch * Hkv * n_colgroups
+  int q_tokens;               // query columns as in DecodeArgs
+  int g_model;
+  int n_colgroups;
   int grid_per_xcd;
 };
 
@@ -134,7 +137,7 @@ constexpr int kMaxPagesPerSplit = 256;
 // group: columns per work item (1, 2, 4 or 8); n_colgroups column groups per
 // (sequence, KV head)
 DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len);
-DecodePlan plan_decode_bf16(int batch, int hkv, int group, int max_seq_len);
+DecodePlan plan_decode_bf16(int batch, int hkv, int group, int n_colgroups, int max_seq_len);
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st);
 hipError_t launch_demote(const DemoteArgs& a, int batch, int max_count, bool rotated, hipStream_t st);

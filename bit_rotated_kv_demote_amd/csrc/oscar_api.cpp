@@ -52,12 +52,15 @@ struct QueryColumns {
   int group;
   int n_colgroups;
 };
-QueryColumns query_columns(const oscar_layer_desc* d, int n_query) {
+QueryColumns query_columns(const oscar_layer_desc* d, int n_query, int max_group = 8) {
   const int v = n_query * (d->num_q_heads / d->num_kv_heads);
-  int group = 8;
+  int group = max_group;
   while (v % group != 0) group >>= 1;
   return QueryColumns{group, v / group};
 }
+// The BF16 baseline scores without a hi/lo split, so a work item takes up
+// to 16 columns.
+constexpr int kMaxBf16Columns = 16;
 }  // namespace
 
 extern "C" {
@@ -266,22 +269,39 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
 }
 
 size_t oscar_decode_bf16_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
-  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0) return 0;
-  const int g = desc->num_q_heads / desc->num_kv_heads;
-  return plan_decode_bf16(batch, desc->num_kv_heads, g, max_seq_len).workspace_bytes;
+  return oscar_decode_bf16_multi_workspace_bytes(desc, batch, 1, max_seq_len);
+}
+
+size_t oscar_decode_bf16_multi_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t n_query,
+                                               int32_t max_seq_len) {
+  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0 || n_query < 1 || n_query > kMaxQueryTokens)
+    return 0;
+  const QueryColumns c = query_columns(desc, n_query, kMaxBf16Columns);
+  return plan_decode_bf16(batch, desc->num_kv_heads, c.group, c.n_colgroups, max_seq_len).workspace_bytes;
 }
 
 oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_pool* pool, const int32_t* seq_slot,
                                const int32_t* seq_len, const void* q, float* out, void* workspace, size_t ws_bytes,
                                int32_t batch, int32_t max_seq_len, void* stream) {
+  return oscar_decode_bf16_multi(desc, pool, seq_slot, seq_len, q, 1, out, workspace, ws_bytes, batch, max_seq_len,
+                                 stream);
+}
+
+oscar_status oscar_decode_bf16_multi(const oscar_layer_desc* desc, const oscar_bf16_pool* pool,
+                                     const int32_t* seq_slot, const int32_t* seq_len, const void* q, int32_t n_query,
+                                     float* out, void* workspace, size_t ws_bytes, int32_t batch,
+                                     int32_t max_seq_len, void* stream) {
   oscar_status st = check_desc(desc);
   if (st != OSCAR_OK) return st;
   if (!pool || !pool->kv || !pool->page_table || pool->n_slots <= 0) return OSCAR_ERR_INVALID;
   if (!seq_len || !q || !out || !workspace || batch <= 0 || max_seq_len <= 0) return OSCAR_ERR_INVALID;
+  if (n_query < 1 || max_seq_len < n_query) return OSCAR_ERR_INVALID;
+  if (n_query > kMaxQueryTokens) return OSCAR_ERR_UNSUPPORTED;
   if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
   if ((max_seq_len + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
   const int hkv = desc->num_kv_heads, g = desc->num_q_heads / hkv;
-  const DecodePlan plan = plan_decode_bf16(batch, hkv, g, max_seq_len);
+  const QueryColumns c = query_columns(desc, n_query, kMaxBf16Columns);
+  const DecodePlan plan = plan_decode_bf16(batch, hkv, c.group, c.n_colgroups, max_seq_len);
   if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
   DecodeBf16Args a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -295,25 +315,28 @@ oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_po
   a.max_pages = pool->max_pages_per_seq;
   a.n_splits = plan.n_splits_total;
   a.pages_per_split = plan.pages_per_split;
-  a.n_groups_total = batch * hkv;
+  a.n_groups_total = batch * hkv * c.n_colgroups;
   a.grid_per_xcd = plan.grid / 8;
+  a.q_tokens = n_query;
+  a.g_model = g;
+  a.n_colgroups = c.n_colgroups;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(launch_decode_bf16(a, g, plan.grid, hs))) != OSCAR_OK) return st;
+  if ((st = hip_status(launch_decode_bf16(a, c.group, plan.grid, hs))) != OSCAR_OK) return st;
   MergeArgs m{};
   m.partials = a.partials;
   m.seq_len = seq_len;
   m.rot = nullptr;
   m.out = out;
   m.hkv = hkv;
-  m.group = g;
-  m.q_tokens = 1;
+  m.group = c.group;
+  m.q_tokens = n_query;
   m.g_model = g;
-  m.n_colgroups = 1;
+  m.n_colgroups = c.n_colgroups;
   m.n_splits_total = plan.n_splits_total;
   m.n_plain_slots = plan.n_splits_total;
   m.pages_per_split = plan.pages_per_split;
   m.tiered = 0;
-  return hip_status(launch_merge(m, batch * desc->num_q_heads, hs));
+  return hip_status(launch_merge(m, batch * n_query * desc->num_q_heads, hs));
 }
 
 }  // extern "C"

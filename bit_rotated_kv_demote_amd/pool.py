@@ -112,3 +112,15 @@ class PagedBF16:
             self._ws = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=self.device)
         binding.oscar_decode_bf16(self.desc, self.pool, seq_slot, seq_len, q, out, self._ws, batch, max_seq_len)
         return out
+
+    def decode_multi(self, q, seq_len, max_seq_len, out=None, seq_slot=None):
+        """q: bf16 [B, T, Hq, 128], the queries of each sequence's last T positions."""
+        batch, n_query = q.shape[0], q.shape[1]
+        if out is None:
+            out = torch.empty((batch, n_query, self.hq, HEAD_DIM), dtype=torch.float32, device=self.device)
+        nbytes = binding.oscar_decode_bf16_multi_workspace_bytes(self.desc, batch, n_query, max_seq_len)
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=self.device)
+        binding.oscar_decode_bf16_multi(self.desc, self.pool, seq_slot, seq_len, q, n_query, out, self._ws, batch,
+                                        max_seq_len)
+        return out

@@ -303,6 +303,22 @@ oscar_status oscar_decode_bf16(const oscar_layer_desc* desc, const oscar_bf16_po
 size_t oscar_decode_bf16_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
                                          int32_t max_seq_len);
 
+/*
+ * oscar_decode_bf16_multi -- the baseline for oscar_decode_multi: the last
+ * n_query positions of each sequence attend causally over the BF16 paged
+ * cache (query t at position n - n_query + t sees [0, n - n_query + t]).
+ * q, out, seq_len and errors as for oscar_decode_multi; n_query = 1 is
+ * exactly oscar_decode_bf16.  Workspace:
+ * oscar_decode_bf16_multi_workspace_bytes(desc, batch, n_query, max_seq_len).
+ */
+oscar_status oscar_decode_bf16_multi(const oscar_layer_desc* desc, const oscar_bf16_pool* pool,
+                                     const int32_t* seq_slot, const int32_t* seq_len, const void* q,
+                                     int32_t n_query, float* out, void* workspace, size_t ws_bytes,
+                                     int32_t batch, int32_t max_seq_len, void* stream);
+
+size_t oscar_decode_bf16_multi_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
+                                               int32_t n_query, int32_t max_seq_len);
+
 #ifdef __cplusplus
 }
 #endif

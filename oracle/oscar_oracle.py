@@ -665,3 +665,21 @@ def decode_bf16(q_bits, pool_bits, page_table, seq_slot, seq_len) -> np.ndarray:
         for h in range(hq):
             out[b, h] = attention(q[b, h], k[h // g], v[h // g])
     return out
+
+
+def attend_tail_bf16(q_bits, pool_bits, page_table, seq_slot, seq_len) -> np.ndarray:
+    """The BF16 baseline for several query tokens (reading R11): query t of
+    sequence b (position n_b - T + t) attends causally over the BF16 paged
+    pool.  q_bits [B, T, Hq, 128]; out [B, T, Hq, 128] fp64."""
+    q = bf16_to_f64(q_bits)
+    b_n, t_n, hq, _ = q.shape
+    g = hq // pool_bits.shape[1]
+    out = np.zeros((b_n, t_n, hq, HEAD_DIM))
+    for b in range(b_n):
+        n = int(seq_len[b])
+        k, v = bf16_pool_gather(pool_bits, page_table[int(seq_slot[b])], n)
+        for t in range(t_n):
+            p = n - t_n + t
+            for h in range(hq):
+                out[b, t, h] = attention(q[b, t, h], k[h // g][:p + 1], v[h // g][:p + 1])
+    return out

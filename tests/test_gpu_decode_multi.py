@@ -8,13 +8,15 @@ every column grouping the library picks (T * G virtual heads in work items
 of 1, 2, 4 or 8 columns), causal limits inside the sink, inside the recent
 ring and across the ring's wrap, ragged batches with slot indirection, and a
 64-token chunk."""
+import math
+
 import numpy as np
 import pytest
 import torch
 
 import oracle as orc
 from bit_rotated_kv_demote_amd import synth
-from bit_rotated_kv_demote_amd.pool import bf16_tensor
+from bit_rotated_kv_demote_amd.pool import PagedBF16, bf16_tensor
 
 from _gpu_util import Layer, i32, rel_l2, upload
 
@@ -80,3 +82,28 @@ def test_multi_query_ragged_batch_with_slots():
     out, ref = _multi_vs_oracle(layer, lengths, 4, 11, seq_slot=[2, 0, 1])
     for b in range(3):
         assert rel_l2(out[b], ref[b]) <= TOL, b
+
+
+@pytest.mark.parametrize("n_query", [1, 3, 4, 16])
+def test_bf16_baseline_multi_query(n_query):
+    # 8 q / 2 KV heads: T * 4 virtual heads in work items of up to 16 columns
+    lengths = [1200, 70]
+    hq, hkv = 8, 2
+    st = synth.streams(1150 + n_query)
+    out_ch = synth.outlier_channels(st["outliers"])
+    max_pages = math.ceil(max(lengths) / 16)
+    num_pages = len(lengths) * max_pages
+    pt = synth.page_permutation(st["perm"], num_pages).reshape(len(lengths), max_pages)
+    kv = np.zeros((num_pages, hkv, 2, 16, 128), np.uint16)
+    for b, n in enumerate(lengths):
+        k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out_ch)
+        v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out_ch)
+        for p in range(n):
+            kv[pt[b, p // 16], :, 0, p % 16] = k[p]
+            kv[pt[b, p // 16], :, 1, p % 16] = v[p]
+    q = synth.queries(st["q"], (len(lengths), n_query, hq, 128))
+    pool = PagedBF16(hq, hkv, kv, pt)
+    out = pool.decode_multi(bf16_tensor(q), i32(lengths), max(lengths)).cpu().numpy()
+    ref = orc.attend_tail_bf16(q, kv, pt, [0, 1], lengths)
+    for b in range(len(lengths)):
+        assert rel_l2(out[b], ref[b]) <= TOL, lengths[b]

@@ -596,3 +596,31 @@ def test_tail_attention_last_query_equals_single_token_decode():
     out = orc.attend_tail_tiered(q, pool, [0], [n], r, r)
     one = orc.decode_tiered(np.ascontiguousarray(q[:, -1]), pool, [0], [n], r, r)
     assert np.allclose(out[0, -1], one[0], rtol=0, atol=1e-12)
+
+
+
+def _bf16_pool_of(n, hkv, seed):
+    st = synth.streams(seed)
+    out = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out)
+    pages = (n + 15) // 16
+    pt = synth.page_permutation(st["perm"], pages)[None, :]
+    kv = np.zeros((pages, hkv, 2, 16, 128), np.uint16)
+    for p in range(n):
+        kv[pt[0, p // 16], :, 0, p % 16] = k[p]
+        kv[pt[0, p // 16], :, 1, p % 16] = v[p]
+    return kv, pt, k, v
+
+
+def test_bf16_tail_first_of_two_sees_only_itself_and_last_equals_decode():
+    kv, pt, k, v = _bf16_pool_of(2, 1, 21)
+    q = synth.queries(np.random.default_rng(6), (1, 2, 2, 128))
+    out = orc.attend_tail_bf16(q, kv, pt, [0], [2])
+    v0 = synth.bf16_bits_to_f32(v[0, 0]).astype(np.float64)
+    assert np.array_equal(out[0, 0, 0], v0) and np.array_equal(out[0, 0, 1], v0)
+    kv, pt, k, v = _bf16_pool_of(300, 2, 22)
+    q = synth.queries(np.random.default_rng(7), (1, 5, 4, 128))
+    out = orc.attend_tail_bf16(q, kv, pt, [0], [300])
+    one = orc.decode_bf16(np.ascontiguousarray(q[:, -1]), kv, pt, [0], [300])
+    assert np.allclose(out[0, -1], one[0], rtol=0, atol=1e-12)
