@@ -83,25 +83,37 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
                           const u32x2_t* m_first) {
   const int x = lane & 15, qa = lane >> 4;
   // ---- score operands: q' in fp16 hi (columns 0..G-1) and lo (G..2G-1)
-  const int col_head = x < G ? x : (x < 2 * G ? x - G : 0);
-  const bool col_used = x < 2 * G;
-  const float col_scale = ldexpf(kC0, (int)sm.sexp[col_head]);
-  half8_t bq[4];
+  // Up to 8 heads per 16-column score tile (hi and lo halves in two columns).
+  // Tile 0 holds heads 0..kGT-1: hi in columns [0, kGT), lo in [kGT, 2 kGT).
+  // With 16 heads, tile 1 holds heads 8..15 the other way round: hi in
+  // columns 8..15 (head = column), lo in columns 0..7, so that one rotate by
+  // 8 lanes pairs the halves of every head of either tile.
+  constexpr int kTiles = G > 8 ? 2 : 1;
+  constexpr int kGT = G > 8 ? 8 : G;
+  half8_t bq[kTiles][4];
+  float be[kTiles];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int tl = 0; tl < kTiles; ++tl) {
+    const bool hi_col = tl == 0 ? x < kGT : x >= 8;
+    const bool col_used = tl == 0 ? x < 2 * kGT : true;
+    const int col_head = !col_used ? 0 : (tl == 0 ? (x < kGT ? x : x - kGT) : 8 + (x & 7));
+    const float col_scale = ldexpf(kC0, (int)sm.sexp[col_head]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int j = 32 * g + 8 * qa + 2 * i + hf;
-        const int sh = field_shift(4 * (g & 1) + i);
-        const float v = ldexpf(sm.qr[col_head][j] * col_scale, -2 * sh);
-        const _Float16 hi = (_Float16)v;
-        const _Float16 e = (x < G) ? hi : (_Float16)(v - (float)hi);
-        bq[g][2 * i + hf] = col_used ? e : (_Float16)0.0f;
-      }
-  // zero-point term operand (fp32 product, 4 groups = K of 4)
-  const float be = (x < G) ? ldexpf(sm.qs[x][qa] * kC0, (int)sm.sexp[x] - 24) : 0.0f;
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int j = 32 * g + 8 * qa + 2 * i + hf;
+          const int sh = field_shift(4 * (g & 1) + i);
+          const float v = ldexpf(sm.qr[col_head][j] * col_scale, -2 * sh);
+          const _Float16 hi = (_Float16)v;
+          const _Float16 e = hi_col ? hi : (_Float16)(v - (float)hi);
+          bq[tl][g][2 * i + hf] = col_used ? e : (_Float16)0.0f;
+        }
+    // zero-point term operand (fp32 product, 4 groups = K of 4), hi columns only
+    be[tl] = (hi_col && col_used) ? ldexpf(sm.qs[col_head][qa] * kC0, (int)sm.sexp[col_head] - 24) : 0.0f;
+  }
   // matrix-core units -> log2 units; 0 for the columns that hold no head, so
   // that their (unused) scores stay at 0 and never move the running maximum
   const float mult = (x < G) ? ldexpf(1.0f, 24 - (int)sm.sexp[x]) : 0.0f;
@@ -149,7 +161,6 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
       const uint8_t* mp = mbuf + 512 * p;
       // sum_g zero[t][g] * (scaled group sums of q'), t = lane's row token
       const _Float16 zk = *reinterpret_cast<const _Float16*>(mp + 128 + 8 * x + 2 * qa);
-      float4_t cacc = __builtin_amdgcn_mfma_f32_16x16x4f32((float)zk, be, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       const uint32_t w0 = c_cur[p][0], w1 = c_cur[p][1];
       const uint32_t w0s = w0 >> 6, w1s = w1 >> 6;
       half8_t ak[4];
@@ -162,27 +173,35 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
       ak32[10] = field_pair<2>(w1, w1s); ak32[11] = field_pair<3>(w1, w1s);
       ak32[12] = field_pair<4>(w1, w1s); ak32[13] = field_pair<5>(w1, w1s);
       ak32[14] = field_pair<6>(w1, w1s); ak32[15] = field_pair<7>(w1, w1s);
-      float4_t d[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        d[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[g], bq[g], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
       // scales of tokens 4qa..4qa+3 (K scale area [token][group])
       const u32x4_t s01 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa);
       const u32x4_t s23 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa + 16);
       const _Float16* sh0 = reinterpret_cast<const _Float16*>(&s01);
       const _Float16* sh1 = reinterpret_cast<const _Float16*>(&s23);
+      float4_t cacc[kTiles];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const _Float16* sr = (r < 2) ? sh0 + 4 * r : sh1 + 4 * (r - 2);
+      for (int tl = 0; tl < kTiles; ++tl) {
+        // sum_g zero[t][g] * (scaled group sums of q'), t = lane's row token
+        cacc[tl] = __builtin_amdgcn_mfma_f32_16x16x4f32((float)zk, be[tl], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        float4_t d[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) cacc[r] = fmaf((float)sr[g], d[g][r], cacc[r]);
+        for (int g = 0; g < 4; ++g)
+          d[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[g], bq[tl][g], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const _Float16* sr = (r < 2) ? sh0 + 4 * r : sh1 + 4 * (r - 2);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) cacc[tl][r] = fmaf((float)sr[g], d[g][r], cacc[tl][r]);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // hi + lo halves of the same head
+        // hi + lo halves of the same head (tile 1: the halves sit the other way round)
+        const float mine = kTiles == 1 ? cacc[0][r] : (x < 8 ? cacc[0][r] : cacc[kTiles - 1][r]);
+        const float peer = kTiles == 1 ? cacc[0][r] : (x < 8 ? cacc[kTiles - 1][r] : cacc[0][r]);
         const float other = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-            0u, __float_as_uint(cacc[r]), 0x120 + (16 - G), 0xF, 0xF, false));
-        sc[p][r] = cacc[r] + other;
+            0u, __float_as_uint(peer), 0x120 + (16 - kGT), 0xF, 0xF, false));
+        sc[p][r] = mine + other;
       }
     }
     if (partial) {
@@ -480,6 +499,7 @@ hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t s
     case 2: hipLaunchKernelGGL(decode_int2_kernel<2>, dim3(grid), dim3(256), 0, st, a); break;
     case 4: hipLaunchKernelGGL(decode_int2_kernel<4>, dim3(grid), dim3(256), 0, st, a); break;
     case 8: hipLaunchKernelGGL(decode_int2_kernel<8>, dim3(grid), dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(decode_int2_kernel<16>, dim3(grid), dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -134,8 +134,8 @@ struct DecodePlan {
 // four waves keeps the page ids of its share in one 64-lane register)
 constexpr int kMaxPagesPerSplit = 256;
 
-// group: columns per work item (1, 2, 4 or 8); n_colgroups column groups per
-// (sequence, KV head)
+// group: columns per work item (1, 2, 4, 8 or 16); n_colgroups column groups
+// per (sequence, KV head)
 DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len);
 DecodePlan plan_decode_bf16(int batch, int hkv, int group, int n_colgroups, int max_seq_len);
 

@@ -46,20 +46,25 @@ oscar_status hip_status(hipError_t e) {
 namespace {
 // Several query tokens per sequence: the query heads' virtual heads (t, h)
 // of one KV head are split into work-item column groups of `group` columns,
-// the largest power of two (at most 8) that divides n_query * G.
+// the largest power of two (at most max_group) that divides n_query * G.
+// The INT2 kernel takes 16 columns (two score tiles) only when that still
+// leaves two or more groups: at 16 virtual heads, two 8-column groups keep
+// twice the workgroups busy and are faster on one long sequence.
 constexpr int kMaxQueryTokens = 256;
 struct QueryColumns {
   int group;
   int n_colgroups;
 };
-QueryColumns query_columns(const oscar_layer_desc* d, int n_query, int max_group = 8) {
+QueryColumns query_columns(const oscar_layer_desc* d, int n_query, int max_group) {
   const int v = n_query * (d->num_q_heads / d->num_kv_heads);
   int group = max_group;
   while (v % group != 0) group >>= 1;
   return QueryColumns{group, v / group};
 }
-// The BF16 baseline scores without a hi/lo split, so a work item takes up
-// to 16 columns.
+QueryColumns int2_query_columns(const oscar_layer_desc* d, int n_query) {
+  const int v = n_query * (d->num_q_heads / d->num_kv_heads);
+  return query_columns(d, n_query, v >= 32 ? 16 : 8);
+}
 constexpr int kMaxBf16Columns = 16;
 }  // namespace
 
@@ -198,7 +203,7 @@ size_t oscar_decode_multi_workspace_bytes(const oscar_layer_desc* desc, int32_t 
                                           int32_t max_seq_len) {
   if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0 || n_query < 1 || n_query > kMaxQueryTokens)
     return 0;
-  const QueryColumns c = query_columns(desc, n_query);
+  const QueryColumns c = int2_query_columns(desc, n_query);
   return plan_decode(batch, desc->num_kv_heads, c.group, c.n_colgroups, max_seq_len).workspace_bytes;
 }
 
@@ -221,7 +226,7 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
   const int hkv = desc->num_kv_heads, g = desc->num_q_heads / hkv;
   const int max_hist = max_seq_len - 320;
   if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
-  const QueryColumns c = query_columns(desc, n_query);
+  const QueryColumns c = int2_query_columns(desc, n_query);
   const DecodePlan plan = plan_decode(batch, hkv, c.group, c.n_colgroups, max_seq_len);
   if (!plan.ok) return OSCAR_ERR_UNSUPPORTED;
   if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;

@@ -263,8 +263,8 @@ size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
  * [batch][n_query][Hq][128]; seq_len[b] must be in [n_query, max_seq_len]
  * (a shorter length leaves queries that see no token, whose output is 0).
  * The work is split as for oscar_decode, with the (query token, head) pairs
- * of a KV head as the columns of the matrix-core products; n_query = 1 is
- * exactly oscar_decode.  Workspace: oscar_decode_multi_workspace_bytes(desc,
+ * of a KV head as the columns of the matrix-core products (up to 16 per work
+ * item); n_query = 1 is exactly oscar_decode.  Workspace: oscar_decode_multi_workspace_bytes(desc,
  * batch, n_query, max_seq_len) bytes, rules as for oscar_decode.  Errors as
  * for oscar_decode, plus OSCAR_ERR_INVALID for n_query < 1 or
  * n_query > max_seq_len and OSCAR_ERR_UNSUPPORTED for n_query > 256.
