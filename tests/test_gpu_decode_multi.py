@@ -107,3 +107,23 @@ def test_bf16_baseline_multi_query(n_query):
     ref = orc.attend_tail_bf16(q, kv, pt, [0, 1], lengths)
     for b in range(len(lengths)):
         assert rel_l2(out[b], ref[b]) <= TOL, lengths[b]
+
+
+@pytest.mark.parametrize("n_query", [4, 8, 64])
+def test_multi_query_qwen3_4b_32k_sampled_heads(n_query):
+    # Full size of the bench's multi-query workload: 32 q / 8 KV heads, 32768
+    # cached tokens, the last T as queries; device prefill for every KV head,
+    # the oracle's bytes for the two compared KV heads.
+    n = 32768
+    layer = Layer(seed=1160 + n_query, batch=1, hq=32, hkv=8, max_len=n)
+    kv_heads = [0, 5]
+    opool = layer.oracle_pool([n], kv_heads)
+    dev = layer.device_pool()
+    dev.prefill(i32([n]), bf16_tensor(layer.k), bf16_tensor(layer.v))
+    upload(dev, opool, kv_heads)
+    q = synth.queries(np.random.default_rng(12), (1, n_query, 32, 128))
+    out = dev.decode_multi(bf16_tensor(q), i32([n]), n).cpu().numpy()
+    heads = [(0, h) for h in range(32) if h // 4 in kv_heads]
+    ref = orc.attend_tail_tiered(q, opool, [0], [n], layer.rot, layer.rot, heads=heads)
+    idx = [h for _, h in heads]
+    assert rel_l2(out[0][:, idx], ref[0][:, idx]) <= TOL
