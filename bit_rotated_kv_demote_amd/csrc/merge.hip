@@ -153,11 +153,129 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (tid < kD) a.out[(size_t)head * kD + tid] = l_all > 0.0f ? (oh[0][tid] + (rr[0][tid] + rr[1][tid])) / l_all : 0.0f;
 }
 
+// Large grids: one workgroup per record group (sequence, KV head, column
+// group) of G columns.  Wave w merges columns w, w + 4, ...; the workgroup
+// then applies R^T to every column with one load of its slice of R, so the
+// R traffic (the bound when thousands of heads are merged) falls G-fold.
+__global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
+  __shared__ float w[4][kMaxSplits];
+  __shared__ float oh[16][2][kD];
+  __shared__ float rr[16][2][kD];
+  __shared__ float lsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.group;
+  const int grp = blockIdx.x;
+  const int b = grp / (a.hkv * a.n_colgroups), hk = (grp / a.n_colgroups) % a.hkv, cg = grp % a.n_colgroups;
+  const int n_slots = a.n_splits_total;
+  const float* gbase = a.partials + (size_t)grp * n_slots * G * kPartStride;
+  const int hq_total = a.hkv * a.g_model;
+  auto out_row = [&](int h) {
+    const int vh = cg * G + h, t = vh / a.g_model;
+    return a.out + (((size_t)b * a.q_tokens + t) * hq_total + hk * a.g_model + (vh - t * a.g_model)) * kD;
+  };
+  const int ri = tid & (kD - 1), jh = tid >> 7;
+  float4 rrow[16];
+  if (a.tiered) {
+    const float4* rp = reinterpret_cast<const float4*>(a.rot + (size_t)ri * kD + 64 * jh);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
+  }
+  const int n = a.seq_len[b];
+  int n_plain, n_rot;
+  if (a.tiered) {
+    const int hist_len = max(0, n - kSink - kRecent);
+    const int n_hist_pages = (hist_len + kPage - 1) / kPage;
+    const int n_tile = min(n, kSink) + min(max(n - kSink, 0), kRecent);
+    n_plain = min((n_tile + kTileTokens - 1) / kTileTokens, a.n_plain_slots);
+    n_rot = min((n_hist_pages + a.pages_per_split - 1) / a.pages_per_split, n_slots - a.n_plain_slots);
+  } else {
+    const int npages = (max(n, 0) + kPage - 1) / kPage;
+    n_plain = min((npages + a.pages_per_split - 1) / a.pages_per_split, a.n_plain_slots);
+    n_rot = 0;
+  }
+  if (n_plain + n_rot <= 0) {       // no tokens: nothing to attend
+    for (int idx = tid; idx < G * kD; idx += 256) out_row(idx / kD)[idx % kD] = 0.0f;
+    return;
+  }
+  auto active = [&](int s) { return s < a.n_plain_slots ? s < n_plain : s - a.n_plain_slots < n_rot; };
+
+  const int c4 = lane & 31, part = lane >> 5;
+  for (int h = wave; h < G; h += 4) {
+    const float* hb = gbase + (size_t)h * kPartStride;
+    auto rec = [&](int s) { return hb + (size_t)min(s, n_slots - 1) * G * kPartStride; };
+    // max, weights and total over the column's active splits (lanes stride 64)
+    float mm = kMInit;
+    for (int s = lane; s < n_slots; s += 64)
+      if (active(s)) mm = fmaxf(mm, rec(s)[kD]);
+    mm = wave_max(mm);
+    float ll = 0.0f;
+    for (int s = lane; s < n_slots; s += 64) {
+      const float2 ml = *reinterpret_cast<const float2*>(rec(s) + kD);
+      const float wk = active(s) ? __builtin_amdgcn_exp2f(ml.x - mm) : 0.0f;
+      w[wave][s] = wk;
+      ll = active(s) ? fmaf(wk, ml.y, ll) : ll;
+    }
+    ll = wave_sum(ll);
+    if (lane == 0) lsum[h] = ll;
+    __builtin_amdgcn_wave_barrier();
+    // weighted sums of the record columns: lanes l and l + 32 take alternate splits
+    float4 ap = make_float4(0.f, 0.f, 0.f, 0.f), ar = ap;
+    for (int s0 = part; s0 < n_slots; s0 += 8) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(rec(s0 + 2 * u) + 4 * c4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = s0 + 2 * u;
+        if (sl >= n_slots || !active(sl)) continue;
+        const float wk = w[wave][sl];
+        float4& acc = sl < a.n_plain_slots ? ap : ar;
+        acc.x = fmaf(wk, v[u].x, acc.x); acc.y = fmaf(wk, v[u].y, acc.y);
+        acc.z = fmaf(wk, v[u].z, acc.z); acc.w = fmaf(wk, v[u].w, acc.w);
+      }
+    }
+    ap.x = half_swap_sum(ap.x); ap.y = half_swap_sum(ap.y); ap.z = half_swap_sum(ap.z); ap.w = half_swap_sum(ap.w);
+    ar.x = half_swap_sum(ar.x); ar.y = half_swap_sum(ar.y); ar.z = half_swap_sum(ar.z); ar.w = half_swap_sum(ar.w);
+    if (part == 0) {
+      *reinterpret_cast<float4*>(&oh[h][0][4 * c4]) = ap;
+      *reinterpret_cast<float4*>(&oh[h][1][4 * c4]) = ar;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // inverse rotation of every column's history part: (y R^T)_i = sum_j y_j R[i][j]
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.0f;
+    if (n_rot > 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float4 y = *reinterpret_cast<const float4*>(&oh[h][1][64 * jh + 4 * e]);
+        acc = fmaf(y.x, rrow[e].x, acc);
+        acc = fmaf(y.y, rrow[e].y, acc);
+        acc = fmaf(y.z, rrow[e].z, acc);
+        acc = fmaf(y.w, rrow[e].w, acc);
+      }
+    }
+    rr[h][jh][ri] = acc;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * kD; idx += 256) {
+    const int h = idx / kD, i = idx % kD;
+    const float l = lsum[h];
+    out_row(h)[i] = l > 0.0f ? (oh[h][0][i] + (rr[h][0][i] + rr[h][1][i])) / l : 0.0f;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, int n_heads, hipStream_t st) {
   if (n_heads <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3(n_heads), dim3(256), 0, st, a);
+  // up to about three workgroups per compute unit: one workgroup per head
+  // spreads the latency; beyond that, one per record group shares R
+  if (n_heads <= 768 || a.group < 2)
+    hipLaunchKernelGGL(merge_kernel, dim3(n_heads), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(merge_group_kernel, dim3(n_heads / a.group), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

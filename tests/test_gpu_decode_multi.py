@@ -127,3 +127,21 @@ def test_multi_query_qwen3_4b_32k_sampled_heads(n_query):
     ref = orc.attend_tail_tiered(q, opool, [0], [n], layer.rot, layer.rot, heads=heads)
     idx = [h for _, h in heads]
     assert rel_l2(out[0][:, idx], ref[0][:, idx]) <= TOL
+
+
+def test_large_grid_merge_per_record_group():
+    # 26 sequences x 32 query heads = 832 merged heads: past the size where
+    # the merge switches to one workgroup per record group (shared R load).
+    lengths = [330 + 14 * b for b in range(26)]
+    layer = Layer(seed=1170, batch=26, hq=32, hkv=8, max_len=max(lengths))
+    out, ref = _multi_vs_oracle(layer, lengths, 1, 13)
+    assert rel_l2(out, ref) <= TOL
+
+
+def test_large_grid_merge_multi_query_16_columns():
+    # 4 sequences x 8 queries x 32 heads = 1024 merged heads in 16-column groups
+    lengths = [900, 410, 1300, 333]
+    layer = Layer(seed=1171, batch=4, hq=32, hkv=8, max_len=max(lengths))
+    out, ref = _multi_vs_oracle(layer, lengths, 8, 14)
+    for b in range(4):
+        assert rel_l2(out[b], ref[b]) <= TOL, b
