@@ -571,10 +571,42 @@ def cpu_baseline(hq, hkv, n0, host, seed, kv_sample=8, min_seconds=10.0):
         n_steps += 1
     secs = time.time() - t0
     scaled_us = secs * 1e6 / n_steps * hkv / kv_sample
-    return {"value": round(scaled_us, 1), "unit": "us/step", "cores": int(blas), "kind": "oracle",
+    base = {"value": round(scaled_us, 1), "unit": "us/step", "cores": int(blas), "kind": "oracle",
             "sample": f"{n_steps} successive steps, each one append (all {hkv} KV heads) + decode of {kv_sample} of "
                       f"{hkv} KV heads ({kv_sample * g} q heads) from {n0 + 1} tokens, {secs:.1f} s in total"
                       + (f", scaled x{hkv / kv_sample:g}" if kv_sample != hkv else "")}
+    # the same step on one thread, and the oracle's demotion of one
+    # 4096-token chunk (all KV heads, K and V) on all threads and on one
+    extra = {"threads_all": int(blas)}
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    n = n0 + n_steps
+    heads_all = [(0, hh) for hh in range(kv_sample * g)]
+
+    def one_step():
+        t = time.time()
+        pool.append(0, k[n], v[n], rot_k, rot_v, tau_k, tau_v)
+        orc.decode_tiered(q, pool, [0], [n + 1], rot_k, rot_v, heads=heads_all)
+        return (time.time() - t) * 1e6 * hkv / kv_sample
+
+    def demote_chunk():
+        cp = orc.Pool(1, hkv, 4096 // 16, np.arange(4096 // 16, dtype=np.int32)[None, :])
+        t = time.time()
+        cp.demote_many(0, np.arange(4096), k[64:64 + 4096], v[64:64 + 4096], rot_k, rot_v, tau_k, tau_v)
+        return (time.time() - t) * 1e6
+
+    if n < len(k):
+        extra["decode_step_us_one_thread"] = None
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                extra["decode_step_us_one_thread"] = round(one_step(), 1)
+    extra["demote_chunk_4096x8_us"] = round(demote_chunk(), 1)
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            extra["demote_chunk_4096x8_us_one_thread"] = round(demote_chunk(), 1)
+    return base, extra
 
 
 def main():
@@ -641,7 +673,7 @@ def main():
         torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(hq, hkv, n0, res["host"], 1001)
+        cpu, extra["cpu_oracle"] = cpu_baseline(hq, hkv, n0, res["host"], 1001)
     line = {
         "metric": METRIC,
         "value": round(res["us_per_step"], 3),
