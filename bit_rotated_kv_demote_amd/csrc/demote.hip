@@ -89,6 +89,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     // Its 64 R values are requested together with the ring slot.
     const float* R = is_v ? a.rot_v : a.rot_k;
     const int j = tid & (kD - 1), half = tid >> 7;
+    // the page id of the demoted token and the clip threshold depend only on
+    // the position: their loads go out with R's, not after the product
+    const int h = p - kSink - kRecent;
+    const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
+    const float* tau = is_v ? a.clip_v : a.clip_k;
+    const float tau_j = tau[j];
     float rc[64];
 #pragma unroll
     for (int e = 0; e < 64; ++e) rc[e] = R[(64 * half + e) * kD + j];
@@ -103,11 +109,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     for (int e = 0; e < 64; ++e) acc = fmaf(xs[64 * half + e], rc[e], acc);
     part[half][j] = acc;
     __syncthreads();  // also orders the ring read above before the overwrite below
-    const float* tau = is_v ? a.clip_v : a.clip_k;
     float yc = 0.0f;
-    if (tid < kD) yc = clip_value(part[0][tid] + part[1][tid], tau[tid]);
-    const int h = p - kSink - kRecent;
-    const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
+    if (tid < kD) yc = clip_value(part[0][tid] + part[1][tid], tau_j);
     uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
     quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh);
   }
