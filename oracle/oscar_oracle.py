@@ -59,6 +59,14 @@ R11 Several query tokens per sequence: the T queries of a step are the last
     and query t attends causally to positions [0, n - T + t].  With
     T <= 256 every INT2 history token precedes every query, so the causal
     limit only ever falls inside the BF16 tiers.
+R12 Scope of a calibration ([zingnex] 离线优化的优势: layers may share their
+    rotation).  Shared across layers: the key and value targets are the mean
+    of the layers' own targets (each layer's attention stays causal within
+    that layer's tokens), and tau pools every layer's rotated activations.
+    Per KV head: each KV head is calibrated as a layer of its own, from its
+    G query heads and its own keys and values, giving R and tau per KV head
+    ([Hkv, 128, 128] and [Hkv, 128]); every vector of that KV head is
+    rotated, clipped and inverse-rotated with its own pair.
 """
 from __future__ import annotations
 
@@ -215,18 +223,32 @@ def key_attention_covariance(q: np.ndarray, k: np.ndarray) -> np.ndarray:
 ROTATIONS = ("spectral", "key_attn", "hadamard", "identity")
 
 
-def calibrate(q, k, v, hadamard_block_size: int = GROUP, percentile: float = 99.0, rotation: str = "spectral"):
-    """Offline calibration of one layer: returns (R_K, R_V, tau_K, tau_V),
-    R as float32 [d, d] (y = x . R) and tau as float32 [d].
+def calibrate_layers(qs, ks, vs, hadamard_block_size: int = GROUP, percentile: float = 99.0,
+                     rotation: str = "spectral", per_kv_head: bool = False):
+    """Offline calibration shared by L layers (reading R12): returns
+    (R_K, R_V, tau_K, tau_V), R as float32 [d, d] (y = x . R), tau as
+    float32 [d]; with per_kv_head, float32 [Hkv, d, d] and [Hkv, d].
 
+    qs: [L, N, Hq, d], ks / vs: [L, N, Hkv, d] (L = 1 is one layer).
     rotation "spectral" is the method ([gist] 2.2 A: R_K = U_Q H P_br,
     R_V = U_S H P_br); "key_attn" takes the key eigenbasis from C_SK instead
     of C_Q; "hadamard" (R = H P_br, data-blind) and "identity" (R = I, plain
     INT2) are the baselines of [gist] 3 and 4."""
+    qs, ks, vs = (np.asarray(x) for x in (qs, ks, vs))
+    if per_kv_head:
+        g = qs.shape[2] // ks.shape[2]
+        parts = [calibrate_layers(qs[:, :, j * g:(j + 1) * g], ks[:, :, j:j + 1], vs[:, :, j:j + 1],
+                                  hadamard_block_size, percentile, rotation)
+                 for j in range(ks.shape[2])]
+        return tuple(np.stack([p[i] for p in parts]) for i in range(4))
     d = HEAD_DIM
+    n_layers = qs.shape[0]
     if rotation in ("spectral", "key_attn"):
-        c_k = query_covariance(q) if rotation == "spectral" else key_attention_covariance(q, k)
-        c_s = score_covariance(q, k, v)
+        if rotation == "spectral":
+            c_k = sum(query_covariance(qs[l]) for l in range(n_layers)) / n_layers
+        else:
+            c_k = sum(key_attention_covariance(qs[l], ks[l]) for l in range(n_layers)) / n_layers
+        c_s = sum(score_covariance(qs[l], ks[l], vs[l]) for l in range(n_layers)) / n_layers
         r_k = composite_rotation(eigenbasis(c_k), hadamard_block_size)
         r_v = composite_rotation(eigenbasis(c_s), hadamard_block_size)
     elif rotation == "hadamard":
@@ -237,9 +259,17 @@ def calibrate(q, k, v, hadamard_block_size: int = GROUP, percentile: float = 99.
         raise ValueError(rotation)
     r_k = np.asarray(r_k, np.float32)
     r_v = np.asarray(r_v, np.float32)
-    tau_k = clip_thresholds(k, r_k, percentile)
-    tau_v = clip_thresholds(v, r_v, percentile)
+    tau_k = clip_thresholds(ks, r_k, percentile)
+    tau_v = clip_thresholds(vs, r_v, percentile)
     return r_k, r_v, tau_k, tau_v
+
+
+def calibrate(q, k, v, hadamard_block_size: int = GROUP, percentile: float = 99.0, rotation: str = "spectral",
+              per_kv_head: bool = False):
+    """Offline calibration of one layer (q [N, Hq, d], k, v [N, Hkv, d]):
+    calibrate_layers with L = 1."""
+    return calibrate_layers(np.asarray(q)[None], np.asarray(k)[None], np.asarray(v)[None], hadamard_block_size,
+                            percentile, rotation, per_kv_head)
 
 
 # ---------------------------------------------------------------------------
@@ -247,8 +277,21 @@ def calibrate(q, k, v, hadamard_block_size: int = GROUP, percentile: float = 99.
 # ---------------------------------------------------------------------------
 
 def rotate_fp32(x: np.ndarray, r: np.ndarray) -> np.ndarray:
-    """y = fp32(x . R) with the product taken in fp64 (reading R1)."""
-    return (np.asarray(x, np.float64) @ np.asarray(r, np.float64)).astype(np.float32)
+    """y = fp32(x . R) with the product taken in fp64 (reading R1).
+
+    r: [d, d], or [H, d, d] with one R per KV head (R12) for x [..., H, d]."""
+    x = np.asarray(x, np.float64)
+    r = np.asarray(r, np.float64)
+    if r.ndim == 2:
+        return (x @ r).astype(np.float32)
+    return np.matmul(x[..., None, :], r)[..., 0, :].astype(np.float32)
+
+
+def heads_of(a, kv_heads, per_head_ndim: int):
+    """The KV heads' own entries of a per-KV-head R or tau (R12); a layer's
+    single R or tau (fewer dimensions) is returned as it is."""
+    a = np.asarray(a)
+    return a[list(kv_heads)] if a.ndim == per_head_ndim else a
 
 
 def clip(y: np.ndarray, tau: np.ndarray) -> np.ndarray:
@@ -466,15 +509,16 @@ class Pool:
         heads = list(range(self.hkv)) if kv_heads is None else list(kv_heads)
         h = np.asarray(h_indices, np.int64)
         pages = self.page_table[slot, h // PAGE]
-        kc, ks, kz = quantize_rotated(yk, tau_k)
-        vc, vs, vz = quantize_rotated(yv, tau_v)
+        kc, ks, kz = quantize_rotated(yk, heads_of(tau_k, heads, 2))
+        vc, vs, vz = quantize_rotated(yv, heads_of(tau_v, heads, 2))
         for i, hd in enumerate(heads):
             write_tokens(self.hist, hd, pages, h % PAGE, kc[:, i], ks[:, i], kz[:, i], vc[:, i], vs[:, i], vz[:, i])
 
     def demote_many(self, slot, h_indices, k_bits, v_bits, r_k, r_v, tau_k, tau_v, kv_heads=None):
         """Rotate (fp64 product rounded to fp32) and demote many bf16 tokens [N, H, 128]."""
-        yk = rotate_fp32(bf16_to_f64(k_bits), r_k)
-        yv = rotate_fp32(bf16_to_f64(v_bits), r_v)
+        heads = list(range(self.hkv)) if kv_heads is None else list(kv_heads)
+        yk = rotate_fp32(bf16_to_f64(k_bits), heads_of(r_k, heads, 3))
+        yv = rotate_fp32(bf16_to_f64(v_bits), heads_of(r_v, heads, 3))
         self.demote_rotated_many(slot, h_indices, yk, yv, tau_k, tau_v, kv_heads)
 
     @classmethod
@@ -506,9 +550,19 @@ class Pool:
             pages = self.page_table[slot, h // PAGE]
             blocks = self.hist[pages][:, heads]                        # [n_hist, H, 1536]
             kc, ks, kz, vc, vs, vz = unpack_tokens(blocks, h % PAGE)   # [n_hist, Hkv, ...]
-            kt[:, hist] = np.moveaxis(dequantize(kc, ks, kz) @ np.asarray(r_k, np.float64).T, 1, 0)
-            vt[:, hist] = np.moveaxis(dequantize(vc, vs, vz) @ np.asarray(r_v, np.float64).T, 1, 0)
+            kt[:, hist] = np.moveaxis(rotate_back(dequantize(kc, ks, kz), heads_of(r_k, heads, 3)), 1, 0)
+            vt[:, hist] = np.moveaxis(rotate_back(dequantize(vc, vs, vz), heads_of(r_v, heads, 3)), 1, 0)
         return kt, vt
+
+
+def rotate_back(y: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """y . R^T in fp64 (the inverse rotation, R1); r [d, d] or, per KV head,
+    [H, d, d] for y [..., H, d] (R12)."""
+    y = np.asarray(y, np.float64)
+    r = np.asarray(r, np.float64)
+    if r.ndim == 2:
+        return y @ r.T
+    return np.matmul(y[..., None, :], np.swapaxes(r, -1, -2))[..., 0, :]
 
 
 _BIT_TABLES = None

@@ -624,3 +624,136 @@ def test_bf16_tail_first_of_two_sees_only_itself_and_last_equals_decode():
     out = orc.attend_tail_bf16(q, kv, pt, [0], [300])
     one = orc.decode_bf16(np.ascontiguousarray(q[:, -1]), kv, pt, [0], [300])
     assert np.allclose(out[0, -1], one[0], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Calibration scope (reading R12): per KV head and shared across layers
+# ---------------------------------------------------------------------------
+
+def _exact_covariance_rows(basis, lam, n_tokens, n_heads):
+    """q [n_tokens, n_heads, 128] whose (token, head) rows are +-sqrt(lam_i) b_i
+    (b_i the basis columns), each direction on 2 n_tokens n_heads / 256 rows
+    with both signs: the pooled second moment is exactly B diag(lam) B^T / 128."""
+    rows = np.zeros((n_tokens * n_heads, 128))
+    for r in range(n_tokens * n_heads):
+        i, sign = (r // 2) % 128, (1.0 if r % 2 == 0 else -1.0)
+        rows[r] = sign * math.sqrt(lam[i]) * basis[:, i]
+    return rows.reshape(n_tokens, n_heads, 128)
+
+
+def _signed_columns(b):
+    out = b.copy()
+    for col in range(b.shape[1]):
+        i = int(np.argmax(np.abs(out[:, col])))
+        if out[i, col] < 0:
+            out[:, col] = -out[:, col]
+    return out
+
+
+def _eigvecs_of_rotation(r):
+    # R = U H P_br with H, P orthogonal and pinned above: U = R (H P_br)^T
+    hp = orc.hadamard_block() @ orc.bitrev_permutation()
+    return np.asarray(r, np.float64) @ hp.T
+
+
+def test_per_kv_head_calibration_planted_bases_closed_form():
+    # KV head j's two query heads carry covariance B_j diag(lam) B_j^T exactly;
+    # per-KV-head calibration must return U_j = B_j (sign rule) for each head,
+    # while the layer-wide R_K mixes the two bases.
+    rng = np.random.default_rng(40)
+    lam = np.linspace(50.0, 1.0, 128)
+    bases = [np.linalg.qr(rng.standard_normal((128, 128)))[0] for _ in range(2)]
+    q = np.concatenate([_exact_covariance_rows(b, lam, 128, 2) for b in bases], axis=1)   # [128, 4, 128]
+    _, k, v = _tiny_layer(128, 4, 2, 41)
+    r_k, r_v, t_k, t_v = orc.calibrate(q.astype(np.float32), k, v, per_kv_head=True)
+    assert r_k.shape == (2, 128, 128) and r_v.shape == (2, 128, 128) and t_k.shape == (2, 128)
+    for j in range(2):
+        assert np.allclose(_eigvecs_of_rotation(r_k[j]), _signed_columns(bases[j]), atol=2e-4), j
+        assert np.linalg.norm(r_v[j].astype(np.float64) @ r_v[j].T - np.eye(128)) < 1e-5
+    shared, _, _, _ = orc.calibrate(q.astype(np.float32), k, v)
+    assert not np.allclose(_eigvecs_of_rotation(shared), _signed_columns(bases[0]), atol=1e-2)
+
+
+def test_per_kv_head_clip_thresholds_use_only_that_heads_tokens():
+    # Head 1's keys are 100x head 0's: each tau_j must sit at the percentile
+    # order statistic of its own head's rotated values.
+    q, k, v = _tiny_layer(200, 4, 2, 42)
+    k = k.copy()
+    k[:, 1] *= 100.0
+    r_k, _, t_k, _ = orc.calibrate(q, k, v, per_kv_head=True)
+    want = 200 - 1 - math.floor(0.99 * 199)
+    for j in range(2):
+        y = np.abs(k[:, j].astype(np.float64) @ r_k[j].astype(np.float64))
+        above = (y > t_k[j].astype(np.float64)[None, :] * (1 + 1e-6)).sum(0)
+        assert np.all(np.abs(above - want) <= 1), j
+    assert np.all(t_k[1] > 20 * t_k[0])
+
+
+def test_layer_shared_calibration_planted_mean_spectrum():
+    # Two layers with the same basis and different spectra: the shared key
+    # target is B diag((lam1 + lam2) / 2) B^T, so U = B ordered by the mean
+    # spectrum, which differs from either layer's own order.
+    rng = np.random.default_rng(43)
+    basis = np.linalg.qr(rng.standard_normal((128, 128)))[0]
+    mean = rng.permutation(np.linspace(64.0, 1.0, 128))
+    alt = 0.45 * np.where(np.arange(128) % 2 == 0, 1.0, -1.0)
+    lam1, lam2 = mean * (1 + alt), mean * (1 - alt)
+    order = np.argsort(-mean)
+    assert not np.array_equal(order, np.argsort(-lam1)) and not np.array_equal(order, np.argsort(-lam2))
+    assert np.diff(np.sort(mean)).min() > 0.05
+    qs = np.stack([_exact_covariance_rows(basis, lam, 128, 2) for lam in (lam1, lam2)]).astype(np.float32)
+    _, k, v = _tiny_layer(128, 2, 1, 44)
+    ks, vs = np.stack([k, 2 * k]), np.stack([v, v])
+    r_k, r_v, t_k, t_v = orc.calibrate_layers(qs, ks, vs)
+    assert np.allclose(_eigvecs_of_rotation(r_k), _signed_columns(basis[:, order]), atol=2e-4)
+    # tau pools both layers' rotated keys: 256 samples per channel
+    y = np.abs(ks.reshape(-1, 128).astype(np.float64) @ r_k.astype(np.float64))
+    above = (y > t_k.astype(np.float64)[None, :] * (1 + 1e-6)).sum(0)
+    assert np.all(np.abs(above - (256 - 1 - math.floor(0.99 * 255))) <= 1)
+    # identical layers give the single layer's rotations
+    one = orc.calibrate(qs[0], k, v)
+    two = orc.calibrate_layers(np.stack([qs[0], qs[0]]), np.stack([k, k]), np.stack([v, v]))
+    assert np.array_equal(one[0], two[0]) and np.array_equal(one[1], two[1])
+
+
+def test_per_kv_head_pool_equals_independent_single_head_pools():
+    # With one R and tau per KV head, a 2-head pool holds, head by head, the
+    # bytes of a 1-head pool built with that head's own pair, and decodes to
+    # the same outputs; with both heads' pairs equal it is the shared-R pool.
+    n, hkv = 400, 2
+    st = synth.streams(45)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out_ch)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out_ch)
+    rs = [synth.random_rotation(st["rot"]) for _ in range(2 * hkv)]
+    r_k, r_v = np.stack(rs[:hkv]), np.stack(rs[hkv:])
+    t_k = np.stack([orc.clip_thresholds(synth.bf16_bits_to_f32(k[:, j]), r_k[j]) for j in range(hkv)])
+    t_v = np.stack([orc.clip_thresholds(synth.bf16_bits_to_f32(v[:, j]), r_v[j]) for j in range(hkv)])
+    pt = synth.page_permutation(st["perm"], 8)[None, :]
+    both = orc.Pool(1, hkv, 8, pt)
+    for p in range(n):
+        both.append(0, k[p], v[p], r_k, r_v, t_k, t_v)
+    q = synth.queries(st["q"], (1, 4, 128))
+    out = orc.decode_tiered(q, both, [0], [n], r_k, r_v)
+    # many-token demotion (all heads, or head 1 alone) writes the same bytes
+    h = np.arange(n - 320)
+    bulk = orc.Pool(1, hkv, 8, pt)
+    bulk.demote_many(0, h, k[64 + h], v[64 + h], r_k, r_v, t_k, t_v)
+    assert np.array_equal(bulk.hist, both.hist)
+    bulk1 = orc.Pool(1, hkv, 8, pt)
+    bulk1.demote_many(0, h, k[64 + h][:, [1]], v[64 + h][:, [1]], r_k, r_v, t_k, t_v, kv_heads=[1])
+    assert np.array_equal(bulk1.hist[:, 1], both.hist[:, 1])
+    for j in range(hkv):
+        one = orc.Pool(1, 1, 8, pt)
+        for p in range(n):
+            one.append(0, k[p, j:j + 1], v[p, j:j + 1], r_k[j], r_v[j], t_k[j], t_v[j])
+        assert np.array_equal(one.hist[:, 0], both.hist[:, j]), j
+        ref = orc.decode_tiered(q[:, 2 * j:2 * j + 2], one, [0], [n], r_k[j], r_v[j])
+        assert np.allclose(out[0, 2 * j:2 * j + 2], ref[0], rtol=0, atol=1e-12), j
+    same = orc.Pool(1, hkv, 8, pt)
+    shared = orc.Pool(1, hkv, 8, pt)
+    for p in range(n):
+        same.append(0, k[p], v[p], np.stack([r_k[0]] * hkv), np.stack([r_v[0]] * hkv), np.stack([t_k[0]] * hkv),
+                    np.stack([t_v[0]] * hkv))
+        shared.append(0, k[p], v[p], r_k[0], r_v[0], t_k[0], t_v[0])
+    assert np.array_equal(same.hist, shared.hist)
