@@ -16,9 +16,9 @@ LIB_PATH = os.path.join(HERE, "libamdoscar.so")
 
 OSCAR_SRC_BF16 = 0
 OSCAR_SRC_F32_ROTATED = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
-EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_append", "oscar_demote",
+EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_calibrate_layers", "oscar_append", "oscar_demote",
             "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_multi",
             "oscar_decode_multi_workspace_bytes", "oscar_decode_bf16", "oscar_decode_bf16_workspace_bytes",
             "oscar_decode_bf16_multi", "oscar_decode_bf16_multi_workspace_bytes")
@@ -41,7 +41,7 @@ class Pool(ctypes.Structure):
                 ("recent_v", ctypes.c_void_p), ("hist", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
                 ("n_slots", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("rot_k", ctypes.c_void_p), ("rot_v", ctypes.c_void_p), ("clip_k", ctypes.c_void_p),
-                ("clip_v", ctypes.c_void_p)]
+                ("clip_v", ctypes.c_void_p), ("rot_per_kv_head", ctypes.c_int32)]
 
 
 class Bf16Pool(ctypes.Structure):
@@ -50,7 +50,8 @@ class Bf16Pool(ctypes.Structure):
 
 
 class CalibOpts(ctypes.Structure):
-    _fields_ = [("hadamard_block", ctypes.c_int32), ("clip_percentile", ctypes.c_float), ("rotation", ctypes.c_int32)]
+    _fields_ = [("hadamard_block", ctypes.c_int32), ("clip_percentile", ctypes.c_float), ("rotation", ctypes.c_int32),
+                ("per_kv_head", ctypes.c_int32)]
 
 
 # oscar_calib_opts.rotation
@@ -74,6 +75,8 @@ def load():
     lib.oscar_status_string.argtypes = [ctypes.c_int]
     lib.oscar_calibrate.restype = ctypes.c_int
     lib.oscar_calibrate.argtypes = [P, P, P, P, P, I64, P, P, P, P]
+    lib.oscar_calibrate_layers.restype = ctypes.c_int
+    lib.oscar_calibrate_layers.argtypes = [P, P, I32, P, P, P, I64, P, P, P, P]
     lib.oscar_append.restype = ctypes.c_int
     lib.oscar_append.argtypes = [P, P, P, P, P, P, I32, P]
     lib.oscar_demote.restype = ctypes.c_int
@@ -123,13 +126,14 @@ def layer_desc(num_q_heads: int, num_kv_heads: int) -> LayerDesc:
     return LayerDesc(num_q_heads, num_kv_heads, 128, 16, 64, 256, 32)
 
 
-def make_pool(sink_k, sink_v, recent_k, recent_v, hist, page_table, rot_k, rot_v, clip_k, clip_v) -> Pool:
+def make_pool(sink_k, sink_v, recent_k, recent_v, hist, page_table, rot_k, rot_v, clip_k, clip_v,
+              rot_per_kv_head=False) -> Pool:
     return Pool(sink_k.data_ptr(), sink_v.data_ptr(), recent_k.data_ptr(), recent_v.data_ptr(),
                 hist.data_ptr() if hist is not None else None,
                 page_table.data_ptr() if page_table is not None else None,
                 sink_k.shape[0], page_table.shape[1] if page_table is not None else 0,
                 hist.shape[0] if hist is not None else 0,
-                rot_k.data_ptr(), rot_v.data_ptr(), clip_k.data_ptr(), clip_v.data_ptr())
+                rot_k.data_ptr(), rot_v.data_ptr(), clip_k.data_ptr(), clip_v.data_ptr(), int(bool(rot_per_kv_head)))
 
 
 def make_bf16_pool(kv, page_table) -> Bf16Pool:
@@ -137,12 +141,23 @@ def make_bf16_pool(kv, page_table) -> Bf16Pool:
 
 
 def oscar_calibrate(desc, q, k, v, rot_k, rot_v, clip_k, clip_v, hadamard_block=32, clip_percentile=99.0,
-                    rotation=ROT_SPECTRAL):
-    """Host tensors: q [N,Hq,128], k/v [N,Hkv,128] fp32; outputs fp32 [128,128] / [128]."""
-    opts = CalibOpts(hadamard_block, clip_percentile, rotation)
+                    rotation=ROT_SPECTRAL, per_kv_head=False):
+    """Host tensors: q [N,Hq,128], k/v [N,Hkv,128] fp32; outputs fp32 [128,128] / [128]
+    (per KV head: [Hkv,128,128] / [Hkv,128])."""
+    opts = CalibOpts(hadamard_block, clip_percentile, rotation, int(bool(per_kv_head)))
     _check("oscar_calibrate", load().oscar_calibrate(ctypes.byref(desc), ctypes.byref(opts), _ptr(q), _ptr(k),
                                                       _ptr(v), q.shape[0], _ptr(rot_k), _ptr(rot_v),
                                                       _ptr(clip_k), _ptr(clip_v)))
+
+
+def oscar_calibrate_layers(desc, q, k, v, rot_k, rot_v, clip_k, clip_v, hadamard_block=32, clip_percentile=99.0,
+                           rotation=ROT_SPECTRAL, per_kv_head=False):
+    """Host tensors: q [L,N,Hq,128], k/v [L,N,Hkv,128] fp32; one calibration shared by the L layers."""
+    opts = CalibOpts(hadamard_block, clip_percentile, rotation, int(bool(per_kv_head)))
+    _check("oscar_calibrate_layers",
+           load().oscar_calibrate_layers(ctypes.byref(desc), ctypes.byref(opts), q.shape[0], _ptr(q), _ptr(k),
+                                         _ptr(v), q.shape[1], _ptr(rot_k), _ptr(rot_v), _ptr(clip_k),
+                                         _ptr(clip_v)))
 
 
 def oscar_append(desc, pool, seq_slot, position, k_new, v_new, batch, stream=None):

@@ -9,7 +9,9 @@
 // R_K = U_Q H P_br and R_V = U_S H P_br; per-layer clip thresholds come from
 // the rotated calibration activations.  "OSCAR：面向2-bit KV缓存量化的谱协方差感知
 // 旋转方法" (zingnex.cn), 离线优化的优势: the rotation is computed once offline and
-// applied unchanged at inference.
+// applied unchanged at inference, and layers may share it (here: the mean of
+// the layers' targets, tau over all of their activations).  Per KV head, each
+// KV head is calibrated from its own query heads, keys and values.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -23,18 +25,19 @@ namespace {
 
 constexpr int D = 128;
 
-// C_Q: pooled over tokens and query heads.
-void query_covariance(const float* q, int64_t n, int hq, double* c) {
-  std::fill(c, c + D * D, 0.0);
+// Sum of q^T q over tokens and query heads, added per KV head into
+// c[hkv][D*D] (query head h belongs to KV head h / (hq / hkv)).
+void add_query_moments(const float* q, int64_t n, int hq, int hkv, double* c) {
+  const int g = hq / hkv;
   const int64_t rows = n * hq;
   const unsigned nt = std::max(1u, std::min(8u, std::thread::hardware_concurrency()));
-  std::vector<std::vector<double>> part(nt, std::vector<double>(D * D, 0.0));
+  std::vector<std::vector<double>> part(nt, std::vector<double>((size_t)hkv * D * D, 0.0));
   std::vector<std::thread> th;
   for (unsigned t = 0; t < nt; ++t)
     th.emplace_back([&, t] {
-      double* acc = part[t].data();
       for (int64_t r = t; r < rows; r += nt) {
         const float* x = q + r * D;
+        double* acc = part[t].data() + (size_t)((r % hq) / g) * D * D;
         for (int i = 0; i < D; ++i) {
           const double xi = x[i];
           double* row = acc + i * D;
@@ -44,28 +47,27 @@ void query_covariance(const float* q, int64_t n, int hq, double* c) {
     });
   for (auto& t : th) t.join();
   for (unsigned t = 0; t < nt; ++t)
-    for (int i = 0; i < D * D; ++i) c[i] += part[t][i];
-  for (int i = 0; i < D * D; ++i) c[i] /= (double)rows;
+    for (size_t i = 0; i < (size_t)hkv * D * D; ++i) c[i] += part[t][i];
 }
 
-// C_S = (1/(N Hq)) sum_h sum_n o_{h,n}^T o_{h,n}, o_{h,n} = sum_{m<=n} softmax_m(q_n . k_m / sqrt(d)) v_m.
-// With the keys passed as v this is the attention-weighted key covariance
-// C_SK = (1/(N Hq)) sum_h (S_h K)^T (S_h K).
-void score_covariance(const float* q, const float* k, const float* v, int64_t n, int hq, int hkv, double* c) {
-  std::fill(c, c + D * D, 0.0);
+// Sum over query heads h and tokens n of o_{h,n}^T o_{h,n}, with
+// o_{h,n} = sum_{m<=n} softmax_m(q_n . k_m / sqrt(d)) v_m, added per KV head
+// into c[hkv][D*D] (the value target C_S before its 1/(N Hq)).  With the keys
+// passed as v this is the attention-weighted key moment (S_h K)^T (S_h K).
+void add_score_moments(const float* q, const float* k, const float* v, int64_t n, int hq, int hkv, double* c) {
   const int g = hq / hkv;
   const unsigned nt = std::max(1u, std::min(8u, std::thread::hardware_concurrency()));
-  std::vector<std::vector<double>> part(nt, std::vector<double>(D * D, 0.0));
+  std::vector<std::vector<double>> part(nt, std::vector<double>((size_t)hkv * D * D, 0.0));
   std::vector<std::thread> th;
   const double inv_sqrt_d = 1.0 / std::sqrt((double)D);
   for (unsigned t = 0; t < nt; ++t)
     th.emplace_back([&, t] {
-      double* acc = part[t].data();
       std::vector<double> logit(n), o(D), qd(D);
       for (int64_t work = t; work < (int64_t)hq * n; work += nt) {
         const int h = (int)(work / n);
         const int64_t row = work % n;
         const int kv = h / g;
+        double* acc = part[t].data() + (size_t)kv * D * D;
         const float* qr = q + (row * hq + h) * D;
         for (int i = 0; i < D; ++i) qd[i] = qr[i];
         double mx = -INFINITY;
@@ -92,8 +94,7 @@ void score_covariance(const float* q, const float* k, const float* v, int64_t n,
     });
   for (auto& t : th) t.join();
   for (unsigned t = 0; t < nt; ++t)
-    for (int i = 0; i < D * D; ++i) c[i] += part[t][i];
-  for (int i = 0; i < D * D; ++i) c[i] /= (double)(n * hq);
+    for (size_t i = 0; i < (size_t)hkv * D * D; ++i) c[i] += part[t][i];
 }
 
 // Cyclic Jacobi eigen-decomposition of a symmetric matrix; eigenvectors as
@@ -169,12 +170,14 @@ void compose_rotation(const double* u, int block, float* r) {
     for (int j = 0; j < D; ++j) r[i * D + j] = (float)uh[i * D + bit_reverse7(j)];
 }
 
-// tau_j = linear-interpolated percentile of |x . R|_j over all rows of x.
-void clip_thresholds(const float* x, int64_t rows, const float* r, double pct, float* tau) {
+// tau_j = linear-interpolated percentile of |x . R|_j over the rows
+// x + (first + step * m) * D, m = 0 .. rows-1.
+void clip_thresholds(const float* x, int64_t rows, int64_t first, int64_t step, const float* r, double pct,
+                     float* tau) {
   std::vector<std::vector<double>> col(D, std::vector<double>(rows));
   std::vector<double> y(D);
   for (int64_t n = 0; n < rows; ++n) {
-    const float* xr = x + n * D;
+    const float* xr = x + (first + step * n) * D;
     std::fill(y.begin(), y.end(), 0.0);
     for (int i = 0; i < D; ++i) {
       const double xi = xr[i];
@@ -195,42 +198,75 @@ void clip_thresholds(const float* x, int64_t rows, const float* r, double pct, f
 
 }  // namespace
 
-int calibrate_layer(int hq, int hkv, int hadamard_block, float percentile, int rotation, const float* q,
-                    const float* k, const float* v, int64_t n, float* rot_k, float* rot_v, float* clip_k,
-                    float* clip_v) {
+int calibrate_layers(int hq, int hkv, int n_layers, int hadamard_block, float percentile, int rotation,
+                     bool per_kv_head, const float* q, const float* k, const float* v, int64_t n, float* rot_k,
+                     float* rot_v, float* clip_k, float* clip_v) {
+  if (rotation < kRotSpectral || rotation > kRotIdentity) return -2;
   for (const float* p : {q, k, v}) {
-    const int64_t cnt = n * (p == q ? hq : hkv) * D;
+    const int64_t cnt = (int64_t)n_layers * n * (p == q ? hq : hkv) * D;
     for (int64_t i = 0; i < cnt; ++i)
       if (!std::isfinite(p[i])) return -1;
   }
-  std::vector<double> ck(D * D), cs(D * D), uk(D * D, 0.0), us(D * D, 0.0);
-  switch (rotation) {
-    case kRotSpectral:                 // key target C_Q, value target C_S
-    case kRotKeyAttn:                  // key target C_SK, value target C_S
+  // Per-KV-head sums of the key and value moments over every layer; a set
+  // (one KV head, or all of them) then averages its share: the targets of
+  // each layer, averaged over the layers.
+  const int n_sets = per_kv_head ? hkv : 1;
+  const int heads_per_set = per_kv_head ? 1 : hkv;
+  const double rows_per_set = (double)n_layers * (double)n * (double)(hq / hkv) * heads_per_set;
+  std::vector<double> mk((size_t)hkv * D * D, 0.0), ms((size_t)hkv * D * D, 0.0);
+  if (rotation == kRotSpectral || rotation == kRotKeyAttn) {
+    for (int l = 0; l < n_layers; ++l) {
+      const float* ql = q + (int64_t)l * n * hq * D;
+      const float* kl = k + (int64_t)l * n * hkv * D;
+      const float* vl = v + (int64_t)l * n * hkv * D;
       if (rotation == kRotSpectral)
-        query_covariance(q, n, hq, ck.data());
+        add_query_moments(ql, n, hq, hkv, mk.data());
       else
-        score_covariance(q, k, k, n, hq, hkv, ck.data());
-      score_covariance(q, k, v, n, hq, hkv, cs.data());
-      eigenbasis(ck.data(), uk.data());
-      eigenbasis(cs.data(), us.data());
-      compose_rotation(uk.data(), hadamard_block, rot_k);
-      compose_rotation(us.data(), hadamard_block, rot_v);
-      break;
-    case kRotHadamard:                 // U = I: R = H P_br
-      for (int i = 0; i < D; ++i) uk[i * D + i] = 1.0;
-      compose_rotation(uk.data(), hadamard_block, rot_k);
-      std::copy(rot_k, rot_k + D * D, rot_v);
-      break;
-    case kRotIdentity:                 // R = I
-      for (int i = 0; i < D * D; ++i) rot_k[i] = rot_v[i] = (i % (D + 1) == 0) ? 1.0f : 0.0f;
-      break;
-    default:
-      return -2;
+        add_score_moments(ql, kl, kl, n, hq, hkv, mk.data());
+      add_score_moments(ql, kl, vl, n, hq, hkv, ms.data());
+    }
   }
-  clip_thresholds(k, n * hkv, rot_k, percentile, clip_k);
-  clip_thresholds(v, n * hkv, rot_v, percentile, clip_v);
-  for (int j = 0; j < D; ++j)
+  std::vector<double> ck(D * D), cs(D * D), uk(D * D), us(D * D);
+  for (int set = 0; set < n_sets; ++set) {
+    float* rk = rot_k + (size_t)set * D * D;
+    float* rv = rot_v + (size_t)set * D * D;
+    switch (rotation) {
+      case kRotSpectral:               // key target C_Q, value target C_S
+      case kRotKeyAttn:                // key target C_SK, value target C_S
+        std::fill(ck.begin(), ck.end(), 0.0);
+        std::fill(cs.begin(), cs.end(), 0.0);
+        for (int hd = set * heads_per_set; hd < (set + 1) * heads_per_set; ++hd)
+          for (int i = 0; i < D * D; ++i) {
+            ck[i] += mk[(size_t)hd * D * D + i];
+            cs[i] += ms[(size_t)hd * D * D + i];
+          }
+        for (int i = 0; i < D * D; ++i) {
+          ck[i] /= rows_per_set;
+          cs[i] /= rows_per_set;
+        }
+        eigenbasis(ck.data(), uk.data());
+        eigenbasis(cs.data(), us.data());
+        compose_rotation(uk.data(), hadamard_block, rk);
+        compose_rotation(us.data(), hadamard_block, rv);
+        break;
+      case kRotHadamard:               // U = I: R = H P_br
+        std::fill(uk.begin(), uk.end(), 0.0);
+        for (int i = 0; i < D; ++i) uk[i * D + i] = 1.0;
+        compose_rotation(uk.data(), hadamard_block, rk);
+        std::copy(rk, rk + D * D, rv);
+        break;
+      default:                         // kRotIdentity: R = I
+        for (int i = 0; i < D * D; ++i) rk[i] = rv[i] = (i % (D + 1) == 0) ? 1.0f : 0.0f;
+        break;
+    }
+    // the set's rows of every layer: all (layer, token, KV head) rows, or
+    // those of KV head `set`
+    const int64_t rows = per_kv_head ? (int64_t)n_layers * n : (int64_t)n_layers * n * hkv;
+    const int64_t first = per_kv_head ? set : 0, step = per_kv_head ? hkv : 1;
+    clip_thresholds(k, rows, first, step, rk, percentile, clip_k + (size_t)set * D);
+    clip_thresholds(v, rows, first, step, rv, percentile, clip_v + (size_t)set * D);
+  }
+  for (int j = 0; j < n_sets * D; ++j)
     if (!std::isfinite(clip_k[j]) || !std::isfinite(clip_v[j]) || clip_k[j] > 65504.0f || clip_v[j] > 65504.0f ||
         !(clip_k[j] > 0.0f) || !(clip_v[j] > 0.0f))
       return -1;

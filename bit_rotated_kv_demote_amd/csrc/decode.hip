@@ -353,9 +353,10 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
   constexpr int kQPer = (kQWords + 255) / 256;
   float4 rq[16];
   uint32_t qv[kQPer];
+  const float* rot_k = a.rot_k + (size_t)hk * a.rot_kv_stride;
   if (!is_tile) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(a.rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
+    for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {                 // unconditional
       const int w = min(tid + 256 * e, kQWords - 1);

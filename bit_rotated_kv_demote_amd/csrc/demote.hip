@@ -87,13 +87,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if (p >= kSink + kRecent) {
     // y_j = sum_i x_i R[i][j]; thread (j, half) covers i in [64 half, 64 half + 64).
     // Its 64 R values are requested together with the ring slot.
-    const float* R = is_v ? a.rot_v : a.rot_k;
+    const float* R = (is_v ? a.rot_v : a.rot_k) + (size_t)hk * a.rot_kv_stride;
     const int j = tid & (kD - 1), half = tid >> 7;
     // the page id of the demoted token and the clip threshold depend only on
     // the position: their loads go out with R's, not after the product
     const int h = p - kSink - kRecent;
     const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
-    const float* tau = is_v ? a.clip_v : a.clip_k;
+    const float* tau = (is_v ? a.clip_v : a.clip_k) + (size_t)hk * a.clip_kv_stride;
     const float tau_j = tau[j];
     float rc[64];
 #pragma unroll
@@ -247,10 +247,15 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tcol = lane & 15, qa = lane >> 4;
+  // One R and tau per KV head: workgroup z serves KV head z alone (its R is
+  // the one staged in LDS); with a shared pair every workgroup serves all.
+  const bool per_head = a.clip_kv_stride != 0;
+  const int heads_here = per_head ? 1 : a.hkv;
+  const int hk_base = per_head ? (int)blockIdx.z : 0;
 
   if constexpr (!kRotatedInput) {
     // R (row-major fp32) -> LDS R^T split into bf16 hi + lo.
-    const float* R = is_v ? a.rot_v : a.rot_k;
+    const float* R = (is_v ? a.rot_v : a.rot_k) + (size_t)hk_base * a.rot_kv_stride;
     for (int idx = tid; idx < kD * kD / 4; idx += 256) {
       const float4 v4 = reinterpret_cast<const float4*>(R)[idx];
       const int i = idx / (kD / 4), j0 = (idx % (kD / 4)) * 4;
@@ -264,14 +269,14 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
       }
     }
   }
-  if (tid < kD) tau_s[tid] = (is_v ? a.clip_v : a.clip_k)[tid];
+  if (tid < kD) tau_s[tid] = (is_v ? a.clip_v : a.clip_k)[(size_t)hk_base * a.clip_kv_stride + tid];
   __syncthreads();
 
   const int ups = a.unit_tiles;                       // units per (sequence, KV head)
-  const int n_units = a.batch * a.hkv * ups;
+  const int n_units = a.batch * heads_here * ups;
   for (int u = blockIdx.x * 4 + wave; u < n_units; u += gridDim.x * 4) {
-    const int b = u / (a.hkv * ups), rem = u % (a.hkv * ups);
-    const int hk = rem / ups, tok0 = kUnitTokens * (rem % ups);
+    const int b = u / (heads_here * ups), rem = u % (heads_here * ups);
+    const int hk = hk_base + rem / ups, tok0 = kUnitTokens * (rem % ups);
     const int count = a.length ? max(0, a.length[b] - kSink - kRecent) : a.n_tokens;
     if (tok0 >= count) continue;                       // wave-uniform
     const int slot = a.seq_slot ? a.seq_slot[b] : b;
@@ -377,10 +382,13 @@ hipError_t launch_demote(const DemoteArgs& a_in, int batch, int max_count, bool 
   DemoteArgs a = a_in;
   a.batch = batch;
   a.unit_tiles = (max_count + kUnitTokens - 1) / kUnitTokens;
-  const long units = (long)batch * a.hkv * a.unit_tiles;
-  // two workgroups per compute unit per tensor at most (each stages R once)
-  const int nwg = (int)std::min<long>((units + 3) / 4, 256);
-  const dim3 grid(nwg, 2);
+  // two workgroups per compute unit per tensor at most (each stages R once);
+  // with one R per KV head, a slice of them per KV head (grid z)
+  const bool per_head = a.clip_kv_stride != 0;
+  const int heads = per_head ? a.hkv : 1;
+  const long units = (long)batch * (per_head ? 1 : a.hkv) * a.unit_tiles;
+  const int nwg = (int)std::min<long>((units + 3) / 4, std::max(1, 256 / heads));
+  const dim3 grid(nwg, 2, heads);
   if (rotated)
     hipLaunchKernelGGL(demote_bulk_kernel<true>, grid, dim3(256), 0, st, a);
   else

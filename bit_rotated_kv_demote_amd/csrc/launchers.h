@@ -18,6 +18,8 @@ struct AppendArgs {
   const int32_t* page_table;
   const float* rot_k; const float* rot_v;
   const float* clip_k; const float* clip_v;
+  int rot_kv_stride;       // elements from one KV head's R to the next (0: shared)
+  int clip_kv_stride;      // likewise for the clip thresholds
   int hkv;
   int max_pages;
 };
@@ -33,6 +35,8 @@ struct DemoteArgs {
   const int32_t* seq_slot;    // nullable
   const float* rot_k; const float* rot_v;
   const float* clip_k; const float* clip_v;
+  int rot_kv_stride;  // elements from one KV head's R to the next (0: shared)
+  int clip_kv_stride;
   uint8_t* hist;
   const int32_t* page_table;
   int max_pages;
@@ -64,6 +68,7 @@ struct DecodeArgs {
   const uint8_t* hist;
   const int32_t* page_table;
   const float* rot_k; const float* rot_v;
+  int rot_kv_stride;          // elements from one KV head's R to the next (0: shared)
   float* partials;            // workspace: [batch*Hkv][n_splits][G][132]
   int hkv;
   int max_pages;
@@ -105,6 +110,7 @@ struct MergeArgs {
   const float* partials;      // [batch*Hkv*n_colgroups][n_splits_total][group][132]
   const int32_t* seq_len;     // [batch]
   const float* rot;           // R_V for the rotated (history) records; unused when tiered == 0
+  int rot_kv_stride;          // elements from one KV head's R_V to the next (0: shared)
   float* out;                 // fp32 [batch][q_tokens][Hq][128]
   int hkv;
   int group;                  // columns per record group

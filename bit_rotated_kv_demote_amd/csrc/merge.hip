@@ -56,7 +56,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int ri = tid & (kD - 1), jh = tid >> 7;
   float4 rrow[16];
   if (a.tiered) {
-    const float4* rp = reinterpret_cast<const float4*>(a.rot + (size_t)ri * kD + 64 * jh);
+    const float* rot = a.rot + (size_t)(hq / a.g_model) * a.rot_kv_stride;
+    const float4* rp = reinterpret_cast<const float4*>(rot + (size_t)ri * kD + 64 * jh);
 #pragma unroll
     for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
   }
@@ -176,7 +177,8 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
   const int ri = tid & (kD - 1), jh = tid >> 7;
   float4 rrow[16];
   if (a.tiered) {
-    const float4* rp = reinterpret_cast<const float4*>(a.rot + (size_t)ri * kD + 64 * jh);
+    const float* rot = a.rot + (size_t)hk * a.rot_kv_stride;
+    const float4* rp = reinterpret_cast<const float4*>(rot + (size_t)ri * kD + 64 * jh);
 #pragma unroll
     for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
   }

@@ -29,11 +29,17 @@ oscar_status check_pool(const oscar_pool* p, bool need_hist_tiers) {
   if (!p->sink_k || !p->sink_v || !p->recent_k || !p->recent_v) return OSCAR_ERR_INVALID;
   if (need_hist_tiers && (!p->hist || !p->page_table)) return OSCAR_ERR_INVALID;
   if (!p->rot_k || !p->rot_v || !p->clip_k || !p->clip_v) return OSCAR_ERR_INVALID;
+  if (p->rot_per_kv_head != 0 && p->rot_per_kv_head != 1) return OSCAR_ERR_INVALID;
   if (p->n_slots <= 0 || p->max_pages_per_seq < 0 || p->num_pages < 0) return OSCAR_ERR_INVALID;
   return OSCAR_OK;
 }
 
 thread_local char g_hip_error[160] = "";
+
+// elements between consecutive KV heads' rotations / clip thresholds (0:
+// one pair shared by the layer)
+int rot_stride(const oscar_pool* p) { return p->rot_per_kv_head ? 128 * 128 : 0; }
+int clip_stride(const oscar_pool* p) { return p->rot_per_kv_head ? 128 : 0; }
 
 oscar_status hip_status(hipError_t e) {
   if (e == hipSuccess) return OSCAR_OK;
@@ -84,18 +90,27 @@ const char* oscar_status_string(oscar_status s) {
   return "unknown status";
 }
 
-oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opts* opts, const float* q,
-                             const float* k, const float* v, int64_t n_tokens, float* rot_k, float* rot_v,
-                             float* clip_k, float* clip_v) {
+oscar_status oscar_calibrate_layers(const oscar_layer_desc* desc, const oscar_calib_opts* opts, int32_t n_layers,
+                                    const float* q, const float* k, const float* v, int64_t n_tokens, float* rot_k,
+                                    float* rot_v, float* clip_k, float* clip_v) {
   oscar_status st = check_desc(desc);
   if (st != OSCAR_OK) return st;
-  if (!opts || !q || !k || !v || !rot_k || !rot_v || !clip_k || !clip_v || n_tokens < 2) return OSCAR_ERR_INVALID;
+  if (!opts || !q || !k || !v || !rot_k || !rot_v || !clip_k || !clip_v || n_tokens < 2 || n_layers < 1)
+    return OSCAR_ERR_INVALID;
   if (opts->hadamard_block != 32 && opts->hadamard_block != 128) return OSCAR_ERR_UNSUPPORTED;
   if (!(opts->clip_percentile > 0.0f && opts->clip_percentile <= 100.0f)) return OSCAR_ERR_INVALID;
   if (opts->rotation < OSCAR_ROT_SPECTRAL || opts->rotation > OSCAR_ROT_IDENTITY) return OSCAR_ERR_INVALID;
-  const int rc = calibrate_layer(desc->num_q_heads, desc->num_kv_heads, opts->hadamard_block, opts->clip_percentile,
-                                 opts->rotation, q, k, v, n_tokens, rot_k, rot_v, clip_k, clip_v);
+  if (opts->per_kv_head != 0 && opts->per_kv_head != 1) return OSCAR_ERR_INVALID;
+  const int rc = calibrate_layers(desc->num_q_heads, desc->num_kv_heads, n_layers, opts->hadamard_block,
+                                  opts->clip_percentile, opts->rotation, opts->per_kv_head == 1, q, k, v, n_tokens,
+                                  rot_k, rot_v, clip_k, clip_v);
   return rc == 0 ? OSCAR_OK : (rc == -2 ? OSCAR_ERR_INVALID : OSCAR_ERR_NUMERIC);
+}
+
+oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opts* opts, const float* q,
+                             const float* k, const float* v, int64_t n_tokens, float* rot_k, float* rot_v,
+                             float* clip_k, float* clip_v) {
+  return oscar_calibrate_layers(desc, opts, 1, q, k, v, n_tokens, rot_k, rot_v, clip_k, clip_v);
 }
 
 oscar_status oscar_append(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
@@ -119,6 +134,7 @@ oscar_status oscar_append(const oscar_layer_desc* desc, const oscar_pool* pool, 
   a.page_table = pool->page_table;
   a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
   a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
+  a.rot_kv_stride = rot_stride(pool); a.clip_kv_stride = clip_stride(pool);
   a.hkv = desc->num_kv_heads;
   a.max_pages = pool->max_pages_per_seq;
   return hip_status(launch_append(a, batch, static_cast<hipStream_t>(stream)));
@@ -146,6 +162,7 @@ static oscar_status demote_common(const oscar_layer_desc* desc, const oscar_pool
   a.seq_slot = seq_slot;
   a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
   a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
+  a.rot_kv_stride = rot_stride(pool); a.clip_kv_stride = clip_stride(pool);
   a.hist = pool->hist;
   a.page_table = pool->page_table;
   a.max_pages = pool->max_pages_per_seq;
@@ -243,6 +260,7 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
   a.page_table = pool->page_table;
   a.rot_k = pool->rot_k;
   a.rot_v = pool->rot_v;
+  a.rot_kv_stride = rot_stride(pool);
   a.partials = static_cast<float*>(workspace);
   a.hkv = hkv;
   a.max_pages = pool->max_pages_per_seq;
@@ -260,6 +278,7 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
   m.partials = a.partials;
   m.seq_len = seq_len;
   m.rot = pool->rot_v;
+  m.rot_kv_stride = rot_stride(pool);
   m.out = out;
   m.hkv = hkv;
   m.group = c.group;

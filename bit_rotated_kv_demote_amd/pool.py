@@ -43,9 +43,17 @@ class TieredKV:
         self.rot_v = torch.as_tensor(np.asarray(rot_v, np.float32), **f32).contiguous()
         self.clip_k = torch.as_tensor(np.asarray(clip_k, np.float32), **f32).contiguous()
         self.clip_v = torch.as_tensor(np.asarray(clip_v, np.float32), **f32).contiguous()
+        # one R and tau per layer ([128, 128] / [128]) or per KV head ([Hkv, 128, 128] / [Hkv, 128])
+        self.per_kv_head = self.rot_k.dim() == 3
+        want_r = (num_kv_heads, HEAD_DIM, HEAD_DIM) if self.per_kv_head else (HEAD_DIM, HEAD_DIM)
+        want_t = want_r[:-1]
+        for t, want in ((self.rot_k, want_r), (self.rot_v, want_r), (self.clip_k, want_t), (self.clip_v, want_t)):
+            if tuple(t.shape) != want:
+                raise ValueError(f"rotation / clip shape {tuple(t.shape)}, expected {want}")
         self.desc = binding.layer_desc(num_q_heads, num_kv_heads)
         self.pool = binding.make_pool(self.sink_k, self.sink_v, self.recent_k, self.recent_v, self.hist,
-                                      self.page_table, self.rot_k, self.rot_v, self.clip_k, self.clip_v)
+                                      self.page_table, self.rot_k, self.rot_v, self.clip_k, self.clip_v,
+                                      self.per_kv_head)
         self._ws = None
 
     # -- hot path --------------------------------------------------------

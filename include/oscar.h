@@ -20,7 +20,9 @@
  *   OSCAR_ERR_UNSUPPORTED.  num_q_heads / num_kv_heads (the GQA group G) must
  *   be 1, 2, 4 or 8.
  * - Rotations act on row vectors: y = x . R, R stored row-major fp32
- *   [128][128]; the inverse rotation is y . R^T.
+ *   [128][128]; the inverse rotation is y . R^T.  A pool holds either one
+ *   R_K, R_V and clip-threshold pair per layer, shared by its KV heads, or
+ *   one per KV head (oscar_pool.rot_per_kv_head).
  * - "device" pointers are HIP device memory owned by the caller (for example
  *   torch tensors); "host" pointers are ordinary host memory.  The library
  *   never allocates, frees or retains any caller buffer.
@@ -74,7 +76,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 2
+#define OSCAR_ABI_VERSION 3
 
 typedef enum {
   OSCAR_OK = 0,
@@ -110,6 +112,12 @@ typedef struct {
   const float* rot_v;          /* device fp32 [128][128]: R_V                */
   const float* clip_k;         /* device fp32 [128]: per rotated channel     */
   const float* clip_v;         /*   clip thresholds, 0 < tau <= 65504        */
+  int32_t rot_per_kv_head;     /* 0: the four arrays above are the layer's,
+                                  shared by every KV head.  1: one per KV
+                                  head, rot_k/rot_v [Hkv][128][128] and
+                                  clip_k/clip_v [Hkv][128]; KV head j's
+                                  vectors (and its query heads' queries) are
+                                  rotated by its own pair.                   */
 } oscar_pool;
 
 /* Rotation that oscar_calibrate builds (oscar_calib_opts.rotation). */
@@ -130,6 +138,10 @@ typedef struct {
   int32_t hadamard_block;      /* 32 (one quantisation group) or 128         */
   float clip_percentile;       /* e.g. 99.0                                   */
   int32_t rotation;            /* OSCAR_ROT_*                                 */
+  int32_t per_kv_head;         /* 0: one R_K, R_V, tau per layer; 1: one per
+                                  KV head (outputs [Hkv][128][128] and
+                                  [Hkv][128]), each calibrated from that KV
+                                  head's G query heads, keys and values alone */
 } oscar_calib_opts;
 
 /* Source formats accepted by oscar_demote. */
@@ -162,13 +174,33 @@ const char* oscar_status_string(oscar_status s);
  * others are the baselines and the alternative key target above); the clip
  * thresholds are always the percentiles of the chosen rotation's outputs.
  * Out: rot_k, rot_v host fp32 [128][128]; clip_k, clip_v host fp32 [128].
+ * With opts->per_kv_head = 1 every KV head j is calibrated as a layer of its
+ * own (its query heads jG..jG+G-1, its keys and values), and the outputs are
+ * rot_k, rot_v [Hkv][128][128], clip_k, clip_v [Hkv][128].
  * Synchronous, CPU only, uses up to the machine's cores.  Errors:
- * OSCAR_ERR_INVALID (null pointer, n_tokens < 2, unknown rotation),
- * OSCAR_ERR_UNSUPPORTED, OSCAR_ERR_NUMERIC (non-finite input or tau > 65504).
+ * OSCAR_ERR_INVALID (null pointer, n_tokens < 2, unknown rotation or
+ * per_kv_head not 0/1), OSCAR_ERR_UNSUPPORTED, OSCAR_ERR_NUMERIC (non-finite
+ * input or tau > 65504).
  */
 oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opts* opts,
                              const float* q, const float* k, const float* v, int64_t n_tokens,
                              float* rot_k, float* rot_v, float* clip_k, float* clip_v);
+
+/*
+ * oscar_calibrate_layers -- one calibration shared by n_layers layers of the
+ * same shape ([zingnex] 离线优化的优势: layers may share their rotation
+ * parameters).  The key and value targets are the means of the layers' own
+ * targets (each layer's attention causal within its own n_tokens tokens);
+ * the clip thresholds are the percentiles over every layer's rotated keys
+ * (values).  In: q host fp32 [n_layers][n_tokens][Hq][128]; k, v host fp32
+ * [n_layers][n_tokens][Hkv][128].  Outputs, options and errors as for
+ * oscar_calibrate (n_layers < 1: OSCAR_ERR_INVALID); n_layers = 1 is
+ * oscar_calibrate.
+ */
+oscar_status oscar_calibrate_layers(const oscar_layer_desc* desc, const oscar_calib_opts* opts,
+                                    int32_t n_layers, const float* q, const float* k, const float* v,
+                                    int64_t n_tokens, float* rot_k, float* rot_v, float* clip_k,
+                                    float* clip_v);
 
 /*
  * oscar_append -- route one new token per sequence into the tiered pool

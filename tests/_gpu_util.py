@@ -31,7 +31,8 @@ def rel_l2(got, ref):
 class Layer:
     """Seeded synthetic layer: B sequences of up to max_len tokens (bf16 bits)."""
 
-    def __init__(self, seed, batch, hq, hkv, max_len, n_q=1, tau_tokens=4096, shuffle=True, extra_pages=0):
+    def __init__(self, seed, batch, hq, hkv, max_len, n_q=1, tau_tokens=4096, shuffle=True, extra_pages=0,
+                 per_kv_head=False):
         st = synth.streams(seed)
         self.batch, self.hq, self.hkv, self.max_len = batch, hq, hkv, max_len
         out = synth.outlier_channels(st["outliers"])
@@ -43,13 +44,23 @@ class Layer:
         samp_v = self.v[0, :min(tau_tokens, max_len)]
         self.tau_k = orc.clip_thresholds(synth.bf16_bits_to_f32(sample), self.rot)
         self.tau_v = orc.clip_thresholds(synth.bf16_bits_to_f32(samp_v), self.rot)
+        # the pool's rotations: the layer's one R for K and V, or (per_kv_head)
+        # a distinct R_K and R_V per KV head with each head's own tau
+        self.r_k = self.r_v = self.rot
+        if per_kv_head:
+            self.r_k = np.stack([synth.random_rotation(st["rot"]) for _ in range(hkv)])
+            self.r_v = np.stack([synth.random_rotation(st["rot"]) for _ in range(hkv)])
+            self.tau_k = np.stack([orc.clip_thresholds(synth.bf16_bits_to_f32(sample[:, j]), self.r_k[j])
+                                   for j in range(hkv)])
+            self.tau_v = np.stack([orc.clip_thresholds(synth.bf16_bits_to_f32(samp_v[:, j]), self.r_v[j])
+                                   for j in range(hkv)])
         self.max_pages = max(1, math.ceil(max(0, max_len - 320) / 16) + extra_pages)
         self.num_pages = batch * self.max_pages
         perm = synth.page_permutation(st["perm"], self.num_pages) if shuffle else np.arange(self.num_pages)
         self.page_table = perm.reshape(batch, self.max_pages).astype(np.int32)
 
     def device_pool(self, n_slots=None):
-        return TieredKV(self.hq, self.hkv, n_slots or self.batch, self.max_pages, self.num_pages, self.rot, self.rot,
+        return TieredKV(self.hq, self.hkv, n_slots or self.batch, self.max_pages, self.num_pages, self.r_k, self.r_v,
                         self.tau_k, self.tau_v, page_table=self.page_table)
 
     def oracle_pool(self, lengths, kv_heads=None):
@@ -66,7 +77,7 @@ class Layer:
             pool.recent_v[b][:, (pos - 64) % 256] = self.v[b, pos].transpose(1, 0, 2)
             if n > 320:
                 h = np.arange(n - 320)
-                pool.demote_many(b, h, self.k[b, 64 + h][:, heads], self.v[b, 64 + h][:, heads], self.rot, self.rot,
+                pool.demote_many(b, h, self.k[b, 64 + h][:, heads], self.v[b, 64 + h][:, heads], self.r_k, self.r_v,
                                  self.tau_k, self.tau_v, kv_heads=heads)
             pool.length[b] = n
         return pool

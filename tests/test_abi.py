@@ -97,13 +97,15 @@ def _calib_inputs(n=192, hq=4, hkv=2, seed=0):
     return q, k, v
 
 
-def _host_calibrate(q, k, v, hq, hkv, block=32, pct=99.0, rotation=0):
+def _host_calibrate(q, k, v, hq, hkv, block=32, pct=99.0, rotation=0, per_kv_head=False, layers=False):
     import torch
-    outs = [torch.zeros((128, 128), dtype=torch.float32), torch.zeros((128, 128), dtype=torch.float32),
-            torch.zeros(128, dtype=torch.float32), torch.zeros(128, dtype=torch.float32)]
-    binding.oscar_calibrate(binding.layer_desc(hq, hkv), torch.from_numpy(np.ascontiguousarray(q)),
-                            torch.from_numpy(np.ascontiguousarray(k)), torch.from_numpy(np.ascontiguousarray(v)),
-                            *outs, hadamard_block=block, clip_percentile=pct, rotation=rotation)
+    lead = (hkv,) if per_kv_head else ()
+    outs = [torch.zeros(lead + (128, 128), dtype=torch.float32), torch.zeros(lead + (128, 128), dtype=torch.float32),
+            torch.zeros(lead + (128,), dtype=torch.float32), torch.zeros(lead + (128,), dtype=torch.float32)]
+    fn = binding.oscar_calibrate_layers if layers else binding.oscar_calibrate
+    fn(binding.layer_desc(hq, hkv), torch.from_numpy(np.ascontiguousarray(q)),
+       torch.from_numpy(np.ascontiguousarray(k)), torch.from_numpy(np.ascontiguousarray(v)),
+       *outs, hadamard_block=block, clip_percentile=pct, rotation=rotation, per_kv_head=per_kv_head)
     return [o.numpy() for o in outs]
 
 
@@ -214,3 +216,89 @@ def test_multi_query_validation_and_workspace(lib):
     assert one == binding.oscar_decode_workspace_bytes(d, 2, 32768)
     assert binding.oscar_decode_multi_workspace_bytes(d, 2, 4, 32768) > one
     assert binding.oscar_decode_multi_workspace_bytes(d, 2, 0, 32768) == 0
+
+
+def _planted_q(n, hq, seed):
+    # distinct well-separated spectra per query-head pair, so that every
+    # eigenbasis is unique up to sign and the host and oracle R agree outright
+    rng = np.random.default_rng(seed)
+    q = np.zeros((n, hq, 128))
+    for h in range(0, hq, 2):
+        basis = np.linalg.qr(rng.standard_normal((128, 128)))[0]
+        z = rng.standard_normal((n, 2, 128))
+        q[:, h:h + 2] = (z * np.linspace(4.0, 0.5, 128)) @ basis.T
+    return q.astype(np.float32)
+
+
+def test_host_calibrate_per_kv_head_matches_oracle():
+    _, k, v = _calib_inputs(256, 4, 2, 7)
+    q = _planted_q(256, 4, 8)
+    r_k, r_v, t_k, t_v = _host_calibrate(q, k, v, 4, 2, per_kv_head=True)
+    o_rk, o_rv, o_tk, o_tv = orc.calibrate(q, k, v, per_kv_head=True)
+    assert r_k.shape == (2, 128, 128) and t_v.shape == (2, 128)
+    assert np.allclose(r_k, o_rk, atol=2e-4)
+    hp = orc.hadamard_block() @ orc.bitrev_permutation()
+    for j in range(2):
+        # value side: same target spectrum per head (eigenvectors unique up to degeneracy)
+        c_s = orc.score_covariance(q[:, 2 * j:2 * j + 2], k[:, j:j + 1], v[:, j:j + 1])
+        uv = r_v[j].astype(np.float64) @ hp.T
+        wv = np.sort(np.linalg.eigvalsh(c_s))[::-1]
+        assert np.allclose(np.diag(uv.T @ c_s @ uv), wv, rtol=1e-5, atol=1e-9), j
+        assert np.allclose(t_k[j], orc.clip_thresholds(k[:, j], r_k[j]), rtol=1e-5), j
+        assert np.allclose(t_v[j], orc.clip_thresholds(v[:, j], r_v[j]), rtol=1e-5), j
+
+
+def test_host_calibrate_layers_matches_oracle():
+    ks, vs, qs = [], [], []
+    for layer in range(3):
+        _, k, v = _calib_inputs(160, 4, 2, 20 + layer)
+        qs.append(_planted_q(160, 4, 30 + layer))
+        ks.append(k)
+        vs.append(v)
+    qs, ks, vs = np.stack(qs), np.stack(ks), np.stack(vs)
+    r_k, r_v, t_k, t_v = _host_calibrate(qs, ks, vs, 4, 2, layers=True)
+    o_rk, o_rv, o_tk, o_tv = orc.calibrate_layers(qs, ks, vs)
+    hp = orc.hadamard_block() @ orc.bitrev_permutation()
+    for r, c in ((r_k, np.mean([orc.query_covariance(qs[l]) for l in range(3)], axis=0)),
+                 (r_v, np.mean([orc.score_covariance(qs[l], ks[l], vs[l]) for l in range(3)], axis=0))):
+        u = r.astype(np.float64) @ hp.T
+        w = np.sort(np.linalg.eigvalsh(c))[::-1]
+        assert np.allclose(np.diag(u.T @ c @ u), w, rtol=1e-5, atol=1e-9)
+    assert np.allclose(t_k, o_tk, rtol=1e-5) and np.allclose(t_v, o_tv, rtol=1e-5)
+    assert np.allclose(t_k, orc.clip_thresholds(ks, r_k), rtol=1e-5)
+    # per KV head and shared across the layers at once
+    p_rk, _, p_tk, _ = _host_calibrate(qs, ks, vs, 4, 2, layers=True, per_kv_head=True)
+    op_rk, _, op_tk, _ = orc.calibrate_layers(qs, ks, vs, per_kv_head=True)
+    assert np.allclose(p_tk, op_tk, rtol=1e-5)
+    for j in range(2):
+        c = np.mean([orc.query_covariance(qs[l][:, 2 * j:2 * j + 2]) for l in range(3)], axis=0)
+        u = p_rk[j].astype(np.float64) @ hp.T
+        assert np.allclose(np.diag(u.T @ c @ u), np.sort(np.linalg.eigvalsh(c))[::-1], rtol=1e-5, atol=1e-9), j
+    # one layer through the layers entry point is oscar_calibrate
+    one = _host_calibrate(qs[0], ks[0], vs[0], 4, 2)
+    via = _host_calibrate(qs[:1], ks[:1], vs[:1], 4, 2, layers=True)
+    for a, b in zip(one, via):
+        assert np.array_equal(a, b)
+
+
+def test_calibration_scope_and_pool_flag_validation(lib):
+    import torch
+    d = binding.layer_desc(4, 2)
+    z = torch.zeros((2, 8, 4, 128), dtype=torch.float32)
+    zk = torch.zeros((2, 8, 2, 128), dtype=torch.float32)
+    out = [torch.zeros((2, 128, 128)), torch.zeros((2, 128, 128)), torch.zeros((2, 128)), torch.zeros((2, 128))]
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in out]
+    bad = binding.CalibOpts(32, 99.0, 0, 2)
+    assert lib.oscar_calibrate_layers(ctypes.byref(d), ctypes.byref(bad), 2, ctypes.c_void_p(z.data_ptr()),
+                                      ctypes.c_void_p(zk.data_ptr()), ctypes.c_void_p(zk.data_ptr()), 8,
+                                      *ptrs) == -1
+    ok = binding.CalibOpts(32, 99.0, 0, 1)
+    assert lib.oscar_calibrate_layers(ctypes.byref(d), ctypes.byref(ok), 0, ctypes.c_void_p(z.data_ptr()),
+                                      ctypes.c_void_p(zk.data_ptr()), ctypes.c_void_p(zk.data_ptr()), 8,
+                                      *ptrs) == -1
+    pool = _null_pool()
+    pool.rot_per_kv_head = 2
+    good = binding.layer_desc(32, 8)
+    assert lib.oscar_append(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 1, None) == -1
+    assert lib.oscar_decode(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 256, 1 << 30, 1, 100,
+                            None) == -1
