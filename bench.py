@@ -410,50 +410,103 @@ def run_multi_query(torch, steps, calib, seed=1007, hq=32, hkv=8, n=32768, n_poo
                         f"(causal among them), {n_pools} pools cycled", "by_query_tokens": res}
 
 
-def run_rotation_study(torch, seed=1006, hq=32, hkv=8, n_calib=1024, n_ctx=8192):
-    """Rotation variants on a layer with planted covariance structure (Qwen3-4B
-    attention shape): host calibration with each rotation on n_calib tokens,
-    device prefill of an n_ctx-token sequence (bulk demotion) and one device
-    decode; error = relative L2 of the output against fp64 attention over the
-    BF16 keys and values (the tiers' quantisation error only).  The exact
-    reference is plain attention, computed in NumPy here."""
-    from bit_rotated_kv_demote_amd import binding, synth
+def _planted_split(seed, n_calib, n_ctx, hq, hkv, per_head_bases=False, q_scale=1.0):
+    """Calibration tokens and a decode context drawn from one planted layer
+    (same covariance structure, disjoint tokens); q_scale sharpens attention."""
+    from bit_rotated_kv_demote_amd import synth
+    q, k, v = synth.planted_layer(np.random.default_rng(seed), n_calib + n_ctx, hq, hkv,
+                                  per_head_bases=per_head_bases)
+    q = (q * np.float32(q_scale)).astype(np.float32)
+    calib = (np.ascontiguousarray(q[:n_calib]), synth.bf16_bits_to_f32(k[:n_calib]),
+             synth.bf16_bits_to_f32(v[:n_calib]))
+    return calib, (q[n_calib:], np.ascontiguousarray(k[n_calib:]), np.ascontiguousarray(v[n_calib:]))
+
+
+def _decode_error(torch, ctx, hq, hkv, rots, seed, n_query=16):
+    """Device prefill of the context and a decode of its last n_query
+    positions (each query attending causally, every query head); relative L2
+    over all outputs against fp64 attention over the BF16 keys and values,
+    computed in NumPy here: the tiers' quantisation error only."""
+    from bit_rotated_kv_demote_amd import synth
     from bit_rotated_kv_demote_amd.pool import TieredKV, bf16_tensor
-    qc, kc, vc = synth.planted_layer(np.random.default_rng(seed), n_calib, hq, hkv)
-    qt, kt, vt = synth.planted_layer(np.random.default_rng(seed + 1), n_ctx, hq, hkv)
-    kc, vc = synth.bf16_bits_to_f32(kc), synth.bf16_bits_to_f32(vc)
-    q = np.ascontiguousarray(synth.to_bf16_bits(qt[-1:]))
+    qt, kt, vt = ctx
+    n_ctx = kt.shape[0]
+    q = np.ascontiguousarray(synth.to_bf16_bits(qt[-n_query:]))[None]          # [1, T, Hq, 128]
     qf = synth.bf16_bits_to_f32(q)[0].astype(np.float64)
     kf = synth.bf16_bits_to_f32(kt).astype(np.float64)
     vf = synth.bf16_bits_to_f32(vt).astype(np.float64)
     g = hq // hkv
-    exact = np.empty((hq, 128))
-    for h in range(hq):
-        lg = kf[:, h // g] @ qf[h] / math.sqrt(128.0)
-        w = np.exp(lg - lg.max())
-        exact[h] = (w / w.sum()) @ vf[:, h // g]
+    exact = np.empty((n_query, hq, 128))
+    for t in range(n_query):
+        p = n_ctx - n_query + t
+        for h in range(hq):
+            lg = kf[:p + 1, h // g] @ qf[t, h] / math.sqrt(128.0)
+            w = np.exp(lg - lg.max())
+            exact[t, h] = (w / w.sum()) @ vf[:p + 1, h // g]
     max_pages = math.ceil((n_ctx - 320) / 16)
-    pt = synth.page_permutation(np.random.default_rng(seed + 2), max_pages)[None, :].astype(np.int32)
+    pt = synth.page_permutation(np.random.default_rng(seed), max_pages)[None, :].astype(np.int32)
     lens = torch.tensor([n_ctx], dtype=torch.int32, device="cuda")
+    pool = TieredKV(hq, hkv, 1, max_pages, max_pages, *rots, page_table=pt)
+    pool.prefill(lens, bf16_tensor(kt[None]), bf16_tensor(vt[None]))
+    out = pool.decode_multi(bf16_tensor(q), lens, n_ctx).cpu().numpy()[0].astype(np.float64)
+    del pool
+    return round(float(np.linalg.norm(out - exact) / np.linalg.norm(exact)), 4)
+
+
+def _host_calibration(torch, hq, hkv, calibs, rotation, per_kv_head=False):
+    """oscar_calibrate (one layer) or oscar_calibrate_layers (several) on host tensors."""
+    from bit_rotated_kv_demote_amd import binding
+    lead = (hkv,) if per_kv_head else ()
+    outs = [torch.zeros(lead + (128, 128), dtype=torch.float32), torch.zeros(lead + (128, 128), dtype=torch.float32),
+            torch.zeros(lead + (128,), dtype=torch.float32), torch.zeros(lead + (128,), dtype=torch.float32)]
+    desc = binding.layer_desc(hq, hkv)
+    t0 = time.perf_counter()
+    if len(calibs) == 1:
+        q, k, v = (torch.from_numpy(x) for x in calibs[0])
+        binding.oscar_calibrate(desc, q, k, v, *outs, rotation=rotation, per_kv_head=per_kv_head)
+    else:
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(np.stack([c[i] for c in calibs]))) for i in range(3))
+        binding.oscar_calibrate_layers(desc, q, k, v, *outs, rotation=rotation, per_kv_head=per_kv_head)
+    return [o.numpy() for o in outs], round(time.perf_counter() - t0, 2)
+
+
+def run_rotation_study(torch, seed=1006, hq=32, hkv=8, n_calib=1024, n_ctx=8192, q_scale=1.0):
+    """Rotation variants on a layer with planted covariance structure (Qwen3-4B
+    attention shape): host calibration with each rotation on n_calib tokens
+    of the layer, device prefill of an n_ctx-token context of the same layer
+    (bulk demotion) and one device decode; error = relative L2 of the output
+    against fp64 attention over the BF16 keys and values.
+
+    Second part, the calibration's scope: a layer whose KV heads each have
+    their own planted bases, calibrated layer-wide, per KV head, and shared
+    with a second such layer (different bases), each decoded on the first
+    layer's context."""
+    from bit_rotated_kv_demote_amd import binding
+    calib, ctx = _planted_split(seed, n_calib, n_ctx, hq, hkv, q_scale=q_scale)
     errs, calib_s = {}, {}
     for name, code in (("spectral", binding.ROT_SPECTRAL), ("key_attn", binding.ROT_KEY_ATTN),
                        ("hadamard", binding.ROT_HADAMARD), ("identity", binding.ROT_IDENTITY)):
-        outs = [torch.zeros((128, 128), dtype=torch.float32), torch.zeros((128, 128), dtype=torch.float32),
-                torch.zeros(128, dtype=torch.float32), torch.zeros(128, dtype=torch.float32)]
-        t0 = time.perf_counter()
-        binding.oscar_calibrate(binding.layer_desc(hq, hkv), torch.from_numpy(qc), torch.from_numpy(kc),
-                                torch.from_numpy(vc), *outs, rotation=code)
-        calib_s[name] = round(time.perf_counter() - t0, 2)
-        r_k, r_v, t_k, t_v = [o.numpy() for o in outs]
-        pool = TieredKV(hq, hkv, 1, max_pages, max_pages, r_k, r_v, t_k, t_v, page_table=pt)
-        pool.prefill(lens, bf16_tensor(kt[None]), bf16_tensor(vt[None]))
-        out = pool.decode(bf16_tensor(q), lens, n_ctx).cpu().numpy()[0].astype(np.float64)
-        errs[name] = round(float(np.linalg.norm(out - exact) / np.linalg.norm(exact)), 4)
-        del pool
+        rots, calib_s[name] = _host_calibration(torch, hq, hkv, [calib], code)
+        errs[name] = _decode_error(torch, ctx, hq, hkv, rots, seed + 2)
+    calib_a, ctx_a = _planted_split(seed + 10, n_calib, n_ctx, hq, hkv, per_head_bases=True, q_scale=q_scale)
+    calib_b, _ = _planted_split(seed + 11, n_calib, 1, hq, hkv, per_head_bases=True, q_scale=q_scale)
+    scope_errs, scope_s = {}, {}
+    for name, calibs, per_head in (("layer", [calib_a], False), ("per_kv_head", [calib_a], True),
+                                   ("shared_with_other_layer", [calib_a, calib_b], False),
+                                   ("shared_with_other_layer_per_kv_head", [calib_a, calib_b], True)):
+        rots, scope_s[name] = _host_calibration(torch, hq, hkv, calibs, binding.ROT_SPECTRAL, per_head)
+        scope_errs[name] = _decode_error(torch, ctx_a, hq, hkv, rots, seed + 12)
+    rots, _ = _host_calibration(torch, hq, hkv, [calib_a], binding.ROT_IDENTITY)
+    scope_errs["identity"] = _decode_error(torch, ctx_a, hq, hkv, rots, seed + 12)
     torch.cuda.empty_cache()
     return {"workload": f"planted covariance layer, {hq} q / {hkv} KV heads, calibration {n_calib} tokens, "
-                        f"context {n_ctx} tokens (64 sink / {n_ctx - 320} INT2 / 256 recent), one decode query per head",
-            "rel_l2_vs_bf16_attention": errs, "calibrate_host_s": calib_s}
+                        f"context {n_ctx} further tokens of the same layer (64 sink / {n_ctx - 320} INT2 / 256 recent), "
+                        "16 decode queries per head",
+            "error": "relative L2 over the decode of the context's last 16 positions (causal), all query heads",
+            "rel_l2_vs_bf16_attention": errs, "calibrate_host_s": calib_s,
+            "scope": {"workload": "spectral rotation on a layer whose KV heads have distinct planted bases; "
+                                  "'shared' calibrates over it and a second such layer",
+                      "rel_l2_vs_bf16_attention": scope_errs, "calibrate_host_s": scope_s}}
 
 
 def run_demote(torch, reps, seed):

@@ -115,7 +115,7 @@ CONFIGS = {
 
 
 def planted_layer(rng: np.random.Generator, n: int, hq: int, hkv: int, n_query_dirs: int = 16,
-                  key_side_scale: float = 8.0, n_key_side_dirs: int = 8):
+                  key_side_scale: float = 8.0, n_key_side_dirs: int = 8, per_head_bases: bool = False):
     """A layer with planted covariance structure, for comparing rotations.
 
     One seeded orthonormal basis B: queries have energy 1 in its first
@@ -123,22 +123,34 @@ def planted_layer(rng: np.random.Generator, n: int, hq: int, hkv: int, n_query_d
     deviation ``key_side_scale`` in the next ``n_key_side_dirs`` directions
     (energy the queries never look at) and 1 elsewhere; values have standard
     deviation 3 in the first 8 directions of a second basis and 1 elsewhere.
-    Four seeded raw channels of K are scaled by 6 and two of V by 4.
+    With ``per_head_bases`` every KV head has its own pair of bases (its
+    query heads use its B).  Four seeded raw channels of K are scaled by 6
+    and two of V by 4.  The structure is drawn first, then the n tokens:
+    calibration and context tokens of one layer come from one call, split.
     Returns q as float32 [n, hq, 128] (bf16-representable) and K, V as bf16
     bits [n, hkv, 128].  Random draws and casts only.
     """
     d = HEAD_DIM
     b_qk = random_rotation(rng, d).astype(np.float64)
     b_v = random_rotation(rng, d).astype(np.float64)
+    g = hq // hkv
+    bq = [b_qk] * hkv
+    bv = [b_v] * hkv
+    if per_head_bases:
+        bq = [random_rotation(rng, d).astype(np.float64) for _ in range(hkv)]
+        bv = [random_rotation(rng, d).astype(np.float64) for _ in range(hkv)]
     sq = np.full(d, 0.05)
     sq[:n_query_dirs] = 1.0
     sk = np.ones(d)
     sk[n_query_dirs:n_query_dirs + n_key_side_dirs] = key_side_scale
     sv = np.ones(d)
     sv[:8] = 3.0
-    q = (rng.standard_normal((n, hq, d)) * sq) @ b_qk.T
-    k = (rng.standard_normal((n, hkv, d)) * sk) @ b_qk.T
-    v = (rng.standard_normal((n, hkv, d)) * sv) @ b_v.T
+    zq = rng.standard_normal((n, hq, d)) * sq
+    zk = rng.standard_normal((n, hkv, d)) * sk
+    zv = rng.standard_normal((n, hkv, d)) * sv
+    q = np.stack([zq[:, h] @ bq[h // g].T for h in range(hq)], axis=1)
+    k = np.stack([zk[:, j] @ bq[j].T for j in range(hkv)], axis=1)
+    v = np.stack([zv[:, j] @ bv[j].T for j in range(hkv)], axis=1)
     oc = np.sort(rng.choice(d, 4, replace=False))
     k[..., oc] *= 6.0
     v[..., oc[:2]] *= 4.0

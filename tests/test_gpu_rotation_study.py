@@ -34,9 +34,11 @@ ROTATIONS = {"spectral": binding.ROT_SPECTRAL, "key_attn": binding.ROT_KEY_ATTN,
 
 
 def _layer():
-    rng = np.random.default_rng(2024)
-    qc, kc, vc = synth.planted_layer(rng, N_CALIB, HQ, HKV)
-    qt, kt, vt = synth.planted_layer(np.random.default_rng(2025), N_CTX, HQ, HKV)
+    # calibration tokens and the decode context come from one planted layer
+    # (same structure, disjoint tokens)
+    q, k, v = synth.planted_layer(np.random.default_rng(2024), N_CALIB + N_CTX, HQ, HKV)
+    qc, kc, vc = np.ascontiguousarray(q[:N_CALIB]), k[:N_CALIB], v[:N_CALIB]
+    qt, kt, vt = q[N_CALIB:], np.ascontiguousarray(k[N_CALIB:]), np.ascontiguousarray(v[N_CALIB:])
     return qc, synth.bf16_bits_to_f32(kc), synth.bf16_bits_to_f32(vc), qt, kt, vt
 
 
