@@ -67,6 +67,11 @@ R12 Scope of a calibration ([zingnex] 离线优化的优势: layers may share th
     G query heads and its own keys and values, giving R and tau per KV head
     ([Hkv, 128, 128] and [Hkv, 128]); every vector of that KV head is
     rotated, clipped and inverse-rotated with its own pair.
+R13 INT4 variant of the pool ([gist] 4 runs an INT4 baseline): the same
+    quantiser with 16 levels, scale = fp16 rounded toward +inf of
+    fp32((max - z) / 15), code = clamp(rint_even(...), 0, 15), two codes per
+    byte; the history block of one (page, KV head) is 2560 bytes (1024 of K
+    codes, 1024 of V codes, the same 512 bytes of scale/zero metadata).
 """
 from __future__ import annotations
 
@@ -79,7 +84,17 @@ N_GROUPS = HEAD_DIM // GROUP
 PAGE = 16
 N_SINK = 64
 N_RECENT = 256
-BLOCK_BYTES = 1536
+BLOCK_BYTES = 1536                 # INT2 history block (reading R7)
+BLOCK_BYTES_INT4 = 2560            # INT4 history block (reading R13)
+
+
+def block_bytes(bits: int = 2) -> int:
+    return {2: BLOCK_BYTES, 4: BLOCK_BYTES_INT4}[bits]
+
+
+def levels(bits: int = 2) -> int:
+    """Largest code: 3 for INT2 (four levels, [yunpan] 二), 15 for INT4."""
+    return (1 << bits) - 1
 MAX_TAU = 65504.0
 
 
@@ -301,8 +316,9 @@ def clip(y: np.ndarray, tau: np.ndarray) -> np.ndarray:
     return np.fmin(np.fmax(y, -t), t)
 
 
-def group_params(yc: np.ndarray):
-    """Per 32-channel group: (scale, zero) as float16, reading R6.
+def group_params(yc: np.ndarray, bits: int = 2):
+    """Per 32-channel group: (scale, zero) as float16, reading R6 (R13 for
+    bits = 4: the span is divided by 15 instead of 3).
 
     yc: float32 [..., 128] -> scale, zero: float16 [..., 4].
     """
@@ -311,19 +327,20 @@ def group_params(yc: np.ndarray):
     mx = g.max(axis=-1)
     zero = f16_round_down(mn)
     span = (mx - zero.astype(np.float32)).astype(np.float32)
-    scale = f16_round_up((span / np.float32(3.0)).astype(np.float32))
+    scale = f16_round_up((span / np.float32(levels(bits))).astype(np.float32))
     return scale, zero
 
 
-def quant_codes(yc: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.ndarray:
-    """INT2 codes (4 levels; [yunpan] 二) for clipped rotated values, R6."""
+def quant_codes(yc: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int = 2) -> np.ndarray:
+    """INT2 codes (4 levels; [yunpan] 二) for clipped rotated values, R6; INT4
+    codes (16 levels) for bits = 4, R13."""
     g = np.asarray(yc, np.float32).reshape(yc.shape[:-1] + (N_GROUPS, GROUP))
     s = scale.astype(np.float32)[..., None]
     z = zero.astype(np.float32)[..., None]
     diff = (g - z).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         quot = np.where(s > 0, diff / np.where(s > 0, s, np.float32(1)), np.float32(0))
-    c = np.clip(np.rint(quot.astype(np.float32)), 0, 3).astype(np.uint8)
+    c = np.clip(np.rint(quot.astype(np.float32)), 0, levels(bits)).astype(np.uint8)
     return c.reshape(yc.shape)
 
 
@@ -334,11 +351,11 @@ def dequantize(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.nda
     return out.reshape(codes.shape)
 
 
-def quantize_rotated(y: np.ndarray, tau: np.ndarray):
+def quantize_rotated(y: np.ndarray, tau: np.ndarray, bits: int = 2):
     """Clip + quantise already-rotated fp32 vectors: returns codes, scale, zero."""
     yc = clip(y, tau)
-    scale, zero = group_params(yc)
-    return quant_codes(yc, scale, zero), scale, zero
+    scale, zero = group_params(yc, bits)
+    return quant_codes(yc, scale, zero, bits), scale, zero
 
 
 # ---------------------------------------------------------------------------
@@ -354,10 +371,26 @@ def quantize_rotated(y: np.ndarray, tau: np.ndarray):
 #   [1408, 1536)  V zeros   fp16, same index
 # Codes are 2-bit fields of little-endian 32-bit words; field f occupies
 # bits 2f, 2f+1 of its word.
+#
+# INT4 block (reading R13), 2560 bytes:
+#   [   0, 1024)  K codes: 64 chunks of 16 bytes; chunk 16*a + t holds token
+#                 t's channels j with (j >> 3) & 3 == a, word j >> 5 (one
+#                 group per word), nibble at bit 16*(j & 1) + 4*((j >> 1) & 3)
+#   [1024, 2048)  V codes: chunk 16*a + b holds tokens 4a..4a+3, channels j
+#                 with j & 15 == b; word 2*((j >> 4) >> 2) + ((t & 3) >> 1),
+#                 nibble at bit 16*(t & 1) + 4*((j >> 4) & 3)
+#   [2048, 2560)  scales and zeros, laid out as the INT2 block's [1024, 1536)
 # ---------------------------------------------------------------------------
 
-def k_code_bitpos(t: int, j: int) -> int:
+def meta_base(bits: int = 2) -> int:
+    return {2: 1024, 4: 2048}[bits]
+
+
+def k_code_bitpos(t: int, j: int, bits: int = 2) -> int:
     """Absolute bit index (byte*8 + bit) of K code (token t, channel j)."""
+    if bits == 4:
+        byte = 16 * (16 * ((j >> 3) & 3) + t) + 4 * (j >> 5)
+        return byte * 8 + 16 * (j & 1) + 4 * ((j >> 1) & 3)
     a = (j >> 3) & 3                 # which quarter of the group
     word = j >> 6                    # groups {0,1} -> word 0, {2,3} -> word 1
     field = 4 * ((j >> 5) & 1) + ((j >> 1) & 3) + 8 * (j & 1)
@@ -365,8 +398,12 @@ def k_code_bitpos(t: int, j: int) -> int:
     return byte * 8 + 2 * field
 
 
-def v_code_bitpos(t: int, j: int) -> int:
+def v_code_bitpos(t: int, j: int, bits: int = 2) -> int:
     """Absolute bit index of V code (token t, channel j)."""
+    if bits == 4:
+        m = j >> 4
+        byte = 1024 + 16 * (16 * (t >> 2) + (j & 15)) + 4 * (2 * (m >> 2) + ((t & 3) >> 1))
+        return byte * 8 + 16 * (t & 1) + 4 * (m & 3)
     x = j & 15
     blk = j >> 4
     tq, u = t >> 2, t & 3
@@ -376,30 +413,31 @@ def v_code_bitpos(t: int, j: int) -> int:
     return byte * 8 + 2 * field
 
 
-def k_scale_offset(t: int, g: int) -> int:
-    return 1024 + 8 * t + 2 * g
+def k_scale_offset(t: int, g: int, bits: int = 2) -> int:
+    return meta_base(bits) + 8 * t + 2 * g
 
 
-def k_zero_offset(t: int, g: int) -> int:
-    return 1152 + 8 * t + 2 * g
+def k_zero_offset(t: int, g: int, bits: int = 2) -> int:
+    return meta_base(bits) + 128 + 8 * t + 2 * g
 
 
-def v_scale_offset(t: int, g: int) -> int:
-    return 1280 + 32 * (t >> 2) + 8 * g + 2 * (t & 3)
+def v_scale_offset(t: int, g: int, bits: int = 2) -> int:
+    return meta_base(bits) + 256 + 32 * (t >> 2) + 8 * g + 2 * (t & 3)
 
 
-def v_zero_offset(t: int, g: int) -> int:
-    return 1408 + 32 * (t >> 2) + 8 * g + 2 * (t & 3)
+def v_zero_offset(t: int, g: int, bits: int = 2) -> int:
+    return meta_base(bits) + 384 + 32 * (t >> 2) + 8 * g + 2 * (t & 3)
 
 
-def _put_code(block: np.ndarray, bitpos: int, c: int) -> None:
+def _put_code(block: np.ndarray, bitpos: int, c: int, bits: int = 2) -> None:
     byte, bit = divmod(bitpos, 8)
-    block[byte] = (int(block[byte]) & ~(3 << bit) | ((int(c) & 3) << bit)) & 0xFF
+    mask = levels(bits)
+    block[byte] = (int(block[byte]) & ~(mask << bit) | ((int(c) & mask) << bit)) & 0xFF
 
 
-def _get_code(block: np.ndarray, bitpos: int) -> int:
+def _get_code(block: np.ndarray, bitpos: int, bits: int = 2) -> int:
     byte, bit = divmod(bitpos, 8)
-    return (int(block[byte]) >> bit) & 3
+    return (int(block[byte]) >> bit) & levels(bits)
 
 
 def _put_f16(block: np.ndarray, off: int, val) -> None:
@@ -412,26 +450,26 @@ def _get_f16(block: np.ndarray, off: int) -> np.float16:
     return block[off:off + 2].copy().view(np.float16)[0]
 
 
-def write_token(block: np.ndarray, slot: int, kc, ks, kz, vc, vs, vz) -> None:
+def write_token(block: np.ndarray, slot: int, kc, ks, kz, vc, vs, vz, bits: int = 2) -> None:
     """Store one token's K and V codes [128] and scale/zero [4] into a block."""
     for j in range(HEAD_DIM):
-        _put_code(block, k_code_bitpos(slot, j), kc[j])
-        _put_code(block, v_code_bitpos(slot, j), vc[j])
+        _put_code(block, k_code_bitpos(slot, j, bits), kc[j], bits)
+        _put_code(block, v_code_bitpos(slot, j, bits), vc[j], bits)
     for g in range(N_GROUPS):
-        _put_f16(block, k_scale_offset(slot, g), ks[g])
-        _put_f16(block, k_zero_offset(slot, g), kz[g])
-        _put_f16(block, v_scale_offset(slot, g), vs[g])
-        _put_f16(block, v_zero_offset(slot, g), vz[g])
+        _put_f16(block, k_scale_offset(slot, g, bits), ks[g])
+        _put_f16(block, k_zero_offset(slot, g, bits), kz[g])
+        _put_f16(block, v_scale_offset(slot, g, bits), vs[g])
+        _put_f16(block, v_zero_offset(slot, g, bits), vz[g])
 
 
-def read_token(block: np.ndarray, slot: int):
+def read_token(block: np.ndarray, slot: int, bits: int = 2):
     """Inverse of write_token: (kc, ks, kz, vc, vs, vz)."""
-    kc = np.array([_get_code(block, k_code_bitpos(slot, j)) for j in range(HEAD_DIM)], np.uint8)
-    vc = np.array([_get_code(block, v_code_bitpos(slot, j)) for j in range(HEAD_DIM)], np.uint8)
-    ks = np.array([_get_f16(block, k_scale_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
-    kz = np.array([_get_f16(block, k_zero_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
-    vs = np.array([_get_f16(block, v_scale_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
-    vz = np.array([_get_f16(block, v_zero_offset(slot, g)) for g in range(N_GROUPS)], np.float16)
+    kc = np.array([_get_code(block, k_code_bitpos(slot, j, bits), bits) for j in range(HEAD_DIM)], np.uint8)
+    vc = np.array([_get_code(block, v_code_bitpos(slot, j, bits), bits) for j in range(HEAD_DIM)], np.uint8)
+    ks = np.array([_get_f16(block, k_scale_offset(slot, g, bits)) for g in range(N_GROUPS)], np.float16)
+    kz = np.array([_get_f16(block, k_zero_offset(slot, g, bits)) for g in range(N_GROUPS)], np.float16)
+    vs = np.array([_get_f16(block, v_scale_offset(slot, g, bits)) for g in range(N_GROUPS)], np.float16)
+    vz = np.array([_get_f16(block, v_zero_offset(slot, g, bits)) for g in range(N_GROUPS)], np.float16)
     return kc, ks, kz, vc, vs, vz
 
 
@@ -456,16 +494,18 @@ class Pool:
     """Tiered KV pool state, byte-for-byte in the library's formats.
 
     sink_k/v, recent_k/v: uint16 bf16 bits [S, Hkv, 64|256, 128]
-    hist: uint8 [num_pages, Hkv, 1536]; page_table: int32 [S, max_pages]
+    hist: uint8 [num_pages, Hkv, 1536] (INT2; 2560 for INT4, bits = 4);
+    page_table: int32 [S, max_pages]
     """
 
-    def __init__(self, n_slots, n_kv_heads, num_pages, page_table):
+    def __init__(self, n_slots, n_kv_heads, num_pages, page_table, bits: int = 2):
         self.hkv = n_kv_heads
+        self.bits = bits
         self.sink_k = np.zeros((n_slots, n_kv_heads, N_SINK, HEAD_DIM), np.uint16)
         self.sink_v = np.zeros_like(self.sink_k)
         self.recent_k = np.zeros((n_slots, n_kv_heads, N_RECENT, HEAD_DIM), np.uint16)
         self.recent_v = np.zeros_like(self.recent_k)
-        self.hist = np.zeros((num_pages, n_kv_heads, BLOCK_BYTES), np.uint8)
+        self.hist = np.zeros((num_pages, n_kv_heads, block_bytes(bits)), np.uint8)
         self.page_table = np.asarray(page_table, np.int32)
         self.length = np.zeros(n_slots, np.int64)
 
@@ -473,10 +513,10 @@ class Pool:
         """Quantise already-rotated fp32 K/V [Hkv, 128] into history index h."""
         page = int(self.page_table[slot, h_index // PAGE])
         ps = h_index % PAGE
-        kc, ks, kz = quantize_rotated(yk, tau_k)
-        vc, vs, vz = quantize_rotated(yv, tau_v)
+        kc, ks, kz = quantize_rotated(yk, tau_k, self.bits)
+        vc, vs, vz = quantize_rotated(yv, tau_v, self.bits)
         for hd in range(self.hkv):
-            write_token(self.hist[page, hd], ps, kc[hd], ks[hd], kz[hd], vc[hd], vs[hd], vz[hd])
+            write_token(self.hist[page, hd], ps, kc[hd], ks[hd], kz[hd], vc[hd], vs[hd], vz[hd], self.bits)
 
     def demote(self, slot, h_index, k_bits, v_bits, r_k, r_v, tau_k, tau_v) -> None:
         """Rotate bf16 K/V [Hkv, 128] by R and demote them ([yunpan] 三.2)."""
@@ -509,10 +549,11 @@ class Pool:
         heads = list(range(self.hkv)) if kv_heads is None else list(kv_heads)
         h = np.asarray(h_indices, np.int64)
         pages = self.page_table[slot, h // PAGE]
-        kc, ks, kz = quantize_rotated(yk, heads_of(tau_k, heads, 2))
-        vc, vs, vz = quantize_rotated(yv, heads_of(tau_v, heads, 2))
+        kc, ks, kz = quantize_rotated(yk, heads_of(tau_k, heads, 2), self.bits)
+        vc, vs, vz = quantize_rotated(yv, heads_of(tau_v, heads, 2), self.bits)
         for i, hd in enumerate(heads):
-            write_tokens(self.hist, hd, pages, h % PAGE, kc[:, i], ks[:, i], kz[:, i], vc[:, i], vs[:, i], vz[:, i])
+            write_tokens(self.hist, hd, pages, h % PAGE, kc[:, i], ks[:, i], kz[:, i], vc[:, i], vs[:, i], vz[:, i],
+                         self.bits)
 
     def demote_many(self, slot, h_indices, k_bits, v_bits, r_k, r_v, tau_k, tau_v, kv_heads=None):
         """Rotate (fp64 product rounded to fp32) and demote many bf16 tokens [N, H, 128]."""
@@ -524,7 +565,8 @@ class Pool:
     @classmethod
     def from_state(cls, state, n_kv_heads):
         """Oracle pool holding given bytes (e.g. copied back from a device)."""
-        pool = cls(state["sink_k"].shape[0], n_kv_heads, state["hist"].shape[0], state["page_table"])
+        bits = {BLOCK_BYTES: 2, BLOCK_BYTES_INT4: 4}[state["hist"].shape[-1]]
+        pool = cls(state["sink_k"].shape[0], n_kv_heads, state["hist"].shape[0], state["page_table"], bits)
         for name in ("sink_k", "sink_v", "recent_k", "recent_v", "hist"):
             setattr(pool, name, np.array(state[name], copy=True))
         return pool
@@ -549,7 +591,7 @@ class Pool:
             h = pos[hist] - N_SINK
             pages = self.page_table[slot, h // PAGE]
             blocks = self.hist[pages][:, heads]                        # [n_hist, H, 1536]
-            kc, ks, kz, vc, vs, vz = unpack_tokens(blocks, h % PAGE)   # [n_hist, Hkv, ...]
+            kc, ks, kz, vc, vs, vz = unpack_tokens(blocks, h % PAGE, self.bits)   # [n_hist, Hkv, ...]
             kt[:, hist] = np.moveaxis(rotate_back(dequantize(kc, ks, kz), heads_of(r_k, heads, 3)), 1, 0)
             vt[:, hist] = np.moveaxis(rotate_back(dequantize(vc, vs, vz), heads_of(r_v, heads, 3)), 1, 0)
         return kt, vt
@@ -565,46 +607,48 @@ def rotate_back(y: np.ndarray, r: np.ndarray) -> np.ndarray:
     return np.matmul(y[..., None, :], np.swapaxes(r, -1, -2))[..., 0, :]
 
 
-_BIT_TABLES = None
+_BIT_TABLES = {}
 
 
-def _bit_tables():
+def _bit_tables(bits: int = 2):
     """(byte, bit) of every K and V code of a block, from the *_bitpos definitions."""
-    global _BIT_TABLES
-    if _BIT_TABLES is None:
-        kb = np.array([[k_code_bitpos(t, j) for j in range(HEAD_DIM)] for t in range(PAGE)])
-        vb = np.array([[v_code_bitpos(t, j) for j in range(HEAD_DIM)] for t in range(PAGE)])
-        ks = np.array([[k_scale_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
-        kz = np.array([[k_zero_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
-        vs = np.array([[v_scale_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
-        vz = np.array([[v_zero_offset(t, g) for g in range(N_GROUPS)] for t in range(PAGE)])
-        _BIT_TABLES = (kb // 8, kb % 8, vb // 8, vb % 8, ks, kz, vs, vz)
-    return _BIT_TABLES
+    if bits not in _BIT_TABLES:
+        kb = np.array([[k_code_bitpos(t, j, bits) for j in range(HEAD_DIM)] for t in range(PAGE)])
+        vb = np.array([[v_code_bitpos(t, j, bits) for j in range(HEAD_DIM)] for t in range(PAGE)])
+        ks = np.array([[k_scale_offset(t, g, bits) for g in range(N_GROUPS)] for t in range(PAGE)])
+        kz = np.array([[k_zero_offset(t, g, bits) for g in range(N_GROUPS)] for t in range(PAGE)])
+        vs = np.array([[v_scale_offset(t, g, bits) for g in range(N_GROUPS)] for t in range(PAGE)])
+        vz = np.array([[v_zero_offset(t, g, bits) for g in range(N_GROUPS)] for t in range(PAGE)])
+        _BIT_TABLES[bits] = (kb // 8, kb % 8, vb // 8, vb % 8, ks, kz, vs, vz)
+    return _BIT_TABLES[bits]
 
 
-def write_tokens(hist, head, pages, slots, kc, ks, kz, vc, vs, vz):
-    """Vectorised write_token into a pool hist array uint8 [num_pages, Hkv, 1536]:
+def write_tokens(hist, head, pages, slots, kc, ks, kz, vc, vs, vz, bits: int = 2):
+    """Vectorised write_token into a pool hist array uint8 [num_pages, Hkv, block]:
     token i goes to block (pages[i], head), slot slots[i]."""
-    kby, kbi, vby, vbi, kso, kzo, vso, vzo = _bit_tables()
+    kby, kbi, vby, vbi, kso, kzo, vso, vzo = _bit_tables(bits)
     flat = hist.reshape(-1)
     assert np.shares_memory(flat, hist), "hist must be contiguous"
-    base = ((np.asarray(pages, np.int64) * hist.shape[1] + head) * BLOCK_BYTES)[:, None]
+    assert hist.shape[-1] == block_bytes(bits)
+    mask = np.uint8(levels(bits))
+    base = ((np.asarray(pages, np.int64) * hist.shape[1] + head) * block_bytes(bits))[:, None]
     t = np.asarray(slots, np.int64)
     for byt, bit, codes in ((kby, kbi, kc), (vby, vbi, vc)):
         idx = (base + byt[t]).ravel()
         sh = bit[t].ravel().astype(np.uint8)
-        np.bitwise_and.at(flat, idx, (~(np.uint8(3) << sh)).astype(np.uint8))
-        np.bitwise_or.at(flat, idx, ((np.asarray(codes, np.uint8).ravel() & 3) << sh).astype(np.uint8))
+        np.bitwise_and.at(flat, idx, (~(mask << sh)).astype(np.uint8))
+        np.bitwise_or.at(flat, idx, ((np.asarray(codes, np.uint8).ravel() & mask) << sh).astype(np.uint8))
     for off, vals in ((kso, ks), (kzo, kz), (vso, vs), (vzo, vz)):
         b = np.asarray(vals, np.float16).view(np.uint16)
         idx = base + off[t]
         flat[idx] = (b & 0xFF).astype(np.uint8)
         flat[idx + 1] = (b >> 8).astype(np.uint8)
 
-def unpack_tokens(blocks: np.ndarray, slots: np.ndarray):
+def unpack_tokens(blocks: np.ndarray, slots: np.ndarray, bits: int = 2):
     """Codes and scale/zero of token slot slots[i] of blocks[i, ...] (vectorised
-    read_token).  blocks: uint8 [N, ..., 1536]; slots: [N]."""
-    kby, kbi, vby, vbi, kso, kzo, vso, vzo = _bit_tables()
+    read_token).  blocks: uint8 [N, ..., block bytes]; slots: [N]."""
+    kby, kbi, vby, vbi, kso, kzo, vso, vzo = _bit_tables(bits)
+    mask = levels(bits)
     b = np.asarray(blocks)
     idx = np.asarray(slots)
     extra = (1,) * (b.ndim - 2)
@@ -620,8 +664,8 @@ def unpack_tokens(blocks: np.ndarray, slots: np.ndarray):
 
     sh_k = kbi[idx].reshape((len(idx),) + extra + (HEAD_DIM,))
     sh_v = vbi[idx].reshape((len(idx),) + extra + (HEAD_DIM,))
-    kc = ((gather(kby) >> sh_k) & 3).astype(np.uint8)
-    vc = ((gather(vby) >> sh_v) & 3).astype(np.uint8)
+    kc = ((gather(kby) >> sh_k) & mask).astype(np.uint8)
+    vc = ((gather(vby) >> sh_v) & mask).astype(np.uint8)
     return kc, f16(kso), f16(kzo), vc, f16(vso), f16(vzo)
 
 

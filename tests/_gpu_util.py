@@ -96,9 +96,11 @@ def upload(dev: TieredKV, opool: orc.Pool, kv_heads=None):
 
 
 def code_diff_stats(hist_a, hist_b, pages, slots):
-    """Compare codes of given (page, slot) tokens of two hist arrays [P, Hkv, 1536]."""
-    ua = orc.unpack_tokens(hist_a[pages], slots)
-    ub = orc.unpack_tokens(hist_b[pages], slots)
+    """Compare codes of given (page, slot) tokens of two hist arrays [P, Hkv, block]
+    (INT2 or INT4 blocks, told apart by their size)."""
+    bits = 4 if hist_a.shape[-1] == orc.BLOCK_BYTES_INT4 else 2
+    ua = orc.unpack_tokens(hist_a[pages], slots, bits)
+    ub = orc.unpack_tokens(hist_b[pages], slots, bits)
     kd = ua[0].astype(int) - ub[0].astype(int)
     vd = ua[3].astype(int) - ub[3].astype(int)
     diffs = np.concatenate([kd.ravel(), vd.ravel()])

@@ -757,3 +757,146 @@ def test_per_kv_head_pool_equals_independent_single_head_pools():
                     np.stack([t_v[0]] * hkv))
         shared.append(0, k[p], v[p], r_k[0], r_v[0], t_k[0], t_v[0])
     assert np.array_equal(same.hist, shared.hist)
+
+
+# ---------------------------------------------------------------------------
+# INT4 variant of the pool (reading R13)
+# ---------------------------------------------------------------------------
+
+def test_int4_quant_hand_worked_groups():
+    g = _gold("int4_format.json")
+    y = np.array([np.float32(s) for s in g["y"]], np.float32)
+    c, s, z = orc.quantize_rotated(y[None], np.full(128, 65504, np.float32), bits=4)
+    assert [float(v) for v in s[0]] == [float(x) for x in g["scale"]]
+    assert [float(v) for v in z[0]] == [float(x) for x in g["zero"]]
+    assert c[0].tolist() == g["codes"]
+
+
+def test_int4_layout_fixture_points_and_bijection():
+    g = _gold("int4_format.json")
+    for t, j, b in g["k_code"]:
+        assert orc.k_code_bitpos(t, j, 4) == b, (t, j)
+    for t, j, b in g["v_code"]:
+        assert orc.v_code_bitpos(t, j, 4) == b, (t, j)
+    for t, gg, o in g["k_scale"]:
+        assert orc.k_scale_offset(t, gg, 4) == o
+    for t, gg, o in g["v_scale"]:
+        assert orc.v_scale_offset(t, gg, 4) == o
+    for t, gg, o in g["v_zero"]:
+        assert orc.v_zero_offset(t, gg, 4) == o
+    kb = {orc.k_code_bitpos(t, j, 4) for t in range(16) for j in range(128)}
+    vb = {orc.v_code_bitpos(t, j, 4) for t in range(16) for j in range(128)}
+    assert len(kb) == 2048 and len(vb) == 2048 and all(b % 4 == 0 for b in kb | vb)
+    assert {b // 8 for b in kb} == set(range(1024)) and {b // 8 for b in vb} == set(range(1024, 2048))
+    meta = set()
+    for t in range(16):
+        for gg in range(4):
+            for f in (orc.k_scale_offset, orc.k_zero_offset, orc.v_scale_offset, orc.v_zero_offset):
+                o = f(t, gg, 4)
+                meta |= {o, o + 1}
+    assert meta == set(range(2048, 2560))
+
+
+def test_int4_block_pack_roundtrip_exhaustive():
+    rng = np.random.default_rng(2)
+    block = np.zeros(2560, np.uint8)
+    toks = []
+    for slot in range(16):
+        kc, vc = rng.integers(0, 16, 128).astype(np.uint8), rng.integers(0, 16, 128).astype(np.uint8)
+        ks, kz, vs, vz = (rng.standard_normal(4).astype(np.float16) for _ in range(4))
+        orc.write_token(block, slot, kc, ks, kz, vc, vs, vz, bits=4)
+        toks.append((kc, ks, kz, vc, vs, vz))
+    for slot in range(16):
+        for a, b in zip(orc.read_token(block, slot, bits=4), toks[slot]):
+            assert np.array_equal(a, b)
+    # the vectorised reader agrees with the per-token one
+    got = orc.unpack_tokens(np.stack([block] * 16), np.arange(16), bits=4)
+    for slot in range(16):
+        for a, b in zip(got, toks[slot]):
+            assert np.array_equal(a[slot], b)
+    # every value of a K byte and of a V byte survives (two codes per byte)
+    for byte in (0, 1024 + 37):
+        for val in range(256):
+            blk = np.zeros(2560, np.uint8)
+            blk[byte] = val
+            slot = 0 if byte < 1024 else 4 * ((byte - 1024) // 256)
+            kc, ks, kz, vc, vs, vz = orc.read_token(blk, slot, bits=4)
+            # bytes of tokens 4a..4a+3 share words: rebuild from every token
+            ref = np.zeros(2560, np.uint8)
+            for t in range(16):
+                tok = orc.read_token(blk, t, bits=4)
+                orc.write_token(ref, t, *tok, bits=4)
+            assert ref[byte] == val
+
+
+def test_int4_quant_error_bound_grid_roundtrip_and_nearest_level():
+    y = _random_rotated(2000, 0)
+    c, s, z = orc.quantize_rotated(y, np.full(128, 65504, np.float32), bits=4)
+    assert c.min() >= 0 and c.max() <= 15 and c.max() == 15
+    err = np.abs(orc.dequantize(c, s, z) - y.astype(np.float64)).reshape(-1, 4, 32)
+    ulp = np.spacing(np.abs(y).astype(np.float32)).reshape(-1, 4, 32).astype(np.float64)
+    assert np.all(err <= s.astype(np.float64)[..., None] / 2 * (1 + 2 ** -20) + ulp)
+    # on-grid values round-trip losslessly
+    rng = np.random.default_rng(6)
+    for _ in range(100):
+        zz = np.float16(rng.integers(-512, 512) / 8.0)
+        ss = np.float16(rng.integers(1, 64) / 64.0)
+        codes = rng.integers(0, 16, size=32)
+        codes[0], codes[1] = 0, 15
+        yy = (np.float32(zz) + codes.astype(np.float32) * np.float32(ss)).astype(np.float32)
+        cc, sc, zc = orc.quantize_rotated(np.tile(yy, 4)[None], np.full(128, 65504, np.float32), bits=4)
+        assert np.all(sc == ss) and np.all(zc == zz) and np.array_equal(cc[0, :32], codes)
+    # brute force: each code is the nearest of the 16 levels (ties aside)
+    g = y[:300].reshape(-1, 4, 32).astype(np.float64)
+    cg = c[:300].reshape(-1, 4, 32)
+    for i in range(g.shape[0]):
+        for gg in range(4):
+            lv = float(z[i, gg]) + np.arange(16) * float(s[i, gg])
+            d = np.abs(g[i, gg][:, None] - lv[None, :])
+            tie = np.sort(d, 1)[:, 1] - np.sort(d, 1)[:, 0] < 1e-6 * float(s[i, gg])
+            assert np.all((d.argmin(1) == cg[i, gg]) | tie)
+
+
+def test_int4_identity_rotation_is_textbook_minmax_int4():
+    rng = np.random.default_rng(19)
+    x = synth.bf16_bits_to_f32(synth.to_bf16_bits(rng.standard_normal((64, 128)).astype(np.float32)))
+    c, s, z = orc.quantize_rotated(x, np.full(128, 65504, np.float32), bits=4)
+    g = x.reshape(64, 4, 32).astype(np.float64)
+    step = (g.max(-1) - g.min(-1)) / 15
+    assert np.all(s.astype(np.float64) >= step) and np.all(s.astype(np.float64) <= step * (1 + 2 ** -9) + 2 ** -24)
+    assert c.reshape(64, 4, 32)[np.arange(64)[:, None], np.arange(4)[None], g.argmin(-1)].max() == 0
+    assert c.reshape(64, 4, 32)[np.arange(64)[:, None], np.arange(4)[None], g.argmax(-1)].min() >= 14
+
+
+def test_int4_history_decode_equals_brute_force_and_beats_int2():
+    n = 380
+    st = synth.streams(50)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, 1, out_ch)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, 1, out_ch)
+    r = synth.random_rotation(st["rot"])
+    tau = orc.clip_thresholds(synth.bf16_bits_to_f32(k), r)
+    pt = synth.page_permutation(st["perm"], 8)[None, :]
+    q = synth.queries(st["q"], (1, 2, 128))
+    qq = synth.bf16_bits_to_f32(q).astype(np.float64)
+    kk0 = synth.bf16_bits_to_f32(k[:, 0]).astype(np.float64)
+    vv0 = synth.bf16_bits_to_f32(v[:, 0]).astype(np.float64)
+    errs = {}
+    for bits in (2, 4):
+        pool = orc.Pool(1, 1, 8, pt, bits=bits)
+        assert pool.hist.shape[-1] == (1536 if bits == 2 else 2560)
+        for p in range(n):
+            pool.append(0, k[p], v[p], r, r, tau, tau)
+        out = orc.decode_tiered(q, pool, [0], [n], r, r)
+        kk, vv = kk0.copy(), vv0.copy()
+        r64 = r.astype(np.float64)
+        for p in range(64, n - 256):           # history rebuilt from the rotated originals
+            ck, sk, zk = orc.quantize_rotated(orc.rotate_fp32(kk0[p][None], r), tau, bits)
+            cv, sv, zv = orc.quantize_rotated(orc.rotate_fp32(vv0[p][None], r), tau, bits)
+            kk[p] = orc.dequantize(ck, sk, zk)[0] @ r64.T
+            vv[p] = orc.dequantize(cv, sv, zv)[0] @ r64.T
+        for h in range(2):
+            assert np.allclose(out[0, h], _brute_attention(qq[0, h], kk.tolist(), vv.tolist()), atol=1e-9)
+        exact = np.stack([orc.attention(qq[0, h], kk0, vv0) for h in range(2)])
+        errs[bits] = np.linalg.norm(out[0] - exact)
+    assert errs[4] < errs[2] / 2
