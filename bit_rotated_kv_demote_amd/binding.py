@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libamdoscar.so")
 
 OSCAR_SRC_BF16 = 0
 OSCAR_SRC_F32_ROTATED = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_calibrate_layers", "oscar_append", "oscar_demote",
             "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_multi",
@@ -41,7 +41,7 @@ class Pool(ctypes.Structure):
                 ("recent_v", ctypes.c_void_p), ("hist", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
                 ("n_slots", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
                 ("rot_k", ctypes.c_void_p), ("rot_v", ctypes.c_void_p), ("clip_k", ctypes.c_void_p),
-                ("clip_v", ctypes.c_void_p), ("rot_per_kv_head", ctypes.c_int32)]
+                ("clip_v", ctypes.c_void_p), ("code_bits", ctypes.c_int32), ("rot_per_kv_head", ctypes.c_int32)]
 
 
 class Bf16Pool(ctypes.Structure):
@@ -127,13 +127,14 @@ def layer_desc(num_q_heads: int, num_kv_heads: int) -> LayerDesc:
 
 
 def make_pool(sink_k, sink_v, recent_k, recent_v, hist, page_table, rot_k, rot_v, clip_k, clip_v,
-              rot_per_kv_head=False) -> Pool:
+              rot_per_kv_head=False, code_bits=2) -> Pool:
     return Pool(sink_k.data_ptr(), sink_v.data_ptr(), recent_k.data_ptr(), recent_v.data_ptr(),
                 hist.data_ptr() if hist is not None else None,
                 page_table.data_ptr() if page_table is not None else None,
                 sink_k.shape[0], page_table.shape[1] if page_table is not None else 0,
                 hist.shape[0] if hist is not None else 0,
-                rot_k.data_ptr(), rot_v.data_ptr(), clip_k.data_ptr(), clip_v.data_ptr(), int(bool(rot_per_kv_head)))
+                rot_k.data_ptr(), rot_v.data_ptr(), clip_k.data_ptr(), clip_v.data_ptr(), int(code_bits),
+                int(bool(rot_per_kv_head)))
 
 
 def make_bf16_pool(kv, page_table) -> Bf16Pool:

@@ -36,6 +36,26 @@ __device__ __forceinline__ uint32_t field_pair(uint32_t w, uint32_t w6) {
 }
 __host__ __device__ constexpr int field_shift(int f) { return f <= 4 ? f : f - 3; }
 
+// INT4: nibble field f (0..3) of both 16-bit halves of w as fp16 subnormals
+// c * 16^(f & 1) * 2^-24 (w8 = w >> 8 brings nibbles 2 and 3 down).
+template <int F>
+__device__ __forceinline__ uint32_t nibble_pair(uint32_t w, uint32_t w8) {
+  constexpr uint32_t mask = (F & 1) ? 0x00F000F0u : 0x000F000Fu;
+  return (F < 2 ? w : w8) & mask;
+}
+
+// One page's codes as a lane loads them: INT2, K codes in words 0-1 and V
+// codes in words 2-3 of one 16-byte chunk; INT4, a 16-byte K chunk and a
+// 16-byte V chunk.
+template <int kBits>
+struct PageCodes {
+  u32x4_t w;
+};
+template <>
+struct PageCodes<4> {
+  u32x4_t k, v;
+};
+
 // A wave walks its share of a split in steps of kStepPages pages: wave w
 // takes steps w, w + 4, ...  While one step is processed the next one is in
 // flight.
@@ -62,24 +82,31 @@ struct alignas(16) DecodeSmem : SplitSmem<G> {
 // ids, lane kStepPages k + i holding page kStepPages (wave + 4k) + i of the
 // split (clamped to its last page), so the k-th step of the wave needs no
 // memory access for its page ids.
+template <int kBits>
 __device__ __forceinline__ void issue_step(const DecodeArgs& a, int32_t ids, int hk, int k, int lane,
-                                           u32x4_t* c, u32x2_t* md) {
+                                           PageCodes<kBits>* c, u32x2_t* md) {
+  constexpr int kBytes = block_bytes(kBits);
 #pragma unroll
   for (int i = 0; i < kStepPages; ++i) {
     const int pid = __builtin_amdgcn_readlane(ids, kStepPages * k + i);
-    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.hist) + ((size_t)pid * a.hkv + hk) * kBlock,
-                                                     (short)0, kBlock, 0x00020000);
-    c[i] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 0);
-    md[i] = __builtin_amdgcn_raw_buffer_load_b64(r, 1024 + 8 * lane, 0, 0);
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.hist) + ((size_t)pid * a.hkv + hk) * kBytes,
+                                                     (short)0, kBytes, 0x00020000);
+    if constexpr (kBits == 4) {
+      c[i].k = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 0);
+      c[i].v = __builtin_amdgcn_raw_buffer_load_b128(r, kVCodeOff4 + 16 * lane, 0, 0);
+    } else {
+      c[i].w = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 0, 0);
+    }
+    md[i] = __builtin_amdgcn_raw_buffer_load_b64(r, 1024 + meta_shift(kBits) + 8 * lane, 0, 0);
   }
 }
 
 // masked score (finite, so that a zero weight times it stays 0)
 constexpr float kMasked = -1.0e30f;
 
-template <int G>
+template <int G, int kBits>
 __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, int hk, int hist_len,
-                          int pg_begin, int pg_end, int wave, int lane, const u32x4_t* c_first,
+                          int pg_begin, int pg_end, int wave, int lane, const PageCodes<kBits>* c_first,
                           const u32x2_t* m_first) {
   const int x = lane & 15, qa = lane >> 4;
   // ---- score operands: q' in fp16 hi (columns 0..G-1) and lo (G..2G-1)
@@ -105,8 +132,10 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int j = 32 * g + 8 * qa + 2 * i + hf;
-          const int sh = field_shift(4 * (g & 1) + i);
-          const float v = ldexpf(sm.qr[col_head][j] * col_scale, -2 * sh);
+          // the code of channel j enters the product as c * 4^sh * 2^-24
+          // (INT2) or c * 16^(i & 1) * 2^-24 (INT4): q' carries the inverse
+          const int lsh = kBits == 4 ? 4 * (i & 1) : 2 * field_shift(4 * (g & 1) + i);
+          const float v = ldexpf(sm.qr[col_head][j] * col_scale, -lsh);
           const _Float16 hi = (_Float16)v;
           const _Float16 e = hi_col ? hi : (_Float16)(v - (float)hi);
           bq[tl][g][2 * i + hf] = col_used ? e : (_Float16)0.0f;
@@ -132,17 +161,19 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
 
   // two-stage prefetch ring: while step st is processed, step st + 4 of this
   // wave is in flight (the first step was issued before the prologue)
-  u32x4_t cA[kStepPages], cB[kStepPages];
+  PageCodes<kBits> cA[kStepPages], cB[kStepPages];
   u32x2_t mA[kStepPages], mB[kStepPages];
 #pragma unroll
   for (int i = 0; i < kStepPages; ++i) { cA[i] = c_first[i]; mA[i] = m_first[i]; }
-  auto issue = [&](int st_, u32x4_t* c, u32x2_t* md) { issue_step(a, ids, hk, (st_ - wave) >> 2, lane, c, md); };
+  auto issue = [&](int st_, PageCodes<kBits>* c, u32x2_t* md) {
+    issue_step<kBits>(a, ids, hk, (st_ - wave) >> 2, lane, c, md);
+  };
   int st = wave;
   // A partial step (only the last step of a sequence) has tokens past the end
   // of the history: their scores are masked, so their weights are exactly 0.
   // Their slots hold either zeros or bytes an earlier demotion wrote (finite
   // scales and zeros), so 0 times them stays 0.
-  auto body = [&](const u32x4_t* c_cur, const u32x2_t* m_cur) __attribute__((always_inline)) {
+  auto body = [&](const PageCodes<kBits>* c_cur, const u32x2_t* m_cur) __attribute__((always_inline)) {
     const int pg0 = pg_begin + kStepPages * st;
     const int n_valid = min(kStepPages, pg_end - pg0);
     // valid tokens of the step: token t of page p is history index 16 (pg0 + p) + t
@@ -161,18 +192,30 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
       const uint8_t* mp = mbuf + 512 * p;
       // sum_g zero[t][g] * (scaled group sums of q'), t = lane's row token
       const _Float16 zk = *reinterpret_cast<const _Float16*>(mp + 128 + 8 * x + 2 * qa);
-      const uint32_t w0 = c_cur[p][0], w1 = c_cur[p][1];
-      const uint32_t w0s = w0 >> 6, w1s = w1 >> 6;
       half8_t ak[4];
       uint32_t* ak32 = reinterpret_cast<uint32_t*>(ak);
-      ak32[0] = field_pair<0>(w0, w0s);  ak32[1] = field_pair<1>(w0, w0s);
-      ak32[2] = field_pair<2>(w0, w0s);  ak32[3] = field_pair<3>(w0, w0s);
-      ak32[4] = field_pair<4>(w0, w0s);  ak32[5] = field_pair<5>(w0, w0s);
-      ak32[6] = field_pair<6>(w0, w0s);  ak32[7] = field_pair<7>(w0, w0s);
-      ak32[8] = field_pair<0>(w1, w1s);  ak32[9] = field_pair<1>(w1, w1s);
-      ak32[10] = field_pair<2>(w1, w1s); ak32[11] = field_pair<3>(w1, w1s);
-      ak32[12] = field_pair<4>(w1, w1s); ak32[13] = field_pair<5>(w1, w1s);
-      ak32[14] = field_pair<6>(w1, w1s); ak32[15] = field_pair<7>(w1, w1s);
+      if constexpr (kBits == 4) {
+        // word g holds group g's eight channels of this lane: one operand
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t w = c_cur[p].k[g], w8 = w >> 8;
+          ak32[4 * g + 0] = nibble_pair<0>(w, w8);
+          ak32[4 * g + 1] = nibble_pair<1>(w, w8);
+          ak32[4 * g + 2] = nibble_pair<2>(w, w8);
+          ak32[4 * g + 3] = nibble_pair<3>(w, w8);
+        }
+      } else {
+        const uint32_t w0 = c_cur[p].w[0], w1 = c_cur[p].w[1];
+        const uint32_t w0s = w0 >> 6, w1s = w1 >> 6;
+        ak32[0] = field_pair<0>(w0, w0s);  ak32[1] = field_pair<1>(w0, w0s);
+        ak32[2] = field_pair<2>(w0, w0s);  ak32[3] = field_pair<3>(w0, w0s);
+        ak32[4] = field_pair<4>(w0, w0s);  ak32[5] = field_pair<5>(w0, w0s);
+        ak32[6] = field_pair<6>(w0, w0s);  ak32[7] = field_pair<7>(w0, w0s);
+        ak32[8] = field_pair<0>(w1, w1s);  ak32[9] = field_pair<1>(w1, w1s);
+        ak32[10] = field_pair<2>(w1, w1s); ak32[11] = field_pair<3>(w1, w1s);
+        ak32[12] = field_pair<4>(w1, w1s); ak32[13] = field_pair<5>(w1, w1s);
+        ak32[14] = field_pair<6>(w1, w1s); ak32[15] = field_pair<7>(w1, w1s);
+      }
       // scales of tokens 4qa..4qa+3 (K scale area [token][group])
       const u32x4_t s01 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa);
       const u32x4_t s23 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa + 16);
@@ -265,21 +308,49 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
           b32[i] = mul_h2(pp[i], sw);
         }
       }
-      const uint32_t v00 = c_cur[2 * j][2], v01 = c_cur[2 * j][3], v10 = c_cur[2 * j + 1][2], v11 = c_cur[2 * j + 1][3];
-      const uint32_t v00s = v00 >> 6, v01s = v01 >> 6, v10s = v10 >> 6, v11s = v11 >> 6;
+      if constexpr (kBits == 4) {
+        // block M (channels 16M + row): nibble M & 3 of words 2(M >> 2) and
+        // 2(M >> 2) + 1 of each page's V chunk (tokens 4qa + 0, 1 and + 2, 3)
+        uint32_t vw[2][4], vw8[2][4];
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vw[p][e] = c_cur[2 * j + p].v[e];
+            vw8[p][e] = vw[p][e] >> 8;
+          }
+#define OSCAR_VBLOCK4(M)                                                                  \
+        {                                                                                 \
+          half8_t av;                                                                     \
+          uint32_t* a32 = reinterpret_cast<uint32_t*>(&av);                               \
+          constexpr int e0 = 2 * ((M) >> 2);                                              \
+          a32[0] = nibble_pair<(M) & 3>(vw[0][e0], vw8[0][e0]);                           \
+          a32[1] = nibble_pair<(M) & 3>(vw[0][e0 + 1], vw8[0][e0 + 1]);                   \
+          a32[2] = nibble_pair<(M) & 3>(vw[1][e0], vw8[1][e0]);                           \
+          a32[3] = nibble_pair<(M) & 3>(vw[1][e0 + 1], vw8[1][e0 + 1]);                   \
+          acc_o[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[(M) >> 1], acc_o[M], 0, 0, 0); \
+        }
+        OSCAR_VBLOCK4(0) OSCAR_VBLOCK4(1) OSCAR_VBLOCK4(2) OSCAR_VBLOCK4(3)
+        OSCAR_VBLOCK4(4) OSCAR_VBLOCK4(5) OSCAR_VBLOCK4(6) OSCAR_VBLOCK4(7)
+#undef OSCAR_VBLOCK4
+      } else {
+        const uint32_t v00 = c_cur[2 * j].w[2], v01 = c_cur[2 * j].w[3], v10 = c_cur[2 * j + 1].w[2],
+                       v11 = c_cur[2 * j + 1].w[3];
+        const uint32_t v00s = v00 >> 6, v01s = v01 >> 6, v10s = v10 >> 6, v11s = v11 >> 6;
 #define OSCAR_VBLOCK(M)                                                                   \
-      {                                                                                   \
-        half8_t av;                                                                       \
-        uint32_t* a32 = reinterpret_cast<uint32_t*>(&av);                                 \
-        a32[0] = field_pair<M>(v00, v00s);                                                \
-        a32[1] = field_pair<M>(v01, v01s);                                                \
-        a32[2] = field_pair<M>(v10, v10s);                                                \
-        a32[3] = field_pair<M>(v11, v11s);                                                \
-        acc_o[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[(M) >> 1], acc_o[M], 0, 0, 0); \
-      }
-      OSCAR_VBLOCK(0) OSCAR_VBLOCK(1) OSCAR_VBLOCK(2) OSCAR_VBLOCK(3)
-      OSCAR_VBLOCK(4) OSCAR_VBLOCK(5) OSCAR_VBLOCK(6) OSCAR_VBLOCK(7)
+        {                                                                                 \
+          half8_t av;                                                                     \
+          uint32_t* a32 = reinterpret_cast<uint32_t*>(&av);                               \
+          a32[0] = field_pair<M>(v00, v00s);                                              \
+          a32[1] = field_pair<M>(v01, v01s);                                              \
+          a32[2] = field_pair<M>(v10, v10s);                                              \
+          a32[3] = field_pair<M>(v11, v11s);                                              \
+          acc_o[M] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[(M) >> 1], acc_o[M], 0, 0, 0); \
+        }
+        OSCAR_VBLOCK(0) OSCAR_VBLOCK(1) OSCAR_VBLOCK(2) OSCAR_VBLOCK(3)
+        OSCAR_VBLOCK(4) OSCAR_VBLOCK(5) OSCAR_VBLOCK(6) OSCAR_VBLOCK(7)
 #undef OSCAR_VBLOCK
+      }
       {
         // rows 0..3: sum_t p_t zero[t][g]; row 4: sum_t p_t
         half8_t az, bz;
@@ -315,7 +386,9 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
   if (x < G) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float scl = ldexpf(1.0f, 24 - 2 * field_shift(m));
+      // codes of block m entered as c * 4^field_shift(m) (INT2) or
+      // c * 16^(m & 1) (INT4) times 2^-24
+      const float scl = ldexpf(1.0f, 24 - (kBits == 4 ? 4 * (m & 1) : 2 * field_shift(m)));
       const float zg = sm.zs[wave][m >> 1][x];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.wo[wave][x][16 * m + 4 * qa + r] = fmaf(acc_o[m][r], scl, zg);
@@ -323,9 +396,8 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(DecodeArgs a) {
-  __shared__ DecodeSmem<G> sm;
+template <int G, int kBits>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so work
@@ -404,13 +476,13 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
     // loads in flight that every later iteration also has.
     const int32_t ids = pt_row[pg_begin + min(kStepPages * (wave + 4 * (lane / kStepPages)) + lane % kStepPages,
                                               pg_end - pg_begin - 1)];
-    u32x4_t c_first[kStepPages];
+    PageCodes<kBits> c_first[kStepPages];
     u32x2_t m_first[kStepPages];
     // unconditional (the ids are clamped to pages of this split): the same
     // loads are in flight on every path into the loop
     // (kept in the loop's issue order, so the wait counts the loop computes
     // for its first iteration are exact)
-    issue_step(a, ids, hk, 0, lane, c_first, m_first);
+    issue_step<kBits>(a, ids, hk, 0, lane, c_first, m_first);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {
@@ -464,9 +536,23 @@ __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(Decode
       if (lane == 32) { sm.qs[h][1] = g0; sm.qs[h][3] = g1; }
     }
     __syncthreads();
-    hist_wave<G>(a, sm, ids, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first);
+    hist_wave<G, kBits>(a, sm, ids, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first);
   }
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
+}
+
+template <int G>
+__global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(DecodeArgs a) {
+  __shared__ DecodeSmem<G> sm;
+  decode_body<G, 2>(a, sm);
+}
+
+// INT4 pool: the same kernel over 2560-byte blocks (twice the code registers
+// per step in flight, so two workgroups per compute unit)
+template <int G>
+__global__ __launch_bounds__(256, 2) void decode_int4_kernel(DecodeArgs a) {
+  __shared__ DecodeSmem<G> sm;
+  decode_body<G, 4>(a, sm);
 }
 
 DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len) {
@@ -495,6 +581,17 @@ DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_s
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t st) {
+  if (a.code_bits == 4) {
+    switch (group) {
+      case 1: hipLaunchKernelGGL(decode_int4_kernel<1>, dim3(grid), dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL(decode_int4_kernel<2>, dim3(grid), dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL(decode_int4_kernel<4>, dim3(grid), dim3(256), 0, st, a); break;
+      case 8: hipLaunchKernelGGL(decode_int4_kernel<8>, dim3(grid), dim3(256), 0, st, a); break;
+      case 16: hipLaunchKernelGGL(decode_int4_kernel<16>, dim3(grid), dim3(256), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (group) {
     case 1: hipLaunchKernelGGL(decode_int2_kernel<1>, dim3(grid), dim3(256), 0, st, a); break;
     case 2: hipLaunchKernelGGL(decode_int2_kernel<2>, dim3(grid), dim3(256), 0, st, a); break;

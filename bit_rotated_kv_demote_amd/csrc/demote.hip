@@ -27,10 +27,11 @@ namespace oscar {
 // ---------------------------------------------------------------------------
 // Quantise + pack one vector held one channel per thread (threads 0..127 of
 // the block; every thread of the block must call it).  `sh` is 32 words of
-// LDS.  Writes token slot `ps` of the block `blk`.
+// LDS.  Writes token slot `ps` of the block `blk` (an INT2 block, or an INT4
+// block when bits == 4).
 // ---------------------------------------------------------------------------
 __device__ void quantize_pack_channel_per_thread(float yc, bool is_v, uint8_t* blk, int ps,
-                                                 uint32_t* sh) {
+                                                 uint32_t* sh, int bits) {
   const int c = threadIdx.x;
   const bool act = c < kD;
   float mn = yc, mx = yc;
@@ -40,26 +41,41 @@ __device__ void quantize_pack_channel_per_thread(float yc, bool is_v, uint8_t* b
     mx = fmaxf(mx, __shfl_xor(mx, m));
   }
   __half s, z;
-  group_scale_zero(mn, mx, &s, &z);
-  const uint32_t code = quant_code(yc, __half2float(z), __half2float(s));
+  const bool int4 = bits == 4;
+  group_scale_zero(mn, mx, &s, &z, int4 ? 15.0f : 3.0f);
+  const uint32_t code = quant_code(yc, __half2float(z), __half2float(s), int4 ? 15.0f : 3.0f);
   if (c < 32) sh[c] = 0u;
   __syncthreads();
   if (act) {
-    if (!is_v)
+    if (int4) {
+      // K: word (chunk (c >> 3) & 3, group c >> 5); V: half-word (channel
+      // c & 15, channels 16m with m >> 2 == c >> 6) of this token
+      if (!is_v)
+        atomicOr(&sh[4 * ((c >> 3) & 3) + (c >> 5)], code << (16 * (c & 1) + 4 * ((c >> 1) & 3)));
+      else
+        atomicOr(&sh[2 * (c & 15) + (c >> 6)], code << (4 * ((c >> 4) & 3)));
+    } else if (!is_v) {
       atomicOr(&sh[2 * ((c >> 3) & 3) + (c >> 6)], code << (2 * k_field(c)));
-    else
+    } else {
       atomicOr(&sh[8 + (c & 15)], code << (2 * v_field_in_half(c)));
+    }
   }
   __syncthreads();
-  if (!is_v) {
+  if (int4) {
+    if (!is_v) {
+      if (c < 16) *reinterpret_cast<uint32_t*>(blk + 16 * (16 * (c >> 2) + ps) + 4 * (c & 3)) = sh[c];
+    } else {
+      if (c < 32) *reinterpret_cast<uint16_t*>(blk + v4_halfword_byte(ps, c >> 1, c & 1)) = (uint16_t)sh[c];
+    }
+  } else if (!is_v) {
     if (c < 8) *reinterpret_cast<uint32_t*>(blk + 16 * (16 * (c >> 1) + ps) + 4 * (c & 1)) = sh[c];
   } else {
     if (c < 16) *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, c)) = (uint16_t)sh[8 + c];
   }
   if (act && (c & 31) == 0) {
     const int g = c >> 5;
-    const int so = is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g);
-    const int zo = is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g);
+    const int so = (is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g)) + meta_shift(bits);
+    const int zo = (is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g)) + meta_shift(bits);
     *reinterpret_cast<uint16_t*>(blk + so) = half_bits(s);
     *reinterpret_cast<uint16_t*>(blk + zo) = half_bits(z);
   }
@@ -111,8 +127,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     __syncthreads();  // also orders the ring read above before the overwrite below
     float yc = 0.0f;
     if (tid < kD) yc = clip_value(part[0][tid] + part[1][tid], tau_j);
-    uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
-    quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh);
+    uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(a.code_bits);
+    quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh, a.code_bits);
   }
   if (tid < kD / 2) reinterpret_cast<uint32_t*>(ring)[tid] = reinterpret_cast<const uint32_t*>(src)[tid];
 }
@@ -135,6 +151,8 @@ __device__ __forceinline__ int rt_index(int j, int i) { return j * kD + ((((i >>
 // Clip, quantise, pack and store one token's vector held as y[m][i] =
 // channel 16 m + 4 qa + i (the lanes qa = 0..3 with the same token hold the
 // rest).  tau: LDS [128].  Every lane of the wave must call it (lane swaps).
+// kBits: 2 (INT2 block) or 4 (INT4 block).
+template <int kBits>
 __device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float* tau, bool is_v, bool valid,
                                                   uint8_t* blk, int ps, int qa) {
   float gmn[4], gmx[4];
@@ -170,7 +188,7 @@ __device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float*
   CodeCut cut[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    group_scale_zero(gmn[g], gmx[g], &sc[g], &zr[g]);
+    group_scale_zero(gmn[g], gmx[g], &sc[g], &zr[g], kBits == 4 ? 15.0f : 3.0f);
     zf[g] = __half2float(zr[g]);
     cut[g] = code_cut(__half2float(sc[g]));
   }
@@ -178,10 +196,42 @@ __device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float*
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) code[m][i] = quant_code_cut(y[m][i] - zf[m >> 1], cut[m >> 1]);
+    for (int i = 0; i < 4; ++i)
+      code[m][i] = kBits == 4 ? quant_code(y[m][i], zf[m >> 1], __half2float(sc[m >> 1]), 15.0f)
+                              : quant_code_cut(y[m][i] - zf[m >> 1], cut[m >> 1]);
   auto push = [&](uint32_t acc, int sh, int m, int i) { return (acc << sh) + code[m][i]; };
 
-  if (!is_v) {
+  if constexpr (kBits == 4) {
+    if (!is_v) {
+      // K: channel j = 16m + 4a + i is in chunk 2(m & 1) + (a >> 1), word
+      // m >> 1, nibble at bit 16(i & 1) + 8(a & 1) + 4(i >> 1); lanes a and
+      // a ^ 1 fill the two byte halves of each 16-bit half of the same word.
+      uint32_t wd[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        uint32_t w = code[m][0] | (code[m][1] << 16) | (code[m][2] << 4) | (code[m][3] << 20);
+        w <<= 8 * (qa & 1);
+        const auto pr = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+        wd[m] = pr[0] | pr[1];
+      }
+      if (valid && (qa & 1) == 0) {
+        *reinterpret_cast<u32x4_t*>(blk + 16 * (16 * (qa >> 1) + ps)) = (u32x4_t){wd[0], wd[2], wd[4], wd[6]};
+        *reinterpret_cast<u32x4_t*>(blk + 16 * (16 * (2 + (qa >> 1)) + ps)) = (u32x4_t){wd[1], wd[3], wd[5], wd[7]};
+      }
+    } else {
+      // V: channel 4a + i of this token: codes of channels 16m with m < 4 in
+      // one half-word (nibble m), m >= 4 in another (nibble m - 4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = code[0][i] | (code[1][i] << 4) | (code[2][i] << 8) | (code[3][i] << 12);
+        const uint32_t hi = code[4][i] | (code[5][i] << 4) | (code[6][i] << 8) | (code[7][i] << 12);
+        if (valid) {
+          *reinterpret_cast<uint16_t*>(blk + v4_halfword_byte(ps, 4 * qa + i, 0)) = (uint16_t)lo;
+          *reinterpret_cast<uint16_t*>(blk + v4_halfword_byte(ps, 4 * qa + i, 1)) = (uint16_t)hi;
+        }
+      }
+    }
+  } else if (!is_v) {
     // K: channel j = 16m + 4a + i lands in word (2(m&1) + (a>>1), m>>2) at
     // field 4((m>>1)&1) + 2(a&1) + (i>>1) + 8(i&1); lanes a and a^1 fill
     // complementary fields of the same four words.  A lane builds its eight
@@ -231,14 +281,14 @@ __device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float*
     const uint32_t z01 = half_bits(zr[0]) | ((uint32_t)half_bits(zr[1]) << 16);
     const uint32_t z23 = half_bits(zr[2]) | ((uint32_t)half_bits(zr[3]) << 16);
     const int sh = 16 * (g & 1);
-    const int so = is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g);
-    const int zo = is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g);
+    const int so = (is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g)) + meta_shift(kBits);
+    const int zo = (is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g)) + meta_shift(kBits);
     *reinterpret_cast<uint16_t*>(blk + so) = (uint16_t)(((g < 2) ? s01 : s23) >> sh);
     *reinterpret_cast<uint16_t*>(blk + zo) = (uint16_t)(((g < 2) ? z01 : z23) >> sh);
   }
 }
 
-template <bool kRotatedInput>
+template <bool kRotatedInput, int kBits>
 __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
   __shared__ __bf16 rt_hi[kRotatedInput ? 1 : kD * kD];
   __shared__ __bf16 rt_lo[kRotatedInput ? 1 : kD * kD];
@@ -286,8 +336,8 @@ __global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
     auto page_of = [&](int t) { return a.page_table[(size_t)slot * a.max_pages + ((h0 + src_token(t)) >> 4)]; };
     auto store = [&](float (&y)[8][4], int t, int page) {
       const int tok = tok0 + 16 * t + tcol;
-      uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * kBlock;
-      quant_store_token(y, tau_s, is_v != 0, tok < count, blk, (h0 + src_token(t)) & 15, qa);
+      uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(kBits);
+      quant_store_token<kBits>(y, tau_s, is_v != 0, tok < count, blk, (h0 + src_token(t)) & 15, qa);
     };
     if constexpr (kRotatedInput) {
       for (int t = 0; t < kUnitTokens / 16; ++t) {
@@ -389,10 +439,17 @@ hipError_t launch_demote(const DemoteArgs& a_in, int batch, int max_count, bool 
   const long units = (long)batch * (per_head ? 1 : a.hkv) * a.unit_tiles;
   const int nwg = (int)std::min<long>((units + 3) / 4, std::max(1, 256 / heads));
   const dim3 grid(nwg, 2, heads);
-  if (rotated)
-    hipLaunchKernelGGL(demote_bulk_kernel<true>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(demote_bulk_kernel<false>, grid, dim3(256), 0, st, a);
+  if (a.code_bits == 4) {
+    if (rotated)
+      hipLaunchKernelGGL((demote_bulk_kernel<true, 4>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((demote_bulk_kernel<false, 4>), grid, dim3(256), 0, st, a);
+  } else {
+    if (rotated)
+      hipLaunchKernelGGL((demote_bulk_kernel<true, 2>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((demote_bulk_kernel<false, 2>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

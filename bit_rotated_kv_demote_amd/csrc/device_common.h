@@ -47,21 +47,40 @@ __device__ __forceinline__ int k_zero_byte(int t, int g) { return kKZeroOff + 8 
 __device__ __forceinline__ int v_scale_byte(int t, int g) { return kVScaleOff + 32 * (t >> 2) + 8 * g + 2 * (t & 3); }
 __device__ __forceinline__ int v_zero_byte(int t, int g) { return kVZeroOff + 32 * (t >> 2) + 8 * g + 2 * (t & 3); }
 
+// ---- INT4 blocks (2560 bytes per (page, KV head)).  Lane l = 16a + b of a
+// decode wave loads the 16-byte K chunk l at 16 l (token b's channels j with
+// (j >> 3) & 3 == a: word j >> 5 holds one group's eight, channel j's nibble at
+// bit 16 (j & 1) + 4 ((j >> 1) & 3)) and the 16-byte V chunk l at 1024 + 16 l
+// (tokens 4a..4a+3, channels j with j & 15 == b: word 2 ((j >> 4) >> 2) +
+// ((t & 3) >> 1), nibble at bit 16 (t & 1) + 4 ((j >> 4) & 3)).  The
+// scale/zero metadata follows at 2048, laid out as in the INT2 block.
+constexpr int kBlock4 = 2560;
+constexpr int kVCodeOff4 = 1024;
+constexpr int kMetaShift4 = 1024;   // INT4 metadata offset minus the INT2 one
+__host__ __device__ constexpr int block_bytes(int bits) { return bits == 4 ? kBlock4 : kBlock; }
+__host__ __device__ constexpr int meta_shift(int bits) { return bits == 4 ? kMetaShift4 : 0; }
+__device__ __forceinline__ int v4_halfword_byte(int t, int b, int hi_m) {
+  return kVCodeOff4 + 16 * (16 * (t >> 2) + b) + 4 * (2 * hi_m + ((t & 3) >> 1)) + 2 * (t & 1);
+}
+
 // ---- INT2 quantiser of one 32-channel group (asymmetric min-max, four levels).
 // zero = fp16 rounded toward -inf of the group minimum, scale = fp16 rounded
 // toward +inf of (max - zero) / 3, code = clamp(rint((y - zero) / scale), 0, 3)
 // in IEEE fp32 with a correctly rounded division; code 0 when scale == 0.
-__device__ __forceinline__ void group_scale_zero(float mn, float mx, __half* scale, __half* zero) {
+// The INT4 quantiser is the same with 16 levels: (max - zero) / 15 and codes
+// clamped to [0, 15].
+__device__ __forceinline__ void group_scale_zero(float mn, float mx, __half* scale, __half* zero,
+                                                 float n_steps = 3.0f) {
   const __half z = __float2half_rd(mn);
   const float span = mx - __half2float(z);
   *zero = z;
-  *scale = __float2half_ru(span / 3.0f);
+  *scale = __float2half_ru(span / n_steps);
 }
 
-__device__ __forceinline__ uint32_t quant_code(float yc, float zf, float sf) {
+__device__ __forceinline__ uint32_t quant_code(float yc, float zf, float sf, float max_code = 3.0f) {
   if (!(sf > 0.0f)) return 0u;
   const float q = (yc - zf) / sf;
-  const float c = fminf(fmaxf(rintf(q), 0.0f), 3.0f);
+  const float c = fminf(fmaxf(rintf(q), 0.0f), max_code);
   return (uint32_t)c;
 }
 

@@ -20,6 +20,7 @@ struct AppendArgs {
   const float* clip_k; const float* clip_v;
   int rot_kv_stride;       // elements from one KV head's R to the next (0: shared)
   int clip_kv_stride;      // likewise for the clip thresholds
+  int code_bits;           // 2: INT2 history blocks, 4: INT4
   int hkv;
   int max_pages;
 };
@@ -37,6 +38,7 @@ struct DemoteArgs {
   const float* clip_k; const float* clip_v;
   int rot_kv_stride;  // elements from one KV head's R to the next (0: shared)
   int clip_kv_stride;
+  int code_bits;      // 2: INT2 history blocks, 4: INT4
   uint8_t* hist;
   const int32_t* page_table;
   int max_pages;
@@ -69,6 +71,7 @@ struct DecodeArgs {
   const int32_t* page_table;
   const float* rot_k; const float* rot_v;
   int rot_kv_stride;          // elements from one KV head's R to the next (0: shared)
+  int code_bits;              // 2: INT2 history blocks, 4: INT4
   float* partials;            // workspace: [batch*Hkv][n_splits][G][132]
   int hkv;
   int max_pages;

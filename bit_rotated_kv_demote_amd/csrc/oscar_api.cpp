@@ -30,6 +30,7 @@ oscar_status check_pool(const oscar_pool* p, bool need_hist_tiers) {
   if (need_hist_tiers && (!p->hist || !p->page_table)) return OSCAR_ERR_INVALID;
   if (!p->rot_k || !p->rot_v || !p->clip_k || !p->clip_v) return OSCAR_ERR_INVALID;
   if (p->rot_per_kv_head != 0 && p->rot_per_kv_head != 1) return OSCAR_ERR_INVALID;
+  if (p->code_bits != 2 && p->code_bits != 4) return OSCAR_ERR_UNSUPPORTED;
   if (p->n_slots <= 0 || p->max_pages_per_seq < 0 || p->num_pages < 0) return OSCAR_ERR_INVALID;
   return OSCAR_OK;
 }
@@ -135,6 +136,7 @@ oscar_status oscar_append(const oscar_layer_desc* desc, const oscar_pool* pool, 
   a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
   a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
   a.rot_kv_stride = rot_stride(pool); a.clip_kv_stride = clip_stride(pool);
+  a.code_bits = pool->code_bits;
   a.hkv = desc->num_kv_heads;
   a.max_pages = pool->max_pages_per_seq;
   return hip_status(launch_append(a, batch, static_cast<hipStream_t>(stream)));
@@ -163,6 +165,7 @@ static oscar_status demote_common(const oscar_layer_desc* desc, const oscar_pool
   a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
   a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
   a.rot_kv_stride = rot_stride(pool); a.clip_kv_stride = clip_stride(pool);
+  a.code_bits = pool->code_bits;
   a.hist = pool->hist;
   a.page_table = pool->page_table;
   a.max_pages = pool->max_pages_per_seq;
@@ -261,6 +264,7 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
   a.rot_k = pool->rot_k;
   a.rot_v = pool->rot_v;
   a.rot_kv_stride = rot_stride(pool);
+  a.code_bits = pool->code_bits;
   a.partials = static_cast<float*>(workspace);
   a.hkv = hkv;
   a.max_pages = pool->max_pages_per_seq;

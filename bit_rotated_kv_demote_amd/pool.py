@@ -28,14 +28,18 @@ class TieredKV:
     """One layer's three-tier pool (BF16 sink, INT2 history, BF16 recent ring)."""
 
     def __init__(self, num_q_heads, num_kv_heads, n_slots, max_pages_per_seq, num_pages,
-                 rot_k, rot_v, clip_k, clip_v, page_table=None, device="cuda"):
+                 rot_k, rot_v, clip_k, clip_v, page_table=None, device="cuda", code_bits=2):
         self.hq, self.hkv, self.device = num_q_heads, num_kv_heads, device
+        if code_bits not in (2, 4):
+            raise ValueError("code_bits must be 2 (INT2 history) or 4 (INT4)")
+        self.code_bits = code_bits
         f32 = dict(dtype=torch.float32, device=device)
         self.sink_k = torch.zeros((n_slots, num_kv_heads, 64, HEAD_DIM), dtype=torch.bfloat16, device=device)
         self.sink_v = torch.zeros_like(self.sink_k)
         self.recent_k = torch.zeros((n_slots, num_kv_heads, 256, HEAD_DIM), dtype=torch.bfloat16, device=device)
         self.recent_v = torch.zeros_like(self.recent_k)
-        self.hist = torch.zeros((max(num_pages, 1), num_kv_heads, 1536), dtype=torch.uint8, device=device)
+        self.hist = torch.zeros((max(num_pages, 1), num_kv_heads, 1536 if code_bits == 2 else 2560),
+                                dtype=torch.uint8, device=device)
         if page_table is None:
             page_table = np.arange(n_slots * max_pages_per_seq, dtype=np.int32).reshape(n_slots, max_pages_per_seq)
         self.page_table = torch.as_tensor(np.asarray(page_table, np.int32), device=device).contiguous()
@@ -53,7 +57,7 @@ class TieredKV:
         self.desc = binding.layer_desc(num_q_heads, num_kv_heads)
         self.pool = binding.make_pool(self.sink_k, self.sink_v, self.recent_k, self.recent_v, self.hist,
                                       self.page_table, self.rot_k, self.rot_v, self.clip_k, self.clip_v,
-                                      self.per_kv_head)
+                                      self.per_kv_head, code_bits)
         self._ws = None
 
     # -- hot path --------------------------------------------------------

@@ -1,6 +1,7 @@
 /*
  * oscar.h -- C ABI of libamdoscar.so: OSCAR-style 2-bit KV-cache demotion and
- * tiered single-token decode attention on AMD Instinct MI355X (gfx950).
+ * tiered decode attention on AMD Instinct MI355X (gfx950), with an INT4
+ * variant of the same history pool.
  *
  * Pages cited (title, site):
  *   [gist]    "OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV
@@ -62,6 +63,18 @@
  *   [1280,1408) V scale fp16 [token/4][group][token%4]
  *   [1408,1536) V zero  fp16 [token/4][group][token%4]
  * A code c of group g dequantises to c * scale + zero in the rotated space.
+ *
+ * INT4 pools (oscar_pool.code_bits = 4; the INT4 baseline of [gist] 4): 16
+ * levels (scale from (max - zero) / 15, codes 0..15), two codes per byte, one
+ * 2560-byte block per (page, KV head), so hist is u8 [num_pages][Hkv][2560]:
+ *   [0,1024)    K codes, 64 chunks of 16 bytes.  Chunk 16a + t holds token
+ *               t's channels j with ((j>>3)&3)==a: 32-bit word j>>5, 4-bit
+ *               field at bit 16(j&1) + 4((j>>1)&3).
+ *   [1024,2048) V codes, 64 chunks of 16 bytes.  Chunk 16a + b holds tokens
+ *               4a..4a+3, channels j with (j&15)==b: word 2((j>>4)>>2) +
+ *               ((t&3)>>1), field at bit 16(t&1) + 4((j>>4)&3).
+ *   [2048,2560) K scale, K zero, V scale, V zero: the INT2 block's
+ *               [1024,1536) layout moved up by 1024 bytes.
  * The caller zero-fills hist when it allocates it; afterwards every byte of
  * a block is either zero or written by this library.  (Decode reads whole
  * pages and relies on the metadata of not-yet-written slots being finite.)
@@ -76,7 +89,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 3
+#define OSCAR_ABI_VERSION 4
 
 typedef enum {
   OSCAR_OK = 0,
@@ -103,7 +116,8 @@ typedef struct {
   void* sink_v;
   void* recent_k;              /* device bf16, layout above                  */
   void* recent_v;
-  uint8_t* hist;               /* device, [num_pages][Hkv][1536]             */
+  uint8_t* hist;               /* device, [num_pages][Hkv][1536] (INT2) or
+                                  [num_pages][Hkv][2560] (INT4)              */
   const int32_t* page_table;   /* device, [n_slots][max_pages_per_seq]       */
   int32_t n_slots;
   int32_t max_pages_per_seq;
@@ -112,6 +126,8 @@ typedef struct {
   const float* rot_v;          /* device fp32 [128][128]: R_V                */
   const float* clip_k;         /* device fp32 [128]: per rotated channel     */
   const float* clip_v;         /*   clip thresholds, 0 < tau <= 65504        */
+  int32_t code_bits;           /* 2: INT2 history (1536-byte blocks); 4: INT4
+                                  (2560-byte blocks, see above)              */
   int32_t rot_per_kv_head;     /* 0: the four arrays above are the layer's,
                                   shared by every KV head.  1: one per KV
                                   head, rot_k/rot_v [Hkv][128][128] and

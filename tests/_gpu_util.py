@@ -32,7 +32,8 @@ class Layer:
     """Seeded synthetic layer: B sequences of up to max_len tokens (bf16 bits)."""
 
     def __init__(self, seed, batch, hq, hkv, max_len, n_q=1, tau_tokens=4096, shuffle=True, extra_pages=0,
-                 per_kv_head=False):
+                 per_kv_head=False, code_bits=2):
+        self.code_bits = code_bits
         st = synth.streams(seed)
         self.batch, self.hq, self.hkv, self.max_len = batch, hq, hkv, max_len
         out = synth.outlier_channels(st["outliers"])
@@ -61,11 +62,11 @@ class Layer:
 
     def device_pool(self, n_slots=None):
         return TieredKV(self.hq, self.hkv, n_slots or self.batch, self.max_pages, self.num_pages, self.r_k, self.r_v,
-                        self.tau_k, self.tau_v, page_table=self.page_table)
+                        self.tau_k, self.tau_v, page_table=self.page_table, code_bits=self.code_bits)
 
     def oracle_pool(self, lengths, kv_heads=None):
         """Oracle pool after each sequence b has taken lengths[b] tokens."""
-        pool = orc.Pool(self.batch, self.hkv, self.num_pages, self.page_table)
+        pool = orc.Pool(self.batch, self.hkv, self.num_pages, self.page_table, bits=self.code_bits)
         heads = list(range(self.hkv)) if kv_heads is None else list(kv_heads)
         for b, n in enumerate(lengths):
             ns = min(n, 64)

@@ -43,7 +43,7 @@ def test_status_strings(lib):
 def _null_pool(n_slots=1, max_pages=4):
     # Non-null dummy pointers: validation must fail on something else first.
     one = 256
-    return binding.Pool(one, one, one, one, one, one, n_slots, max_pages, 8, one, one, one, one)
+    return binding.Pool(one, one, one, one, one, one, n_slots, max_pages, 8, one, one, one, one, 2)
 
 
 def test_validation_rejects_bad_shapes_without_launching(lib):
@@ -299,6 +299,12 @@ def test_calibration_scope_and_pool_flag_validation(lib):
     pool = _null_pool()
     pool.rot_per_kv_head = 2
     good = binding.layer_desc(32, 8)
+    assert lib.oscar_append(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 1, None) == -1
+    pool = _null_pool()
+    pool.code_bits = 3                                   # only INT2 and INT4 pools
+    assert lib.oscar_append(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 1, None) == -2
+    pool = _null_pool()
+    pool.rot_per_kv_head = 2
     assert lib.oscar_append(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 1, None) == -1
     assert lib.oscar_decode(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 256, 1 << 30, 1, 100,
                             None) == -1
