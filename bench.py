@@ -33,12 +33,17 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "INT2 decode-attn µs/step + HBM GB/s (% roofline) at 32K–128K ctx; demote tok/s"
 
 
-def decode_bytes(lengths, hq, hkv):
+def hist_token_bytes(code_bits=2):
+    """History bytes per token per KV head, K + V codes and metadata: INT2 96, INT4 160."""
+    return 2 * (128 * code_bits // 8) + 2 * 16
+
+
+def decode_bytes(lengths, hq, hkv, code_bits=2):
     """Algorithmic HBM bytes of one oscar_decode call (see the design notes)."""
     total = 0
     for n in lengths:
         hist = max(0, n - 320)
-        total += hist * hkv * 96 + min(n, 320) * hkv * 512 + 4 * math.ceil(hist / 16)
+        total += hist * hkv * hist_token_bytes(code_bits) + min(n, 320) * hkv * 512 + 4 * math.ceil(hist / 16)
     total += len(lengths) * hq * 128 * (2 + 4) + 2 * 128 * 128 * 4
     return total
 
@@ -94,7 +99,7 @@ class Timer:
         return 1000.0 * sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
 
 
-def build_layers(torch, hq, hkv, n0, n_layers, steps_per_layer, seed, calib_tokens=4096, calib=None):
+def build_layers(torch, hq, hkv, n0, n_layers, steps_per_layer, seed, calib_tokens=4096, calib=None, code_bits=2):
     """n_layers distinct pools holding the same seeded context of n0 tokens.
     calib: (rot_k, rot_v, tau_k, tau_v) to reuse; default: oscar_calibrate."""
     from bit_rotated_kv_demote_amd import binding, synth
@@ -126,7 +131,7 @@ def build_layers(torch, hq, hkv, n0, n_layers, steps_per_layer, seed, calib_toke
     vd = bf16_tensor(v[None, :n0])
     for li in range(n_layers):
         pt = synth.page_permutation(np.random.default_rng(seed * 100 + li), max_pages)[None, :]
-        pool = TieredKV(hq, hkv, 1, max_pages, max_pages, *calib, page_table=pt)
+        pool = TieredKV(hq, hkv, 1, max_pages, max_pages, *calib, page_table=pt, code_bits=code_bits)
         pool.prefill(torch.tensor([n0], dtype=torch.int32, device="cuda"), kd, vd)
         layers.append(pool)
     new_k = bf16_tensor(np.ascontiguousarray(k[n0:]))    # [steps, Hkv, 128]
@@ -137,11 +142,12 @@ def build_layers(torch, hq, hkv, n0, n_layers, steps_per_layer, seed, calib_toke
     return layers, new_k, new_v, q, calib_s, (k, v) + tuple(calib)
 
 
-def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None):
+def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None, code_bits=2):
     """Time exactly `steps` append+decode steps cycling through n_layers pools,
     then as many again with HIP events around every launch (kernel durations)."""
     rounds = math.ceil((warmup + 2 * steps) / n_layers)
-    layers, new_k, new_v, q, calib_s, host = build_layers(torch, hq, hkv, n0, n_layers, rounds, seed, calib=calib)
+    layers, new_k, new_v, q, calib_s, host = build_layers(torch, hq, hkv, n0, n_layers, rounds, seed, calib=calib,
+                                                          code_bits=code_bits)
     positions = torch.arange(n0, n0 + rounds, dtype=torch.int32, device="cuda")
     lens = positions + 1
     max_len = n0 + rounds
@@ -181,7 +187,7 @@ def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None):
     pool_bytes = sum(p.hist.numel() + 4 * p.sink_k.numel() + 4 * p.recent_k.numel() for p in layers)
     mid_len = n0 + (warmup + steps) // n_layers + 1
     return dict(total_ms=total_ms, us_per_step=1000.0 * total_ms / steps, decode_us=t_dec.mean_us(),
-                append_us=t_app.mean_us(), decode_bytes=decode_bytes([mid_len], hq, hkv), layers=n_layers,
+                append_us=t_app.mean_us(), decode_bytes=decode_bytes([mid_len], hq, hkv, code_bits), layers=n_layers,
                 pool_mb=pool_bytes / 1e6, calib_s=calib_s, host=host, n_mid=mid_len, max_len=max_len)
 
 
@@ -229,15 +235,15 @@ def _seq_kv(hkv, n, seed):
             synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out))
 
 
-def _int2_pool(torch, hq, hkv, lengths, k1, v1, calib, seed, chunk=4):
-    """INT2 tiered pool holding len(lengths) sequences; sequence b holds the first
-    lengths[b] tokens of the seeded sequence (k1, v1); shuffled page table."""
+def _int2_pool(torch, hq, hkv, lengths, k1, v1, calib, seed, chunk=4, code_bits=2):
+    """INT2 (or INT4) tiered pool holding len(lengths) sequences; sequence b holds
+    the first lengths[b] tokens of the seeded sequence (k1, v1); shuffled page table."""
     from bit_rotated_kv_demote_amd import synth
     from bit_rotated_kv_demote_amd.pool import TieredKV, bf16_tensor
     B = len(lengths)
     max_pages = max(1, math.ceil((max(lengths) + 1 - 320) / 16))
     perm = synth.page_permutation(np.random.default_rng(seed), B * max_pages).reshape(B, max_pages)
-    pool = TieredKV(hq, hkv, B, max_pages, B * max_pages, *calib, page_table=perm)
+    pool = TieredKV(hq, hkv, B, max_pages, B * max_pages, *calib, page_table=perm, code_bits=code_bits)
     kd, vd = bf16_tensor(k1), bf16_tensor(v1)
     for b0 in range(0, B, chunk):
         bs = list(range(b0, min(B, b0 + chunk)))
@@ -321,21 +327,33 @@ def run_fixed_memory(torch, steps, calib, seed=1004, layers=36, budget_gb=64.0, 
     from bit_rotated_kv_demote_amd.pool import bf16_tensor
     hq, hkv = 32, 8
     per_layer = budget_gb * 1e9 / layers
-    int2_seq = (n - 320) * hkv * 96 + 320 * hkv * 512
+    int2_seq = (n - 320) * hkv * hist_token_bytes(2) + 320 * hkv * 512
+    int4_seq = (n - 320) * hkv * hist_token_bytes(4) + 320 * hkv * 512
     bf16_seq = n * hkv * 512
     max_int2, max_bf16 = int(per_layer // int2_seq), int(per_layer // bf16_seq)
+    max_int4 = int(per_layer // int4_seq)
     st = synth.streams(seed)
     k1, v1 = _seq_kv(hkv, n, seed)
     q_all = bf16_tensor(synth.queries(st["q"], (max_int2, hq, 128)))
-    batches = sorted({b for b in (1, 2, 4, 8, 16, 32, 64, 128) if b <= max_int2} | {max_int2, max_bf16})
+    batches = sorted({b for b in (1, 2, 4, 8, 16, 32, 64, 128) if b <= max_int2} | {max_int2, max_int4, max_bf16})
     res = {"workload": f"32 q / 8 KV heads, {n} tokens per sequence, {budget_gb:g} GB over {layers} layers "
                        f"= {per_layer / 1e9:.3f} GB per layer",
-           "max_batch_int2": max_int2, "max_batch_bf16": max_bf16, "int2_tok_per_s": {}, "bf16_tok_per_s": {}}
+           "max_batch_int2": max_int2, "max_batch_int4": max_int4, "max_batch_bf16": max_bf16,
+           "int2_tok_per_s": {}, "int4_tok_per_s": {}, "bf16_tok_per_s": {}}
     pool = _int2_pool(torch, hq, hkv, [n] * max_int2, k1, v1, calib, seed)
     for b in batches:
         lens = torch.full((b,), n, dtype=torch.int32, device="cuda")
         us = _time_decode(torch, pool, q_all[:b], lens, n, steps)
         res["int2_tok_per_s"][str(b)] = round(b / (us * 1e-6), 1)
+    del pool
+    torch.cuda.empty_cache()
+    pool = _int2_pool(torch, hq, hkv, [n] * max_int4, k1, v1, calib, seed, code_bits=4)
+    for b in batches:
+        if b > max_int4:
+            continue
+        lens = torch.full((b,), n, dtype=torch.int32, device="cuda")
+        us = _time_decode(torch, pool, q_all[:b], lens, n, steps)
+        res["int4_tok_per_s"][str(b)] = round(b / (us * 1e-6), 1)
     del pool
     torch.cuda.empty_cache()
     bpool = _bf16_pool(torch, hq, hkv, max_bf16, n, k1, v1, seed + 1)
@@ -349,6 +367,8 @@ def run_fixed_memory(torch, steps, calib, seed=1004, layers=36, budget_gb=64.0, 
     torch.cuda.empty_cache()
     res["throughput_ratio_at_max_batch"] = round(res["int2_tok_per_s"][str(max_int2)] /
                                                  res["bf16_tok_per_s"][str(max_bf16)], 3)
+    res["int2_vs_int4_at_max_batch"] = round(res["int2_tok_per_s"][str(max_int2)] /
+                                             res["int4_tok_per_s"][str(max_int4)], 3)
     return res
 
 
@@ -509,7 +529,7 @@ def run_rotation_study(torch, seed=1006, hq=32, hkv=8, n_calib=1024, n_ctx=8192,
                       "rel_l2_vs_bf16_attention": scope_errs, "calibrate_host_s": scope_s}}
 
 
-def run_demote(torch, reps, seed):
+def run_demote(torch, reps, seed, code_bits=2):
     """Bulk demotion of a 4096-token chunk for 16 sequences x 8 KV heads."""
     from bit_rotated_kv_demote_amd import synth
     from bit_rotated_kv_demote_amd.pool import TieredKV, bf16_tensor
@@ -523,7 +543,8 @@ def run_demote(torch, reps, seed):
     tau = np.full(128, 64.0, np.float32)
     max_pages = 4096 // 16 + 2
     pt = synth.page_permutation(st["perm"], batch * max_pages).reshape(batch, max_pages)
-    pool = TieredKV(hq, hkv, batch, max_pages, batch * max_pages, rot, rot, tau, tau, page_table=pt)
+    pool = TieredKV(hq, hkv, batch, max_pages, batch * max_pages, rot, rot, tau, tau, page_table=pt,
+                    code_bits=code_bits)
     starts = torch.tensor(synth.ragged_lengths(st["lengths"], batch, 0, 15), dtype=torch.int32, device="cuda")
     kd, vd = bf16_tensor(k), bf16_tensor(v)
     pool.demote(starts, kd, vd)
@@ -537,7 +558,7 @@ def run_demote(torch, reps, seed):
     torch.cuda.synchronize()
     us = t.mean_us()
     tokens = batch * chunk
-    nbytes = tokens * hkv * (2 * 256 + 96)
+    nbytes = tokens * hkv * (2 * 256 + hist_token_bytes(code_bits))
     return dict(us=us, tok_per_s=tokens / (us * 1e-6), gbps=nbytes / (us * 1e3), tokens=tokens, bytes=nbytes)
 
 
@@ -716,6 +737,21 @@ def main():
         extra["demote_us_per_chunk"] = round(d["us"], 2)
         extra["demote_GBps"] = round(d["gbps"], 1)
         extra["demote_workload"] = "16 sequences x 4096-token chunk, 8 KV heads, K+V, bf16 in, MFMA rotation"
+        # INT4 variant of the pool: the same step, the 128K decode and bulk demotion
+        r4 = run_tiered(torch, hq, hkv, n0, args.layers, min(args.steps, 200), args.warmup, seed=1001,
+                        calib=res["host"][2:], code_bits=4)
+        r4_128 = run_tiered(torch, hq, hkv, 131072, 8, min(args.steps, 160), 8, seed=1002, calib=res["host"][2:],
+                            code_bits=4)
+        d4 = run_demote(torch, 20, 1004, code_bits=4)
+        extra["int4"] = {"us_per_step": round(r4["us_per_step"], 3), "decode_call_us": round(r4["decode_us"], 3),
+                         "append_kernel_us": round(r4["append_us"], 3),
+                         "decode_algorithmic_bytes": r4["decode_bytes"],
+                         "decode_GBps": round(r4["decode_bytes"] / (r4["decode_us"] * 1e3), 1),
+                         "int2_vs_int4_decode_speedup": round(r4["decode_us"] / res["decode_us"], 3),
+                         "ctx128k_decode_call_us": round(r4_128["decode_us"], 3),
+                         "ctx128k_decode_GBps": round(r4_128["decode_bytes"] / (r4_128["decode_us"] * 1e3), 1),
+                         "demote_tok_per_s": round(d4["tok_per_s"], 0), "demote_us_per_chunk": round(d4["us"], 2)}
+        del r4, r4_128
     if args.copy_probe_mb:
         # a plain streaming kernel of known size (reads and writes n bytes once):
         # the counter calibration for the traffic figure
