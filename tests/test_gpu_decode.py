@@ -120,6 +120,59 @@ def test_decode_ragged_batch_gqa8_shuffled_pages():
     assert rel_l2(out, ref) <= TOL
 
 
+def test_decode_ragged_gqa8_full_size_sampled_heads():
+    # The ragged Qwen3-32B-shaped workload at full size, in the launch
+    # configuration the bench times: 64 q / 8 KV heads, 16 sequences with
+    # seeded lengths U[8192, 65536], each a prefix of one seeded token stream,
+    # shuffled pages.  The device prefills and decodes the whole batch; the
+    # oracle's bytes replace the device's for two KV heads, and their 16 query
+    # heads are checked on four sequences (the longest, the shortest and two
+    # others; the oracle's share stays at seconds).
+    from bit_rotated_kv_demote_amd.pool import TieredKV
+    hq, hkv, B, kv_heads = 64, 8, 16, [2, 7]
+    st = synth.streams(1005)
+    lengths = [int(x) for x in synth.ragged_lengths(st["lengths"], B, 8192, 65536)]
+    n_max = max(lengths)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n_max, hkv, out_ch)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n_max, hkv, out_ch)
+    rot = synth.random_rotation(st["rot"])
+    tau_k = orc.clip_thresholds(synth.bf16_bits_to_f32(k[:4096]), rot)
+    tau_v = orc.clip_thresholds(synth.bf16_bits_to_f32(v[:4096]), rot)
+    max_pages = math.ceil((n_max - 320) / 16)
+    pt = synth.page_permutation(st["perm"], B * max_pages).reshape(B, max_pages).astype(np.int32)
+    dev = TieredKV(hq, hkv, B, max_pages, B * max_pages, rot, rot, tau_k, tau_v, page_table=pt)
+    kd, vd = bf16_tensor(k), bf16_tensor(v)
+    for b0 in range(0, B, 4):
+        bs = list(range(b0, b0 + 4))
+        n = max(lengths[b] for b in bs)
+        dev.prefill(i32([lengths[b] for b in bs]), kd[None, :n].expand(4, -1, -1, -1).contiguous(),
+                    vd[None, :n].expand(4, -1, -1, -1).contiguous(), seq_slot=i32(bs))
+    del kd, vd
+    checked = sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), 0, 5})
+    opool = orc.Pool(B, hkv, B * max_pages, pt)
+    for b in checked:
+        n = lengths[b]
+        opool.sink_k[b] = k[:64].transpose(1, 0, 2)
+        opool.sink_v[b] = v[:64].transpose(1, 0, 2)
+        pos = np.arange(n - 256, n)
+        opool.recent_k[b][:, (pos - 64) % 256] = k[pos].transpose(1, 0, 2)
+        opool.recent_v[b][:, (pos - 64) % 256] = v[pos].transpose(1, 0, 2)
+        h = np.arange(n - 320)
+        opool.demote_many(b, h, k[64 + h][:, kv_heads], v[64 + h][:, kv_heads], rot, rot, tau_k, tau_v,
+                          kv_heads=kv_heads)
+        opool.length[b] = n
+    # (the unchecked sequences' blocks of these heads become zeros: their
+    # outputs are computed but not compared)
+    upload(dev, opool, kv_heads)
+    q = synth.queries(st["q"], (B, hq, 128))
+    out = dev.decode(bf16_tensor(q), i32(lengths), n_max).cpu().numpy()
+    heads = [(b, h) for b in checked for h in range(hq) if h // 8 in kv_heads]
+    ref = orc.decode_tiered(q, opool, list(range(B)), lengths, rot, rot, heads=heads)
+    idx = tuple(np.array(heads).T)
+    assert rel_l2(out[idx], ref[idx]) <= TOL
+
+
 def test_decode_qwen3_4b_32k_sampled_heads():
     # Full size of the 32K workload, in the bench's launch configuration:
     # 32 q / 8 KV heads, 32768 cached tokens + the appended one.
