@@ -173,6 +173,50 @@ def test_decode_ragged_gqa8_full_size_sampled_heads():
     assert rel_l2(out[idx], ref[idx]) <= TOL
 
 
+def test_decode_fixed_memory_max_batch_sampled():
+    # The fixed-memory workload's largest INT2 batch: 130 sequences of 16384
+    # tokens (32 q / 8 KV heads), 4160 merged heads (the per-record-group
+    # merge), all sequences prefixes of one seeded stream, shuffled pages.
+    # The oracle's bytes replace the device's for two KV heads; three
+    # sequences are checked.
+    from bit_rotated_kv_demote_amd.pool import TieredKV
+    hq, hkv, B, n, kv_heads = 32, 8, 130, 16384, [1, 6]
+    st = synth.streams(1004)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out_ch)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out_ch)
+    rot = synth.random_rotation(st["rot"])
+    tau_k = orc.clip_thresholds(synth.bf16_bits_to_f32(k[:4096]), rot)
+    tau_v = orc.clip_thresholds(synth.bf16_bits_to_f32(v[:4096]), rot)
+    max_pages = math.ceil((n - 320) / 16)
+    pt = synth.page_permutation(st["perm"], B * max_pages).reshape(B, max_pages).astype(np.int32)
+    dev = TieredKV(hq, hkv, B, max_pages, B * max_pages, rot, rot, tau_k, tau_v, page_table=pt)
+    kd = bf16_tensor(k)[None].expand(10, -1, -1, -1).contiguous()
+    vd = bf16_tensor(v)[None].expand(10, -1, -1, -1).contiguous()
+    for b0 in range(0, B, 10):
+        dev.prefill(i32([n] * 10), kd, vd, seq_slot=i32(list(range(b0, b0 + 10))))
+    del kd, vd
+    checked = [0, 77, 129]
+    opool = orc.Pool(B, hkv, B * max_pages, pt)
+    h = np.arange(n - 320)
+    pos = np.arange(n - 256, n)
+    for b in checked:
+        opool.sink_k[b] = k[:64].transpose(1, 0, 2)
+        opool.sink_v[b] = v[:64].transpose(1, 0, 2)
+        opool.recent_k[b][:, (pos - 64) % 256] = k[pos].transpose(1, 0, 2)
+        opool.recent_v[b][:, (pos - 64) % 256] = v[pos].transpose(1, 0, 2)
+        opool.demote_many(b, h, k[64 + h][:, kv_heads], v[64 + h][:, kv_heads], rot, rot, tau_k, tau_v,
+                          kv_heads=kv_heads)
+        opool.length[b] = n
+    upload(dev, opool, kv_heads)
+    q = synth.queries(st["q"], (B, hq, 128))
+    out = dev.decode(bf16_tensor(q), i32([n] * B), n).cpu().numpy()
+    heads = [(b, hh) for b in checked for hh in range(hq) if hh // 4 in kv_heads]
+    ref = orc.decode_tiered(q, opool, list(range(B)), [n] * B, rot, rot, heads=heads)
+    idx = tuple(np.array(heads).T)
+    assert rel_l2(out[idx], ref[idx]) <= TOL
+
+
 def test_decode_qwen3_4b_32k_sampled_heads():
     # Full size of the 32K workload, in the bench's launch configuration:
     # 32 q / 8 KV heads, 32768 cached tokens + the appended one.
