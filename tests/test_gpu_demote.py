@@ -134,3 +134,44 @@ def test_prefill_ragged_matches_oracle():
         sl.append(h % 16)
     rate, maxd, meta_ulp = code_diff_stats(st["hist"], ref.hist, np.concatenate(pages), np.concatenate(sl))
     assert rate <= FLIP_RATE and maxd <= 1 and meta_ulp <= 2, (rate, maxd, meta_ulp)
+
+
+@pytest.mark.parametrize("code_bits", [2, 4])
+def test_bulk_demotion_full_size_sampled(code_bits):
+    # The bulk-demotion workload at full size, one launch: 16 sequences x
+    # 4096 tokens x 8 KV heads, bf16 in, seeded mid-page starts, shuffled
+    # fresh pages.  Three sequences are compared with the oracle (all heads,
+    # K and V) within the fused-rotation budget; the rest of the pool is
+    # untouched outside the demoted pages.
+    import math
+    from bit_rotated_kv_demote_amd.pool import TieredKV
+    batch, chunk, hkv, hq = 16, 4096, 8, 64
+    st = synth.streams(1004)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], batch * chunk, hkv, out_ch).reshape(batch, chunk, hkv, 128)
+    v = synth.kv_tokens(st["v"], st["lognormal"], batch * chunk, hkv, out_ch).reshape(batch, chunk, hkv, 128)
+    rot = synth.random_rotation(st["rot"])
+    tau_k = orc.clip_thresholds(synth.bf16_bits_to_f32(k[0, :2048]), rot)
+    tau_v = orc.clip_thresholds(synth.bf16_bits_to_f32(v[0, :2048]), rot)
+    max_pages = chunk // 16 + 2
+    pt = synth.page_permutation(st["perm"], batch * max_pages).reshape(batch, max_pages).astype(np.int32)
+    starts = [int(x) for x in synth.ragged_lengths(st["lengths"], batch, 0, 15)]
+    dev = TieredKV(hq, hkv, batch, max_pages, batch * max_pages, rot, rot, tau_k, tau_v, page_table=pt,
+                   code_bits=code_bits)
+    dev.demote(i32(starts), bf16_tensor(k), bf16_tensor(v))
+    torch.cuda.synchronize()
+    got = dev.hist.cpu().numpy()
+    checked = [0, 7, 15]
+    ref = orc.Pool(batch, hkv, batch * max_pages, pt, bits=code_bits)
+    pages, slots = [], []
+    for b in checked:
+        h = starts[b] + np.arange(chunk)
+        ref.demote_many(b, h, k[b], v[b], rot, rot, tau_k, tau_v)
+        pages.append(pt[b, h // 16])
+        slots.append(h % 16)
+    rate, maxd, meta_ulp = code_diff_stats(got, ref.hist, np.concatenate(pages), np.concatenate(slots))
+    assert rate <= FLIP_RATE and maxd <= 1 and meta_ulp <= 2, (rate, maxd, meta_ulp)
+    used = np.zeros(got.shape[0], bool)
+    for b in range(batch):
+        used[pt[b, (starts[b] + np.arange(chunk)) // 16]] = True
+    assert not got[~used].any()
