@@ -46,11 +46,13 @@ def test_per_head_demote_from_rotated_fp32_is_bit_exact():
     assert np.array_equal(got, ref.hist), f"{np.count_nonzero(got != ref.hist)} bytes differ"
 
 
-def test_per_head_prefill_and_append_within_flip_budget():
+@pytest.mark.parametrize("code_bits", [2, 4])
+def test_per_head_prefill_and_append_within_flip_budget(code_bits):
     # prefill (bulk demotion, one R per KV head staged per workgroup slice),
     # then appends that demote one token per step (per-token rotation)
     lengths, n_app = [700, 333, 1000], 40
-    layer = Layer(seed=1301, batch=3, hq=16, hkv=8, max_len=max(lengths) + n_app, per_kv_head=True)
+    layer = Layer(seed=1301, batch=3, hq=16, hkv=8, max_len=max(lengths) + n_app, per_kv_head=True,
+                  code_bits=code_bits)
     dev = layer.device_pool()
     dev.prefill(i32(lengths), bf16_tensor(np.ascontiguousarray(layer.k[:, :max(lengths)])),
                 bf16_tensor(np.ascontiguousarray(layer.v[:, :max(lengths)])))
@@ -73,10 +75,11 @@ def test_per_head_prefill_and_append_within_flip_budget():
     assert rate <= FLIP_RATE and maxd <= 1 and meta_ulp <= 2, (rate, maxd, meta_ulp)
 
 
-@pytest.mark.parametrize("n_query", [1, 4])
-def test_per_head_decode_matches_oracle(n_query):
+@pytest.mark.parametrize("n_query,code_bits", [(1, 2), (4, 2), (1, 4), (4, 4)])
+def test_per_head_decode_matches_oracle(n_query, code_bits):
     lengths = [1500, 420]
-    layer = Layer(seed=1310 + n_query, batch=2, hq=8, hkv=2, max_len=max(lengths), per_kv_head=True)
+    layer = Layer(seed=1310 + n_query, batch=2, hq=8, hkv=2, max_len=max(lengths), per_kv_head=True,
+                  code_bits=code_bits)
     opool = layer.oracle_pool(lengths)
     dev = layer.device_pool()
     upload(dev, opool)
