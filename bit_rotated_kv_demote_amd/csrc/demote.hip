@@ -86,10 +86,21 @@ __device__ void quantize_pack_channel_per_thread(float yc, bool is_v, uint8_t* b
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ float xs[kD];
-  __shared__ float part[2][kD];
+  __shared__ float part[4][kD];
   __shared__ uint32_t sh[32];
   const int b = blockIdx.x, hk = blockIdx.y, is_v = blockIdx.z;
   const int tid = threadIdx.x;
+  // y_j = sum_i x_i R[i][j].  The rotation's operands do not depend on the
+  // position, so they are requested first: thread (c4, rs) takes columns
+  // [4 c4, 4 c4 + 4) and rows [16 rs, 16 rs + 16) of R (16 float4 loads).
+  // (Unused when the token only enters the sink or a free ring slot.)
+  const int c4 = tid & 31, rs = tid >> 5;
+  const float* R = (is_v ? a.rot_v : a.rot_k) + (size_t)hk * a.rot_kv_stride;
+  float4 rq[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(R + (size_t)(16 * rs + e) * kD + 4 * c4);
+  const float* tau = (is_v ? a.clip_v : a.clip_k) + (size_t)hk * a.clip_kv_stride;
+  const float tau_j = tau[tid & (kD - 1)];
   const int slot = a.seq_slot ? a.seq_slot[b] : b;
   const int p = a.position[b];
   const uint16_t* src = (is_v ? a.v_new : a.k_new) + ((size_t)b * a.hkv + hk) * kD;
@@ -101,32 +112,34 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int r = (p - kSink) & (kRecent - 1);
   uint16_t* ring = (is_v ? a.recent_v : a.recent_k) + (((size_t)slot * a.hkv + hk) * kRecent + r) * kD;
   if (p >= kSink + kRecent) {
-    // y_j = sum_i x_i R[i][j]; thread (j, half) covers i in [64 half, 64 half + 64).
-    // Its 64 R values are requested together with the ring slot.
-    const float* R = (is_v ? a.rot_v : a.rot_k) + (size_t)hk * a.rot_kv_stride;
-    const int j = tid & (kD - 1), half = tid >> 7;
-    // the page id of the demoted token and the clip threshold depend only on
-    // the position: their loads go out with R's, not after the product
+    // the token leaving the ring (position p - 256) goes to history index h
     const int h = p - kSink - kRecent;
     const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
-    const float* tau = (is_v ? a.clip_v : a.clip_k) + (size_t)hk * a.clip_kv_stride;
-    const float tau_j = tau[j];
-    float rc[64];
-#pragma unroll
-    for (int e = 0; e < 64; ++e) rc[e] = R[(64 * half + e) * kD + j];
     if (tid < kD / 2) {
       const uint32_t w = reinterpret_cast<const uint32_t*>(ring)[tid];
       xs[2 * tid] = bf16_bits_to_float(w & 0xFFFFu);
       xs[2 * tid + 1] = bf16_bits_to_float(w >> 16);
     }
     __syncthreads();
-    float acc = 0.0f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int e = 0; e < 64; ++e) acc = fmaf(xs[64 * half + e], rc[e], acc);
-    part[half][j] = acc;
+    for (int e = 0; e < 16; ++e) {
+      const float xe = xs[16 * rs + e];
+      acc.x = fmaf(xe, rq[e].x, acc.x);
+      acc.y = fmaf(xe, rq[e].y, acc.y);
+      acc.z = fmaf(xe, rq[e].z, acc.z);
+      acc.w = fmaf(xe, rq[e].w, acc.w);
+    }
+    // lanes l and l + 32 of a wave hold row slices 2w and 2w + 1 of the same
+    // columns: one lane swap, then the four waves' sums through LDS
+    acc.x += __shfl_xor(acc.x, 32);
+    acc.y += __shfl_xor(acc.y, 32);
+    acc.z += __shfl_xor(acc.z, 32);
+    acc.w += __shfl_xor(acc.w, 32);
+    if ((tid & 32) == 0) *reinterpret_cast<float4*>(&part[tid >> 6][4 * c4]) = acc;
     __syncthreads();  // also orders the ring read above before the overwrite below
     float yc = 0.0f;
-    if (tid < kD) yc = clip_value(part[0][tid] + part[1][tid], tau_j);
+    if (tid < kD) yc = clip_value((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]), tau_j);
     uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(a.code_bits);
     quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh, a.code_bits);
   }
