@@ -1,8 +1,10 @@
 """Benchmark of the OSCAR-style INT2 tiered decode step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: oscar_append (route
-the new token; demote the ring slot it reuses: rotate, clip, quantise, pack)
-followed by oscar_decode (tiered decode attention).  The default workload is
+A step is one pass of the whole hot path over one batch: the append of the
+new token (route it; demote the ring slot it reuses: rotate, clip, quantise,
+pack) followed by tiered decode attention, as one oscar_step call (the
+append launch also computes q . R_K for the decode).  The same steps as
+separate oscar_append + oscar_decode calls are timed beside it.  The default workload is
 the Qwen3-4B-shaped layer: 32 q / 8 KV heads, head_dim 128, batch 1, 32768
 cached tokens (64 BF16 sink + INT2 history + 256 BF16 recent, 16-token pages),
 seeded synthetic K/V/q, R and clip thresholds from oscar_calibrate on 4096
@@ -142,10 +144,13 @@ def build_layers(torch, hq, hkv, n0, n_layers, steps_per_layer, seed, calib_toke
     return layers, new_k, new_v, q, calib_s, (k, v) + tuple(calib)
 
 
-def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None, code_bits=2):
-    """Time exactly `steps` append+decode steps cycling through n_layers pools,
-    then as many again with HIP events around every launch (kernel durations)."""
-    rounds = math.ceil((warmup + 2 * steps) / n_layers)
+def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None, code_bits=2, fused=True):
+    """Time exactly `steps` decode steps cycling through n_layers pools (fused:
+    oscar_step, append and decode in one call; else oscar_append then
+    oscar_decode), then as many again as separate calls with HIP events around
+    every call (append and decode-call durations), then as many fused steps
+    with events around every call."""
+    rounds = math.ceil((warmup + 4 * steps) / n_layers)
     layers, new_k, new_v, q, calib_s, host = build_layers(torch, hq, hkv, n0, n_layers, rounds, seed, calib=calib,
                                                           code_bits=code_bits)
     positions = torch.arange(n0, n0 + rounds, dtype=torch.int32, device="cuda")
@@ -154,6 +159,13 @@ def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None, co
     outs = [torch.empty((1, hq, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
     for pool in layers:
         pool.workspace(1, max_len)
+
+    def fused_step(i, t_step=None):
+        li, r = i % n_layers, i // n_layers
+        s = t_step.start() if t_step else None
+        layers[li].step(positions[r:r + 1], new_k[r:r + 1], new_v[r:r + 1], q[r], max_len, out=outs[i & 1])
+        if t_step:
+            t_step.stop(s)
 
     def step(i, t_dec=None, t_app=None):
         li, r = i % n_layers, i // n_layers
@@ -167,26 +179,41 @@ def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None, co
         if t_dec:
             t_dec.stop(s)
 
+    run = fused_step if fused else step
     for i in range(warmup):
-        step(i)
+        run(i)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     gpu_hold(torch, 20 + 0.1 * steps)
     e0.record()
     for i in range(warmup, warmup + steps):
-        step(i)
+        run(i)
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
-    t_dec, t_app = Timer(torch), Timer(torch)
-    gpu_hold(torch, 20 + 0.2 * steps)
+    # the same number of steps as separate oscar_append + oscar_decode calls
+    torch.cuda.synchronize()
+    gpu_hold(torch, 20 + 0.1 * steps)
+    e0.record()
     for i in range(warmup + steps, warmup + 2 * steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    separate_ms = e0.elapsed_time(e1)
+    t_dec, t_app, t_step = Timer(torch), Timer(torch), Timer(torch)
+    gpu_hold(torch, 20 + 0.2 * steps)
+    for i in range(warmup + 2 * steps, warmup + 3 * steps):
         step(i, t_dec, t_app)
+    torch.cuda.synchronize()
+    gpu_hold(torch, 20 + 0.2 * steps)
+    for i in range(warmup + 3 * steps, warmup + 4 * steps):
+        fused_step(i, t_step)
     torch.cuda.synchronize()
     pool_bytes = sum(p.hist.numel() + 4 * p.sink_k.numel() + 4 * p.recent_k.numel() for p in layers)
     mid_len = n0 + (warmup + steps) // n_layers + 1
     return dict(total_ms=total_ms, us_per_step=1000.0 * total_ms / steps, decode_us=t_dec.mean_us(),
+                us_per_step_separate=1000.0 * separate_ms / steps, step_call_us=t_step.mean_us(),
                 append_us=t_app.mean_us(), decode_bytes=decode_bytes([mid_len], hq, hkv, code_bits), layers=n_layers,
                 pool_mb=pool_bytes / 1e6, calib_s=calib_s, host=host, n_mid=mid_len, max_len=max_len)
 
@@ -705,7 +732,10 @@ def main():
     hq, hkv, n0 = 32, 8, 32768
     res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001)
     dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
-    extra = {"decode_call_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),
+    extra = {"step_mode": "oscar_step (append + decode in one call; the append launch also computes q . R_K)",
+             "us_per_step_separate_calls": round(res["us_per_step_separate"], 3),
+             "step_call_us": round(res["step_call_us"], 3),
+             "decode_call_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),
              "decode_algorithmic_bytes": res["decode_bytes"], "decode_GBps": round(dec_gbps, 1),
              "pools": res["layers"], "pool_MB_total": round(res["pool_mb"], 1),
              "calibrate_host_s": round(res["calib_s"], 2)}
@@ -717,7 +747,9 @@ def main():
         del b
         r128 = run_tiered(torch, hq, hkv, 131072, 8, min(args.steps, 160), 8, seed=1002, calib=res["host"][2:])
         g128 = r128["decode_bytes"] / (r128["decode_us"] * 1e3)
-        extra["ctx128k"] = {"us_per_step": round(r128["us_per_step"], 3), "decode_call_us": round(r128["decode_us"], 3),
+        extra["ctx128k"] = {"us_per_step": round(r128["us_per_step"], 3),
+                            "us_per_step_separate_calls": round(r128["us_per_step_separate"], 3),
+                            "decode_call_us": round(r128["decode_us"], 3),
                             "append_kernel_us": round(r128["append_us"], 3), "decode_GBps": round(g128, 1),
                             "decode_frac_of_8TBps": round(g128 / HBM_PEAK_GBPS, 4),
                             "decode_algorithmic_bytes": r128["decode_bytes"], "pools": r128["layers"],
@@ -743,7 +775,9 @@ def main():
         r4_128 = run_tiered(torch, hq, hkv, 131072, 8, min(args.steps, 160), 8, seed=1002, calib=res["host"][2:],
                             code_bits=4)
         d4 = run_demote(torch, 20, 1004, code_bits=4)
-        extra["int4"] = {"us_per_step": round(r4["us_per_step"], 3), "decode_call_us": round(r4["decode_us"], 3),
+        extra["int4"] = {"us_per_step": round(r4["us_per_step"], 3),
+                         "us_per_step_separate_calls": round(r4["us_per_step_separate"], 3),
+                         "decode_call_us": round(r4["decode_us"], 3),
                          "append_kernel_us": round(r4["append_us"], 3),
                          "decode_algorithmic_bytes": r4["decode_bytes"],
                          "decode_GBps": round(r4["decode_bytes"] / (r4["decode_us"] * 1e3), 1),
@@ -776,7 +810,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int2-kv/fp32-acc",
         "data": "synthetic",
-        "config": {"workload": "qwen3-4b-shaped tiered decode step (append + decode): 32 q / 8 KV heads, "
+        "config": {"workload": "qwen3-4b-shaped tiered decode step (oscar_step: append + decode): 32 q / 8 KV heads, "
                                "head_dim 128, batch 1, 32768 cached tokens + 1 appended per step, "
                                "64 bf16 sink / int2 history / 256 bf16 recent, 16-token pages",
                    "global_batch": 1, "seq_len": n0, "parallelism": "single-gpu"},

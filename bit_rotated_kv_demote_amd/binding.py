@@ -21,7 +21,8 @@ ABI_VERSION = 4
 EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_calibrate_layers", "oscar_append", "oscar_demote",
             "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_multi",
             "oscar_decode_multi_workspace_bytes", "oscar_decode_bf16", "oscar_decode_bf16_workspace_bytes",
-            "oscar_decode_bf16_multi", "oscar_decode_bf16_multi_workspace_bytes")
+            "oscar_decode_bf16_multi", "oscar_decode_bf16_multi_workspace_bytes", "oscar_step",
+            "oscar_step_workspace_bytes")
 
 
 class OscarError(RuntimeError):
@@ -87,6 +88,10 @@ def load():
     lib.oscar_decode.argtypes = [P, P, P, P, P, P, P, SZ, I32, I32, P]
     lib.oscar_decode_workspace_bytes.restype = SZ
     lib.oscar_decode_workspace_bytes.argtypes = [P, I32, I32]
+    lib.oscar_step.restype = ctypes.c_int
+    lib.oscar_step.argtypes = [P, P, P, P, P, P, P, P, P, SZ, I32, I32, P]
+    lib.oscar_step_workspace_bytes.restype = SZ
+    lib.oscar_step_workspace_bytes.argtypes = [P, I32, I32]
     lib.oscar_decode_multi.restype = ctypes.c_int
     lib.oscar_decode_multi.argtypes = [P, P, P, P, P, I32, P, P, SZ, I32, I32, P]
     lib.oscar_decode_multi_workspace_bytes.restype = SZ
@@ -186,6 +191,17 @@ def oscar_decode(desc, pool, seq_slot, seq_len, q, out, workspace, batch, max_se
     _check("oscar_decode", load().oscar_decode(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_slot),
                                                 _ptr(seq_len), _ptr(q), _ptr(out), _ptr(workspace), ws_bytes,
                                                 batch, max_seq_len, _stream(stream)))
+
+
+def oscar_step_workspace_bytes(desc, batch, max_seq_len) -> int:
+    return int(load().oscar_step_workspace_bytes(ctypes.byref(desc), batch, max_seq_len))
+
+
+def oscar_step(desc, pool, seq_slot, position, k_new, v_new, q, out, workspace, batch, max_seq_len, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("oscar_step", load().oscar_step(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_slot), _ptr(position),
+                                            _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(workspace), ws_bytes,
+                                            batch, max_seq_len, _stream(stream)))
 
 
 def oscar_decode_multi_workspace_bytes(desc, batch, n_query, max_seq_len) -> int:

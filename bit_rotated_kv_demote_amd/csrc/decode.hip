@@ -396,7 +396,7 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
   }
 }
 
-template <int G, int kBits>
+template <int G, int kBits, bool kPreRot>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -426,7 +426,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
   float4 rq[16];
   uint32_t qv[kQPer];
   const float* rot_k = a.rot_k + (size_t)hk * a.rot_kv_stride;
-  if (!is_tile) {
+  // With q . R_K precomputed (the fused step), history splits read it
+  // (G rows of fp32) instead of R_K and q.
+  constexpr bool pre_rot = kPreRot;
+  constexpr int kQRPer = (G * kD + 255) / 256;
+  float qrv[kQRPer];
+  if constexpr (pre_rot) {
+   if (!is_tile) {
+#pragma unroll
+    for (int e = 0; e < kQRPer; ++e) {
+      const int idx = min(tid + 256 * e, G * kD - 1);
+      const int x = idx / kD, vh = cg * G + x, t = vh / a.g_model, h = vh - t * a.g_model;
+      qrv[e] = a.q_rot[(((size_t)b * a.q_tokens + t) * hq_total + hk * a.g_model + h) * kD + idx % kD];
+    }
+   }
+  }
+  if (!is_tile && !pre_rot) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
 #pragma unroll
@@ -484,6 +499,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
     // for its first iteration are exact)
     issue_step<kBits>(a, ids, hk, 0, lane, c_first, m_first);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (pre_rot) {
+#pragma unroll
+      for (int e = 0; e < kQRPer; ++e) {
+        const int idx = tid + 256 * e;
+        if (idx < G * kD) sm.qr[idx / kD][idx % kD] = qrv[e];
+      }
+      __syncthreads();
+    } else {
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {
       const int idx = tid + 256 * e;
@@ -523,6 +546,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
       sm.qr[h][jj] = (sm.wo[0][h][jj] + sm.wo[1][h][jj]) + (sm.wo[2][h][jj] + sm.wo[3][h][jj]);
     }
     __syncthreads();
+    }
     for (int h = wave; h < G; h += 4) {
       const float v0 = sm.qr[h][lane], v1 = sm.qr[h][lane + 64];
       const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1))) * kC0;
@@ -541,18 +565,19 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
 }
 
-template <int G>
+// kPreRot: q . R_K comes precomputed (the fused step) instead of R_K and q
+template <int G, bool kPreRot = false>
 __global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
-  decode_body<G, 2>(a, sm);
+  decode_body<G, 2, kPreRot>(a, sm);
 }
 
 // INT4 pool: the same kernel over 2560-byte blocks (twice the code registers
 // per step in flight, so two workgroups per compute unit)
-template <int G>
+template <int G, bool kPreRot = false>
 __global__ __launch_bounds__(256, 2) void decode_int4_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
-  decode_body<G, 4>(a, sm);
+  decode_body<G, 4, kPreRot>(a, sm);
 }
 
 DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len) {
@@ -580,27 +605,32 @@ DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_s
   return p;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t st) {
+template <bool kPreRot>
+static hipError_t launch_decode_as(const DecodeArgs& a, int group, int grid, hipStream_t st) {
   if (a.code_bits == 4) {
     switch (group) {
-      case 1: hipLaunchKernelGGL(decode_int4_kernel<1>, dim3(grid), dim3(256), 0, st, a); break;
-      case 2: hipLaunchKernelGGL(decode_int4_kernel<2>, dim3(grid), dim3(256), 0, st, a); break;
-      case 4: hipLaunchKernelGGL(decode_int4_kernel<4>, dim3(grid), dim3(256), 0, st, a); break;
-      case 8: hipLaunchKernelGGL(decode_int4_kernel<8>, dim3(grid), dim3(256), 0, st, a); break;
-      case 16: hipLaunchKernelGGL(decode_int4_kernel<16>, dim3(grid), dim3(256), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((decode_int4_kernel<1, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((decode_int4_kernel<2, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((decode_int4_kernel<4, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((decode_int4_kernel<8, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((decode_int4_kernel<16, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (group) {
-    case 1: hipLaunchKernelGGL(decode_int2_kernel<1>, dim3(grid), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL(decode_int2_kernel<2>, dim3(grid), dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(decode_int2_kernel<4>, dim3(grid), dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(decode_int2_kernel<8>, dim3(grid), dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL(decode_int2_kernel<16>, dim3(grid), dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((decode_int2_kernel<1, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_int2_kernel<2, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_int2_kernel<4, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decode_int2_kernel<8, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_int2_kernel<16, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t st) {
+  return a.q_rot != nullptr ? launch_decode_as<true>(a, group, grid, st) : launch_decode_as<false>(a, group, grid, st);
 }
 
 }  // namespace oscar

@@ -84,11 +84,18 @@ __device__ void quantize_pack_channel_per_thread(float yc, bool is_v, uint8_t* b
 // ---------------------------------------------------------------------------
 // append: grid (batch, Hkv, 2 = {K, V}), 256 threads.
 // ---------------------------------------------------------------------------
+// kFused: the fused step's instance (also computes q . R_K, see below).
+template <bool kFused>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   __shared__ float xs[kD];
   __shared__ float part[4][kD];
   __shared__ uint32_t sh[32];
-  const int b = blockIdx.x, hk = blockIdx.y, is_v = blockIdx.z;
+  __shared__ float qsh[kFused ? 8 : 1][kD];         // fused step: the KV head's queries
+  __shared__ float qpart[kFused ? 8 : 1][4][kD];    //   and their per-wave partial products
+  // z = 0: K, z = 1: V; the fused instance has a third slice (z = 2) that
+  // computes q . R_K beside the demotion
+  const int b = blockIdx.x, hk = blockIdx.y, is_v = blockIdx.z == 1;
+  const bool fq = kFused && blockIdx.z == 2;
   const int tid = threadIdx.x;
   // y_j = sum_i x_i R[i][j].  The rotation's operands do not depend on the
   // position, so they are requested first: thread (c4, rs) takes columns
@@ -99,51 +106,95 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   float4 rq[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(R + (size_t)(16 * rs + e) * kD + 4 * c4);
+  // Fused step: the third slice computes q' = q . R_K of the KV head's G
+  // query heads (rows (b Hkv + hk) G + h of q).
+  const int G = a.g_model;
+  const size_t qrow0 = ((size_t)b * a.hkv + hk) * G;
+  uint32_t qw[2] = {0u, 0u};
+  if constexpr (kFused) {
+    if (fq) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int idx = tid + 256 * e;
+        if (idx < G * kD / 2) qw[e] = reinterpret_cast<const uint32_t*>(a.q + qrow0 * kD)[idx];
+      }
+    }
+  }
   const float* tau = (is_v ? a.clip_v : a.clip_k) + (size_t)hk * a.clip_kv_stride;
   const float tau_j = tau[tid & (kD - 1)];
   const int slot = a.seq_slot ? a.seq_slot[b] : b;
   const int p = a.position[b];
   const uint16_t* src = (is_v ? a.v_new : a.k_new) + ((size_t)b * a.hkv + hk) * kD;
-  if (p < kSink) {
-    uint16_t* dst = (is_v ? a.sink_v : a.sink_k) + (((size_t)slot * a.hkv + hk) * kSink + p) * kD;
-    if (tid < kD / 2) reinterpret_cast<uint32_t*>(dst)[tid] = reinterpret_cast<const uint32_t*>(src)[tid];
-    return;
-  }
+  if (fq && hk == 0 && tid == 0) a.len_out[b] = p + 1;
   const int r = (p - kSink) & (kRecent - 1);
   uint16_t* ring = (is_v ? a.recent_v : a.recent_k) + (((size_t)slot * a.hkv + hk) * kRecent + r) * kD;
-  if (p >= kSink + kRecent) {
-    // the token leaving the ring (position p - 256) goes to history index h
-    const int h = p - kSink - kRecent;
-    const int page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
+  // from position 320 on, the token leaving the ring (p - 256) is demoted
+  // into history index h
+  const bool demote = !fq && p >= kSink + kRecent;
+  const int h = p - kSink - kRecent;
+  int page = 0;
+  if constexpr (kFused) {
+    for (int e = 0; e < 2 && fq; ++e) {
+      const int idx = tid + 256 * e;
+      if (idx < G * kD / 2) {
+        qsh[(2 * idx) / kD][(2 * idx) % kD] = bf16_bits_to_float(qw[e] & 0xFFFFu);
+        qsh[(2 * idx) / kD][(2 * idx) % kD + 1] = bf16_bits_to_float(qw[e] >> 16);
+      }
+    }
+  }
+  if (demote) {
+    page = a.page_table[(size_t)slot * a.max_pages + (h >> 4)];
     if (tid < kD / 2) {
       const uint32_t w = reinterpret_cast<const uint32_t*>(ring)[tid];
       xs[2 * tid] = bf16_bits_to_float(w & 0xFFFFu);
       xs[2 * tid + 1] = bf16_bits_to_float(w >> 16);
     }
+  }
+  if (fq || demote) {                  // block-uniform
     __syncthreads();
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float xe = xs[16 * rs + e];
-      acc.x = fmaf(xe, rq[e].x, acc.x);
-      acc.y = fmaf(xe, rq[e].y, acc.y);
-      acc.z = fmaf(xe, rq[e].z, acc.z);
-      acc.w = fmaf(xe, rq[e].w, acc.w);
-    }
     // lanes l and l + 32 of a wave hold row slices 2w and 2w + 1 of the same
     // columns: one lane swap, then the four waves' sums through LDS
-    acc.x += __shfl_xor(acc.x, 32);
-    acc.y += __shfl_xor(acc.y, 32);
-    acc.z += __shfl_xor(acc.z, 32);
-    acc.w += __shfl_xor(acc.w, 32);
-    if ((tid & 32) == 0) *reinterpret_cast<float4*>(&part[tid >> 6][4 * c4]) = acc;
+    auto rotate_into = [&](const float* x, float* dst_row /* [4][kD] */) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float xe = x[16 * rs + e];
+        acc.x = fmaf(xe, rq[e].x, acc.x);
+        acc.y = fmaf(xe, rq[e].y, acc.y);
+        acc.z = fmaf(xe, rq[e].z, acc.z);
+        acc.w = fmaf(xe, rq[e].w, acc.w);
+      }
+      acc.x += __shfl_xor(acc.x, 32);
+      acc.y += __shfl_xor(acc.y, 32);
+      acc.z += __shfl_xor(acc.z, 32);
+      acc.w += __shfl_xor(acc.w, 32);
+      if ((tid & 32) == 0) *reinterpret_cast<float4*>(&dst_row[(tid >> 6) * kD + 4 * c4]) = acc;
+    };
+    if (demote) rotate_into(xs, &part[0][0]);
+    if constexpr (kFused) {
+      if (fq)
+        for (int hh = 0; hh < G; ++hh) rotate_into(qsh[hh], &qpart[hh][0][0]);
+    }
     __syncthreads();  // also orders the ring read above before the overwrite below
-    float yc = 0.0f;
-    if (tid < kD) yc = clip_value((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]), tau_j);
-    uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(a.code_bits);
-    quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh, a.code_bits);
+    if constexpr (kFused) {
+      if (fq)
+        for (int idx = tid; idx < G * kD; idx += 256) {
+          const int hh = idx / kD, j = idx % kD;
+          a.q_rot[(qrow0 + hh) * kD + j] = (qpart[hh][0][j] + qpart[hh][1][j]) + (qpart[hh][2][j] + qpart[hh][3][j]);
+        }
+    }
+    if (demote) {
+      float yc = 0.0f;
+      if (tid < kD) yc = clip_value((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]), tau_j);
+      uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(a.code_bits);
+      quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh, a.code_bits);
+    }
   }
-  if (tid < kD / 2) reinterpret_cast<uint32_t*>(ring)[tid] = reinterpret_cast<const uint32_t*>(src)[tid];
+  // then the new token enters the sink or the ring slot
+  if (!fq && tid < kD / 2) {
+    uint16_t* dst = p < kSink ? (is_v ? a.sink_v : a.sink_k) + (((size_t)slot * a.hkv + hk) * kSink + p) * kD : ring;
+    reinterpret_cast<uint32_t*>(dst)[tid] = reinterpret_cast<const uint32_t*>(src)[tid];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -436,7 +487,10 @@ __global__ __launch_bounds__(256) void prefill_route_kernel(PrefillArgs a) {
 }
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL(append_kernel, dim3(batch, a.hkv, 2), dim3(256), 0, st, a);
+  if (a.q_rot != nullptr)
+    hipLaunchKernelGGL(append_kernel<true>, dim3(batch, a.hkv, 3), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(append_kernel<false>, dim3(batch, a.hkv, 2), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -23,6 +23,13 @@ struct AppendArgs {
   int code_bits;           // 2: INT2 history blocks, 4: INT4
   int hkv;
   int max_pages;
+  // fused step (all nullable): q' = q . R_K of each sequence's query heads
+  // (bf16 q [batch][Hq][128] in, fp32 q_rot out, same layout) and the
+  // decode length position + 1 (len_out [batch])
+  const uint16_t* q;
+  float* q_rot;
+  int32_t* len_out;
+  int g_model;             // query heads per KV head
 };
 
 struct DemoteArgs {
@@ -72,6 +79,7 @@ struct DecodeArgs {
   const float* rot_k; const float* rot_v;
   int rot_kv_stride;          // elements from one KV head's R to the next (0: shared)
   int code_bits;              // 2: INT2 history blocks, 4: INT4
+  const float* q_rot;         // nullable: q . R_K precomputed (fp32, q's layout); history splits skip R_K
   float* partials;            // workspace: [batch*Hkv][n_splits][G][132]
   int hkv;
   int max_pages;

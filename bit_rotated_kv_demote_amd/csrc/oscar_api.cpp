@@ -75,6 +75,54 @@ QueryColumns int2_query_columns(const oscar_layer_desc* d, int n_query) {
 constexpr int kMaxBf16Columns = 16;
 }  // namespace
 
+static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                                  const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
+                                  float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
+                                  void* stream);
+
+namespace {
+// fused step workspace: q . R_K (fp32, q's layout), the decode lengths, then
+// the decode partials; each part starts on a 256-byte boundary
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+size_t step_qrot_bytes(const oscar_layer_desc* d, int batch) {
+  return align256((size_t)batch * d->num_q_heads * 128 * sizeof(float));
+}
+size_t step_len_bytes(int batch) { return align256((size_t)batch * sizeof(int32_t)); }
+
+oscar_status check_append(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                          const int32_t* position, const void* k_new, const void* v_new, int32_t batch) {
+  oscar_status st = check_desc(desc);
+  if (st != OSCAR_OK) return st;
+  if ((st = check_pool(pool, true)) != OSCAR_OK) return st;
+  if (!position || !k_new || !v_new || batch <= 0) return OSCAR_ERR_INVALID;
+  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
+  return OSCAR_OK;
+}
+
+AppendArgs append_args(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                       const int32_t* position, const void* k_new, const void* v_new) {
+  AppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.seq_slot = seq_slot;
+  a.position = position;
+  a.sink_k = static_cast<uint16_t*>(pool->sink_k);
+  a.sink_v = static_cast<uint16_t*>(pool->sink_v);
+  a.recent_k = static_cast<uint16_t*>(pool->recent_k);
+  a.recent_v = static_cast<uint16_t*>(pool->recent_v);
+  a.hist = pool->hist;
+  a.page_table = pool->page_table;
+  a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
+  a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
+  a.rot_kv_stride = rot_stride(pool); a.clip_kv_stride = clip_stride(pool);
+  a.code_bits = pool->code_bits;
+  a.hkv = desc->num_kv_heads;
+  a.max_pages = pool->max_pages_per_seq;
+  a.g_model = desc->num_q_heads / desc->num_kv_heads;
+  return a;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t oscar_abi_version(void) { return OSCAR_ABI_VERSION; }
@@ -117,28 +165,9 @@ oscar_status oscar_calibrate(const oscar_layer_desc* desc, const oscar_calib_opt
 oscar_status oscar_append(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                           const int32_t* position, const void* k_new, const void* v_new, int32_t batch,
                           void* stream) {
-  oscar_status st = check_desc(desc);
+  const oscar_status st = check_append(desc, pool, seq_slot, position, k_new, v_new, batch);
   if (st != OSCAR_OK) return st;
-  if ((st = check_pool(pool, true)) != OSCAR_OK) return st;
-  if (!position || !k_new || !v_new || batch <= 0) return OSCAR_ERR_INVALID;
-  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
-  AppendArgs a{};
-  a.k_new = static_cast<const uint16_t*>(k_new);
-  a.v_new = static_cast<const uint16_t*>(v_new);
-  a.seq_slot = seq_slot;
-  a.position = position;
-  a.sink_k = static_cast<uint16_t*>(pool->sink_k);
-  a.sink_v = static_cast<uint16_t*>(pool->sink_v);
-  a.recent_k = static_cast<uint16_t*>(pool->recent_k);
-  a.recent_v = static_cast<uint16_t*>(pool->recent_v);
-  a.hist = pool->hist;
-  a.page_table = pool->page_table;
-  a.rot_k = pool->rot_k; a.rot_v = pool->rot_v;
-  a.clip_k = pool->clip_k; a.clip_v = pool->clip_v;
-  a.rot_kv_stride = rot_stride(pool); a.clip_kv_stride = clip_stride(pool);
-  a.code_bits = pool->code_bits;
-  a.hkv = desc->num_kv_heads;
-  a.max_pages = pool->max_pages_per_seq;
+  const AppendArgs a = append_args(desc, pool, seq_slot, position, k_new, v_new);
   return hip_status(launch_append(a, batch, static_cast<hipStream_t>(stream)));
 }
 
@@ -236,6 +265,16 @@ oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, 
 oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                                 const int32_t* seq_len, const void* q, int32_t n_query, float* out, void* workspace,
                                 size_t ws_bytes, int32_t batch, int32_t max_seq_len, void* stream) {
+  return decode_tiered(desc, pool, seq_slot, seq_len, q, nullptr, n_query, out, workspace, ws_bytes, batch,
+                       max_seq_len, stream);
+}
+}  // extern "C"
+
+// Tiered decode (split kernel + merge); q_rot: nullable precomputed q . R_K.
+static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                                  const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
+                                  float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
+                                  void* stream) {
   oscar_status st = check_desc(desc);
   if (st != OSCAR_OK) return st;
   if ((st = check_pool(pool, max_seq_len > 320)) != OSCAR_OK) return st;
@@ -265,6 +304,7 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
   a.rot_v = pool->rot_v;
   a.rot_kv_stride = rot_stride(pool);
   a.code_bits = pool->code_bits;
+  a.q_rot = q_rot;
   a.partials = static_cast<float*>(workspace);
   a.hkv = hkv;
   a.max_pages = pool->max_pages_per_seq;
@@ -295,6 +335,8 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
   m.tiered = 1;
   return hip_status(launch_merge(m, batch * n_query * desc->num_q_heads, hs));
 }
+
+extern "C" {
 
 size_t oscar_decode_bf16_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
   return oscar_decode_bf16_multi_workspace_bytes(desc, batch, 1, max_seq_len);
@@ -365,6 +407,36 @@ oscar_status oscar_decode_bf16_multi(const oscar_layer_desc* desc, const oscar_b
   m.pages_per_split = plan.pages_per_split;
   m.tiered = 0;
   return hip_status(launch_merge(m, batch * n_query * desc->num_q_heads, hs));
+}
+
+size_t oscar_step_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
+  const size_t dec = oscar_decode_workspace_bytes(desc, batch, max_seq_len);
+  if (dec == 0) return 0;
+  return step_qrot_bytes(desc, batch) + step_len_bytes(batch) + dec;
+}
+
+oscar_status oscar_step(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                        const int32_t* position, const void* k_new, const void* v_new, const void* q, float* out,
+                        void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len, void* stream) {
+  oscar_status st = check_append(desc, pool, seq_slot, position, k_new, v_new, batch);
+  if (st != OSCAR_OK) return st;
+  if (!q || !out || !workspace || max_seq_len < 1) return OSCAR_ERR_INVALID;
+  const size_t need = oscar_step_workspace_bytes(desc, batch, max_seq_len);
+  if (need == 0) return OSCAR_ERR_UNSUPPORTED;
+  if (ws_bytes < need) return OSCAR_ERR_CAPACITY;
+  const int max_hist = max_seq_len - 320;
+  if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* q_rot = reinterpret_cast<float*>(ws);
+  int32_t* lens = reinterpret_cast<int32_t*>(ws + step_qrot_bytes(desc, batch));
+  void* partials = ws + step_qrot_bytes(desc, batch) + step_len_bytes(batch);
+  AppendArgs a = append_args(desc, pool, seq_slot, position, k_new, v_new);
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_rot = q_rot;
+  a.len_out = lens;
+  if ((st = hip_status(launch_append(a, batch, static_cast<hipStream_t>(stream)))) != OSCAR_OK) return st;
+  return decode_tiered(desc, pool, seq_slot, lens, q, q_rot, 1, out, partials,
+                       ws_bytes - step_qrot_bytes(desc, batch) - step_len_bytes(batch), batch, max_seq_len, stream);
 }
 
 }  // extern "C"

@@ -59,6 +59,7 @@ class TieredKV:
                                       self.page_table, self.rot_k, self.rot_v, self.clip_k, self.clip_v,
                                       self.per_kv_head, code_bits)
         self._ws = None
+        self._step_ws = None
 
     # -- hot path --------------------------------------------------------
     def append(self, position, k_new, v_new, seq_slot=None):
@@ -82,6 +83,19 @@ class TieredKV:
             out = torch.empty((batch, self.hq, HEAD_DIM), dtype=torch.float32, device=self.device)
         ws = self.workspace(batch, max_seq_len)
         binding.oscar_decode(self.desc, self.pool, seq_slot, seq_len, q, out, ws, batch, max_seq_len)
+        return out
+
+    def step(self, position, k_new, v_new, q, max_seq_len, out=None, seq_slot=None):
+        """One fused decode step: append (k_new, v_new) at position, then decode q
+        over position + 1 tokens.  k_new, v_new: bf16 [B, Hkv, 128]; q: bf16 [B, Hq, 128]."""
+        batch = q.shape[0]
+        if out is None:
+            out = torch.empty((batch, self.hq, HEAD_DIM), dtype=torch.float32, device=self.device)
+        nbytes = binding.oscar_step_workspace_bytes(self.desc, batch, max_seq_len)
+        if self._step_ws is None or self._step_ws.numel() < nbytes:
+            self._step_ws = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=self.device)
+        binding.oscar_step(self.desc, self.pool, seq_slot, position, k_new, v_new, q, out, self._step_ws, batch,
+                           max_seq_len)
         return out
 
     def decode_multi(self, q, seq_len, max_seq_len, out=None, seq_slot=None):
@@ -123,6 +137,19 @@ class PagedBF16:
         if self._ws is None or self._ws.numel() < nbytes:
             self._ws = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=self.device)
         binding.oscar_decode_bf16(self.desc, self.pool, seq_slot, seq_len, q, out, self._ws, batch, max_seq_len)
+        return out
+
+    def step(self, position, k_new, v_new, q, max_seq_len, out=None, seq_slot=None):
+        """One fused decode step: append (k_new, v_new) at position, then decode q
+        over position + 1 tokens.  k_new, v_new: bf16 [B, Hkv, 128]; q: bf16 [B, Hq, 128]."""
+        batch = q.shape[0]
+        if out is None:
+            out = torch.empty((batch, self.hq, HEAD_DIM), dtype=torch.float32, device=self.device)
+        nbytes = binding.oscar_step_workspace_bytes(self.desc, batch, max_seq_len)
+        if self._step_ws is None or self._step_ws.numel() < nbytes:
+            self._step_ws = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=self.device)
+        binding.oscar_step(self.desc, self.pool, seq_slot, position, k_new, v_new, q, out, self._step_ws, batch,
+                           max_seq_len)
         return out
 
     def decode_multi(self, q, seq_len, max_seq_len, out=None, seq_slot=None):

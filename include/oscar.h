@@ -296,6 +296,31 @@ size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
                                     int32_t max_seq_len);
 
 /*
+ * oscar_step -- one decode step of a layer in one call: oscar_append of the
+ * new token (k_new, v_new at position[b], as there) followed by oscar_decode
+ * of q over the position[b] + 1 cached tokens ([yunpan] 三.1: the new token is
+ * appended before it attends; [gist] 2.2 B).  The append launch gets a third
+ * slice of workgroups that computes q . R_K of each sequence's query heads
+ * beside the demotion; the decode's history splits read those rotated
+ * queries instead of loading R_K themselves.  Results equal oscar_append
+ * followed by oscar_decode up to fp32 summation order.
+ * position, seq_slot: device int32 [batch] (positions before the append, not
+ * advanced by the call); q: device bf16 [batch][Hq][128]; out: device fp32
+ * [batch][Hq][128]; max_seq_len >= max(position) + 1.  workspace: device,
+ * at least oscar_step_workspace_bytes(desc, batch, max_seq_len) bytes, no
+ * initialisation needed, one call at a time.  Errors as oscar_append and
+ * oscar_decode.
+ */
+oscar_status oscar_step(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                        const int32_t* position, const void* k_new, const void* v_new, const void* q,
+                        float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
+                        void* stream);
+
+/* Workspace of oscar_step: the decode's plus batch * Hq * 512 bytes of
+ * rotated queries and the step's lengths; 0 for an unsupported shape. */
+size_t oscar_step_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len);
+
+/*
  * oscar_decode_multi -- several query tokens per sequence over the tiered
  * pool (speculative verification of draft tokens, chunked prefill), the
  * same attention as oscar_decode ([gist] 2.2 B; [zingnex] 自定义INT2注意力内核)

@@ -308,3 +308,19 @@ def test_calibration_scope_and_pool_flag_validation(lib):
     assert lib.oscar_append(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 1, None) == -1
     assert lib.oscar_decode(ctypes.byref(good), ctypes.byref(pool), None, 256, 256, 256, 256, 1 << 30, 1, 100,
                             None) == -1
+
+
+def test_step_validation_and_workspace(lib):
+    d = binding.layer_desc(32, 8)
+    pool = _null_pool(max_pages=4096)
+    dec = binding.oscar_decode_workspace_bytes(d, 2, 32768)
+    step = binding.oscar_step_workspace_bytes(d, 2, 32768)
+    assert step >= dec + 2 * 32 * 512 and step % 256 == dec % 256
+    assert binding.oscar_step_workspace_bytes(d, 0, 32768) == 0
+    # null q, too small a workspace, bad slot count: rejected before any launch
+    assert lib.oscar_step(ctypes.byref(d), ctypes.byref(pool), None, 256, 256, 256, None, 256, 256, 1 << 30, 1,
+                          1000, None) == -1
+    assert lib.oscar_step(ctypes.byref(d), ctypes.byref(pool), None, 256, 256, 256, 256, 256, 256, 64, 1, 1000,
+                          None) == -3
+    assert lib.oscar_step(ctypes.byref(d), ctypes.byref(pool), None, 256, 256, 256, 256, 256, 256, 1 << 30, 2,
+                          1000, None) == -1
