@@ -50,6 +50,16 @@ def decode_bytes(lengths, hq, hkv, code_bits=2):
     return total
 
 
+def split_kernel_bytes(lengths, hq, hkv, code_bits=2):
+    """Algorithmic HBM bytes of the decode's split kernel alone (oscar_decode_partials):
+    history, sink/recent tiles, page ids, q and R_K; not the merge's R_V and output."""
+    total = 0
+    for n in lengths:
+        hist = max(0, n - 320)
+        total += hist * hkv * hist_token_bytes(code_bits) + min(n, 320) * hkv * 512 + 4 * math.ceil(hist / 16)
+    return total + len(lengths) * hq * 128 * 2 + 128 * 128 * 4
+
+
 def bf16_decode_bytes(lengths, hq, hkv):
     total = 0
     for n in lengths:
@@ -210,11 +220,34 @@ def run_tiered(torch, hq, hkv, n0, n_layers, steps, warmup, seed, calib=None, co
     for i in range(warmup + 3 * steps, warmup + 4 * steps):
         fused_step(i, t_step)
     torch.cuda.synchronize()
+    # the decode's two kernels apart: `steps` back-to-back oscar_decode_partials
+    # launches (the split kernel) between two events, then as many
+    # oscar_decode_merge launches; each layer decodes at the length it has reached
+    n_done = warmup + 4 * steps
+    last_len = [n0 + (n_done - 1 - li) // n_layers + 1 for li in range(n_layers)]
+    last_lens = torch.tensor(last_len, dtype=torch.int32, device="cuda")
+    q_last = q[(n_done - 1) // n_layers]
+    phase_ms = []
+    for phase in ("partials", "merge"):
+        torch.cuda.synchronize()
+        gpu_hold(torch, 20 + 0.1 * steps)
+        e0.record()
+        for i in range(steps):
+            li = i % n_layers
+            if phase == "partials":
+                layers[li].decode_partials(q_last, last_lens[li:li + 1], max_len)
+            else:
+                layers[li].decode_merge(last_lens[li:li + 1], 1, max_len, out=outs[i & 1])
+        e1.record()
+        torch.cuda.synchronize()
+        phase_ms.append(e0.elapsed_time(e1))
     pool_bytes = sum(p.hist.numel() + 4 * p.sink_k.numel() + 4 * p.recent_k.numel() for p in layers)
     mid_len = n0 + (warmup + steps) // n_layers + 1
     return dict(total_ms=total_ms, us_per_step=1000.0 * total_ms / steps, decode_us=t_dec.mean_us(),
                 us_per_step_separate=1000.0 * separate_ms / steps, step_call_us=t_step.mean_us(),
                 append_us=t_app.mean_us(), decode_bytes=decode_bytes([mid_len], hq, hkv, code_bits), layers=n_layers,
+                split_us=1000.0 * phase_ms[0] / steps, merge_us=1000.0 * phase_ms[1] / steps,
+                split_bytes=sum(split_kernel_bytes([n], hq, hkv, code_bits) for n in last_len) / n_layers,
                 pool_mb=pool_bytes / 1e6, calib_s=calib_s, host=host, n_mid=mid_len, max_len=max_len)
 
 
@@ -732,11 +765,17 @@ def main():
     hq, hkv, n0 = 32, 8, 32768
     res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001)
     dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
+    # the roofline kernel: the decode's split kernel (oscar_decode_partials)
+    split_gbps = res["split_bytes"] / (res["split_us"] * 1e3)
     extra = {"step_mode": "oscar_step (append + decode in one call; the append launch also computes q . R_K)",
              "us_per_step_separate_calls": round(res["us_per_step_separate"], 3),
              "step_call_us": round(res["step_call_us"], 3),
              "decode_call_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),
              "decode_algorithmic_bytes": res["decode_bytes"], "decode_GBps": round(dec_gbps, 1),
+             "roofline_kernel": "decode_int2_kernel<4, false>: the decode's split kernel alone "
+                                 "(oscar_decode_partials, back-to-back launches between two events)",
+             "split_kernel_us": round(res["split_us"], 3), "split_kernel_bytes": round(res["split_bytes"]),
+             "merge_kernel_us": round(res["merge_us"], 3),
              "pools": res["layers"], "pool_MB_total": round(res["pool_mb"], 1),
              "calibrate_host_s": round(res["calib_s"], 2)}
     if not args.no_extra:
@@ -752,6 +791,11 @@ def main():
                             "decode_call_us": round(r128["decode_us"], 3),
                             "append_kernel_us": round(r128["append_us"], 3), "decode_GBps": round(g128, 1),
                             "decode_frac_of_8TBps": round(g128 / HBM_PEAK_GBPS, 4),
+                            "split_kernel_us": round(r128["split_us"], 3),
+                            "split_kernel_GBps": round(r128["split_bytes"] / (r128["split_us"] * 1e3), 1),
+                            "split_kernel_frac_of_8TBps": round(r128["split_bytes"] / (r128["split_us"] * 1e3)
+                                                                / HBM_PEAK_GBPS, 4),
+                            "merge_kernel_us": round(r128["merge_us"], 3),
                             "decode_algorithmic_bytes": r128["decode_bytes"], "pools": r128["layers"],
                             "pool_MB_total": round(r128["pool_mb"], 1)}
         b128 = run_bf16(torch, hq, hkv, r128["n_mid"], 4, 60, 1002, r128["host"][0], r128["host"][1])
@@ -814,8 +858,8 @@ def main():
                                "head_dim 128, batch 1, 32768 cached tokens + 1 appended per step, "
                                "64 bf16 sink / int2 history / 256 bf16 recent, 16-token pages",
                    "global_batch": 1, "seq_len": n0, "parallelism": "single-gpu"},
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic()},
+        "roofline": {"bound": "hbm", "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -16,10 +16,10 @@ LIB_PATH = os.path.join(HERE, "libamdoscar.so")
 
 OSCAR_SRC_BF16 = 0
 OSCAR_SRC_F32_ROTATED = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_calibrate_layers", "oscar_append", "oscar_demote",
-            "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_multi",
+            "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_partials", "oscar_decode_merge", "oscar_decode_multi",
             "oscar_decode_multi_workspace_bytes", "oscar_decode_bf16", "oscar_decode_bf16_workspace_bytes",
             "oscar_decode_bf16_multi", "oscar_decode_bf16_multi_workspace_bytes", "oscar_step",
             "oscar_step_workspace_bytes")
@@ -88,6 +88,10 @@ def load():
     lib.oscar_decode.argtypes = [P, P, P, P, P, P, P, SZ, I32, I32, P]
     lib.oscar_decode_workspace_bytes.restype = SZ
     lib.oscar_decode_workspace_bytes.argtypes = [P, I32, I32]
+    lib.oscar_decode_partials.restype = ctypes.c_int
+    lib.oscar_decode_partials.argtypes = [P, P, P, P, P, P, SZ, I32, I32, P]
+    lib.oscar_decode_merge.restype = ctypes.c_int
+    lib.oscar_decode_merge.argtypes = [P, P, P, P, P, SZ, I32, I32, P]
     lib.oscar_step.restype = ctypes.c_int
     lib.oscar_step.argtypes = [P, P, P, P, P, P, P, P, P, SZ, I32, I32, P]
     lib.oscar_step_workspace_bytes.restype = SZ
@@ -191,6 +195,21 @@ def oscar_decode(desc, pool, seq_slot, seq_len, q, out, workspace, batch, max_se
     _check("oscar_decode", load().oscar_decode(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_slot),
                                                 _ptr(seq_len), _ptr(q), _ptr(out), _ptr(workspace), ws_bytes,
                                                 batch, max_seq_len, _stream(stream)))
+
+
+def oscar_decode_partials(desc, pool, seq_slot, seq_len, q, workspace, batch, max_seq_len, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("oscar_decode_partials", load().oscar_decode_partials(ctypes.byref(desc), ctypes.byref(pool),
+                                                                  _ptr(seq_slot), _ptr(seq_len), _ptr(q),
+                                                                  _ptr(workspace), ws_bytes, batch, max_seq_len,
+                                                                  _stream(stream)))
+
+
+def oscar_decode_merge(desc, pool, seq_len, out, workspace, batch, max_seq_len, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("oscar_decode_merge", load().oscar_decode_merge(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_len),
+                                                            _ptr(out), _ptr(workspace), ws_bytes, batch,
+                                                            max_seq_len, _stream(stream)))
 
 
 def oscar_step_workspace_bytes(desc, batch, max_seq_len) -> int:

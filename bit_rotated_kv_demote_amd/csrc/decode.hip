@@ -451,6 +451,19 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
     }
   }
   const int slot = a.seq_slot ? a.seq_slot[b] : b;
+  // History splits: this wave's page ids are requested before the length is
+  // known (clamped to the page-table row: the split's first page lies in it),
+  // together with the split's first page id.  Lanes past the split's last
+  // valid page are given that first page once the length has arrived, so
+  // no page past the sequence's end is ever addressed.
+  const int idx_in_split = kStepPages * (wave + 4 * (lane / kStepPages)) + lane % kStepPages;
+  int32_t ids_spec = 0, first_id = 0;
+  if (!is_tile) {
+    const int pg0 = (split - a.n_tile_splits) * a.pages_per_split;
+    const int32_t* row = a.page_table + (size_t)slot * a.max_pages;
+    ids_spec = row[pg0 + min(idx_in_split, a.max_pages - 1 - pg0)];
+    first_id = row[pg0];
+  }
   const int n = a.seq_len[b];
   const int hist_len = max(0, n - kSink - kRecent);
   const int n_hist_pages = (hist_len + kPage - 1) / kPage;
@@ -484,13 +497,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
   } else {
     const int pg_begin = hs * a.pages_per_split;
     const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);
-    const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
-    // page ids of this wave's steps (steps wave, wave + 4, ...): one load
-    // per lane, then this wave's first step: the prologue below waits only
-    // for the older loads, so the loop is entered with exactly the page
-    // loads in flight that every later iteration also has.
-    const int32_t ids = pt_row[pg_begin + min(kStepPages * (wave + 4 * (lane / kStepPages)) + lane % kStepPages,
-                                              pg_end - pg_begin - 1)];
+    // page ids of this wave's steps (steps wave, wave + 4, ...), lane
+    // kStepPages k + i holding page i of the k-th; then this wave's first
+    // step: the prologue below waits only for the older loads, so the loop
+    // is entered with exactly the page loads in flight that every later
+    // iteration also has.
+    const int32_t ids = idx_in_split < pg_end - pg_begin ? ids_spec : first_id;
     PageCodes<kBits> c_first[kStepPages];
     u32x2_t m_first[kStepPages];
     // unconditional (the ids are clamped to pages of this split): the same
@@ -580,14 +592,13 @@ __global__ __launch_bounds__(256, 2) void decode_int4_kernel(DecodeArgs a) {
   decode_body<G, 4, kPreRot>(a, sm);
 }
 
-DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len) {
+DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len, int target) {
   DecodePlan p{};
   const int max_hist = max(0, max_seq_len - kSink - kRecent);
   const int max_pages = (max_hist + kPage - 1) / kPage;
   const long n_groups = (long)batch * hkv * n_colgroups;
   const long total_pages = n_groups * max_pages;
-  // aim at roughly two workgroups per compute unit (256 CUs)
-  long pps = (total_pages + 479) / 480;
+  long pps = (total_pages + target - 1) / target;
   pps = ((pps + 7) / 8) * 8;
   if (pps < 8) pps = 8;
   if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;

@@ -151,9 +151,16 @@ struct DecodePlan {
 // four waves keeps the page ids of its share in one 64-lane register)
 constexpr int kMaxPagesPerSplit = 256;
 
+// Workgroups a decode launch aims at (history pages split evenly over them):
+// about two per compute unit for oscar_decode, whose history splits each load
+// all of R_K; the fused step's splits read q . R_K precomputed instead.
+constexpr int kDecodeSplitTarget = 480;
+constexpr int kStepSplitTarget = 480;
+
 // group: columns per work item (1, 2, 4, 8 or 16); n_colgroups column groups
 // per (sequence, KV head)
-DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len);
+DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len,
+                       int target = kDecodeSplitTarget);
 DecodePlan plan_decode_bf16(int batch, int hkv, int group, int n_colgroups, int max_seq_len);
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st);

@@ -75,10 +75,12 @@ QueryColumns int2_query_columns(const oscar_layer_desc* d, int n_query) {
 constexpr int kMaxBf16Columns = 16;
 }  // namespace
 
+// which launches of a tiered decode call run
+enum DecodePhases { kPhaseSplits = 1, kPhaseMerge = 2, kPhaseBoth = 3 };
 static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                                   const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
                                   float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
-                                  void* stream);
+                                  void* stream, int phases = kPhaseBoth);
 
 namespace {
 // fused step workspace: q . R_K (fp32, q's layout), the decode lengths, then
@@ -268,25 +270,42 @@ oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* 
   return decode_tiered(desc, pool, seq_slot, seq_len, q, nullptr, n_query, out, workspace, ws_bytes, batch,
                        max_seq_len, stream);
 }
+
+oscar_status oscar_decode_partials(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                                   const int32_t* seq_len, const void* q, void* workspace, size_t ws_bytes,
+                                   int32_t batch, int32_t max_seq_len, void* stream) {
+  return decode_tiered(desc, pool, seq_slot, seq_len, q, nullptr, 1, nullptr, workspace, ws_bytes, batch,
+                       max_seq_len, stream, kPhaseSplits);
+}
+
+oscar_status oscar_decode_merge(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_len,
+                                float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
+                                void* stream) {
+  return decode_tiered(desc, pool, nullptr, seq_len, nullptr, nullptr, 1, out, workspace, ws_bytes, batch,
+                       max_seq_len, stream, kPhaseMerge);
+}
 }  // extern "C"
 
-// Tiered decode (split kernel + merge); q_rot: nullable precomputed q . R_K.
+// Tiered decode (split kernel + merge, or one of them); q_rot: nullable
+// precomputed q . R_K.
 static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                                   const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
                                   float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
-                                  void* stream) {
+                                  void* stream, int phases) {
   oscar_status st = check_desc(desc);
   if (st != OSCAR_OK) return st;
   if ((st = check_pool(pool, max_seq_len > 320)) != OSCAR_OK) return st;
-  if (!seq_len || !q || !out || !workspace || batch <= 0 || max_seq_len <= 0) return OSCAR_ERR_INVALID;
+  if (!seq_len || !workspace || batch <= 0 || max_seq_len <= 0) return OSCAR_ERR_INVALID;
+  if (((phases & kPhaseSplits) && !q) || ((phases & kPhaseMerge) && !out)) return OSCAR_ERR_INVALID;
   if (n_query < 1 || max_seq_len < n_query) return OSCAR_ERR_INVALID;
   if (n_query > kMaxQueryTokens) return OSCAR_ERR_UNSUPPORTED;
-  if (!seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
+  if ((phases & kPhaseSplits) && !seq_slot && batch > pool->n_slots) return OSCAR_ERR_INVALID;
   const int hkv = desc->num_kv_heads, g = desc->num_q_heads / hkv;
   const int max_hist = max_seq_len - 320;
   if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
   const QueryColumns c = int2_query_columns(desc, n_query);
-  const DecodePlan plan = plan_decode(batch, hkv, c.group, c.n_colgroups, max_seq_len);
+  const DecodePlan plan = plan_decode(batch, hkv, c.group, c.n_colgroups, max_seq_len,
+                                      q_rot ? kStepSplitTarget : kDecodeSplitTarget);
   if (!plan.ok) return OSCAR_ERR_UNSUPPORTED;
   if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
   DecodeArgs a{};
@@ -317,7 +336,8 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   a.g_model = g;
   a.n_colgroups = c.n_colgroups;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(launch_decode(a, c.group, plan.grid, hs))) != OSCAR_OK) return st;
+  if ((phases & kPhaseSplits) && (st = hip_status(launch_decode(a, c.group, plan.grid, hs))) != OSCAR_OK) return st;
+  if (!(phases & kPhaseMerge)) return OSCAR_OK;
   MergeArgs m{};
   m.partials = a.partials;
   m.seq_len = seq_len;
@@ -410,7 +430,10 @@ oscar_status oscar_decode_bf16_multi(const oscar_layer_desc* desc, const oscar_b
 }
 
 size_t oscar_step_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
-  const size_t dec = oscar_decode_workspace_bytes(desc, batch, max_seq_len);
+  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0) return 0;
+  const QueryColumns c = int2_query_columns(desc, 1);
+  const size_t dec =
+      plan_decode(batch, desc->num_kv_heads, c.group, c.n_colgroups, max_seq_len, kStepSplitTarget).workspace_bytes;
   if (dec == 0) return 0;
   return step_qrot_bytes(desc, batch) + step_len_bytes(batch) + dec;
 }

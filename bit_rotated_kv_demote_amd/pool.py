@@ -85,6 +85,20 @@ class TieredKV:
         binding.oscar_decode(self.desc, self.pool, seq_slot, seq_len, q, out, ws, batch, max_seq_len)
         return out
 
+    def decode_partials(self, q, seq_len, max_seq_len, seq_slot=None):
+        """The split phase of decode alone: partial records into this pool's workspace."""
+        batch = q.shape[0]
+        ws = self.workspace(batch, max_seq_len)
+        binding.oscar_decode_partials(self.desc, self.pool, seq_slot, seq_len, q, ws, batch, max_seq_len)
+
+    def decode_merge(self, seq_len, batch, max_seq_len, out=None):
+        """The merge phase of decode alone, over the records decode_partials left."""
+        if out is None:
+            out = torch.empty((batch, self.hq, HEAD_DIM), dtype=torch.float32, device=self.device)
+        ws = self.workspace(batch, max_seq_len)
+        binding.oscar_decode_merge(self.desc, self.pool, seq_len, out, ws, batch, max_seq_len)
+        return out
+
     def step(self, position, k_new, v_new, q, max_seq_len, out=None, seq_slot=None):
         """One fused decode step: append (k_new, v_new) at position, then decode q
         over position + 1 tokens.  k_new, v_new: bf16 [B, Hkv, 128]; q: bf16 [B, Hq, 128]."""

@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 4
+#define OSCAR_ABI_VERSION 5
 
 typedef enum {
   OSCAR_OK = 0,
@@ -294,6 +294,32 @@ oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool,
 
 size_t oscar_decode_workspace_bytes(const oscar_layer_desc* desc, int32_t batch,
                                     int32_t max_seq_len);
+
+/*
+ * oscar_decode_partials, oscar_decode_merge -- the two phases of
+ * oscar_decode as separate calls ([gist] 2.2 B; split-K over the paged
+ * history with a log-sum-exp merge).  oscar_decode_partials runs the split
+ * kernel only: every split of every (sequence, KV head) writes its running
+ * maximum, softmax sum and unnormalised output (history splits in the
+ * rotated space) to the workspace.  oscar_decode_merge then merges them,
+ * rotates the history part back with R_V^T and writes out.  The two calls in
+ * this order on one stream, with the same desc, pool, seq_len, batch,
+ * max_seq_len and workspace, compute exactly what oscar_decode computes (it
+ * is these two launches).  The records are private to the library: the
+ * workspace holds them only from a partials call to the next call that uses
+ * the workspace, and a merge is meaningful only after a partials call with
+ * the same arguments.  For callers that schedule or time the phases apart.
+ * Arguments as for oscar_decode; the partials call does not read `out`, the
+ * merge does not read q or seq_slot (either may be NULL there).  Errors as
+ * for oscar_decode.
+ */
+oscar_status oscar_decode_partials(const oscar_layer_desc* desc, const oscar_pool* pool,
+                                   const int32_t* seq_slot, const int32_t* seq_len, const void* q,
+                                   void* workspace, size_t ws_bytes, int32_t batch,
+                                   int32_t max_seq_len, void* stream);
+oscar_status oscar_decode_merge(const oscar_layer_desc* desc, const oscar_pool* pool,
+                                const int32_t* seq_len, float* out, void* workspace, size_t ws_bytes,
+                                int32_t batch, int32_t max_seq_len, void* stream);
 
 /*
  * oscar_step -- one decode step of a layer in one call: oscar_append of the

@@ -324,3 +324,23 @@ def test_step_validation_and_workspace(lib):
                           None) == -3
     assert lib.oscar_step(ctypes.byref(d), ctypes.byref(pool), None, 256, 256, 256, 256, 256, 256, 1 << 30, 2,
                           1000, None) == -1
+
+
+def test_decode_phase_calls_validation(lib):
+    d = binding.layer_desc(32, 8)
+    pool = _null_pool(max_pages=4096)
+    P = lambda fn, *a: getattr(lib, fn)(ctypes.byref(d), ctypes.byref(pool), *a)  # noqa: E731
+    # partials: null q or seq_len, small workspace, short page table, batch beyond the slots
+    assert P("oscar_decode_partials", None, 256, None, 256, 1 << 30, 1, 1000, None) == -1
+    assert P("oscar_decode_partials", None, None, 256, 256, 1 << 30, 1, 1000, None) == -1
+    assert P("oscar_decode_partials", None, 256, 256, 256, 16, 1, 1000, None) == -3
+    assert P("oscar_decode_partials", None, 256, 256, 256, 1 << 30, 1, 320 + 16 * 4097, None) == -3
+    assert P("oscar_decode_partials", None, 256, 256, 256, 1 << 30, 2, 1000, None) == -1
+    # merge: null out or workspace, small workspace; it needs no slot map (batch 2 > 1 slot is fine to validate)
+    assert P("oscar_decode_merge", 256, None, 256, 1 << 30, 1, 1000, None) == -1
+    assert P("oscar_decode_merge", 256, 256, None, 1 << 30, 1, 1000, None) == -1
+    assert P("oscar_decode_merge", 256, 256, 256, 16, 1, 1000, None) == -3
+    bad = binding.layer_desc(32, 8)
+    bad.page_size = 8
+    assert lib.oscar_decode_merge(ctypes.byref(bad), ctypes.byref(pool), 256, 256, 256, 1 << 30, 1, 1000,
+                                  None) == -2

@@ -254,3 +254,24 @@ def test_bf16_baseline_matches_oracle():
     ref = orc.decode_bf16(q, kv, pt, [0, 1, 2], lengths)
     for b in range(len(lengths)):
         assert rel_l2(out[b], ref[b]) <= TOL, lengths[b]
+
+
+@pytest.mark.parametrize("hq,hkv,lengths", [(8, 2, [1500, 300, 2047]), (16, 2, [5000, 64])])
+def test_decode_phases_equal_decode_and_oracle(hq, hkv, lengths):
+    # oscar_decode_partials then oscar_decode_merge on one stream are the two
+    # launches of oscar_decode: the outputs are identical, and match the oracle.
+    layer = Layer(seed=1011, batch=len(lengths), hq=hq, hkv=hkv, max_len=max(lengths) + 16)
+    opool = layer.oracle_pool(lengths)
+    dev = layer.device_pool()
+    upload(dev, opool)
+    q = bf16_tensor(np.ascontiguousarray(layer.q[0]))
+    lens = i32(lengths)
+    max_len = max(lengths) + 16
+    whole = dev.decode(q, lens, max_len).cpu().numpy()
+    dev.workspace(len(lengths), max_len).fill_(0xA5)     # stale bytes: the partials call must overwrite them
+    dev.decode_partials(q, lens, max_len)
+    split = dev.decode_merge(lens, len(lengths), max_len).cpu().numpy()
+    assert np.array_equal(whole, split)
+    ref = orc.decode_tiered(np.ascontiguousarray(layer.q[0]), opool, list(range(len(lengths))), lengths, layer.rot,
+                            layer.rot)
+    assert rel_l2(split, ref) <= TOL
