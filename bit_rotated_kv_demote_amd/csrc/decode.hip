@@ -597,17 +597,21 @@ DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_s
   const int max_hist = max(0, max_seq_len - kSink - kRecent);
   const int max_pages = (max_hist + kPage - 1) / kPage;
   const long n_groups = (long)batch * hkv * n_colgroups;
-  const long total_pages = n_groups * max_pages;
-  long pps = (total_pages + target - 1) / target;
-  pps = ((pps + 7) / 8) * 8;
+  const int max_tile = min(max_seq_len, kSink + kRecent);
+  const int n_tile = (max_tile + kTileTokens - 1) / kTileTokens;
+  // The most history splits per group that keep the grid within `target`
+  // workgroups; each split then gets the smallest even page count that
+  // covers the history with that many (a page pair is one wave step).
+  const long hist_max = target / n_groups - n_tile;
+  long pps = hist_max >= 1 ? (max_pages + hist_max - 1) / hist_max : kMaxPagesPerSplit;
+  pps = (pps + 1) & ~1L;
   if (pps < 8) pps = 8;
   if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
   while (max_pages > 0 && (max_pages + pps - 1) / pps > kMaxSplits - 4 && pps < kMaxPagesPerSplit) pps += 8;
   p.ok = max_pages == 0 || (max_pages + pps - 1) / pps <= kMaxSplits - 4;
   p.pages_per_split = (int)pps;
   p.n_hist_splits = max_pages > 0 ? (int)((max_pages + pps - 1) / pps) : 0;
-  const int max_tile = min(max_seq_len, kSink + kRecent);
-  p.n_tile_splits = (max_tile + kTileTokens - 1) / kTileTokens;
+  p.n_tile_splits = n_tile;
   p.n_splits_total = p.n_hist_splits + p.n_tile_splits;
   p.n_work = (int)(n_groups * p.n_splits_total);
   p.grid = ((p.n_work + 7) / 8) * 8;

@@ -84,7 +84,7 @@ struct DecodeArgs {
   int hkv;
   int max_pages;
   int n_hist_splits;          // history splits per (sequence, KV head)
-  int pages_per_split;        // multiple of 8
+  int pages_per_split;        // even
   int n_tile_splits;          // BF16 sink/recent splits per (sequence, KV head)
   int n_groups_total;         // batch * Hkv * n_colgroups
   int grid_per_xcd;
@@ -151,11 +151,11 @@ struct DecodePlan {
 // four waves keeps the page ids of its share in one 64-lane register)
 constexpr int kMaxPagesPerSplit = 256;
 
-// Workgroups a decode launch aims at (history pages split evenly over them):
-// about two per compute unit for oscar_decode, whose history splits each load
-// all of R_K; the fused step's splits read q . R_K precomputed instead.
-constexpr int kDecodeSplitTarget = 480;
-constexpr int kStepSplitTarget = 480;
+// Workgroups a decode launch may fill with its splits: two per compute unit
+// (256 CUs), for oscar_decode and for the fused step alike.  Larger batches
+// than this can split exceed it (every group keeps at least one history split).
+constexpr int kDecodeSplitTarget = 512;
+constexpr int kStepSplitTarget = 512;
 
 // group: columns per work item (1, 2, 4, 8 or 16); n_colgroups column groups
 // per (sequence, KV head)
