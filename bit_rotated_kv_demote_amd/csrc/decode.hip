@@ -56,10 +56,12 @@ struct PageCodes<4> {
   u32x4_t k, v;
 };
 
-// A wave walks its share of a split in steps of kStepPages pages: wave w
-// takes steps w, w + 4, ...  While one step is processed the next one is in
-// flight.
-constexpr int kStepPages = 2;
+// A wave walks its share of a split in steps of kStepPages pages (64
+// tokens, 6 KiB of INT2 blocks): wave w takes steps w, w + 4, ...  While one
+// step is processed the next one is in flight.  The two steps' registers
+// take the kernel past three workgroups per compute unit; the decode plan
+// fills two.
+constexpr int kStepPages = 4;
 
 // Shared memory of one workgroup (256 threads = 4 waves).
 template <int G>
@@ -577,15 +579,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
 }
 
-// kPreRot: q . R_K comes precomputed (the fused step) instead of R_K and q
+// kPreRot: q . R_K comes precomputed (the fused step) instead of R_K and q.
+// Two workgroups per compute unit (up to 256 VGPRs per lane).
 template <int G, bool kPreRot = false>
-__global__ __launch_bounds__(256, G <= 4 ? 3 : 2) void decode_int2_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_int2_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
   decode_body<G, 2, kPreRot>(a, sm);
 }
 
 // INT4 pool: the same kernel over 2560-byte blocks (twice the code registers
-// per step in flight, so two workgroups per compute unit)
+// per step in flight)
 template <int G, bool kPreRot = false>
 __global__ __launch_bounds__(256, 2) void decode_int4_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
@@ -600,11 +603,11 @@ DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_s
   const int max_tile = min(max_seq_len, kSink + kRecent);
   const int n_tile = (max_tile + kTileTokens - 1) / kTileTokens;
   // The most history splits per group that keep the grid within `target`
-  // workgroups; each split then gets the smallest even page count that
-  // covers the history with that many (a page pair is one wave step).
+  // workgroups; each split then gets the smallest multiple of kStepPages
+  // pages (one wave step) that covers the history with that many.
   const long hist_max = target / n_groups - n_tile;
   long pps = hist_max >= 1 ? (max_pages + hist_max - 1) / hist_max : kMaxPagesPerSplit;
-  pps = (pps + 1) & ~1L;
+  pps = (pps + kStepPages - 1) / kStepPages * kStepPages;
   if (pps < 8) pps = 8;
   if (pps > kMaxPagesPerSplit) pps = kMaxPagesPerSplit;
   while (max_pages > 0 && (max_pages + pps - 1) / pps > kMaxSplits - 4 && pps < kMaxPagesPerSplit) pps += 8;

@@ -84,7 +84,7 @@ struct DecodeArgs {
   int hkv;
   int max_pages;
   int n_hist_splits;          // history splits per (sequence, KV head)
-  int pages_per_split;        // even
+  int pages_per_split;        // a multiple of the wave step (4 pages)
   int n_tile_splits;          // BF16 sink/recent splits per (sequence, KV head)
   int n_groups_total;         // batch * Hkv * n_colgroups
   int grid_per_xcd;
