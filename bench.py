@@ -749,7 +749,10 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--layers", type=int, default=24, help="distinct pools cycled (>512 MB total)")
-    ap.add_argument("--no-extra", action="store_true", help="only the 32K tiered step")
+    ap.add_argument("--no-extra", action="store_true", help="only the tiered step")
+    ap.add_argument("--ctx", type=int, default=32768,
+                    help="cached tokens of the timed step (default 32768, the Qwen3-4B-shaped workload; "
+                         "other values for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="append one plain device copy of this many MB (counter calibration runs)")
@@ -762,8 +765,8 @@ def main():
     from bit_rotated_kv_demote_amd import binding
     binding.load()
 
-    hq, hkv, n0 = 32, 8, 32768
-    res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001)
+    hq, hkv, n0 = 32, 8, args.ctx
+    res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001 if n0 == 32768 else 1002)
     dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
     # the roofline kernel: the decode's split kernel (oscar_decode_partials)
     split_gbps = res["split_bytes"] / (res["split_us"] * 1e3)
@@ -854,12 +857,14 @@ def main():
         "vs_baseline": None,
         "dtype": "int2-kv/fp32-acc",
         "data": "synthetic",
-        "config": {"workload": "qwen3-4b-shaped tiered decode step (oscar_step: append + decode): 32 q / 8 KV heads, "
-                               "head_dim 128, batch 1, 32768 cached tokens + 1 appended per step, "
+        "config": {"workload": {32768: "qwen3-4b-shaped ", 131072: "qwen3-8b-shaped "}.get(n0, "") +
+                               "tiered decode step (oscar_step: append + decode): 32 q / 8 KV heads, "
+                               f"head_dim 128, batch 1, {n0} cached tokens + 1 appended per step, "
                                "64 bf16 sink / int2 history / 256 bf16 recent, 16-token pages",
                    "global_batch": 1, "seq_len": n0, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(split_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(split_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic()},
+                     "frac": round(split_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic() if n0 == 32768 else None},
         "cpu_baseline": cpu,
         "extra": extra,
     }
