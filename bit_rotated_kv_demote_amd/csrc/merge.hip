@@ -21,11 +21,19 @@ namespace {
 constexpr int kParts = 8;          // record rows handled side by side (256 threads / 32 float4 columns)
 constexpr int kMergeBatch = 8;     // record loads in flight per thread: 64 splits per round
 
+// kRB workgroups per head, each writing kD / kRB output rows: every one
+// merges the head's records (the whole rotated sum is needed for any output
+// row) but loads only its kD / kRB rows of R.  kRB = 4 when the heads are
+// few (the loads of R, 64 KiB per head, then dominate each workgroup).
+template <int kRB>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int kRows = kD / kRB;          // output rows of this workgroup
+  constexpr int kColParts = 256 / kRows;   // threads sharing one row of R
+  constexpr int kCols = kD / kColParts;    // columns of R per thread
   __shared__ float w[kMaxSplits];
   __shared__ float4 red[kParts][2][kD / 4];
   __shared__ float oh[2][kD];      // weighted sums: plain part, rotated part
-  __shared__ float rr[2][kD];      // the two halves of (rotated part . R^T)
+  __shared__ float rr[kColParts][kRows];   // partial sums of (rotated part . R^T)
   __shared__ float wred[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
@@ -43,23 +51,25 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const float* base = a.partials + (size_t)grp * n_slots * G * kPartStride + (size_t)h * kPartStride;
   auto rec = [&](int s) { return base + (size_t)min(s, n_slots - 1) * G * kPartStride; };
 
+  const int row0 = kRows * blockIdx.y;     // first output row of this workgroup
   // Every load first, before the sequence length is known: (m, l) of every
   // slot, the first round of record columns and this thread's slice of R
-  // (row ri, columns [64 jh, 64 jh + 64)).  Slots the first kernel left
-  // untouched for this length are masked below, never multiplied in.
+  // (row row0 + ri, columns [kCols jh, kCols jh + kCols)).  Slots the first
+  // kernel left untouched for this length are masked below, never
+  // multiplied in.
   const float2 ml0 = *reinterpret_cast<const float2*>(rec(tid) + kD);
   const float2 ml1 = *reinterpret_cast<const float2*>(rec(tid + 256) + kD);
   const int c4 = tid & 31, part = tid >> 5;
   float4 v[kMergeBatch];
 #pragma unroll
   for (int u = 0; u < kMergeBatch; ++u) v[u] = *reinterpret_cast<const float4*>(rec(part + kParts * u) + 4 * c4);
-  const int ri = tid & (kD - 1), jh = tid >> 7;
-  float4 rrow[16];
+  const int ri = tid % kRows, jh = tid / kRows;
+  float4 rrow[kCols / 4];
   if (a.tiered) {
     const float* rot = a.rot + (size_t)(hq / a.g_model) * a.rot_kv_stride;
-    const float4* rp = reinterpret_cast<const float4*>(rot + (size_t)ri * kD + 64 * jh);
+    const float4* rp = reinterpret_cast<const float4*>(rot + (size_t)(row0 + ri) * kD + kCols * jh);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
+    for (int e = 0; e < kCols / 4; ++e) rrow[e] = rp[e];
   }
 
   // the splits the first kernel filled for this sequence (clamped to the
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     n_rot = 0;
   }
   if (n_plain + n_rot <= 0) {       // no tokens: nothing to attend
-    if (tid < kD) a.out[(size_t)head * kD + tid] = 0.0f;
+    if (tid < kRows) a.out[(size_t)head * kD + row0 + tid] = 0.0f;
     return;
   }
   auto active = [&](int s) { return s < a.n_plain_slots ? s < n_plain : s - a.n_plain_slots < n_rot; };
@@ -139,8 +149,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   float acc = 0.0f;
   if (n_rot > 0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float4 y = *reinterpret_cast<const float4*>(&oh[1][64 * jh + 4 * e]);
+    for (int e = 0; e < kCols / 4; ++e) {
+      const float4 y = *reinterpret_cast<const float4*>(&oh[1][kCols * jh + 4 * e]);
       acc = fmaf(y.x, rrow[e].x, acc);
       acc = fmaf(y.y, rrow[e].y, acc);
       acc = fmaf(y.z, rrow[e].z, acc);
@@ -151,7 +161,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   __syncthreads();
   // (l_all is 0 only if every token was masked for this query, a length
   // shorter than the query count)
-  if (tid < kD) a.out[(size_t)head * kD + tid] = l_all > 0.0f ? (oh[0][tid] + (rr[0][tid] + rr[1][tid])) / l_all : 0.0f;
+  if (tid < kRows) {
+    float r = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kColParts; ++p) r += rr[p][tid];
+    const int i = row0 + tid;
+    a.out[(size_t)head * kD + i] = l_all > 0.0f ? (oh[0][i] + r) / l_all : 0.0f;
+  }
 }
 
 // Large grids: one workgroup per record group (sequence, KV head, column
@@ -272,10 +288,13 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
 
 hipError_t launch_merge(const MergeArgs& a, int n_heads, hipStream_t st) {
   if (n_heads <= 0) return hipSuccess;
-  // up to about three workgroups per compute unit: one workgroup per head
-  // spreads the latency; beyond that, one per record group shares R
-  if (n_heads <= 768 || a.group < 2)
-    hipLaunchKernelGGL(merge_kernel, dim3(n_heads), dim3(256), 0, st, a);
+  // few heads: four workgroups per head (a quarter of R each); up to about
+  // three workgroups per compute unit: one workgroup per head spreads the
+  // latency; beyond that, one per record group shares R
+  if (n_heads <= 64)
+    hipLaunchKernelGGL(merge_kernel<4>, dim3(n_heads, 4), dim3(256), 0, st, a);
+  else if (n_heads <= 768 || a.group < 2)
+    hipLaunchKernelGGL(merge_kernel<1>, dim3(n_heads), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(merge_group_kernel, dim3(n_heads / a.group), dim3(256), 0, st, a);
   return hipGetLastError();
