@@ -483,16 +483,32 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
     const int recent_first = max(kSink, n - kRecent);
     const size_t sink_base = ((size_t)slot * a.hkv + hk) * kSink;
     const size_t ring_base = ((size_t)slot * a.hkv + hk) * kRecent;
-    auto row = [&](const uint16_t* sink, const uint16_t* ring, int uu) -> const uint16_t* {
+    // the fused step: the token at position n - 1 is still in k_new / v_new
+    const size_t new_row = ((size_t)b * a.hkv + hk) * kD;
+    const bool from_args = kPreRot && a.k_new != nullptr;
+    if (from_args && split == 0 && cg == 0 && tid < kD) {
+      // tile split 0 of the group moves it into its sink or ring slot (no
+      // other workgroup of this launch reads that slot)
+      const int pn = n - 1, half_sel = tid >> 6, w = tid & 63;
+      // (the pool's tiers are writable device memory; the decode reads them
+      // through const pointers)
+      uint16_t* dst = const_cast<uint16_t*>(
+          pn < kSink ? (half_sel ? a.sink_v : a.sink_k) + (sink_base + pn) * kD
+                     : (half_sel ? a.recent_v : a.recent_k) + (ring_base + ((pn - kSink) & (kRecent - 1))) * kD);
+      reinterpret_cast<uint32_t*>(dst)[w] =
+          reinterpret_cast<const uint32_t*>((half_sel ? a.v_new : a.k_new) + new_row)[w];
+    }
+    auto row = [&](const uint16_t* sink, const uint16_t* ring, const uint16_t* fresh, int uu) -> const uint16_t* {
       const int u = u0 + uu;
+      const int pos = u < n_sink_used ? u : recent_first + (u - n_sink_used);
+      if (from_args && pos == n - 1) return fresh + new_row;
       if (u < n_sink_used) return sink + (sink_base + u) * kD;
-      const int pos = recent_first + (u - n_sink_used);
       return ring + (ring_base + ((pos - kSink) & (kRecent - 1))) * kD;
     };
     // causal limit of column x: its query's position n - q_tokens + t
     bf16_span_wave<G>(q_row, min(kTileTokens, n_tile - u0),
-                      [&](int uu) { return row(a.sink_k, a.recent_k, uu); },
-                      [&](int uu) { return row(a.sink_v, a.recent_v, uu); },
+                      [&](int uu) { return row(a.sink_k, a.recent_k, a.k_new, uu); },
+                      [&](int uu) { return row(a.sink_v, a.recent_v, a.v_new, uu); },
                       [&](int uu) { const int u = u0 + uu; return u < n_sink_used ? u : recent_first + (u - n_sink_used); },
                       [&](int x) { return n - a.q_tokens + (cg * G + x) / a.g_model; }, n - a.q_tokens, sm, wave,
                       lane);

@@ -95,6 +95,10 @@ struct DecodeArgs {
   int q_tokens;
   int g_model;
   int n_colgroups;
+  // nullable (the fused step): the token appended this step, bf16
+  // [batch][Hkv][128], not yet in its sink or ring slot; the tile splits
+  // read position n - 1 from here and tile split 0 writes it into the slot
+  const uint16_t* k_new; const uint16_t* v_new;
 };
 
 struct DecodeBf16Args {

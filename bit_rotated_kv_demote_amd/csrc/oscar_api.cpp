@@ -80,7 +80,8 @@ enum DecodePhases { kPhaseSplits = 1, kPhaseMerge = 2, kPhaseBoth = 3 };
 static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                                   const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
                                   float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
-                                  void* stream, int phases = kPhaseBoth);
+                                  void* stream, int phases = kPhaseBoth, const void* k_new = nullptr,
+                                  const void* v_new = nullptr);
 
 namespace {
 // fused step workspace: q . R_K (fp32, q's layout), the decode lengths, then
@@ -291,7 +292,7 @@ oscar_status oscar_decode_merge(const oscar_layer_desc* desc, const oscar_pool* 
 static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                                   const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
                                   float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
-                                  void* stream, int phases) {
+                                  void* stream, int phases, const void* k_new, const void* v_new) {
   oscar_status st = check_desc(desc);
   if (st != OSCAR_OK) return st;
   if ((st = check_pool(pool, max_seq_len > 320)) != OSCAR_OK) return st;
@@ -324,6 +325,9 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   a.rot_kv_stride = rot_stride(pool);
   a.code_bits = pool->code_bits;
   a.q_rot = q_rot;
+  // the fused step: this step's token reaches its sink or ring slot in the decode launch
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
   a.partials = static_cast<float*>(workspace);
   a.hkv = hkv;
   a.max_pages = pool->max_pages_per_seq;
@@ -459,7 +463,8 @@ oscar_status oscar_step(const oscar_layer_desc* desc, const oscar_pool* pool, co
   a.len_out = lens;
   if ((st = hip_status(launch_append(a, batch, static_cast<hipStream_t>(stream)))) != OSCAR_OK) return st;
   return decode_tiered(desc, pool, seq_slot, lens, q, q_rot, 1, out, partials,
-                       ws_bytes - step_qrot_bytes(desc, batch) - step_len_bytes(batch), batch, max_seq_len, stream);
+                       ws_bytes - step_qrot_bytes(desc, batch) - step_len_bytes(batch), batch, max_seq_len, stream,
+                       kPhaseBoth, k_new, v_new);
 }
 
 }  // extern "C"

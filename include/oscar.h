@@ -325,11 +325,14 @@ oscar_status oscar_decode_merge(const oscar_layer_desc* desc, const oscar_pool* 
  * oscar_step -- one decode step of a layer in one call: oscar_append of the
  * new token (k_new, v_new at position[b], as there) followed by oscar_decode
  * of q over the position[b] + 1 cached tokens ([yunpan] 三.1: the new token is
- * appended before it attends; [gist] 2.2 B).  The append launch gets a third
- * slice of workgroups that computes q . R_K of each sequence's query heads
- * beside the demotion; the decode's history splits read those rotated
- * queries instead of loading R_K themselves.  Results equal oscar_append
- * followed by oscar_decode up to fp32 summation order.
+ * appended before it attends; [gist] 2.2 B).  The append launch demotes
+ * the token leaving the ring (two workgroups per vector, each rotating half
+ * of the channels) and computes q . R_K of each sequence's query heads
+ * beside it; the decode's history splits read those rotated queries instead
+ * of loading R_K themselves, and the decode launch reads the new token from
+ * k_new / v_new and writes it into its sink or ring slot.  Results equal
+ * oscar_append followed by oscar_decode up to fp32 summation order, and the
+ * pool afterwards holds the same bytes.
  * position, seq_slot: device int32 [batch] (positions before the append, not
  * advanced by the call); q: device bf16 [batch][Hq][128]; out: device fp32
  * [batch][Hq][128]; max_seq_len >= max(position) + 1.  workspace: device,
