@@ -344,3 +344,22 @@ def test_decode_phase_calls_validation(lib):
     bad.page_size = 8
     assert lib.oscar_decode_merge(ctypes.byref(bad), ctypes.byref(pool), 256, 256, 256, 1 << 30, 1, 1000,
                                   None) == -2
+
+
+def test_decode_plan_fills_two_workgroups_per_cu():
+    # The split plan: at most 512 workgroups (two per compute unit), each
+    # (sequence, KV head) group takes ceil(min(n, 320) / 128) tile splits and
+    # as many history splits as fit, each a multiple of four pages (one wave
+    # step); one record of G x 132 fp32 per split and column group.
+    d = binding.layer_desc(32, 8)
+    rec = 4 * 132 * 4                       # G = 4 heads, 132 floats each
+    # 32K: 2029 pages -> 61 splits would need 34 pages, rounded to 36 -> 57 + 3 tile splits
+    assert binding.oscar_decode_workspace_bytes(d, 1, 32769) == 8 * 60 * rec
+    # 128K: 8173 pages -> 136 pages per split -> 61 + 3
+    assert binding.oscar_decode_workspace_bytes(d, 1, 131073) == 8 * 64 * rec
+    # batch 2 at 32K: 29 history splits of 72 pages + 3 per group
+    assert binding.oscar_decode_workspace_bytes(d, 2, 32769) == 16 * 32 * rec
+    # 1040 groups cannot split within 512: one history split of up to 256 pages per 1004 -> 4, + 3
+    assert binding.oscar_decode_workspace_bytes(d, 130, 16384) == 1040 * 7 * rec
+    # the fused step uses the same plan plus its rotated queries and lengths
+    assert binding.oscar_step_workspace_bytes(d, 1, 32769) == 8 * 60 * rec + 32 * 512 + 256
