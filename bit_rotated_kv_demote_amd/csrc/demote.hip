@@ -125,18 +125,29 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
   if (demote) {                        // block-uniform
     __syncthreads();
-    // lanes l and l + 32 of a wave hold row slices 2w and 2w + 1 of the same
-    // columns: one lane swap, then the four waves' sums through LDS
+    // The sum over the 128 rows is associated exactly as in the fused step's
+    // append (append_step_kernel), so both leave the same bytes: fma chains
+    // over 8 rows each (rows [8 r, 8 r + 8)), chains r and r + 1 added,
+    // then the pair sums of lanes l and l + 32 (row slices 2w and 2w + 1),
+    // then the four waves' sums pairwise through LDS.
     auto rotate_into = [&](const float* x, float* dst_row /* [4][kD] */) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), acc2 = acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float xe = x[16 * rs + e];
+      for (int e = 0; e < 8; ++e) {
+        const float xe = x[16 * rs + e], xf = x[16 * rs + 8 + e];
         acc.x = fmaf(xe, rq[e].x, acc.x);
         acc.y = fmaf(xe, rq[e].y, acc.y);
         acc.z = fmaf(xe, rq[e].z, acc.z);
         acc.w = fmaf(xe, rq[e].w, acc.w);
+        acc2.x = fmaf(xf, rq[8 + e].x, acc2.x);
+        acc2.y = fmaf(xf, rq[8 + e].y, acc2.y);
+        acc2.z = fmaf(xf, rq[8 + e].z, acc2.z);
+        acc2.w = fmaf(xf, rq[8 + e].w, acc2.w);
       }
+      acc.x += acc2.x;
+      acc.y += acc2.y;
+      acc.z += acc2.z;
+      acc.w += acc2.w;
       acc.x += __shfl_xor(acc.x, 32);
       acc.y += __shfl_xor(acc.y, 32);
       acc.z += __shfl_xor(acc.z, 32);

@@ -153,19 +153,6 @@ class PagedBF16:
         binding.oscar_decode_bf16(self.desc, self.pool, seq_slot, seq_len, q, out, self._ws, batch, max_seq_len)
         return out
 
-    def step(self, position, k_new, v_new, q, max_seq_len, out=None, seq_slot=None):
-        """One fused decode step: append (k_new, v_new) at position, then decode q
-        over position + 1 tokens.  k_new, v_new: bf16 [B, Hkv, 128]; q: bf16 [B, Hq, 128]."""
-        batch = q.shape[0]
-        if out is None:
-            out = torch.empty((batch, self.hq, HEAD_DIM), dtype=torch.float32, device=self.device)
-        nbytes = binding.oscar_step_workspace_bytes(self.desc, batch, max_seq_len)
-        if self._step_ws is None or self._step_ws.numel() < nbytes:
-            self._step_ws = torch.zeros(((nbytes + 255) // 256) * 256, dtype=torch.uint8, device=self.device)
-        binding.oscar_step(self.desc, self.pool, seq_slot, position, k_new, v_new, q, out, self._step_ws, batch,
-                           max_seq_len)
-        return out
-
     def decode_multi(self, q, seq_len, max_seq_len, out=None, seq_slot=None):
         """q: bf16 [B, T, Hq, 128], the queries of each sequence's last T positions."""
         batch, n_query = q.shape[0], q.shape[1]

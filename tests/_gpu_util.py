@@ -113,3 +113,46 @@ def code_diff_stats(hist_a, hist_b, pages, slots):
         ulp = np.where(same_sign, np.abs(a - b), np.abs(a) + np.abs(b))
         meta.append(ulp.max() if ulp.size else 0)
     return float(np.mean(diffs != 0)), int(np.abs(diffs).max()) if diffs.size else 0, max(meta)
+
+
+# Bounds of the fused path (the spec contract): at most 0.1 % of the
+# codes of demoted tokens differ from the oracle's, each by at most one level,
+# and scale / zero lie within 2 fp16 ulp; decode outputs over identical pool
+# bytes match within 2e-3 relative L2.
+FLIP_RATE, FLIP_MAX, META_ULP = 1e-3, 1, 2
+DECODE_TOL = 2e-3
+
+
+def check_state_vs_oracle(state, opool: orc.Pool, demoted):
+    """Device pool bytes after device appends / demotions against the oracle's
+    pool after the same appends: the BF16 tiers byte for byte, the history
+    codes of the demoted tokens within the flip budget.
+
+    demoted: list of (slot, history indices) the compared path demoted."""
+    for name in ("sink_k", "sink_v", "recent_k", "recent_v"):
+        assert np.array_equal(state[name], getattr(opool, name)), name
+    pages, slots = [], []
+    for slot, h in demoted:
+        h = np.asarray(h, np.int64)
+        if h.size:
+            pages.append(opool.page_table[slot, h // 16])
+            slots.append(h % 16)
+    if not pages:
+        return 0.0
+    pages, slots = np.concatenate(pages), np.concatenate(slots)
+    # in chunks of tokens (a 128K history is 1.6 GB of gathered blocks at once)
+    n_diff = n_codes = maxd = meta_ulp = 0
+    for i in range(0, len(pages), 8192):
+        rate, md, mu = code_diff_stats(state["hist"], opool.hist, pages[i:i + 8192], slots[i:i + 8192])
+        n = len(pages[i:i + 8192]) * opool.hkv * 256
+        n_diff += rate * n
+        n_codes += n
+        maxd, meta_ulp = max(maxd, md), max(meta_ulp, mu)
+    rate = n_diff / n_codes
+    assert rate <= FLIP_RATE and maxd <= FLIP_MAX and meta_ulp <= META_ULP, (rate, maxd, meta_ulp)
+    return rate
+
+
+def decode_over_device_bytes(state, hkv, q_bits, slots, lengths, r_k, r_v, heads=None):
+    """The oracle's decode over the device's own pool bytes (copied back)."""
+    return orc.decode_tiered(q_bits, orc.Pool.from_state(state, hkv), slots, lengths, r_k, r_v, heads=heads)

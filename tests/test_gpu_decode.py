@@ -14,7 +14,7 @@ import oracle as orc
 from bit_rotated_kv_demote_amd import synth
 from bit_rotated_kv_demote_amd.pool import PagedBF16, bf16_tensor
 
-from _gpu_util import Layer, i32, rel_l2, upload
+from _gpu_util import Layer, check_state_vs_oracle, decode_over_device_bytes, i32, rel_l2, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -59,9 +59,11 @@ def test_decode_tiny_config_32_steps():
 
 
 def test_decode_end_to_end_with_device_appends():
-    # Device append + device decode against oracle append + oracle decode.  The
-    # two pools differ by the fused rotation's rare code flips, so this uses
-    # the end-to-end bound 5e-3 rather than the identical-bytes bound.
+    # Device append + device decode, checked in two parts against the oracle:
+    # the device's bytes after its own appends against the oracle's pool after
+    # the same appends (tiers byte for byte, demoted codes within the fused
+    # budget), and each decode against the oracle's decode of the device's
+    # own bytes (2e-3).
     n0, steps = 700, 24
     layer = Layer(seed=1001, batch=1, hq=4, hkv=1, max_len=n0 + steps, n_q=steps)
     opool = layer.oracle_pool([n0])
@@ -74,8 +76,9 @@ def test_decode_end_to_end_with_device_appends():
                    bf16_tensor(np.ascontiguousarray(layer.v[:, p])))
         q = np.ascontiguousarray(layer.q[s])
         out = dev.decode(bf16_tensor(q), i32([p + 1]), n0 + steps).cpu().numpy()
-        ref = orc.decode_tiered(q, opool, [0], [p + 1], layer.rot, layer.rot)
-        assert rel_l2(out, ref) <= 5e-3, s
+        ref = decode_over_device_bytes(dev.host_state(), 1, q, [0], [p + 1], layer.rot, layer.rot)
+        assert rel_l2(out, ref) <= TOL, s
+    check_state_vs_oracle(dev.host_state(), opool, [(0, np.arange(n0 - 320, n0 + steps - 320))])
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
@@ -254,6 +257,33 @@ def test_bf16_baseline_matches_oracle():
     ref = orc.decode_bf16(q, kv, pt, [0, 1, 2], lengths)
     for b in range(len(lengths)):
         assert rel_l2(out[b], ref[b]) <= TOL, lengths[b]
+
+
+@pytest.mark.parametrize("n,kv_heads", [(32768, [0, 3, 6]), (131072, [1, 6])])
+def test_bf16_baseline_full_size_sampled_heads(n, kv_heads):
+    # The BF16 baseline at the sizes the benchmark times it (32 q / 8 KV heads,
+    # one sequence of 32768 or 131072 tokens, shuffled pages): the query heads
+    # of some KV heads against the oracle's decode of the same pool bytes.
+    hq, hkv = 32, 8
+    st = synth.streams(1700 + n % 1000)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], n, hkv, out_ch)
+    v = synth.kv_tokens(st["v"], st["lognormal"], n, hkv, out_ch)
+    pages = math.ceil(n / 16)
+    pt = synth.page_permutation(st["perm"], pages)[None, :].astype(np.int32)
+    kv = np.zeros((pages, hkv, 2, 16, 128), np.uint16)
+    pos = np.arange(n)
+    kv[pt[0, pos // 16], :, 0, pos % 16] = k
+    kv[pt[0, pos // 16], :, 1, pos % 16] = v
+    q = synth.queries(st["q"], (1, hq, 128))
+    pool = PagedBF16(hq, hkv, kv, pt)
+    out = pool.decode(bf16_tensor(q), i32([n]), n).cpu().numpy()
+    # the oracle over the sampled KV heads only (a pool view of those heads)
+    sub = np.ascontiguousarray(kv[:, kv_heads])
+    q_sub = np.ascontiguousarray(np.concatenate([q[:, 4 * j:4 * j + 4] for j in kv_heads], axis=1))
+    ref = orc.decode_bf16(q_sub, sub, pt, [0], [n])
+    got = np.concatenate([out[:, 4 * j:4 * j + 4] for j in kv_heads], axis=1)
+    assert rel_l2(got, ref) <= TOL
 
 
 @pytest.mark.parametrize("hq,hkv,lengths", [(8, 2, [1500, 300, 2047]), (16, 2, [5000, 64])])

@@ -613,6 +613,47 @@ def _bf16_pool_of(n, hkv, seed):
     return kv, pt, k, v
 
 
+def test_bf16_pool_gather_and_decode_by_brute_force():
+    # The BF16 baseline's page gather against the original tokens.  Two
+    # sequences share a pool of 7 physical pages through a shuffled table:
+    # sequence 0 holds 53 tokens (three full pages and a partial fourth),
+    # sequence 1 holds 20 (one full page and a partial one).  Every row no
+    # token was written to holds a sentinel (bf16 1000.0), so a wrong page id,
+    # a wrong row within a page or a wrong table row changes the result.
+    rng = np.random.default_rng(31)
+    hkv, hq = 2, 4
+    lens = [53, 20]
+    table = np.array([[5, 2, 6, 0], [3, 1, 4, 4]], np.int32)   # [sequence][logical page] -> physical page
+    sentinel = synth.to_bf16_bits(np.array([1000.0], np.float32))[0]
+    pool = np.full((7, hkv, 2, 16, 128), sentinel, np.uint16)
+    toks = []
+    for b, n in enumerate(lens):
+        k = synth.to_bf16_bits(rng.standard_normal((n, hkv, 128)).astype(np.float32))
+        v = synth.to_bf16_bits(rng.standard_normal((n, hkv, 128)).astype(np.float32))
+        toks.append((k, v))
+        for j in range((n + 15) // 16):                 # page by page, rows [0, rows)
+            rows = min(16, n - 16 * j)
+            pool[table[b, j], :, 0, :rows] = np.swapaxes(k[16 * j:16 * j + rows], 0, 1)
+            pool[table[b, j], :, 1, :rows] = np.swapaxes(v[16 * j:16 * j + rows], 0, 1)
+    q = synth.to_bf16_bits(rng.standard_normal((2, hq, 128)).astype(np.float32))
+    out = orc.decode_bf16(q, pool, table, [0, 1], lens)
+    for b, n in enumerate(lens):
+        k, v = toks[b]
+        kk, vv = orc.bf16_pool_gather(pool, table[b], n)
+        assert np.array_equal(kk, np.swapaxes(synth.bf16_bits_to_f32(k), 0, 1).astype(np.float64))
+        assert np.array_equal(vv, np.swapaxes(synth.bf16_bits_to_f32(v), 0, 1).astype(np.float64))
+        for h in range(hq):
+            # softmax attention written out token by token
+            qh = synth.bf16_bits_to_f32(q[b, h]).astype(np.float64)
+            kf = synth.bf16_bits_to_f32(k[:, h // 2]).astype(np.float64)
+            vf = synth.bf16_bits_to_f32(v[:, h // 2]).astype(np.float64)
+            logits = [float(np.dot(qh, kf[t])) / math.sqrt(128.0) for t in range(n)]
+            top = max(logits)
+            w = [math.exp(x - top) for x in logits]
+            want = sum(w[t] * vf[t] for t in range(n)) / sum(w)
+            assert np.allclose(out[b, h], want, rtol=0, atol=1e-12), (b, h)
+
+
 def test_bf16_tail_first_of_two_sees_only_itself_and_last_equals_decode():
     kv, pt, k, v = _bf16_pool_of(2, 1, 21)
     q = synth.queries(np.random.default_rng(6), (1, 2, 2, 128))
