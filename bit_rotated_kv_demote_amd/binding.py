@@ -16,13 +16,13 @@ LIB_PATH = os.path.join(HERE, "libamdoscar.so")
 
 OSCAR_SRC_BF16 = 0
 OSCAR_SRC_F32_ROTATED = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTED = ("oscar_abi_version", "oscar_status_string", "oscar_calibrate", "oscar_calibrate_layers", "oscar_append", "oscar_demote",
             "oscar_prefill", "oscar_decode", "oscar_decode_workspace_bytes", "oscar_decode_partials", "oscar_decode_merge", "oscar_decode_multi",
             "oscar_decode_multi_workspace_bytes", "oscar_decode_bf16", "oscar_decode_bf16_workspace_bytes",
             "oscar_decode_bf16_multi", "oscar_decode_bf16_multi_workspace_bytes", "oscar_step",
-            "oscar_step_workspace_bytes")
+            "oscar_step_workspace_bytes", "oscar_step_noalloc")
 
 
 class OscarError(RuntimeError):
@@ -94,6 +94,8 @@ def load():
     lib.oscar_decode_merge.argtypes = [P, P, P, P, P, SZ, I32, I32, P]
     lib.oscar_step.restype = ctypes.c_int
     lib.oscar_step.argtypes = [P, P, P, P, P, P, P, P, P, SZ, I32, I32, P]
+    lib.oscar_step_noalloc.restype = ctypes.c_int
+    lib.oscar_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, I32, I32, P]
     lib.oscar_step_workspace_bytes.restype = SZ
     lib.oscar_step_workspace_bytes.argtypes = [P, I32, I32]
     lib.oscar_decode_multi.restype = ctypes.c_int
@@ -221,6 +223,15 @@ def oscar_step(desc, pool, seq_slot, position, k_new, v_new, q, out, workspace, 
     _check("oscar_step", load().oscar_step(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_slot), _ptr(position),
                                             _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), _ptr(workspace), ws_bytes,
                                             batch, max_seq_len, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def oscar_step_noalloc(desc, pool, seq_slot, position, k_new, v_new, q, out, batch, max_seq_len, stream=None):
+    _check("oscar_step_noalloc", load().oscar_step_noalloc(ctypes.byref(desc), ctypes.byref(pool), _ptr(seq_slot),
+                                                            _ptr(position), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                                            _ptr(out), batch, max_seq_len, _stream(stream)))
 
 
 def oscar_decode_multi_workspace_bytes(desc, batch, n_query, max_seq_len) -> int:

@@ -21,7 +21,7 @@ DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
                 # matrix-core accumulators in VGPRs: no AGPR <-> VGPR copies in
                 # loops whose accumulators are also touched by vector code
                 "-mllvm", "-amdgpu-mfma-vgpr-form"]
-HIP_SOURCES = ["demote.hip", "decode.hip", "decode_bf16.hip", "merge.hip"]
+HIP_SOURCES = ["demote.hip", "decode.hip", "decode_bf16.hip", "merge.hip", "noalloc.hip"]
 HOST_HIP_SOURCES = ["oscar_api.cpp"]      # host code that needs the HIP runtime headers
 HOST_SOURCES = ["calibrate.cpp"]          # plain C++
 

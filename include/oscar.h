@@ -89,7 +89,7 @@
 extern "C" {
 #endif
 
-#define OSCAR_ABI_VERSION 5
+#define OSCAR_ABI_VERSION 6
 
 typedef enum {
   OSCAR_OK = 0,
@@ -348,6 +348,28 @@ oscar_status oscar_step(const oscar_layer_desc* desc, const oscar_pool* pool, co
 /* Workspace of oscar_step: the decode's plus batch * Hq * 512 bytes of
  * rotated queries and the step's lengths; 0 for an unsupported shape. */
 size_t oscar_step_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len);
+
+/*
+ * oscar_step_noalloc -- oscar_step for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results as oscar_step, with the
+ * workspace in a static device array of OSCAR_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on each GPU it runs on until the process ends.
+ * The call allocates and frees nothing.  Arguments as for oscar_step
+ * without workspace and ws_bytes; the GPU is the device of `stream` (the
+ * current device for the null stream).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (concurrent streams or
+ * threads) race and must be serialised by the caller.  No byte of the array
+ * has to start at any value (each call writes everything it reads first).
+ * Errors: as oscar_step; OSCAR_ERR_CAPACITY when
+ * oscar_step_workspace_bytes(desc, batch, max_seq_len) exceeds
+ * OSCAR_NOALLOC_SCRATCH_BYTES (use oscar_step with a caller workspace);
+ * OSCAR_ERR_HIP if the array's device address cannot be resolved.
+ */
+#define OSCAR_NOALLOC_SCRATCH_BYTES (8u << 20)
+oscar_status oscar_step_noalloc(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
+                                const int32_t* position, const void* k_new, const void* v_new, const void* q,
+                                float* out, int32_t batch, int32_t max_seq_len, void* stream);
 
 /*
  * oscar_decode_multi -- several query tokens per sequence over the tiered
