@@ -49,12 +49,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Per-wave partials of a workgroup; slot 4 holds one extra token's record
+// (the history token the fused step demotes inside the decode launch).
 template <int G>
 struct alignas(16) SplitSmem {
   float pt[4][32][G];        // probabilities of a 32-token BF16 chunk, per wave
-  float wm[4][16];           // per-wave running max per column (head)
-  float wl[4][16];           // per-wave running sum per column
-  float wo[4][G][kD];        // per-wave unnormalised outputs
+  float wm[5][16];           // per-wave running max per column (head)
+  float wl[5][16];           // per-wave running sum per column
+  float wo[5][G][kD];        // per-wave unnormalised outputs
 };
 
 // ---------------------------------------------------------------------------
@@ -174,17 +176,16 @@ __device__ void bf16_span_wave(QRow qrow_of, int count, RowK rowk, RowV rowv, Po
 // rec[h * kPartStride + (0..127 acc, 128 m, 129 l)] (16-byte stores; the
 // merge kernel, next on the stream, reads them).
 template <int G>
-__device__ void store_split(SplitSmem<G>& sm, float* rec, int tid) {
+__device__ void store_split(SplitSmem<G>& sm, float* rec, int tid, bool extra = false) {
   __syncthreads();
+  const int n_rec = extra ? 5 : 4;
   for (int c = tid; c < G * kD / 4; c += 256) {
     const int h = c / (kD / 4), j4 = c % (kD / 4);
     float mm = kMInit;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, sm.wm[w][h]);
+    for (int w = 0; w < n_rec; ++w) mm = fmaxf(mm, sm.wm[w][h]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float ll = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < n_rec; ++w) {
       const float f = __builtin_amdgcn_exp2f(sm.wm[w][h] - mm);
       const float4 o = *reinterpret_cast<const float4*>(&sm.wo[w][h][4 * j4]);
       acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);

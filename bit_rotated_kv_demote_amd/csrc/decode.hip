@@ -23,6 +23,7 @@
 // p_t z_{t,g} with one more small product, all in the rotated space.
 #include "attn_common.h"
 #include "launchers.h"
+#include "quant_token.h"
 
 namespace oscar {
 
@@ -398,7 +399,75 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
   }
 }
 
-template <int G, int kBits, bool kPreRot>
+// The fused step's demotion, by the history split that owns the newest
+// history token (history index hidx = n - 321, position n - 257): the token
+// leaves the ring slot that position n - 1 (the step's new token) takes.
+// The workgroup reads the leaving K and V rows, writes the new token into
+// the slot, rotates the leaving token by R_K and R_V, clips, quantises and
+// stores it exactly as oscar_append does (same routine, same association),
+// and records its attention from the dequantised values in the rotated
+// space (record slot 4: score q' . k~' for every query head, weight 1,
+// value v~').  ([yunpan] 三.1 append before attend, 三.2 demotion.)
+// rq holds R_K's row slices on entry (loaded for q . R_K) and is reused for
+// R_V.  Every thread of the workgroup calls it.
+template <int G, int kBits>
+__device__ void demote_in_split(const DecodeArgs& a, DecodeSmem<G>& sm, float4 (&rq)[16], int b, int slot, int hk,
+                                int n, int hidx, int tid, int wave, int lane) {
+  // scratch in the (not yet used) metadata staging area of the page walk
+  float* dx = reinterpret_cast<float*>(&sm.meta[0][0][0]);          // [2][128] leaving K, V
+  float* dpart = dx + 2 * kD;                                        // [4][128] rotation partials
+  uint32_t* dsh = reinterpret_cast<uint32_t*>(dpart + 4 * kD);       // [32] packing words
+  const int p = n - 1;
+  const size_t ring_row = (((size_t)slot * a.hkv + hk) * kRecent + ((p - kSink) & (kRecent - 1))) * kD;
+  const size_t new_row = ((size_t)b * a.hkv + hk) * kD;
+  const int pid = a.page_table[(size_t)slot * a.max_pages + (hidx >> 4)];
+  uint32_t fresh = 0u;
+  if (tid < kD) {
+    const int which = tid >> 6, w = tid & 63;
+    const uint32_t old = reinterpret_cast<const uint32_t*>((which ? a.recent_v : a.recent_k) + ring_row)[w];
+    fresh = reinterpret_cast<const uint32_t*>((which ? a.v_new : a.k_new) + new_row)[w];
+    dx[which * kD + 2 * w] = bf16_bits_to_float(old & 0xFFFFu);
+    dx[which * kD + 2 * w + 1] = bf16_bits_to_float(old >> 16);
+  }
+  __syncthreads();
+  // the leaving token is in LDS (its loads completed): the slot takes the new token
+  // (the pool's tiers are writable device memory; the decode reads them through const pointers)
+  if (tid < kD) {
+    uint16_t* row = const_cast<uint16_t*>((tid >> 6) ? a.recent_v : a.recent_k) + ring_row;
+    reinterpret_cast<uint32_t*>(row)[tid & 63] = fresh;
+  }
+  uint8_t* blk = const_cast<uint8_t*>(a.hist) + ((size_t)pid * a.hkv + hk) * block_bytes(kBits);
+  const float* tau_k = a.clip_k + (size_t)hk * a.clip_kv_stride;
+  const float* tau_v = a.clip_v + (size_t)hk * a.clip_kv_stride;
+  rotate_partial(dx, rq, dpart, tid);
+  __syncthreads();
+  float y = tid < kD ? clip_value(rotated_channel(dpart, tid), tau_k[tid]) : 0.0f;
+  // (the quantiser's barriers order every read of dpart before the V rotation rewrites it)
+  const float kdq = quantize_pack_channel_per_thread(y, false, blk, hidx & 15, dsh, kBits);
+  load_rot_slices(a.rot_v + (size_t)hk * a.rot_kv_stride, rq, tid);
+  rotate_partial(dx + kD, rq, dpart, tid);
+  __syncthreads();
+  y = tid < kD ? clip_value(rotated_channel(dpart, tid), tau_v[tid]) : 0.0f;
+  const float vdq = quantize_pack_channel_per_thread(y, true, blk, hidx & 15, dsh, kBits);
+  // the demoted token's record: dequantised key (rotated) for the scores,
+  // dequantised value row for every column
+  if (tid < kD) {
+    dx[tid] = kdq;
+#pragma unroll
+    for (int h = 0; h < G; ++h) sm.wo[4][h][tid] = vdq;
+  }
+  __syncthreads();
+  for (int h = wave; h < G; h += 4) {
+    const float d = wave_sum(sm.qr[h][lane] * dx[lane] + sm.qr[h][lane + 64] * dx[lane + 64]);
+    if (lane == 0) {
+      sm.wm[4][h] = d * kC0;          // log2 units, as the page walk's scores
+      sm.wl[4][h] = 1.0f;
+    }
+  }
+  __syncthreads();                   // dx (metadata staging) is free again for the page walk
+}
+
+template <int G, int kBits>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& sm) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -427,25 +496,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
   constexpr int kQPer = (kQWords + 255) / 256;
   float4 rq[16];
   uint32_t qv[kQPer];
-  const float* rot_k = a.rot_k + (size_t)hk * a.rot_kv_stride;
-  // With q . R_K precomputed (the fused step), history splits read it
-  // (G rows of fp32) instead of R_K and q.
-  constexpr bool pre_rot = kPreRot;
-  constexpr int kQRPer = (G * kD + 255) / 256;
-  float qrv[kQRPer];
-  if constexpr (pre_rot) {
-   if (!is_tile) {
-#pragma unroll
-    for (int e = 0; e < kQRPer; ++e) {
-      const int idx = min(tid + 256 * e, G * kD - 1);
-      const int x = idx / kD, vh = cg * G + x, t = vh / a.g_model, h = vh - t * a.g_model;
-      qrv[e] = a.q_rot[(((size_t)b * a.q_tokens + t) * hq_total + hk * a.g_model + h) * kD + idx % kD];
-    }
-   }
-  }
-  if (!is_tile && !pre_rot) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(rot_k + (size_t)(16 * rs + e) * kD + 4 * c4);
+  if (!is_tile) {
+    load_rot_slices(a.rot_k + (size_t)hk * a.rot_kv_stride, rq, tid);
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {                 // unconditional
       const int w = min(tid + 256 * e, kQWords - 1);
@@ -466,10 +518,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
     ids_spec = row[pg0 + min(idx_in_split, a.max_pages - 1 - pg0)];
     first_id = row[pg0];
   }
-  const int n = a.seq_len[b];
+  const int n = a.seq_len[b] + a.len_offset;
   const int hist_len = max(0, n - kSink - kRecent);
   const int n_hist_pages = (hist_len + kPage - 1) / kPage;
   const int act_hist = (n_hist_pages + a.pages_per_split - 1) / a.pages_per_split;
+  // The fused step (k_new given) from position 320 on: the newest history
+  // token is the one leaving the ring this step.  The history split that
+  // owns it demotes it inside this launch and attends to it from its own
+  // registers; the page walk covers the older history tokens.
+  const bool step_demote = a.k_new != nullptr && hist_len > 0;
+  const int walk_len = hist_len - (step_demote ? 1 : 0);
+  const int n_walk_pages = (walk_len + kPage - 1) / kPage;
   const int n_sink_used = min(n, kSink);
   const int n_recent_used = min(max(n - kSink, 0), kRecent);
   const int n_tile = n_sink_used + n_recent_used;
@@ -485,10 +544,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
     const size_t ring_base = ((size_t)slot * a.hkv + hk) * kRecent;
     // the fused step: the token at position n - 1 is still in k_new / v_new
     const size_t new_row = ((size_t)b * a.hkv + hk) * kD;
-    const bool from_args = kPreRot && a.k_new != nullptr;
-    if (from_args && split == 0 && cg == 0 && tid < kD) {
-      // tile split 0 of the group moves it into its sink or ring slot (no
-      // other workgroup of this launch reads that slot)
+    const bool from_args = a.k_new != nullptr;
+    if (from_args && !step_demote && split == 0 && cg == 0 && tid < kD) {
+      // before any demotion, tile split 0 of the group moves it into its
+      // sink or free ring slot (no other workgroup of this launch reads that
+      // slot); from position 320 on the demoting history split does
       const int pn = n - 1, half_sel = tid >> 6, w = tid & 63;
       // (the pool's tiers are writable device memory; the decode reads them
       // through const pointers)
@@ -514,7 +574,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
                       lane);
   } else {
     const int pg_begin = hs * a.pages_per_split;
-    const int pg_end = min(pg_begin + a.pages_per_split, n_hist_pages);
+    // (empty for a demoting split whose only page holds just the new token)
+    const int pg_end = min(pg_begin + a.pages_per_split, n_walk_pages);
     // page ids of this wave's steps (steps wave, wave + 4, ...), lane
     // kStepPages k + i holding page i of the k-th; then this wave's first
     // step: the prologue below waits only for the older loads, so the loop
@@ -529,14 +590,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
     // for its first iteration are exact)
     issue_step<kBits>(a, ids, hk, 0, lane, c_first, m_first);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (pre_rot) {
-#pragma unroll
-      for (int e = 0; e < kQRPer; ++e) {
-        const int idx = tid + 256 * e;
-        if (idx < G * kD) sm.qr[idx / kD][idx % kD] = qrv[e];
-      }
-      __syncthreads();
-    } else {
 #pragma unroll
     for (int e = 0; e < kQPer; ++e) {
       const int idx = tid + 256 * e;
@@ -576,7 +629,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
       sm.qr[h][jj] = (sm.wo[0][h][jj] + sm.wo[1][h][jj]) + (sm.wo[2][h][jj] + sm.wo[3][h][jj]);
     }
     __syncthreads();
-    }
     for (int h = wave; h < G; h += 4) {
       const float v0 = sm.qr[h][lane], v1 = sm.qr[h][lane + 64];
       const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1))) * kC0;
@@ -590,25 +642,28 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
       if (lane == 32) { sm.qs[h][1] = g0; sm.qs[h][3] = g1; }
     }
     __syncthreads();
-    hist_wave<G, kBits>(a, sm, ids, hk, hist_len, pg_begin, pg_end, wave, lane, c_first, m_first);
+    const bool demote_here = step_demote && hs == act_hist - 1;
+    if (demote_here) demote_in_split<G, kBits>(a, sm, rq, b, slot, hk, n, hist_len - 1, tid, wave, lane);
+    hist_wave<G, kBits>(a, sm, ids, hk, walk_len, pg_begin, pg_end, wave, lane, c_first, m_first);
+    store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid, demote_here);
+    return;
   }
   store_split<G>(sm, part_base + (size_t)split * G * kPartStride, tid);
 }
 
-// kPreRot: q . R_K comes precomputed (the fused step) instead of R_K and q.
 // Two workgroups per compute unit (up to 256 VGPRs per lane).
-template <int G, bool kPreRot = false>
+template <int G>
 __global__ __launch_bounds__(256, 2) void decode_int2_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
-  decode_body<G, 2, kPreRot>(a, sm);
+  decode_body<G, 2>(a, sm);
 }
 
 // INT4 pool: the same kernel over 2560-byte blocks (twice the code registers
 // per step in flight)
-template <int G, bool kPreRot = false>
+template <int G>
 __global__ __launch_bounds__(256, 2) void decode_int4_kernel(DecodeArgs a) {
   __shared__ DecodeSmem<G> sm;
-  decode_body<G, 4, kPreRot>(a, sm);
+  decode_body<G, 4>(a, sm);
 }
 
 DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_seq_len, int target) {
@@ -639,32 +694,27 @@ DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_s
   return p;
 }
 
-template <bool kPreRot>
-static hipError_t launch_decode_as(const DecodeArgs& a, int group, int grid, hipStream_t st) {
+hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t st) {
   if (a.code_bits == 4) {
     switch (group) {
-      case 1: hipLaunchKernelGGL((decode_int4_kernel<1, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((decode_int4_kernel<2, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((decode_int4_kernel<4, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((decode_int4_kernel<8, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-      case 16: hipLaunchKernelGGL((decode_int4_kernel<16, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+      case 1: hipLaunchKernelGGL((decode_int4_kernel<1>), dim3(grid), dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((decode_int4_kernel<2>), dim3(grid), dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((decode_int4_kernel<4>), dim3(grid), dim3(256), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((decode_int4_kernel<8>), dim3(grid), dim3(256), 0, st, a); break;
+      case 16: hipLaunchKernelGGL((decode_int4_kernel<16>), dim3(grid), dim3(256), 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
   }
   switch (group) {
-    case 1: hipLaunchKernelGGL((decode_int2_kernel<1, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((decode_int2_kernel<2, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((decode_int2_kernel<4, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((decode_int2_kernel<8, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((decode_int2_kernel<16, kPreRot>), dim3(grid), dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((decode_int2_kernel<1>), dim3(grid), dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_int2_kernel<2>), dim3(grid), dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((decode_int2_kernel<4>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((decode_int2_kernel<8>), dim3(grid), dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((decode_int2_kernel<16>), dim3(grid), dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-hipError_t launch_decode(const DecodeArgs& a, int group, int grid, hipStream_t st) {
-  return a.q_rot != nullptr ? launch_decode_as<true>(a, group, grid, st) : launch_decode_as<false>(a, group, grid, st);
 }
 
 }  // namespace oscar

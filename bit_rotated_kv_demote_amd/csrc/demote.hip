@@ -8,14 +8,11 @@
 // Quantization" (gist.science), 2.2 B.  The rotation R and the per-channel
 // clip thresholds are fixed offline (same page, 2.2 A).
 //
-// Four kernels:
+// Three kernels (the fused step, oscar_step, demotes its token inside the
+// decode launch with the same per-token routine as append_kernel):
 //   append_kernel      one decode step: demote the ring slot about to be
 //                      reused (fp32 VALU rotation, latency-bound), then write
 //                      the new token into sink or ring.
-//   append_step_kernel the fused step's append: the same demotion split over
-//                      two workgroups per vector (half the rotated channels
-//                      each) beside q . R_K; the decode launch of the step
-//                      places the new token.
 //   demote_bulk_kernel many tokens: 64-token units per wave; the rotation is
 //                      a 128x128x64 product on the matrix cores with R split
 //                      into bf16 hi + lo terms (fp32 accumulation), or the
@@ -25,65 +22,9 @@
 
 #include "device_common.h"
 #include "launchers.h"
+#include "quant_token.h"
 
 namespace oscar {
-
-// ---------------------------------------------------------------------------
-// Quantise + pack one vector held one channel per thread (threads 0..127 of
-// the block; every thread of the block must call it).  `sh` is 32 words of
-// LDS.  Writes token slot `ps` of the block `blk` (an INT2 block, or an INT4
-// block when bits == 4).
-// ---------------------------------------------------------------------------
-__device__ void quantize_pack_channel_per_thread(float yc, bool is_v, uint8_t* blk, int ps,
-                                                 uint32_t* sh, int bits) {
-  const int c = threadIdx.x;
-  const bool act = c < kD;
-  float mn = yc, mx = yc;
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, m));
-    mx = fmaxf(mx, __shfl_xor(mx, m));
-  }
-  __half s, z;
-  const bool int4 = bits == 4;
-  group_scale_zero(mn, mx, &s, &z, int4 ? 15.0f : 3.0f);
-  const uint32_t code = quant_code(yc, __half2float(z), __half2float(s), int4 ? 15.0f : 3.0f);
-  if (c < 32) sh[c] = 0u;
-  __syncthreads();
-  if (act) {
-    if (int4) {
-      // K: word (chunk (c >> 3) & 3, group c >> 5); V: half-word (channel
-      // c & 15, channels 16m with m >> 2 == c >> 6) of this token
-      if (!is_v)
-        atomicOr(&sh[4 * ((c >> 3) & 3) + (c >> 5)], code << (16 * (c & 1) + 4 * ((c >> 1) & 3)));
-      else
-        atomicOr(&sh[2 * (c & 15) + (c >> 6)], code << (4 * ((c >> 4) & 3)));
-    } else if (!is_v) {
-      atomicOr(&sh[2 * ((c >> 3) & 3) + (c >> 6)], code << (2 * k_field(c)));
-    } else {
-      atomicOr(&sh[8 + (c & 15)], code << (2 * v_field_in_half(c)));
-    }
-  }
-  __syncthreads();
-  if (int4) {
-    if (!is_v) {
-      if (c < 16) *reinterpret_cast<uint32_t*>(blk + 16 * (16 * (c >> 2) + ps) + 4 * (c & 3)) = sh[c];
-    } else {
-      if (c < 32) *reinterpret_cast<uint16_t*>(blk + v4_halfword_byte(ps, c >> 1, c & 1)) = (uint16_t)sh[c];
-    }
-  } else if (!is_v) {
-    if (c < 8) *reinterpret_cast<uint32_t*>(blk + 16 * (16 * (c >> 1) + ps) + 4 * (c & 1)) = sh[c];
-  } else {
-    if (c < 16) *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, c)) = (uint16_t)sh[8 + c];
-  }
-  if (act && (c & 31) == 0) {
-    const int g = c >> 5;
-    const int so = (is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g)) + meta_shift(bits);
-    const int zo = (is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g)) + meta_shift(bits);
-    *reinterpret_cast<uint16_t*>(blk + so) = half_bits(s);
-    *reinterpret_cast<uint16_t*>(blk + zo) = half_bits(z);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // append (oscar_append): grid (batch, Hkv, 2 = {K, V}), 256 threads.
@@ -98,11 +39,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   // position, so they are requested first: thread (c4, rs) takes columns
   // [4 c4, 4 c4 + 4) and rows [16 rs, 16 rs + 16) of R (16 float4 loads).
   // (Unused when the token only enters the sink or a free ring slot.)
-  const int c4 = tid & 31, rs = tid >> 5;
   const float* R = (is_v ? a.rot_v : a.rot_k) + (size_t)hk * a.rot_kv_stride;
   float4 rq[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) rq[e] = *reinterpret_cast<const float4*>(R + (size_t)(16 * rs + e) * kD + 4 * c4);
+  load_rot_slices(R, rq, tid);
   const float* tau = (is_v ? a.clip_v : a.clip_k) + (size_t)hk * a.clip_kv_stride;
   const float tau_j = tau[tid & (kD - 1)];
   const int slot = a.seq_slot ? a.seq_slot[b] : b;
@@ -125,215 +64,18 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
   if (demote) {                        // block-uniform
     __syncthreads();
-    // The sum over the 128 rows is associated exactly as in the fused step's
-    // append (append_step_kernel), so both leave the same bytes: fma chains
-    // over 8 rows each (rows [8 r, 8 r + 8)), chains r and r + 1 added,
-    // then the pair sums of lanes l and l + 32 (row slices 2w and 2w + 1),
-    // then the four waves' sums pairwise through LDS.
-    auto rotate_into = [&](const float* x, float* dst_row /* [4][kD] */) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f), acc2 = acc;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xe = x[16 * rs + e], xf = x[16 * rs + 8 + e];
-        acc.x = fmaf(xe, rq[e].x, acc.x);
-        acc.y = fmaf(xe, rq[e].y, acc.y);
-        acc.z = fmaf(xe, rq[e].z, acc.z);
-        acc.w = fmaf(xe, rq[e].w, acc.w);
-        acc2.x = fmaf(xf, rq[8 + e].x, acc2.x);
-        acc2.y = fmaf(xf, rq[8 + e].y, acc2.y);
-        acc2.z = fmaf(xf, rq[8 + e].z, acc2.z);
-        acc2.w = fmaf(xf, rq[8 + e].w, acc2.w);
-      }
-      acc.x += acc2.x;
-      acc.y += acc2.y;
-      acc.z += acc2.z;
-      acc.w += acc2.w;
-      acc.x += __shfl_xor(acc.x, 32);
-      acc.y += __shfl_xor(acc.y, 32);
-      acc.z += __shfl_xor(acc.z, 32);
-      acc.w += __shfl_xor(acc.w, 32);
-      if ((tid & 32) == 0) *reinterpret_cast<float4*>(&dst_row[(tid >> 6) * kD + 4 * c4]) = acc;
-    };
-    rotate_into(xs, &part[0][0]);
+    rotate_partial(xs, rq, &part[0][0], tid);
     __syncthreads();  // also orders the ring read above before the overwrite below
     float yc = 0.0f;
-    if (tid < kD) yc = clip_value((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]), tau_j);
+    if (tid < kD) yc = clip_value(rotated_channel(&part[0][0], tid), tau_j);
     uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(a.code_bits);
-    quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh, a.code_bits);
+    (void)quantize_pack_channel_per_thread(yc, is_v != 0, blk, h & 15, sh, a.code_bits);
   }
   // then the new token enters the sink or the ring slot
   if (tid < kD / 2) {
     uint16_t* dst = p < kSink ? (is_v ? a.sink_v : a.sink_k) + (((size_t)slot * a.hkv + hk) * kSink + p) * kD : ring;
     reinterpret_cast<uint32_t*>(dst)[tid] = reinterpret_cast<const uint32_t*>(src)[tid];
   }
-}
-
-// ---------------------------------------------------------------------------
-// The fused step's append: grid (batch, Hkv, 6), 256 threads.  z = 2 t + h:
-// t = 0 demotes K, 1 demotes V, 2 computes q' = q . R_K of the KV head's G
-// query heads; h picks the half of the rotated channels [64 h, 64 h + 64)
-// (two quantisation groups), so each workgroup loads only those 64 columns
-// of R (32 KiB).  Both halves read the whole token leaving the ring, so
-// this launch leaves the ring and sink alone: the decode launch that
-// follows in the same step reads the new token from k_new / v_new and
-// writes it into its sink or ring slot.
-// ---------------------------------------------------------------------------
-// Quantise + pack one half of a vector, channel c = 64 h + tid held by
-// threads tid < 64 (wave 0: lanes 0..31 are group 2 h, 32..63 group 2 h + 1).
-// Every thread of the block must call it.  The half's codes occupy whole
-// words (K) or whole bytes / half-words (V) of the block, so the two halves
-// are written by plain stores.
-__device__ void quantize_pack_half(float yc, bool is_v, uint8_t* blk, int ps, uint32_t* sh, int bits, int half) {
-  const int tid = threadIdx.x;
-  const bool act = tid < 64;
-  const int c = 64 * half + tid;
-  float mn = yc, mx = yc;
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, m));
-    mx = fmaxf(mx, __shfl_xor(mx, m));
-  }
-  __half s, z;
-  const bool int4 = bits == 4;
-  group_scale_zero(mn, mx, &s, &z, int4 ? 15.0f : 3.0f);
-  const uint32_t code = quant_code(yc, __half2float(z), __half2float(s), int4 ? 15.0f : 3.0f);
-  if (tid < 32) sh[tid] = 0u;
-  __syncthreads();
-  if (act) {
-    if (int4) {
-      if (!is_v)
-        atomicOr(&sh[4 * ((c >> 3) & 3) + (c >> 5)], code << (16 * (c & 1) + 4 * ((c >> 1) & 3)));
-      else
-        atomicOr(&sh[2 * (c & 15) + (c >> 6)], code << (4 * ((c >> 4) & 3)));
-    } else if (!is_v) {
-      atomicOr(&sh[2 * ((c >> 3) & 3) + (c >> 6)], code << (2 * k_field(c)));
-    } else {
-      atomicOr(&sh[8 + (c & 15)], code << (2 * v_field_in_half(c)));
-    }
-  }
-  __syncthreads();
-  if (int4) {
-    if (!is_v) {
-      // words 4 a + g of chunk row a, groups g = 2 h, 2 h + 1
-      if (tid < 8) {
-        const int aa = tid >> 1, g = 2 * half + (tid & 1);
-        *reinterpret_cast<uint32_t*>(blk + 16 * (16 * aa + ps) + 4 * g) = sh[4 * aa + g];
-      }
-    } else {
-      if (tid < 16) *reinterpret_cast<uint16_t*>(blk + v4_halfword_byte(ps, tid, half)) = (uint16_t)sh[2 * tid + half];
-    }
-  } else if (!is_v) {
-    // word h of chunk row a
-    if (tid < 4) *reinterpret_cast<uint32_t*>(blk + 16 * (16 * tid + ps) + 4 * half) = sh[2 * tid + half];
-  } else {
-    // byte h of channel b's half-word (groups 2 h, 2 h + 1 fill bits 8 h .. 8 h + 7)
-    if (tid < 16) blk[v_halfword_byte(ps, tid) + half] = (uint8_t)(sh[8 + tid] >> (8 * half));
-  }
-  if (act && (c & 31) == 0) {
-    const int g = c >> 5;
-    const int so = (is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g)) + meta_shift(bits);
-    const int zo = (is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g)) + meta_shift(bits);
-    *reinterpret_cast<uint16_t*>(blk + so) = half_bits(s);
-    *reinterpret_cast<uint16_t*>(blk + zo) = half_bits(z);
-  }
-}
-
-__global__ __launch_bounds__(256) void append_step_kernel(AppendArgs a) {
-  __shared__ float xs[kD];
-  __shared__ float part[4][64];
-  __shared__ uint32_t sh[32];
-  __shared__ float qsh[8][kD];          // the KV head's queries (G <= 8)
-  __shared__ float qpart[8][4][64];     //   and their per-wave partial products
-  const int b = blockIdx.x, hk = blockIdx.y, kind = blockIdx.z >> 1, half = blockIdx.z & 1;
-  const bool is_v = kind == 1, fq = kind == 2;
-  const int tid = threadIdx.x;
-  // y_j = sum_i x_i R[i][j] for j in [64 h, 64 h + 64): thread (c4, rs) takes
-  // columns 64 h + [4 c4, 4 c4 + 4) and rows [8 rs, 8 rs + 8) (8 float4 loads),
-  // requested before the position is known
-  const int c4 = tid & 15, rs = tid >> 4;
-  const float* R = (is_v ? a.rot_v : a.rot_k) + (size_t)hk * a.rot_kv_stride;
-  float4 rq[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    rq[e] = *reinterpret_cast<const float4*>(R + (size_t)(8 * rs + e) * kD + 64 * half + 4 * c4);
-  const int G = a.g_model;
-  const size_t qrow0 = ((size_t)b * a.hkv + hk) * G;
-  uint32_t qw[2] = {0u, 0u};
-  if (fq) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int idx = tid + 256 * e;
-      if (idx < G * kD / 2) qw[e] = reinterpret_cast<const uint32_t*>(a.q + qrow0 * kD)[idx];
-    }
-  }
-  const float* tau = (is_v ? a.clip_v : a.clip_k) + (size_t)hk * a.clip_kv_stride;
-  const float tau_j = tau[64 * half + (tid & 63)];
-  const int slot = a.seq_slot ? a.seq_slot[b] : b;
-  const int p = a.position[b];
-  if (fq && half == 0 && hk == 0 && tid == 0) a.len_out[b] = p + 1;
-  const int r = (p - kSink) & (kRecent - 1);
-  const uint16_t* ring = (is_v ? a.recent_v : a.recent_k) + (((size_t)slot * a.hkv + hk) * kRecent + r) * kD;
-  // from position 320 on, the token leaving the ring (p - 256) is demoted
-  // into history index h
-  const bool demote = !fq && p >= kSink + kRecent;
-  const int hidx = p - kSink - kRecent;
-  int page = 0;
-  if (fq) {
-    for (int e = 0; e < 2; ++e) {
-      const int idx = tid + 256 * e;
-      if (idx < G * kD / 2) {
-        qsh[(2 * idx) / kD][(2 * idx) % kD] = bf16_bits_to_float(qw[e] & 0xFFFFu);
-        qsh[(2 * idx) / kD][(2 * idx) % kD + 1] = bf16_bits_to_float(qw[e] >> 16);
-      }
-    }
-  }
-  if (demote) {
-    page = a.page_table[(size_t)slot * a.max_pages + (hidx >> 4)];
-    if (tid < kD / 2) {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(ring)[tid];
-      xs[2 * tid] = bf16_bits_to_float(w & 0xFFFFu);
-      xs[2 * tid + 1] = bf16_bits_to_float(w >> 16);
-    }
-  }
-  if (!fq && !demote) return;            // block-uniform: nothing to rotate
-  __syncthreads();
-  // lanes l, l + 16, l + 32, l + 48 of a wave hold row slices 4 w .. 4 w + 3
-  // of the same columns: two lane swaps, then the four waves' sums via LDS
-  auto rotate_into = [&](const float* x, float* dst /* [4][64] */) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float xe = x[8 * rs + e];
-      acc.x = fmaf(xe, rq[e].x, acc.x);
-      acc.y = fmaf(xe, rq[e].y, acc.y);
-      acc.z = fmaf(xe, rq[e].z, acc.z);
-      acc.w = fmaf(xe, rq[e].w, acc.w);
-    }
-#pragma unroll
-    for (int m = 16; m <= 32; m <<= 1) {
-      acc.x += __shfl_xor(acc.x, m);
-      acc.y += __shfl_xor(acc.y, m);
-      acc.z += __shfl_xor(acc.z, m);
-      acc.w += __shfl_xor(acc.w, m);
-    }
-    if ((tid & 48) == 0) *reinterpret_cast<float4*>(&dst[(tid >> 6) * 64 + 4 * c4]) = acc;
-  };
-  if (fq) {
-    for (int hh = 0; hh < G; ++hh) rotate_into(qsh[hh], &qpart[hh][0][0]);
-    __syncthreads();
-    for (int idx = tid; idx < G * 64; idx += 256) {
-      const int hh = idx / 64, j = idx % 64;
-      a.q_rot[(qrow0 + hh) * kD + 64 * half + j] =
-          (qpart[hh][0][j] + qpart[hh][1][j]) + (qpart[hh][2][j] + qpart[hh][3][j]);
-    }
-    return;
-  }
-  rotate_into(xs, &part[0][0]);
-  __syncthreads();
-  float yc = 0.0f;
-  if (tid < 64) yc = clip_value((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]), tau_j);
-  uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(a.code_bits);
-  quantize_pack_half(yc, is_v, blk, hidx & 15, sh, a.code_bits, half);
 }
 
 // ---------------------------------------------------------------------------
@@ -626,10 +368,7 @@ __global__ __launch_bounds__(256) void prefill_route_kernel(PrefillArgs a) {
 }
 
 hipError_t launch_append(const AppendArgs& a, int batch, hipStream_t st) {
-  if (a.q_rot != nullptr)
-    hipLaunchKernelGGL(append_step_kernel, dim3(batch, a.hkv, 6), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(append_kernel, dim3(batch, a.hkv, 2), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(append_kernel, dim3(batch, a.hkv, 2), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -23,13 +23,6 @@ struct AppendArgs {
   int code_bits;           // 2: INT2 history blocks, 4: INT4
   int hkv;
   int max_pages;
-  // fused step (all nullable): q' = q . R_K of each sequence's query heads
-  // (bf16 q [batch][Hq][128] in, fp32 q_rot out, same layout) and the
-  // decode length position + 1 (len_out [batch])
-  const uint16_t* q;
-  float* q_rot;
-  int32_t* len_out;
-  int g_model;             // query heads per KV head
 };
 
 struct DemoteArgs {
@@ -71,15 +64,17 @@ struct DecodeArgs {
   const uint16_t* q;          // bf16 [batch][q_tokens][Hq][128]
   float* out;                 // fp32 [batch][q_tokens][Hq][128]
   const int32_t* seq_slot;    // nullable
-  const int32_t* seq_len;     // [batch]
+  const int32_t* seq_len;     // [batch]; the cached tokens are seq_len[b] + len_offset
+  int len_offset;             // 0, or 1 when seq_len holds the step's positions
   const uint16_t* sink_k; const uint16_t* sink_v;
   const uint16_t* recent_k; const uint16_t* recent_v;
   const uint8_t* hist;
   const int32_t* page_table;
   const float* rot_k; const float* rot_v;
   int rot_kv_stride;          // elements from one KV head's R to the next (0: shared)
+  const float* clip_k; const float* clip_v;   // the fused step's demotion
+  int clip_kv_stride;
   int code_bits;              // 2: INT2 history blocks, 4: INT4
-  const float* q_rot;         // nullable: q . R_K precomputed (fp32, q's layout); history splits skip R_K
   float* partials;            // workspace: [batch*Hkv][n_splits][G][132]
   int hkv;
   int max_pages;
@@ -96,8 +91,11 @@ struct DecodeArgs {
   int g_model;
   int n_colgroups;
   // nullable (the fused step): the token appended this step, bf16
-  // [batch][Hkv][128], not yet in its sink or ring slot; the tile splits
-  // read position n - 1 from here and tile split 0 writes it into the slot
+  // [batch][Hkv][128], not yet in its sink or ring slot.  The tile splits
+  // read position n - 1 from here.  From position 320 on, the history split
+  // that owns the newest history token demotes the token leaving the ring,
+  // writes the new one into its ring slot and attends to the demoted token
+  // itself; before that, tile split 0 writes the new token into its slot.
   const uint16_t* k_new; const uint16_t* v_new;
 };
 
@@ -123,7 +121,8 @@ struct DecodeBf16Args {
 // Log-sum-exp merge of the decode partials, one workgroup per query head.
 struct MergeArgs {
   const float* partials;      // [batch*Hkv*n_colgroups][n_splits_total][group][132]
-  const int32_t* seq_len;     // [batch]
+  const int32_t* seq_len;     // [batch]; the cached tokens are seq_len[b] + len_offset
+  int len_offset;
   const float* rot;           // R_V for the rotated (history) records; unused when tiered == 0
   int rot_kv_stride;          // elements from one KV head's R_V to the next (0: shared)
   float* out;                 // fp32 [batch][q_tokens][Hq][128]
@@ -159,7 +158,6 @@ constexpr int kMaxPagesPerSplit = 256;
 // (256 CUs), for oscar_decode and for the fused step alike.  Larger batches
 // than this can split exceed it (every group keeps at least one history split).
 constexpr int kDecodeSplitTarget = 512;
-constexpr int kStepSplitTarget = 512;
 
 // group: columns per work item (1, 2, 4, 8 or 16); n_colgroups column groups
 // per (sequence, KV head)

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
   // the splits the first kernel filled for this sequence (clamped to the
   // slots, so that a length outside [1, max_seq_len] stays in bounds)
-  const int n = a.seq_len[b];
+  const int n = a.seq_len[b] + a.len_offset;
   int n_plain, n_rot;
   if (a.tiered) {
     const int hist_len = max(0, n - kSink - kRecent);
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) rrow[e] = rp[e];
   }
-  const int n = a.seq_len[b];
+  const int n = a.seq_len[b] + a.len_offset;
   int n_plain, n_rot;
   if (a.tiered) {
     const int hist_len = max(0, n - kSink - kRecent);

@@ -78,20 +78,12 @@ constexpr int kMaxBf16Columns = 16;
 // which launches of a tiered decode call run
 enum DecodePhases { kPhaseSplits = 1, kPhaseMerge = 2, kPhaseBoth = 3 };
 static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
-                                  const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
-                                  float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
-                                  void* stream, int phases = kPhaseBoth, const void* k_new = nullptr,
-                                  const void* v_new = nullptr);
+                                  const int32_t* seq_len, const void* q, int32_t n_query, float* out,
+                                  void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len, void* stream,
+                                  int phases = kPhaseBoth, const void* k_new = nullptr, const void* v_new = nullptr,
+                                  int len_offset = 0);
 
 namespace {
-// fused step workspace: q . R_K (fp32, q's layout), the decode lengths, then
-// the decode partials; each part starts on a 256-byte boundary
-size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-size_t step_qrot_bytes(const oscar_layer_desc* d, int batch) {
-  return align256((size_t)batch * d->num_q_heads * 128 * sizeof(float));
-}
-size_t step_len_bytes(int batch) { return align256((size_t)batch * sizeof(int32_t)); }
-
 oscar_status check_append(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                           const int32_t* position, const void* k_new, const void* v_new, int32_t batch) {
   oscar_status st = check_desc(desc);
@@ -121,7 +113,6 @@ AppendArgs append_args(const oscar_layer_desc* desc, const oscar_pool* pool, con
   a.code_bits = pool->code_bits;
   a.hkv = desc->num_kv_heads;
   a.max_pages = pool->max_pages_per_seq;
-  a.g_model = desc->num_q_heads / desc->num_kv_heads;
   return a;
 }
 }  // namespace
@@ -268,31 +259,32 @@ oscar_status oscar_decode(const oscar_layer_desc* desc, const oscar_pool* pool, 
 oscar_status oscar_decode_multi(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                                 const int32_t* seq_len, const void* q, int32_t n_query, float* out, void* workspace,
                                 size_t ws_bytes, int32_t batch, int32_t max_seq_len, void* stream) {
-  return decode_tiered(desc, pool, seq_slot, seq_len, q, nullptr, n_query, out, workspace, ws_bytes, batch,
-                       max_seq_len, stream);
+  return decode_tiered(desc, pool, seq_slot, seq_len, q, n_query, out, workspace, ws_bytes, batch, max_seq_len,
+                       stream);
 }
 
 oscar_status oscar_decode_partials(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
                                    const int32_t* seq_len, const void* q, void* workspace, size_t ws_bytes,
                                    int32_t batch, int32_t max_seq_len, void* stream) {
-  return decode_tiered(desc, pool, seq_slot, seq_len, q, nullptr, 1, nullptr, workspace, ws_bytes, batch,
-                       max_seq_len, stream, kPhaseSplits);
+  return decode_tiered(desc, pool, seq_slot, seq_len, q, 1, nullptr, workspace, ws_bytes, batch, max_seq_len,
+                       stream, kPhaseSplits);
 }
 
 oscar_status oscar_decode_merge(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_len,
                                 float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
                                 void* stream) {
-  return decode_tiered(desc, pool, nullptr, seq_len, nullptr, nullptr, 1, out, workspace, ws_bytes, batch,
-                       max_seq_len, stream, kPhaseMerge);
+  return decode_tiered(desc, pool, nullptr, seq_len, nullptr, 1, out, workspace, ws_bytes, batch, max_seq_len,
+                       stream, kPhaseMerge);
 }
 }  // extern "C"
 
-// Tiered decode (split kernel + merge, or one of them); q_rot: nullable
-// precomputed q . R_K.
+// Tiered decode (split kernel + merge, or one of them).  The fused step
+// passes the new token (k_new, v_new) and its positions as seq_len with
+// len_offset 1.
 static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
-                                  const int32_t* seq_len, const void* q, const float* q_rot, int32_t n_query,
-                                  float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
-                                  void* stream, int phases, const void* k_new, const void* v_new) {
+                                  const int32_t* seq_len, const void* q, int32_t n_query, float* out,
+                                  void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len, void* stream,
+                                  int phases, const void* k_new, const void* v_new, int len_offset) {
   oscar_status st = check_desc(desc);
   if (st != OSCAR_OK) return st;
   if ((st = check_pool(pool, max_seq_len > 320)) != OSCAR_OK) return st;
@@ -305,8 +297,7 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   const int max_hist = max_seq_len - 320;
   if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
   const QueryColumns c = int2_query_columns(desc, n_query);
-  const DecodePlan plan = plan_decode(batch, hkv, c.group, c.n_colgroups, max_seq_len,
-                                      q_rot ? kStepSplitTarget : kDecodeSplitTarget);
+  const DecodePlan plan = plan_decode(batch, hkv, c.group, c.n_colgroups, max_seq_len);
   if (!plan.ok) return OSCAR_ERR_UNSUPPORTED;
   if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
   DecodeArgs a{};
@@ -314,6 +305,7 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   a.out = out;
   a.seq_slot = seq_slot;
   a.seq_len = seq_len;
+  a.len_offset = len_offset;
   a.sink_k = static_cast<const uint16_t*>(pool->sink_k);
   a.sink_v = static_cast<const uint16_t*>(pool->sink_v);
   a.recent_k = static_cast<const uint16_t*>(pool->recent_k);
@@ -323,9 +315,12 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   a.rot_k = pool->rot_k;
   a.rot_v = pool->rot_v;
   a.rot_kv_stride = rot_stride(pool);
+  a.clip_k = pool->clip_k;
+  a.clip_v = pool->clip_v;
+  a.clip_kv_stride = clip_stride(pool);
   a.code_bits = pool->code_bits;
-  a.q_rot = q_rot;
-  // the fused step: this step's token reaches its sink or ring slot in the decode launch
+  // the fused step: this step's token reaches its sink or ring slot, and the
+  // token leaving the ring its history slot, in the decode launch
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.partials = static_cast<float*>(workspace);
@@ -345,6 +340,7 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   MergeArgs m{};
   m.partials = a.partials;
   m.seq_len = seq_len;
+  m.len_offset = len_offset;
   m.rot = pool->rot_v;
   m.rot_kv_stride = rot_stride(pool);
   m.out = out;
@@ -434,12 +430,7 @@ oscar_status oscar_decode_bf16_multi(const oscar_layer_desc* desc, const oscar_b
 }
 
 size_t oscar_step_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len) {
-  if (check_desc(desc) != OSCAR_OK || batch <= 0 || max_seq_len <= 0) return 0;
-  const QueryColumns c = int2_query_columns(desc, 1);
-  const size_t dec =
-      plan_decode(batch, desc->num_kv_heads, c.group, c.n_colgroups, max_seq_len, kStepSplitTarget).workspace_bytes;
-  if (dec == 0) return 0;
-  return step_qrot_bytes(desc, batch) + step_len_bytes(batch) + dec;
+  return oscar_decode_workspace_bytes(desc, batch, max_seq_len);
 }
 
 oscar_status oscar_step(const oscar_layer_desc* desc, const oscar_pool* pool, const int32_t* seq_slot,
@@ -451,20 +442,11 @@ oscar_status oscar_step(const oscar_layer_desc* desc, const oscar_pool* pool, co
   const size_t need = oscar_step_workspace_bytes(desc, batch, max_seq_len);
   if (need == 0) return OSCAR_ERR_UNSUPPORTED;
   if (ws_bytes < need) return OSCAR_ERR_CAPACITY;
-  const int max_hist = max_seq_len - 320;
-  if (max_hist > 0 && (max_hist + 15) / 16 > pool->max_pages_per_seq) return OSCAR_ERR_CAPACITY;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* q_rot = reinterpret_cast<float*>(ws);
-  int32_t* lens = reinterpret_cast<int32_t*>(ws + step_qrot_bytes(desc, batch));
-  void* partials = ws + step_qrot_bytes(desc, batch) + step_len_bytes(batch);
-  AppendArgs a = append_args(desc, pool, seq_slot, position, k_new, v_new);
-  a.q = static_cast<const uint16_t*>(q);
-  a.q_rot = q_rot;
-  a.len_out = lens;
-  if ((st = hip_status(launch_append(a, batch, static_cast<hipStream_t>(stream)))) != OSCAR_OK) return st;
-  return decode_tiered(desc, pool, seq_slot, lens, q, q_rot, 1, out, partials,
-                       ws_bytes - step_qrot_bytes(desc, batch) - step_len_bytes(batch), batch, max_seq_len, stream,
-                       kPhaseBoth, k_new, v_new);
+  // one decode launch appends (the new token into its tier; from position
+  // 320 on, the token leaving the ring into history) and attends; the
+  // cached length is position + 1
+  return decode_tiered(desc, pool, seq_slot, position, q, 1, out, workspace, ws_bytes, batch, max_seq_len, stream,
+                       kPhaseBoth, k_new, v_new, 1);
 }
 
 }  // extern "C"

@@ -325,14 +325,17 @@ oscar_status oscar_decode_merge(const oscar_layer_desc* desc, const oscar_pool* 
  * oscar_step -- one decode step of a layer in one call: oscar_append of the
  * new token (k_new, v_new at position[b], as there) followed by oscar_decode
  * of q over the position[b] + 1 cached tokens ([yunpan] 三.1: the new token is
- * appended before it attends; [gist] 2.2 B).  The append launch demotes
- * the token leaving the ring (two workgroups per vector, each rotating half
- * of the channels) and computes q . R_K of each sequence's query heads
- * beside it; the decode's history splits read those rotated queries instead
- * of loading R_K themselves, and the decode launch reads the new token from
- * k_new / v_new and writes it into its sink or ring slot.  Results equal
- * oscar_append followed by oscar_decode up to fp32 summation order, and the
- * pool afterwards holds the same bytes.
+ * appended before it attends; [gist] 2.2 B).  Two launches, the decode's:
+ * the split launch also appends.  Before position 320 the new token goes
+ * into its sink or free ring slot; from position 320 on, the history split
+ * that owns the newest history token reads the token leaving the ring,
+ * writes the new token into that ring slot, demotes the leaving token
+ * (rotate, clip, quantise, pack, store; the same routine and rotation
+ * arithmetic as oscar_append) and attends to it from its registers, while
+ * the page walk covers the older history.  The BF16 tiles read the new
+ * token from k_new / v_new.  Results equal oscar_append followed by
+ * oscar_decode up to fp32 summation order, and the pool afterwards holds
+ * the same bytes.
  * position, seq_slot: device int32 [batch] (positions before the append, not
  * advanced by the call); q: device bf16 [batch][Hq][128]; out: device fp32
  * [batch][Hq][128]; max_seq_len >= max(position) + 1.  workspace: device,
@@ -345,8 +348,8 @@ oscar_status oscar_step(const oscar_layer_desc* desc, const oscar_pool* pool, co
                         float* out, void* workspace, size_t ws_bytes, int32_t batch, int32_t max_seq_len,
                         void* stream);
 
-/* Workspace of oscar_step: the decode's plus batch * Hq * 512 bytes of
- * rotated queries and the step's lengths; 0 for an unsupported shape. */
+/* Workspace of oscar_step: the decode's (oscar_decode_workspace_bytes);
+ * 0 for an unsupported shape. */
 size_t oscar_step_workspace_bytes(const oscar_layer_desc* desc, int32_t batch, int32_t max_seq_len);
 
 /*
