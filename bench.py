@@ -669,61 +669,74 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(hq, hkv, n0, host, seed, kv_sample=8, min_seconds=10.0):
-    """The oracle, as it stands, on a bounded sample of the same step."""
+def _oracle_pool(hkv, n0, k, v, rot_k, rot_v, tau_k, tau_v):
+    """The oracle's pool after n0 tokens of one sequence (its own demotion of the history)."""
     import oracle as orc
-    from bit_rotated_kv_demote_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas = 1
-    k, v, rot_k, rot_v, tau_k, tau_v = host
-    heads = list(range(kv_sample))
     max_pages = math.ceil((n0 + 1 - 320) / 16)
     pt = np.arange(max_pages, dtype=np.int32)[None, :]
     pool = orc.Pool(1, hkv, max_pages, pt)
-    ns = 64
-    pool.sink_k[0][:, :ns] = k[:ns].transpose(1, 0, 2)
-    pool.sink_v[0][:, :ns] = v[:ns].transpose(1, 0, 2)
+    pool.sink_k[0][:, :64] = k[:64].transpose(1, 0, 2)
+    pool.sink_v[0][:, :64] = v[:64].transpose(1, 0, 2)
     pos = np.arange(n0 - 256, n0)
     pool.recent_k[0][:, (pos - 64) % 256] = k[pos].transpose(1, 0, 2)
     pool.recent_v[0][:, (pos - 64) % 256] = v[pos].transpose(1, 0, 2)
     h = np.arange(n0 - 320)
-    pool.demote_many(0, h, k[64 + h][:, heads], v[64 + h][:, heads], rot_k, rot_v, tau_k, tau_v, kv_heads=heads)
+    pool.demote_many(0, h, k[64 + h], v[64 + h], rot_k, rot_v, tau_k, tau_v)
     pool.length[0] = n0
-    q = synth.queries(synth.streams(seed)["q"], (1, hq, 128))
-    g = hq // hkv
-    # successive steps (append token n, decode at length n + 1) until about
-    # min_seconds of CPU work, at most len(k) - n0 steps
-    t0 = time.time()
-    n_steps = 0
-    while n_steps < len(k) - n0 and (n_steps == 0 or time.time() - t0 < min_seconds):
-        n = n0 + n_steps
-        pool.append(0, k[n], v[n], rot_k, rot_v, tau_k, tau_v)
-        orc.decode_tiered(q, pool, [0], [n + 1], rot_k, rot_v, heads=[(0, hh) for hh in range(kv_sample * g)])
-        n_steps += 1
-    secs = time.time() - t0
-    scaled_us = secs * 1e6 / n_steps * hkv / kv_sample
-    base = {"value": round(scaled_us, 1), "unit": "us/step", "cores": int(blas), "kind": "oracle",
-            "sample": f"{n_steps} successive steps, each one append (all {hkv} KV heads) + decode of {kv_sample} of "
-                      f"{hkv} KV heads ({kv_sample * g} q heads) from {n0 + 1} tokens, {secs:.1f} s in total"
-                      + (f", scaled x{hkv / kv_sample:g}" if kv_sample != hkv else "")}
-    # the same step on one thread, and the oracle's demotion of one
-    # 4096-token chunk (all KV heads, K and V) on all threads and on one
-    extra = {"threads_all": int(blas)}
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    n = n0 + n_steps
-    heads_all = [(0, hh) for hh in range(kv_sample * g)]
+    return pool
 
-    def one_step():
+
+def cpu_baseline(hq, hkv, n0, host, seed, min_seconds=10.0, host128=None):
+    """The oracle, as it stands, on bounded samples of the same work: successive
+    32K steps for about min_seconds (all threads), one step on one thread, one
+    128K step, and the oracle's demotion of all 16 bulk chunks."""
+    import oracle as orc
+    from bit_rotated_kv_demote_amd import synth
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threadpool_limits, blas = None, 1
+    k, v, rot_k, rot_v, tau_k, tau_v = host
+    pool = _oracle_pool(hkv, n0, k, v, rot_k, rot_v, tau_k, tau_v)
+    q = synth.queries(synth.streams(seed)["q"], (1, hq, 128))
+
+    def one_step(n):
         t = time.time()
         pool.append(0, k[n], v[n], rot_k, rot_v, tau_k, tau_v)
-        orc.decode_tiered(q, pool, [0], [n + 1], rot_k, rot_v, heads=heads_all)
-        return (time.time() - t) * 1e6 * hkv / kv_sample
+        orc.decode_tiered(q, pool, [0], [n + 1], rot_k, rot_v)
+        return time.time() - t
+
+    # successive steps (append token n, decode all query heads at length n + 1)
+    # until about min_seconds of CPU work; one token is kept for the
+    # single-thread step
+    t0 = time.time()
+    n_steps = 0
+    while n_steps < len(k) - n0 - 1 and (n_steps == 0 or time.time() - t0 < min_seconds):
+        one_step(n0 + n_steps)
+        n_steps += 1
+    secs = time.time() - t0
+    base = {"value": round(secs * 1e6 / n_steps, 1), "unit": "us/step", "cores": int(blas), "kind": "oracle",
+            "sample": f"{n_steps} successive steps of the timed workload, each one append (all {hkv} KV heads) "
+                      f"+ decode of all {hq} query heads from {n0 + 1} tokens, {secs:.1f} s in total"}
+    extra = {"threads_all": int(blas)}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            extra["decode_step_us_one_thread"] = round(one_step(n0 + n_steps) * 1e6, 1)
+    # one step at 131072 cached tokens (Qwen3-8B-shaped), all threads
+    if host128 is not None:
+        k8, v8, rk8, rv8, tk8, tv8, n8 = host128
+        t = time.time()
+        pool8 = _oracle_pool(hkv, n8, k8, v8, rk8, rv8, tk8, tv8)
+        build_s = time.time() - t
+        t = time.time()
+        pool8.append(0, k8[n8], v8[n8], rk8, rv8, tk8, tv8)
+        orc.decode_tiered(q, pool8, [0], [n8 + 1], rk8, rv8)
+        extra["ctx128k_step_us"] = round((time.time() - t) * 1e6, 1)
+        extra["ctx128k_pool_build_s"] = round(build_s, 1)
+        del pool8
+    # the oracle's demotion of the bulk workload: 16 chunks of 4096 tokens x
+    # all KV heads, K and V (the same token rows stand in for each chunk)
 
     def demote_chunk():
         cp = orc.Pool(1, hkv, 4096 // 16, np.arange(4096 // 16, dtype=np.int32)[None, :])
@@ -731,12 +744,9 @@ def cpu_baseline(hq, hkv, n0, host, seed, kv_sample=8, min_seconds=10.0):
         cp.demote_many(0, np.arange(4096), k[64:64 + 4096], v[64:64 + 4096], rot_k, rot_v, tau_k, tau_v)
         return (time.time() - t) * 1e6
 
-    if n < len(k):
-        extra["decode_step_us_one_thread"] = None
-        if threadpool_limits is not None:
-            with threadpool_limits(limits=1):
-                extra["decode_step_us_one_thread"] = round(one_step(), 1)
-    extra["demote_chunk_4096x8_us"] = round(demote_chunk(), 1)
+    chunks = [demote_chunk() for _ in range(16)]
+    extra["demote_16_chunks_4096x8_us"] = round(sum(chunks), 1)
+    extra["demote_tok_per_s"] = round(16 * 4096 / (sum(chunks) * 1e-6), 1)
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
             extra["demote_chunk_4096x8_us_one_thread"] = round(demote_chunk(), 1)
@@ -766,6 +776,7 @@ def main():
     binding.load()
 
     hq, hkv, n0 = 32, 8, args.ctx
+    host128 = None
     res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001 if n0 == 32768 else 1002)
     dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
     # the roofline kernel: the decode's split kernel (oscar_decode_partials)
@@ -805,6 +816,7 @@ def main():
         extra["ctx128k"]["bf16_decode_us"] = round(b128["decode_us"], 3)
         extra["ctx128k"]["bf16_decode_GBps"] = round(b128["decode_bytes"] / (b128["decode_us"] * 1e3), 1)
         extra["ctx128k"]["int2_vs_bf16_decode_speedup"] = round(b128["decode_us"] / r128["decode_us"], 3)
+        host128 = tuple(r128["host"]) + (131072,)
         del r128, b128
         extra["ragged_gqa8"] = run_ragged_gqa8(torch, min(args.steps, 50), res["host"][2:])
         extra["fixed_memory_16k"] = run_fixed_memory(torch, min(args.steps, 20), res["host"][2:])
@@ -843,7 +855,7 @@ def main():
         torch.cuda.synchronize()
     cpu = None
     if not args.no_cpu:
-        cpu, extra["cpu_oracle"] = cpu_baseline(hq, hkv, n0, res["host"], 1001)
+        cpu, extra["cpu_oracle"] = cpu_baseline(hq, hkv, n0, res["host"], 1001, host128=host128)
     line = {
         "metric": METRIC,
         "value": round(res["us_per_step"], 3),

@@ -72,7 +72,7 @@ QueryColumns int2_query_columns(const oscar_layer_desc* d, int n_query) {
   const int v = n_query * (d->num_q_heads / d->num_kv_heads);
   return query_columns(d, n_query, v >= 32 ? 16 : 8);
 }
-constexpr int kMaxBf16Columns = 16;
+constexpr int kMaxBf16Columns = 8;
 }  // namespace
 
 // which launches of a tiered decode call run
@@ -392,6 +392,7 @@ oscar_status oscar_decode_bf16_multi(const oscar_layer_desc* desc, const oscar_b
   const int hkv = desc->num_kv_heads, g = desc->num_q_heads / hkv;
   const QueryColumns c = query_columns(desc, n_query, kMaxBf16Columns);
   const DecodePlan plan = plan_decode_bf16(batch, hkv, c.group, c.n_colgroups, max_seq_len);
+  if (!plan.ok) return OSCAR_ERR_UNSUPPORTED;
   if (ws_bytes < plan.workspace_bytes) return OSCAR_ERR_CAPACITY;
   DecodeBf16Args a{};
   a.q = static_cast<const uint16_t*>(q);
