@@ -79,267 +79,351 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Bulk demotion.  grid (nwg, 2): blockIdx.y picks K or V, 256 threads.  The
-// workgroup stages R^T once (bf16 hi + lo) and its four waves then take work
-// units of 64 tokens of one (sequence, KV head) in turn: unit u goes to wave
-// u mod (4 nwg).  A unit is four 16-token tiles; every R^T fragment read
-// from LDS feeds the four tiles' products.  In a tile, lane l = 16a + t owns
-// token t and channels j = 16 m + 4 a + i (m = 0..7, i = 0..3): the layout
-// of the 16x16 result blocks of the rotation product
-// D[j][t] = sum_i R[i][j] x[t][i].
+// Bulk demotion.  grid (nwg, 1, heads), 512 threads (8 waves), one
+// workgroup per compute unit.  The workgroup stages R_K^T and R_V^T as bf16
+// hi + lo terms in LDS once; each wave then takes work units of kDemPages
+// history pages of one (sequence, KV head) in turn (unit u goes to wave
+// u mod (8 nwg)) and demotes both K and V of their tokens.  K and V codes
+// share every 16-byte chunk of a page block, so a wave assembles whole
+// blocks in a wave-private LDS image and writes them with 16-byte stores.
+// A page only partly covered by the demoted tokens is read into the image
+// first, so its other slots keep their bytes.
+//
+// Rotation: D[c][t] = sum_i R[i][c] x[t][i] on 16x16x32 bf16 matrix-core
+// products, x . R_hi + x . R_lo with fp32 accumulation, one page of tokens
+// in the columns.  The 16 rows of output block m are the rotated channels
+// 32 (r >> 2) + 4 m + (r & 3), so lane l = 16 g + t ends up holding all 32
+// channels of quantisation group g of token t (channel 32 g + 4 m + i in
+// y[m][i]): clip, minimum and maximum, scale and zero and the codes are
+// each computed once per group, in one lane, with no exchange.
 // ---------------------------------------------------------------------------
-// LDS copy of R^T: row j holds R[:, j] as 16 chunks of 8 bf16; chunk c of row j
-// is stored at chunk position c ^ (j & 15) so that the 16 rows read by one
-// fragment load fall on different banks.
-__device__ __forceinline__ int rt_index(int j, int i) { return j * kD + ((((i >> 3) ^ (j & 15))) << 3) + (i & 7); }
-
-// Clip, quantise, pack and store one token's vector held as y[m][i] =
-// channel 16 m + 4 qa + i (the lanes qa = 0..3 with the same token hold the
-// rest).  tau: LDS [128].  Every lane of the wave must call it (lane swaps).
-// kBits: 2 (INT2 block) or 4 (INT4 block).
 template <int kBits>
-__device__ __forceinline__ void quant_store_token(float (&y)[8][4], const float* tau, bool is_v, bool valid,
-                                                  uint8_t* blk, int ps, int qa) {
-  float gmn[4], gmx[4];
+struct DemCfg {
+  static constexpr int kPages = kBits == 4 ? 1 : 2;     // pages per work unit (LDS: 8 images of kPages blocks)
+};
+
+// LDS copy of R^T: row c holds R[:, c] as 16 chunks of 8 bf16; chunk k of row c
+// sits at position k ^ swz(c).  One fragment load reads the rows
+// 32 (r >> 2) + 4 m + (r & 3), r = 0..15, whose swz values are r itself, so
+// the 16 rows fall on different banks.
+__device__ __forceinline__ int rt_swz(int c) { return (c & 3) | (((c >> 5) & 3) << 2); }
+__device__ __forceinline__ int rt_index(int c, int i) { return c * kD + ((((i >> 3) ^ rt_swz(c))) << 3) + (i & 7); }
+__device__ __forceinline__ int out_channel(int m, int r) { return 32 * (r >> 2) + 4 * m + (r & 3); }
+
+// Clip, group parameters and codes of one lane's group (32 values, channel
+// 32 g + 4 m + i in y[m][i]); tau_g: LDS, the group's 32 thresholds.
+template <int kBits>
+__device__ __forceinline__ void quant_lane_group(float (&y)[8][4], const float* tau_g, uint32_t (&code)[8][4],
+                                                 __half& sc, __half& zr) {
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    const float4 t4 = *reinterpret_cast<const float4*>(&tau[16 * m + 4 * qa]);
+    const float4 t4 = *reinterpret_cast<const float4*>(&tau_g[4 * m]);
     y[m][0] = clip_med3(y[m][0], t4.x);
     y[m][1] = clip_med3(y[m][1], t4.y);
     y[m][2] = clip_med3(y[m][2], t4.z);
     y[m][3] = clip_med3(y[m][3], t4.w);
   }
+  float mn = y[0][0], mx = y[0][0];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float mn = y[2 * g][0], mx = y[2 * g][0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) {
-      const float v = y[2 * g + (e >> 2)][e & 3];
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
-    // across the four lanes a = 0..3 that share this token
-    const auto pn = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-    const auto px = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mn = fminf(__uint_as_float(pn[0]), __uint_as_float(pn[1]));
-    mx = fmaxf(__uint_as_float(px[0]), __uint_as_float(px[1]));
-    const auto qn = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-    const auto qx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    gmn[g] = fminf(__uint_as_float(qn[0]), __uint_as_float(qn[1]));
-    gmx[g] = fmaxf(__uint_as_float(qx[0]), __uint_as_float(qx[1]));
+  for (int e = 1; e < 31; e += 2) {
+    const float v0 = y[e >> 2][e & 3], v1 = y[(e + 1) >> 2][(e + 1) & 3];
+    mn = fminf(fminf(mn, v0), v1);
+    mx = fmaxf(fmaxf(mx, v0), v1);
   }
-  __half sc[4], zr[4];
-  float zf[4];
-  CodeCut cut[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    group_scale_zero(gmn[g], gmx[g], &sc[g], &zr[g], kBits == 4 ? 15.0f : 3.0f);
-    zf[g] = __half2float(zr[g]);
-    cut[g] = code_cut(__half2float(sc[g]));
-  }
-  uint32_t code[8][4];
+  mn = fminf(mn, y[7][3]);
+  mx = fmaxf(mx, y[7][3]);
+  group_scale_zero(mn, mx, &sc, &zr, kBits == 4 ? 15.0f : 3.0f);
+  const float zf = __half2float(zr), sf = __half2float(sc);
+  const CodeCut cut = code_cut(sf);
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      code[m][i] = kBits == 4 ? quant_code(y[m][i], zf[m >> 1], __half2float(sc[m >> 1]), 15.0f)
-                              : quant_code_cut(y[m][i] - zf[m >> 1], cut[m >> 1]);
-  auto push = [&](uint32_t acc, int sh, int m, int i) { return (acc << sh) + code[m][i]; };
+      code[m][i] = kBits == 4 ? quant_code(y[m][i], zf, sf, 15.0f) : quant_code_cut(y[m][i] - zf, cut);
+}
 
-  if constexpr (kBits == 4) {
-    if (!is_v) {
-      // K: channel j = 16m + 4a + i is in chunk 2(m & 1) + (a >> 1), word
-      // m >> 1, nibble at bit 16(i & 1) + 8(a & 1) + 4(i >> 1); lanes a and
-      // a ^ 1 fill the two byte halves of each 16-bit half of the same word.
-      uint32_t wd[8];
+// Write one lane's group of codes, scale and zero (token slot t, group g)
+// into the page image `img` (one block).  Every lane of the wave calls it:
+// the K words of an INT2 block combine two groups, the V half-words four
+// (INT4: two), by lane swaps.  Only lanes of valid tokens write.
+template <int kBits>
+__device__ __forceinline__ void pack_lane_group(const uint32_t (&c)[8][4], __half sc, __half zr, bool is_v, int t,
+                                                int g, bool valid, uint8_t* img) {
+  if (!is_v) {
+    // K: chunk row a holds channels 32 g + 8 a + e, e = 0..7 (code c[2a + (e >> 2)][e & 3])
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        uint32_t w = code[m][0] | (code[m][1] << 16) | (code[m][2] << 4) | (code[m][3] << 20);
-        w <<= 8 * (qa & 1);
+    for (int a = 0; a < 4; ++a) {
+      uint32_t w = 0;
+      if constexpr (kBits == 4) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= c[2 * a + (e >> 2)][e & 3] << (16 * (e & 1) + 4 * ((e >> 1) & 3));
+        if (valid) *reinterpret_cast<uint32_t*>(img + 16 * (16 * a + t) + 4 * g) = w;
+      } else {
+        // fields ((e >> 1) & 3) + 8 (e & 1) + 4 (g & 1) of word g >> 1; the
+        // lane of group g ^ 1 fills the other half
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= c[2 * a + (e >> 2)][e & 3] << (2 * (((e >> 1) & 3) + 8 * (e & 1)));
+        w <<= 8 * (g & 1);
         const auto pr = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-        wd[m] = pr[0] | pr[1];
-      }
-      if (valid && (qa & 1) == 0) {
-        *reinterpret_cast<u32x4_t*>(blk + 16 * (16 * (qa >> 1) + ps)) = (u32x4_t){wd[0], wd[2], wd[4], wd[6]};
-        *reinterpret_cast<u32x4_t*>(blk + 16 * (16 * (2 + (qa >> 1)) + ps)) = (u32x4_t){wd[1], wd[3], wd[5], wd[7]};
-      }
-    } else {
-      // V: channel 4a + i of this token: codes of channels 16m with m < 4 in
-      // one half-word (nibble m), m >= 4 in another (nibble m - 4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = code[0][i] | (code[1][i] << 4) | (code[2][i] << 8) | (code[3][i] << 12);
-        const uint32_t hi = code[4][i] | (code[5][i] << 4) | (code[6][i] << 8) | (code[7][i] << 12);
-        if (valid) {
-          *reinterpret_cast<uint16_t*>(blk + v4_halfword_byte(ps, 4 * qa + i, 0)) = (uint16_t)lo;
-          *reinterpret_cast<uint16_t*>(blk + v4_halfword_byte(ps, 4 * qa + i, 1)) = (uint16_t)hi;
-        }
-      }
-    }
-  } else if (!is_v) {
-    // K: channel j = 16m + 4a + i lands in word (2(m&1) + (a>>1), m>>2) at
-    // field 4((m>>1)&1) + 2(a&1) + (i>>1) + 8(i&1); lanes a and a^1 fill
-    // complementary fields of the same four words.  A lane builds its eight
-    // fields at 4hb + (i>>1) + 8(i&1) from the highest down, then moves them
-    // up by 2(a&1) fields.
-    uint32_t wd[2][2];
-#pragma unroll
-    for (int ai = 0; ai < 2; ++ai)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const int m0 = ai + 4 * w, m1 = ai + 2 + 4 * w;   // hb = 0, 1
-        uint32_t acc = push(0u, 0, m1, 3);               // field 13
-        acc = push(acc, 2, m1, 1);                       // 12
-        acc = push(acc, 6, m0, 3);                       // 9
-        acc = push(acc, 2, m0, 1);                       // 8
-        acc = push(acc, 6, m1, 2);                       // 5
-        acc = push(acc, 2, m1, 0);                       // 4
-        acc = push(acc, 6, m0, 2);                       // 1
-        acc = push(acc, 2, m0, 0);                       // 0
-        acc <<= 4 * (qa & 1);
-        const auto pr = __builtin_amdgcn_permlane16_swap(acc, acc, false, false);
-        wd[ai][w] = pr[0] | pr[1];
-      }
-    if (valid && (qa & 1) == 0) {
-#pragma unroll
-      for (int ai = 0; ai < 2; ++ai) {
-        const int aa = 2 * ai + (qa >> 1);
-        *reinterpret_cast<u32x2_t*>(blk + 16 * (16 * aa + ps)) = (u32x2_t){wd[ai][0], wd[ai][1]};
+        w = pr[0] | pr[1];
+        if (valid && (g & 1) == 0) *reinterpret_cast<uint32_t*>(img + 16 * (16 * a + t) + 4 * (g >> 1)) = w;
       }
     }
   } else {
-    // V: the 8 codes of (token, channel 4a + i) form one half-word, code of
-    // channel 16m + 4a + i at bits 2m.
+    // V: the half-word of (token t, channel residue b) holds channels b + 16 k,
+    // k = 0..7 (INT2, 2 bits each) or 4 hi .. 4 hi + 3 (INT4, 4 bits each); this
+    // lane's group g holds k = 2 g and 2 g + 1: codes c[b >> 2][b & 3] and
+    // c[(b >> 2) + 4][b & 3].  dword j carries residues 2 j and 2 j + 1.
+    constexpr int kW = kBits == 4 ? 4 : 2;                 // bits per code
+    const int sh = kBits == 4 ? 8 * (g & 1) : 4 * g;
+    uint32_t d[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t hw = push(0u, 0, 7, i);
+    for (int j = 0; j < 8; ++j) {
+      const int b0 = 2 * j, b1 = 2 * j + 1;
+      const uint32_t h0 = c[b0 >> 2][b0 & 3] | (c[(b0 >> 2) + 4][b0 & 3] << kW);
+      const uint32_t h1 = c[b1 >> 2][b1 & 3] | (c[(b1 >> 2) + 4][b1 & 3] << kW);
+      d[j] = (h0 | (h1 << 16)) << sh;
+    }
+    // lanes g and g ^ 1 (INT4: complete half-words; INT2: two of the four groups)
+    uint32_t e[4];
 #pragma unroll
-      for (int m = 6; m >= 0; --m) hw = push(hw, 2, m, i);
-      if (valid) *reinterpret_cast<uint16_t*>(blk + v_halfword_byte(ps, 4 * qa + i)) = (uint16_t)hw;
+    for (int j = 0; j < 4; ++j) {
+      const auto pr = __builtin_amdgcn_permlane16_swap(d[j], d[j + 4], false, false);
+      e[j] = pr[0] | pr[1];          // g even: residues 2j, 2j+1; g odd: 2j+8, 2j+9
+    }
+    const int tq = t >> 2, tw = (t & 3) >> 1, th = t & 1;
+    if constexpr (kBits == 4) {
+      const int bb = 8 * (g & 1);
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int b = bb + 2 * j + hh;
+            *reinterpret_cast<uint16_t*>(img + kVCodeOff4 + 16 * (16 * tq + b) + 4 * (2 * (g >> 1) + tw) + 2 * th) =
+                (uint16_t)(e[j] >> (16 * hh));
+          }
+      }
+    } else {
+      // lanes g and g ^ 2: all four groups
+      uint32_t f[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const auto pr = __builtin_amdgcn_permlane32_swap(e[j], e[j + 2], false, false);
+        f[j] = pr[0] | pr[1];
+      }
+      // this lane now holds residues bb .. bb + 3
+      const int bb = 8 * (g & 1) + 4 * (g >> 1);
+      if (valid) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<uint16_t*>(img + 16 * (16 * tq + bb + k) + 8 + 4 * tw + 2 * th) =
+              (uint16_t)(f[k >> 1] >> (16 * (k & 1)));
+      }
     }
   }
   if (valid) {
-    // lane a stores group a's scale and zero (selects, not a dynamic index)
-    const int g = qa;
-    const uint32_t s01 = half_bits(sc[0]) | ((uint32_t)half_bits(sc[1]) << 16);
-    const uint32_t s23 = half_bits(sc[2]) | ((uint32_t)half_bits(sc[3]) << 16);
-    const uint32_t z01 = half_bits(zr[0]) | ((uint32_t)half_bits(zr[1]) << 16);
-    const uint32_t z23 = half_bits(zr[2]) | ((uint32_t)half_bits(zr[3]) << 16);
-    const int sh = 16 * (g & 1);
-    const int so = (is_v ? v_scale_byte(ps, g) : k_scale_byte(ps, g)) + meta_shift(kBits);
-    const int zo = (is_v ? v_zero_byte(ps, g) : k_zero_byte(ps, g)) + meta_shift(kBits);
-    *reinterpret_cast<uint16_t*>(blk + so) = (uint16_t)(((g < 2) ? s01 : s23) >> sh);
-    *reinterpret_cast<uint16_t*>(blk + zo) = (uint16_t)(((g < 2) ? z01 : z23) >> sh);
+    const int so = (is_v ? v_scale_byte(t, g) : k_scale_byte(t, g)) + meta_shift(kBits);
+    const int zo = (is_v ? v_zero_byte(t, g) : k_zero_byte(t, g)) + meta_shift(kBits);
+    *reinterpret_cast<uint16_t*>(img + so) = half_bits(sc);
+    *reinterpret_cast<uint16_t*>(img + zo) = half_bits(zr);
   }
 }
 
 template <bool kRotatedInput, int kBits>
-__global__ __launch_bounds__(256) void demote_bulk_kernel(DemoteArgs a) {
-  __shared__ __bf16 rt_hi[kRotatedInput ? 1 : kD * kD];
-  __shared__ __bf16 rt_lo[kRotatedInput ? 1 : kD * kD];
-  __shared__ float tau_s[kD];
-  const int is_v = blockIdx.y;
+__global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
+  constexpr int kPages = DemCfg<kBits>::kPages;
+  constexpr int kBytes = block_bytes(kBits);
+  constexpr int kRt = kRotatedInput ? 1 : kD * kD;
+  __shared__ __bf16 rt_hi[2][kRt];            // [K|V] R^T hi terms
+  __shared__ __bf16 rt_lo[2][kRt];
+  __shared__ float tau_s[2][kD];
+  __shared__ __attribute__((aligned(16))) uint8_t img_all[8][kPages * kBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tcol = lane & 15, qa = lane >> 4;
-  // One R and tau per KV head: workgroup z serves KV head z alone (its R is
-  // the one staged in LDS); with a shared pair every workgroup serves all.
+  const int t = lane & 15, g = lane >> 4;
+  // One R and tau per KV head: workgroup z serves KV head z alone (its Rs are
+  // the ones staged in LDS); with a shared pair every workgroup serves all.
   const bool per_head = a.clip_kv_stride != 0;
   const int heads_here = per_head ? 1 : a.hkv;
   const int hk_base = per_head ? (int)blockIdx.z : 0;
 
   if constexpr (!kRotatedInput) {
-    // R (row-major fp32) -> LDS R^T split into bf16 hi + lo.
-    const float* R = (is_v ? a.rot_v : a.rot_k) + (size_t)hk_base * a.rot_kv_stride;
-    for (int idx = tid; idx < kD * kD / 4; idx += 256) {
-      const float4 v4 = reinterpret_cast<const float4*>(R)[idx];
-      const int i = idx / (kD / 4), j0 = (idx % (kD / 4)) * 4;
-      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+    // R (row-major fp32) -> LDS R^T split into bf16 hi + lo, for K and V, in
+    // chunks of 8 input rows of one column: lanes take consecutive columns
+    // (coalesced reads), each chunk leaves as one 16-byte store per term
+    for (int c = tid; c < 2 * kD * (kD / 8); c += 512) {
+      const int which = c / (kD * (kD / 8)), rem = c % (kD * (kD / 8));
+      const int j = rem % kD, i0 = 8 * (rem / kD);
+      const float* R = (which ? a.rot_v : a.rot_k) + (size_t)hk_base * a.rot_kv_stride;
+      bf16x8_t hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const __bf16 hi = (__bf16)vv[e];
-        const __bf16 lo = (__bf16)(vv[e] - (float)hi);
-        rt_hi[rt_index(j0 + e, i)] = hi;
-        rt_lo[rt_index(j0 + e, i)] = lo;
+      for (int e = 0; e < 8; ++e) {
+        const float v = R[(size_t)(i0 + e) * kD + j];
+        hi[e] = (__bf16)v;
+        lo[e] = (__bf16)(v - (float)hi[e]);
       }
+      *reinterpret_cast<bf16x8_t*>(&rt_hi[which][rt_index(j, i0)]) = hi;
+      *reinterpret_cast<bf16x8_t*>(&rt_lo[which][rt_index(j, i0)]) = lo;
     }
   }
-  if (tid < kD) tau_s[tid] = (is_v ? a.clip_v : a.clip_k)[(size_t)hk_base * a.clip_kv_stride + tid];
+  if (tid < 2 * kD)
+    tau_s[tid >> 7][tid & 127] = ((tid >> 7) ? a.clip_v : a.clip_k)[(size_t)hk_base * a.clip_kv_stride + (tid & 127)];
   __syncthreads();
 
+  uint8_t* img = img_all[wave];
   const int ups = a.unit_tiles;                       // units per (sequence, KV head)
   const int n_units = a.batch * heads_here * ups;
-  for (int u = blockIdx.x * 4 + wave; u < n_units; u += gridDim.x * 4) {
-    const int b = u / (heads_here * ups), rem = u % (heads_here * ups);
-    const int hk = hk_base + rem / ups, tok0 = kUnitTokens * (rem % ups);
-    const int count = a.length ? max(0, a.length[b] - kSink - kRecent) : a.n_tokens;
-    if (tok0 >= count) continue;                       // wave-uniform
-    const int slot = a.seq_slot ? a.seq_slot[b] : b;
-    const int h0 = a.hist_start ? a.hist_start[b] : 0;
-    // token of tile t for this lane (clamped to the last valid token)
-    auto src_token = [&](int t) { return min(tok0 + 16 * t + tcol, count - 1); };
-    auto page_of = [&](int t) { return a.page_table[(size_t)slot * a.max_pages + ((h0 + src_token(t)) >> 4)]; };
-    auto store = [&](float (&y)[8][4], int t, int page) {
-      const int tok = tok0 + 16 * t + tcol;
-      uint8_t* blk = a.hist + ((size_t)page * a.hkv + hk) * block_bytes(kBits);
-      quant_store_token<kBits>(y, tau_s, is_v != 0, tok < count, blk, (h0 + src_token(t)) & 15, qa);
-    };
-    if constexpr (kRotatedInput) {
-      for (int t = 0; t < kUnitTokens / 16; ++t) {
-        if (tok0 + 16 * t >= count) break;             // wave-uniform
-        const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) +
-                           (((size_t)b * a.src_tokens + a.src_tok0 + src_token(t)) * a.hkv + hk) * kD;
-        float y[8][4];
+  // A work unit: kPages history pages of one (sequence, KV head), starting at
+  // the page that holds the sequence's first demoted token.
+  struct Unit {
+    int b, hk, count, h0, page0;
+    bool live;
+  };
+  auto unit_of = [&](int u) {
+    Unit w{};
+    w.live = false;
+    if (u >= n_units) return w;
+    w.b = u / (heads_here * ups);
+    const int rem = u % (heads_here * ups);
+    w.hk = hk_base + rem / ups;
+    const int ui = rem % ups;
+    w.count = a.length ? max(0, a.length[w.b] - kSink - kRecent) : a.n_tokens;
+    w.h0 = a.hist_start ? a.hist_start[w.b] : 0;
+    w.page0 = (w.h0 >> 4) + kPages * ui;
+    w.live = w.count > 0 && 16 * w.page0 < w.h0 + w.count;
+    return w;
+  };
+  // this lane's source token of page p of unit w (clamped to a demoted one)
+  auto src_row = [&](const Unit& w, int p, int is_v) -> size_t {
+    const int idx = min(max(16 * (w.page0 + p) + t - w.h0, 0), w.count - 1);
+    return (((size_t)w.b * a.src_tokens + a.src_tok0 + idx) * a.hkv + w.hk) * kD;
+    (void)is_v;
+  };
+  // the inputs of one tensor of a unit, as the B operands of the rotation
+  // (lane (t, g): token t of each page, input channels 32 kk + 8 g .. + 7)
+  typedef bf16x8_t UnitX[kPages][4];
+  auto load_x = [&](const Unit& w, int is_v, UnitX& x) {
+    if constexpr (!kRotatedInput) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float4 v4 = *reinterpret_cast<const float4*>(src + 16 * m + 4 * qa);
-          y[m][0] = v4.x; y[m][1] = v4.y; y[m][2] = v4.z; y[m][3] = v4.w;
-        }
-        store(y, t, page_of(t));
-      }
-    } else {
-      constexpr int kT = kUnitTokens / 16;
-      bf16x8_t xb[kT][4];
+      for (int p = 0; p < kPages; ++p) {
+        const uint16_t* src = (is_v ? a.src_v : a.src_k) + src_row(w, p, is_v);
 #pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        const uint16_t* src = (is_v ? a.src_v : a.src_k) +
-                              (((size_t)b * a.src_tokens + a.src_tok0 + src_token(t)) * a.hkv + hk) * kD;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) xb[t][kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * qa);
-      }
-      // page ids travel with the inputs, so the stores never wait for them
-      int pg[kT];
-#pragma unroll
-      for (int t = 0; t < kT; ++t) pg[t] = page_of(t);
-      float4_t acc[kT][8];
-#pragma unroll
-      for (int t = 0; t < kT; ++t)
-#pragma unroll
-        for (int m = 0; m < 8; ++m) acc[t][m] = (float4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int row = rt_index(16 * m + tcol, 32 * kk + 8 * qa);
-          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&rt_hi[row]);
-          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&rt_lo[row]);
-#pragma unroll
-          for (int t = 0; t < kT; ++t) acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, xb[t][kk], acc[t][m], 0, 0, 0);
-#pragma unroll
-          for (int t = 0; t < kT; ++t) acc[t][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, xb[t][kk], acc[t][m], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < kT; ++t) {
-        if (tok0 + 16 * t >= count) break;             // wave-uniform
-        float y[8][4];
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) y[m][i] = acc[t][m][i];
-        store(y, t, pg[t]);
+        for (int kk = 0; kk < 4; ++kk) x[p][kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * g);
       }
     }
+  };
+  // acc[p][m] = rotated channels 32 g + 4 m + i of token t of page p
+  auto rotate = [&](int is_v, const UnitX& x, float4_t (&acc)[kPages][8]) {
+#pragma unroll
+    for (int p = 0; p < kPages; ++p)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[p][m] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // the next R^T fragment is read from LDS before the current products go out
+    bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&rt_hi[is_v][rt_index(out_channel(0, t), 8 * g)]);
+    bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&rt_lo[is_v][rt_index(out_channel(0, t), 8 * g)]);
+#pragma unroll
+    for (int f = 0; f < 32; ++f) {
+      const int kk = f >> 3, m = f & 7;
+      bf16x8_t nh = ah, nl = al;
+      if (f + 1 < 32) {
+        const int row = rt_index(out_channel((f + 1) & 7, t), 32 * ((f + 1) >> 3) + 8 * g);
+        nh = *reinterpret_cast<const bf16x8_t*>(&rt_hi[is_v][row]);
+        nl = *reinterpret_cast<const bf16x8_t*>(&rt_lo[is_v][row]);
+      }
+#pragma unroll
+      for (int p = 0; p < kPages; ++p) acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, x[p][kk], acc[p][m], 0, 0, 0);
+#pragma unroll
+      for (int p = 0; p < kPages; ++p) acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, x[p][kk], acc[p][m], 0, 0, 0);
+      ah = nh;
+      al = nl;
+    }
+  };
+  const int stride = gridDim.x * 8;
+  int u = blockIdx.x * 8 + wave;
+  Unit cur = unit_of(u);
+  UnitX xk, xv;
+  if (cur.live) {
+    load_x(cur, 0, xk);
+    load_x(cur, 1, xv);
+  }
+  while (u < n_units) {
+    const int un = u + stride;
+    const Unit nxt = unit_of(un);
+    if (cur.live) {                                          // wave-uniform
+      const int slot = a.seq_slot ? a.seq_slot[cur.b] : cur.b;
+      const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
+      int n_pg = 0;                                          // pages of the unit holding demoted tokens
+      uint8_t* blk[kPages];
+#pragma unroll
+      for (int p = 0; p < kPages; ++p) {
+        const bool has = 16 * (cur.page0 + p) < cur.h0 + cur.count;
+        blk[p] = has ? a.hist + ((size_t)pt_row[cur.page0 + p] * a.hkv + cur.hk) * kBytes : nullptr;
+        n_pg += has ? 1 : 0;
+      }
+      // pages only partly covered keep their other slots: read them into the image
+#pragma unroll
+      for (int p = 0; p < kPages; ++p) {
+        const int first = 16 * (cur.page0 + p);
+        if (p < n_pg && (first < cur.h0 || first + 16 > cur.h0 + cur.count)) {   // wave-uniform
+          for (int o = 16 * lane; o < kBytes; o += 1024)
+            *reinterpret_cast<u32x4_t*>(img + p * kBytes + o) = *reinterpret_cast<const u32x4_t*>(blk[p] + o);
+        }
+      }
+      auto valid_tok = [&](int p) {
+        const int h = 16 * (cur.page0 + p) + t;
+        return p < n_pg && h >= cur.h0 && h < cur.h0 + cur.count;
+      };
+#pragma unroll
+      for (int is_v = 0; is_v < 2; ++is_v) {
+        float4_t acc[kPages][8];
+        if constexpr (kRotatedInput) {
+#pragma unroll
+          for (int p = 0; p < kPages; ++p) {
+            const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) + src_row(cur, p, is_v) + 32 * g;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+              const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * m);
+              acc[p][m] = (float4_t){v4.x, v4.y, v4.z, v4.w};
+            }
+          }
+        } else {
+          rotate(is_v, is_v ? xv : xk, acc);
+          // this tensor's inputs of the next unit go out as soon as the
+          // products have consumed the current ones
+          if (nxt.live) load_x(nxt, is_v, is_v ? xv : xk);
+        }
+#pragma unroll
+        for (int p = 0; p < kPages; ++p) {
+          if (p < n_pg) {                                    // wave-uniform
+            float y[8][4];
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) y[m][i] = acc[p][m][i];
+            uint32_t code[8][4];
+            __half sc, zr;
+            quant_lane_group<kBits>(y, &tau_s[is_v][32 * g], code, sc, zr);
+            pack_lane_group<kBits>(code, sc, zr, is_v != 0, t, g, valid_tok(p), img + p * kBytes);
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // whole blocks out, 16 bytes per lane per store
+#pragma unroll
+      for (int p = 0; p < kPages; ++p) {
+        if (p < n_pg) {
+          for (int o = 16 * lane; o < kBytes; o += 1024)
+            *reinterpret_cast<u32x4_t*>(blk[p] + o) = *reinterpret_cast<const u32x4_t*>(img + p * kBytes + o);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else if (nxt.live) {
+      load_x(nxt, 0, xk);
+      load_x(nxt, 1, xv);
+    }
+    u = un;
+    cur = nxt;
   }
 }
 
@@ -376,24 +460,27 @@ hipError_t launch_demote(const DemoteArgs& a_in, int batch, int max_count, bool 
   if (max_count <= 0) return hipSuccess;
   DemoteArgs a = a_in;
   a.batch = batch;
-  a.unit_tiles = (max_count + kUnitTokens - 1) / kUnitTokens;
-  // two workgroups per compute unit per tensor at most (each stages R once);
-  // with one R per KV head, a slice of them per KV head (grid z)
+  // units of kPages history pages from the page holding each sequence's
+  // first demoted token (up to 15 slots before it)
+  const int pages_per_unit = a.code_bits == 4 ? DemCfg<4>::kPages : DemCfg<2>::kPages;
+  a.unit_tiles = (15 + max_count + 16 * pages_per_unit - 1) / (16 * pages_per_unit);
+  // one workgroup per compute unit (each stages R_K and R_V once); with one
+  // R per KV head, a slice of them per KV head (grid z)
   const bool per_head = a.clip_kv_stride != 0;
   const int heads = per_head ? a.hkv : 1;
   const long units = (long)batch * (per_head ? 1 : a.hkv) * a.unit_tiles;
-  const int nwg = (int)std::min<long>((units + 3) / 4, std::max(1, 256 / heads));
-  const dim3 grid(nwg, 2, heads);
+  const int nwg = (int)std::min<long>((units + 7) / 8, std::max(1, 256 / heads));
+  const dim3 grid(nwg, 1, heads);
   if (a.code_bits == 4) {
     if (rotated)
-      hipLaunchKernelGGL((demote_bulk_kernel<true, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<true, 4>), grid, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((demote_bulk_kernel<false, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<false, 4>), grid, dim3(512), 0, st, a);
   } else {
     if (rotated)
-      hipLaunchKernelGGL((demote_bulk_kernel<true, 2>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<true, 2>), grid, dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((demote_bulk_kernel<false, 2>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<false, 2>), grid, dim3(512), 0, st, a);
   }
   return hipGetLastError();
 }

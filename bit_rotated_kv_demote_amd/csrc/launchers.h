@@ -44,11 +44,8 @@ struct DemoteArgs {
   int max_pages;
   int hkv;
   int batch;          // set by the launcher
-  int unit_tiles;     // set by the launcher: 64-token units per (sequence, KV head)
+  int unit_tiles;     // set by the launcher: work units (runs of history pages) per (sequence, KV head)
 };
-
-// tokens of one bulk-demotion work unit (one wave)
-constexpr int kUnitTokens = 64;
 
 struct PrefillArgs {
   const uint16_t* src_k; const uint16_t* src_v;   // bf16 [batch][max_len][Hkv][128]
