@@ -142,6 +142,107 @@ __device__ __forceinline__ void quant_lane_group(float (&y)[8][4], const float* 
       code[m][i] = kBits == 4 ? quant_code(y[m][i], zf, sf, 15.0f) : quant_code_cut(y[m][i] - zf, cut);
 }
 
+// INT2 fast path of one lane's group: clip, group parameters, then each
+// code as two bits shifted straight into the packed words, with no compare.
+// x = y - zero is >= 0, so the order of x against a cut c >= 0 is the order
+// of their bit patterns as integers, and the cut tests of code_cut are sign
+// bits: x > c0 iff c0 - x < 0, x >= c1 iff (c1 - 1) - x < 0 (bit patterns),
+// x > c2 iff c2 - x < 0.  The three tests are nested, so bit 1 of the code
+// is the middle one and bit 0 the parity of all three;
+// alignbit(w, z, 31) = (w << 1) | (z >> 31) shifts a sign bit into w.
+__device__ __forceinline__ void quant_pack_int2(float (&y)[8][4], const float* tau_g, bool is_v, int t, int g,
+                                                bool valid, uint8_t* img) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const float4 t4 = *reinterpret_cast<const float4*>(&tau_g[4 * m]);
+    y[m][0] = clip_med3(y[m][0], t4.x);
+    y[m][1] = clip_med3(y[m][1], t4.y);
+    y[m][2] = clip_med3(y[m][2], t4.z);
+    y[m][3] = clip_med3(y[m][3], t4.w);
+  }
+  float mn = y[0][0], mx = y[0][0];
+#pragma unroll
+  for (int e = 1; e < 31; e += 2) {
+    const float v0 = y[e >> 2][e & 3], v1 = y[(e + 1) >> 2][(e + 1) & 3];
+    mn = fminf(fminf(mn, v0), v1);
+    mx = fmaxf(fmaxf(mx, v0), v1);
+  }
+  mn = fminf(mn, y[7][3]);
+  mx = fmaxf(mx, y[7][3]);
+  __half sc, zr;
+  group_scale_zero(mn, mx, &sc, &zr, 3.0f);
+  const float zf = __half2float(zr);
+  const CodeCut cut = code_cut(__half2float(sc));
+  const uint32_t k0 = __float_as_uint(cut.c0), k1 = __float_as_uint(cut.c1) - 1u, k2 = __float_as_uint(cut.c2);
+  // w <- 4 w + code of value y[m][i]
+  auto push = [&](uint32_t w, int m, int i) {
+    const uint32_t xb = __float_as_uint(y[m][i] - zf);
+    const uint32_t d1 = k1 - xb;
+    w = __builtin_amdgcn_alignbit(w, d1, 31);
+    return __builtin_amdgcn_alignbit(w, __builtin_amdgcn_bitop3_b32(k0 - xb, d1, k2 - xb, 0x96), 31);   // xor of three
+  };
+  if (!is_v) {
+    // chunk row a: channels 32 g + 8 a + e (value y[2a + (e >> 2)][e & 3]) go to
+    // field ((e >> 1) & 3) + 8 (e & 1) + 4 (g & 1) of word g >> 1; the lane of
+    // group g ^ 1 fills the other fields
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int k = 3; k >= 0; --k) w = push(w, 2 * a + (k >> 1), 2 * (k & 1) + 1);    // e = 2k + 1
+      w <<= 8;
+#pragma unroll
+      for (int k = 3; k >= 0; --k) w = push(w, 2 * a + (k >> 1), 2 * (k & 1));        // e = 2k
+      w <<= 8 * (g & 1);
+      const auto pr = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+      w = pr[0] | pr[1];
+      if (valid && (g & 1) == 0) *reinterpret_cast<uint32_t*>(img + 16 * (16 * a + t) + 4 * (g >> 1)) = w;
+    }
+  } else {
+    // the half-word of (token t, channel residue b) holds channels b + 16 k,
+    // k = 0..7, two bits each; this lane's group has k = 2 g (value
+    // y[b >> 2][b & 3]) and 2 g + 1 (y[(b >> 2) + 4][b & 3]).  dword j carries
+    // residues 2 j and 2 j + 1, this lane's nibble at bit 4 g of each half.
+    uint32_t d[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int b0 = 2 * j, b1 = 2 * j + 1;
+      uint32_t w = push(0u, (b1 >> 2) + 4, b1 & 3);
+      w = push(w, b1 >> 2, b1 & 3);
+      w <<= 12;
+      w = push(w, (b0 >> 2) + 4, b0 & 3);
+      w = push(w, b0 >> 2, b0 & 3);
+      d[j] = w << (4 * g);
+    }
+    // reduce-scatter over the four groups: lanes g and g ^ 1, then g and g ^ 2
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto pr = __builtin_amdgcn_permlane16_swap(d[j], d[j + 4], false, false);
+      e[j] = pr[0] | pr[1];          // g even: residues 2j, 2j+1; g odd: 2j+8, 2j+9
+    }
+    uint32_t f[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto pr = __builtin_amdgcn_permlane32_swap(e[j], e[j + 2], false, false);
+      f[j] = pr[0] | pr[1];
+    }
+    // this lane now holds residues bb .. bb + 3
+    const int bb = 8 * (g & 1) + 4 * (g >> 1);
+    const int tq = t >> 2, tw = (t & 3) >> 1, th = t & 1;
+    if (valid) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<uint16_t*>(img + 16 * (16 * tq + bb + k) + 8 + 4 * tw + 2 * th) =
+            (uint16_t)(f[k >> 1] >> (16 * (k & 1)));
+    }
+  }
+  if (valid) {
+    *reinterpret_cast<uint16_t*>(img + (is_v ? v_scale_byte(t, g) : k_scale_byte(t, g))) = half_bits(sc);
+    *reinterpret_cast<uint16_t*>(img + (is_v ? v_zero_byte(t, g) : k_zero_byte(t, g))) = half_bits(zr);
+  }
+}
+
 // Write one lane's group of codes, scale and zero (token slot t, group g)
 // into the page image `img` (one block).  Every lane of the wave calls it:
 // the K words of an INT2 block combine two groups, the V half-words four
@@ -274,31 +375,69 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
   uint8_t* img = img_all[wave];
   const int ups = a.unit_tiles;                       // units per (sequence, KV head)
   const int n_units = a.batch * heads_here * ups;
+  const int stride = gridDim.x * 8;
+  const int u_first = blockIdx.x * 8 + wave;          // this wave's units: u_first + stride * j
   // A work unit: kPages history pages of one (sequence, KV head), starting at
-  // the page that holds the sequence's first demoted token.
+  // the page that holds the sequence's first demoted token.  Its metadata
+  // (demoted count, first demoted position, physical pages) is loaded for
+  // kMeta units at a time into lanes: lane kPages * jj + p holds page p of
+  // unit jj of the batch, so the loop body issues no dependent loads.
+  constexpr int kMeta = 64 / kPages;
+  int m_pg = 0, m_cnt = 0, m_h0 = 0;
+  auto fill_meta = [&](int j0) {
+    const int jj = lane / kPages, p = lane % kPages;
+    const int uu = u_first + stride * (j0 + jj);
+    m_pg = 0;
+    m_cnt = 0;
+    m_h0 = 0;
+    if (uu < n_units) {
+      const int b = uu / (heads_here * ups), ui = (uu % (heads_here * ups)) % ups;
+      const int cnt = a.length ? max(0, a.length[b] - kSink - kRecent) : a.n_tokens;
+      const int h0 = a.hist_start ? a.hist_start[b] : 0;
+      const int page = (h0 >> 4) + kPages * ui + p;
+      m_cnt = cnt;
+      m_h0 = h0;
+      if (cnt > 0 && 16 * page < h0 + cnt) {
+        const int slot = a.seq_slot ? a.seq_slot[b] : b;
+        m_pg = a.page_table[(size_t)slot * a.max_pages + page];
+      }
+    }
+    // wait here (vmcnt 0), so that reading the lanes later never waits on
+    // the stores and tile loads in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
   struct Unit {
-    int b, hk, count, h0, page0;
+    int b, hk, count, h0, page0, n_pg;
+    int pg[kPages];
     bool live;
   };
-  auto unit_of = [&](int u) {
+  // unit j of the wave, jj = j - (first unit of the loaded metadata)
+  auto unit_at = [&](int j, int jj) {
     Unit w{};
+    const int uu = u_first + stride * j;
     w.live = false;
-    if (u >= n_units) return w;
-    w.b = u / (heads_here * ups);
-    const int rem = u % (heads_here * ups);
+    if (uu >= n_units) return w;
+    w.b = uu / (heads_here * ups);
+    const int rem = uu % (heads_here * ups);
     w.hk = hk_base + rem / ups;
-    const int ui = rem % ups;
-    w.count = a.length ? max(0, a.length[w.b] - kSink - kRecent) : a.n_tokens;
-    w.h0 = a.hist_start ? a.hist_start[w.b] : 0;
-    w.page0 = (w.h0 >> 4) + kPages * ui;
-    w.live = w.count > 0 && 16 * w.page0 < w.h0 + w.count;
+    w.count = __builtin_amdgcn_readlane(m_cnt, kPages * jj);
+    w.h0 = __builtin_amdgcn_readlane(m_h0, kPages * jj);
+    w.page0 = (w.h0 >> 4) + kPages * (rem % ups);
+    w.n_pg = 0;
+#pragma unroll
+    for (int p = 0; p < kPages; ++p) {
+      w.pg[p] = __builtin_amdgcn_readlane(m_pg, kPages * jj + p);
+      w.n_pg += (16 * (w.page0 + p) < w.h0 + w.count) ? 1 : 0;
+    }
+    w.live = w.count > 0 && w.n_pg > 0;
     return w;
   };
-  // this lane's source token of page p of unit w (clamped to a demoted one)
-  auto src_row = [&](const Unit& w, int p, int is_v) -> size_t {
-    const int idx = min(max(16 * (w.page0 + p) + t - w.h0, 0), w.count - 1);
+  // this lane's source token of page p of unit w (clamped to a demoted one;
+  // a unit with no work reads its sequence's first source row, or that of
+  // sequence 0 past the last unit, which a launch always has)
+  auto src_row = [&](const Unit& w, int p) -> size_t {
+    const int idx = w.live ? min(max(16 * (w.page0 + p) + t - w.h0, 0), w.count - 1) : 0;
     return (((size_t)w.b * a.src_tokens + a.src_tok0 + idx) * a.hkv + w.hk) * kD;
-    (void)is_v;
   };
   // the inputs of one tensor of a unit, as the B operands of the rotation
   // (lane (t, g): token t of each page, input channels 32 kk + 8 g .. + 7)
@@ -307,7 +446,7 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     if constexpr (!kRotatedInput) {
 #pragma unroll
       for (int p = 0; p < kPages; ++p) {
-        const uint16_t* src = (is_v ? a.src_v : a.src_k) + src_row(w, p, is_v);
+        const uint16_t* src = (is_v ? a.src_v : a.src_k) + src_row(w, p);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) x[p][kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * g);
       }
@@ -315,114 +454,129 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
   };
   // acc[p][m] = rotated channels 32 g + 4 m + i of token t of page p
   auto rotate = [&](int is_v, const UnitX& x, float4_t (&acc)[kPages][8]) {
+    // R^T fragments f = 8 kk + m stream from LDS kAhead steps ahead of the
+    // products that use them (a ring of kAhead + 1)
+    constexpr int kAhead = 3;
+    bf16x8_t fh[kAhead + 1], fl[kAhead + 1];
+    auto frag = [&](int f, bf16x8_t& h, bf16x8_t& l) {
+      const int row = rt_index(out_channel(f & 7, t), 32 * (f >> 3) + 8 * g);
+      h = *reinterpret_cast<const bf16x8_t*>(&rt_hi[is_v][row]);
+      l = *reinterpret_cast<const bf16x8_t*>(&rt_lo[is_v][row]);
+    };
 #pragma unroll
-    for (int p = 0; p < kPages; ++p)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) acc[p][m] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    // the next R^T fragment is read from LDS before the current products go out
-    bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&rt_hi[is_v][rt_index(out_channel(0, t), 8 * g)]);
-    bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&rt_lo[is_v][rt_index(out_channel(0, t), 8 * g)]);
+    for (int f = 0; f < kAhead; ++f) frag(f, fh[f], fl[f]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);     // LDS reads
 #pragma unroll
     for (int f = 0; f < 32; ++f) {
       const int kk = f >> 3, m = f & 7;
-      bf16x8_t nh = ah, nl = al;
-      if (f + 1 < 32) {
-        const int row = rt_index(out_channel((f + 1) & 7, t), 32 * ((f + 1) >> 3) + 8 * g);
-        nh = *reinterpret_cast<const bf16x8_t*>(&rt_hi[is_v][row]);
-        nl = *reinterpret_cast<const bf16x8_t*>(&rt_lo[is_v][row]);
+      if (f + kAhead < 32) {
+        frag(f + kAhead, fh[(f + kAhead) % (kAhead + 1)], fl[(f + kAhead) % (kAhead + 1)]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kPages, 0);   // matrix products
+      const bf16x8_t ah = fh[f % (kAhead + 1)], al = fl[f % (kAhead + 1)];
+      // the first product of each accumulator takes a zero C operand
 #pragma unroll
-      for (int p = 0; p < kPages; ++p) acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, x[p][kk], acc[p][m], 0, 0, 0);
+      for (int p = 0; p < kPages; ++p)
+        acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, x[p][kk], kk == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : acc[p][m],
+                                                            0, 0, 0);
 #pragma unroll
       for (int p = 0; p < kPages; ++p) acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, x[p][kk], acc[p][m], 0, 0, 0);
-      ah = nh;
-      al = nl;
     }
   };
-  const int stride = gridDim.x * 8;
-  int u = blockIdx.x * 8 + wave;
-  Unit cur = unit_of(u);
+  int jb = 0;                                          // first unit of the loaded metadata
+  fill_meta(0);
+  Unit cur = unit_at(0, 0);
   UnitX xk, xv;
-  if (cur.live) {
-    load_x(cur, 0, xk);
-    load_x(cur, 1, xv);
-  }
-  while (u < n_units) {
-    const int un = u + stride;
-    const Unit nxt = unit_of(un);
-    if (cur.live) {                                          // wave-uniform
-      const int slot = a.seq_slot ? a.seq_slot[cur.b] : cur.b;
-      const int32_t* pt_row = a.page_table + (size_t)slot * a.max_pages;
-      int n_pg = 0;                                          // pages of the unit holding demoted tokens
-      uint8_t* blk[kPages];
+  load_x(cur, 0, xk);
+  load_x(cur, 1, xv);
+  for (int j = 0; u_first + stride * j < n_units; ++j) {
+    if (j + 1 - jb == kMeta) {                           // wave-uniform
+      jb += kMeta;
+      fill_meta(jb);
+    }
+    const Unit nxt = unit_at(j + 1, j + 1 - jb);
+    // (the branches below are wave-uniform; the next unit's loads sit at the
+    // same points whether or not this unit has work, into the same registers)
+    uint8_t* blk[kPages];
 #pragma unroll
-      for (int p = 0; p < kPages; ++p) {
-        const bool has = 16 * (cur.page0 + p) < cur.h0 + cur.count;
-        blk[p] = has ? a.hist + ((size_t)pt_row[cur.page0 + p] * a.hkv + cur.hk) * kBytes : nullptr;
-        n_pg += has ? 1 : 0;
-      }
+    for (int p = 0; p < kPages; ++p) blk[p] = a.hist + ((size_t)cur.pg[p] * a.hkv + cur.hk) * kBytes;
+    if (cur.live) {
       // pages only partly covered keep their other slots: read them into the image
 #pragma unroll
       for (int p = 0; p < kPages; ++p) {
         const int first = 16 * (cur.page0 + p);
-        if (p < n_pg && (first < cur.h0 || first + 16 > cur.h0 + cur.count)) {   // wave-uniform
-          for (int o = 16 * lane; o < kBytes; o += 1024)
-            *reinterpret_cast<u32x4_t*>(img + p * kBytes + o) = *reinterpret_cast<const u32x4_t*>(blk[p] + o);
+        if (p < cur.n_pg && (first < cur.h0 || first + 16 > cur.h0 + cur.count)) {
+#pragma unroll
+          for (int o = 0; o < kBytes; o += 512)
+            *reinterpret_cast<uint64_t*>(img + p * kBytes + o + 8 * lane) =
+                *reinterpret_cast<const uint64_t*>(blk[p] + o + 8 * lane);
         }
       }
-      auto valid_tok = [&](int p) {
-        const int h = 16 * (cur.page0 + p) + t;
-        return p < n_pg && h >= cur.h0 && h < cur.h0 + cur.count;
-      };
+    }
+    auto valid_tok = [&](int p) {
+      const int h = 16 * (cur.page0 + p) + t;
+      return p < cur.n_pg && h >= cur.h0 && h < cur.h0 + cur.count;
+    };
 #pragma unroll
-      for (int is_v = 0; is_v < 2; ++is_v) {
-        float4_t acc[kPages][8];
-        if constexpr (kRotatedInput) {
+    for (int is_v = 0; is_v < 2; ++is_v) {
+      float4_t acc[kPages][8];
+      if constexpr (kRotatedInput) {
+        if (cur.live) {
 #pragma unroll
           for (int p = 0; p < kPages; ++p) {
-            const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) + src_row(cur, p, is_v) + 32 * g;
+            const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) + src_row(cur, p) + 32 * g;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
               const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * m);
               acc[p][m] = (float4_t){v4.x, v4.y, v4.z, v4.w};
             }
           }
-        } else {
-          rotate(is_v, is_v ? xv : xk, acc);
-          // this tensor's inputs of the next unit go out as soon as the
-          // products have consumed the current ones
-          if (nxt.live) load_x(nxt, is_v, is_v ? xv : xk);
         }
+      } else {
+        if (cur.live) rotate(is_v, is_v ? xv : xk, acc);
+        // this tensor's inputs of the next unit go out as soon as the
+        // products have consumed the current ones; they are issued on every
+        // path (a dead unit reads a valid row), so the waits before the next
+        // products count exactly the loads and stores issued since
+        load_x(nxt, is_v, is_v ? xv : xk);
+      }
+      if (cur.live) {
 #pragma unroll
         for (int p = 0; p < kPages; ++p) {
-          if (p < n_pg) {                                    // wave-uniform
+          if (p < cur.n_pg) {
             float y[8][4];
 #pragma unroll
             for (int m = 0; m < 8; ++m)
 #pragma unroll
               for (int i = 0; i < 4; ++i) y[m][i] = acc[p][m][i];
-            uint32_t code[8][4];
-            __half sc, zr;
-            quant_lane_group<kBits>(y, &tau_s[is_v][32 * g], code, sc, zr);
-            pack_lane_group<kBits>(code, sc, zr, is_v != 0, t, g, valid_tok(p), img + p * kBytes);
+            if constexpr (kBits == 2) {
+              quant_pack_int2(y, &tau_s[is_v][32 * g], is_v != 0, t, g, valid_tok(p), img + p * kBytes);
+            } else {
+              uint32_t code[8][4];
+              __half sc, zr;
+              quant_lane_group<kBits>(y, &tau_s[is_v][32 * g], code, sc, zr);
+              pack_lane_group<kBits>(code, sc, zr, is_v != 0, t, g, valid_tok(p), img + p * kBytes);
+            }
           }
         }
       }
+    }
+    if (cur.live) {
       __builtin_amdgcn_wave_barrier();
-      // whole blocks out, 16 bytes per lane per store
+      // whole blocks out, 512 contiguous bytes per store over all lanes (the
+      // same stores on every lane, so waits on later loads need not drain them)
 #pragma unroll
       for (int p = 0; p < kPages; ++p) {
-        if (p < n_pg) {
-          for (int o = 16 * lane; o < kBytes; o += 1024)
-            *reinterpret_cast<u32x4_t*>(blk[p] + o) = *reinterpret_cast<const u32x4_t*>(img + p * kBytes + o);
+        if (p < cur.n_pg) {
+#pragma unroll
+          for (int o = 0; o < kBytes; o += 512)
+            *reinterpret_cast<uint64_t*>(blk[p] + o + 8 * lane) =
+                *reinterpret_cast<const uint64_t*>(img + p * kBytes + o + 8 * lane);
         }
       }
       __builtin_amdgcn_wave_barrier();
-    } else if (nxt.live) {
-      load_x(nxt, 0, xk);
-      load_x(nxt, 1, xv);
     }
-    u = un;
     cur = nxt;
   }
 }
