@@ -19,6 +19,7 @@
 //                      input is already-rotated fp32.
 //   prefill_route_kernel  copies of the sink and recent tiers of a prefill.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launchers.h"
@@ -99,8 +100,24 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // ---------------------------------------------------------------------------
 template <int kBits>
 struct DemCfg {
-  static constexpr int kPages = kBits == 4 ? 1 : 2;     // pages per work unit (LDS: 8 images of kPages blocks)
+  static constexpr int kPages = kBits == 4 ? 1 : 3;        // pages per work unit
+  static constexpr int kCodeBytes = kBits == 4 ? 1024 : 512;   // one tensor's code bytes in a block
+  static constexpr int kPart = kCodeBytes + 256;            // one tensor's bytes in a block (codes + meta)
+  static constexpr int kMetaBase = kBits == 4 ? 2048 : 1024;   // block offset of the K metadata
 };
+
+// Each wave handles one tensor, so its LDS image of a page holds only that
+// tensor's bytes of the block, packed: the code bytes first, then the 256
+// bytes of scales and zeros.  part_off maps a block offset of the tensor's
+// bytes to the image.  INT2: the code area's 16-byte rows carry K in bytes
+// 0..7 and V in bytes 8..15; INT4: K codes in [0, 1024), V in [1024, 2048).
+template <int kBits>
+__device__ __forceinline__ int part_off(bool is_v, int off) {
+  constexpr int kMeta = DemCfg<kBits>::kMetaBase;
+  if (off >= kMeta) return DemCfg<kBits>::kCodeBytes + off - kMeta - (is_v ? 256 : 0);
+  if constexpr (kBits == 4) return off - (is_v ? 1024 : 0);
+  return 8 * (off >> 4) + (off & 7);
+}
 
 // LDS copy of R^T: row c holds R[:, c] as 16 chunks of 8 bf16; chunk k of row c
 // sits at position k ^ swz(c).  One fragment load reads the rows
@@ -196,7 +213,7 @@ __device__ __forceinline__ void quant_pack_int2(float (&y)[8][4], const float* t
       w <<= 8 * (g & 1);
       const auto pr = __builtin_amdgcn_permlane16_swap(w, w, false, false);
       w = pr[0] | pr[1];
-      if (valid && (g & 1) == 0) *reinterpret_cast<uint32_t*>(img + 16 * (16 * a + t) + 4 * (g >> 1)) = w;
+      if (valid && (g & 1) == 0) *reinterpret_cast<uint32_t*>(img + part_off<2>(false, 16 * (16 * a + t) + 4 * (g >> 1))) = w;
     }
   } else {
     // the half-word of (token t, channel residue b) holds channels b + 16 k,
@@ -233,59 +250,46 @@ __device__ __forceinline__ void quant_pack_int2(float (&y)[8][4], const float* t
     if (valid) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<uint16_t*>(img + 16 * (16 * tq + bb + k) + 8 + 4 * tw + 2 * th) =
+        *reinterpret_cast<uint16_t*>(img + part_off<2>(true, 16 * (16 * tq + bb + k) + 8 + 4 * tw + 2 * th)) =
             (uint16_t)(f[k >> 1] >> (16 * (k & 1)));
     }
   }
   if (valid) {
-    *reinterpret_cast<uint16_t*>(img + (is_v ? v_scale_byte(t, g) : k_scale_byte(t, g))) = half_bits(sc);
-    *reinterpret_cast<uint16_t*>(img + (is_v ? v_zero_byte(t, g) : k_zero_byte(t, g))) = half_bits(zr);
+    *reinterpret_cast<uint16_t*>(img + part_off<2>(is_v, is_v ? v_scale_byte(t, g) : k_scale_byte(t, g))) = half_bits(sc);
+    *reinterpret_cast<uint16_t*>(img + part_off<2>(is_v, is_v ? v_zero_byte(t, g) : k_zero_byte(t, g))) = half_bits(zr);
   }
 }
 
-// Write one lane's group of codes, scale and zero (token slot t, group g)
-// into the page image `img` (one block).  Every lane of the wave calls it:
-// the K words of an INT2 block combine two groups, the V half-words four
-// (INT4: two), by lane swaps.  Only lanes of valid tokens write.
-template <int kBits>
-__device__ __forceinline__ void pack_lane_group(const uint32_t (&c)[8][4], __half sc, __half zr, bool is_v, int t,
-                                                int g, bool valid, uint8_t* img) {
+// INT4: write one lane's group of codes, scale and zero (token slot t, group
+// g) into the tensor's page image `img`.  Every lane of the wave calls it:
+// the V half-words combine two groups by a lane swap.  Only lanes of valid
+// tokens write.
+__device__ __forceinline__ void pack_lane_group4(const uint32_t (&c)[8][4], __half sc, __half zr, bool is_v, int t,
+                                                 int g, bool valid, uint8_t* img) {
   if (!is_v) {
     // K: chunk row a holds channels 32 g + 8 a + e, e = 0..7 (code c[2a + (e >> 2)][e & 3])
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       uint32_t w = 0;
-      if constexpr (kBits == 4) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w |= c[2 * a + (e >> 2)][e & 3] << (16 * (e & 1) + 4 * ((e >> 1) & 3));
-        if (valid) *reinterpret_cast<uint32_t*>(img + 16 * (16 * a + t) + 4 * g) = w;
-      } else {
-        // fields ((e >> 1) & 3) + 8 (e & 1) + 4 (g & 1) of word g >> 1; the
-        // lane of group g ^ 1 fills the other half
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w |= c[2 * a + (e >> 2)][e & 3] << (2 * (((e >> 1) & 3) + 8 * (e & 1)));
-        w <<= 8 * (g & 1);
-        const auto pr = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-        w = pr[0] | pr[1];
-        if (valid && (g & 1) == 0) *reinterpret_cast<uint32_t*>(img + 16 * (16 * a + t) + 4 * (g >> 1)) = w;
-      }
+      for (int e = 0; e < 8; ++e) w |= c[2 * a + (e >> 2)][e & 3] << (16 * (e & 1) + 4 * ((e >> 1) & 3));
+      if (valid) *reinterpret_cast<uint32_t*>(img + part_off<4>(false, 16 * (16 * a + t) + 4 * g)) = w;
     }
   } else {
-    // V: the half-word of (token t, channel residue b) holds channels b + 16 k,
-    // k = 0..7 (INT2, 2 bits each) or 4 hi .. 4 hi + 3 (INT4, 4 bits each); this
-    // lane's group g holds k = 2 g and 2 g + 1: codes c[b >> 2][b & 3] and
-    // c[(b >> 2) + 4][b & 3].  dword j carries residues 2 j and 2 j + 1.
-    constexpr int kW = kBits == 4 ? 4 : 2;                 // bits per code
-    const int sh = kBits == 4 ? 8 * (g & 1) : 4 * g;
+    // V: the half-word of (token t, channel residue b) holds channels b + 16 k
+    // for the four k of one half (4 bits each); this lane's group g holds
+    // k = 2 g and 2 g + 1: codes c[b >> 2][b & 3] and c[(b >> 2) + 4][b & 3].
+    // dword j carries residues 2 j and 2 j + 1.
+    const int sh = 8 * (g & 1);
     uint32_t d[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int b0 = 2 * j, b1 = 2 * j + 1;
-      const uint32_t h0 = c[b0 >> 2][b0 & 3] | (c[(b0 >> 2) + 4][b0 & 3] << kW);
-      const uint32_t h1 = c[b1 >> 2][b1 & 3] | (c[(b1 >> 2) + 4][b1 & 3] << kW);
+      const uint32_t h0 = c[b0 >> 2][b0 & 3] | (c[(b0 >> 2) + 4][b0 & 3] << 4);
+      const uint32_t h1 = c[b1 >> 2][b1 & 3] | (c[(b1 >> 2) + 4][b1 & 3] << 4);
       d[j] = (h0 | (h1 << 16)) << sh;
     }
-    // lanes g and g ^ 1 (INT4: complete half-words; INT2: two of the four groups)
+    // lanes g and g ^ 1 complete the half-words
     uint32_t e[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -293,53 +297,38 @@ __device__ __forceinline__ void pack_lane_group(const uint32_t (&c)[8][4], __hal
       e[j] = pr[0] | pr[1];          // g even: residues 2j, 2j+1; g odd: 2j+8, 2j+9
     }
     const int tq = t >> 2, tw = (t & 3) >> 1, th = t & 1;
-    if constexpr (kBits == 4) {
-      const int bb = 8 * (g & 1);
-      if (valid) {
+    const int bb = 8 * (g & 1);
+    if (valid) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int b = bb + 2 * j + hh;
-            *reinterpret_cast<uint16_t*>(img + kVCodeOff4 + 16 * (16 * tq + b) + 4 * (2 * (g >> 1) + tw) + 2 * th) =
-                (uint16_t)(e[j] >> (16 * hh));
-          }
-      }
-    } else {
-      // lanes g and g ^ 2: all four groups
-      uint32_t f[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const auto pr = __builtin_amdgcn_permlane32_swap(e[j], e[j + 2], false, false);
-        f[j] = pr[0] | pr[1];
-      }
-      // this lane now holds residues bb .. bb + 3
-      const int bb = 8 * (g & 1) + 4 * (g >> 1);
-      if (valid) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<uint16_t*>(img + 16 * (16 * tq + bb + k) + 8 + 4 * tw + 2 * th) =
-              (uint16_t)(f[k >> 1] >> (16 * (k & 1)));
-      }
+        for (int hh = 0; hh < 2; ++hh) {
+          const int b = bb + 2 * j + hh;
+          *reinterpret_cast<uint16_t*>(
+              img + part_off<4>(true, kVCodeOff4 + 16 * (16 * tq + b) + 4 * (2 * (g >> 1) + tw) + 2 * th)) =
+              (uint16_t)(e[j] >> (16 * hh));
+        }
     }
   }
   if (valid) {
-    const int so = (is_v ? v_scale_byte(t, g) : k_scale_byte(t, g)) + meta_shift(kBits);
-    const int zo = (is_v ? v_zero_byte(t, g) : k_zero_byte(t, g)) + meta_shift(kBits);
-    *reinterpret_cast<uint16_t*>(img + so) = half_bits(sc);
-    *reinterpret_cast<uint16_t*>(img + zo) = half_bits(zr);
+    const int so = (is_v ? v_scale_byte(t, g) : k_scale_byte(t, g)) + meta_shift(4);
+    const int zo = (is_v ? v_zero_byte(t, g) : k_zero_byte(t, g)) + meta_shift(4);
+    *reinterpret_cast<uint16_t*>(img + part_off<4>(is_v, so)) = half_bits(sc);
+    *reinterpret_cast<uint16_t*>(img + part_off<4>(is_v, zo)) = half_bits(zr);
   }
 }
 
 template <bool kRotatedInput, int kBits>
 __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
   constexpr int kPages = DemCfg<kBits>::kPages;
+  constexpr int kPart = DemCfg<kBits>::kPart;
+  constexpr int kCodeBytes = DemCfg<kBits>::kCodeBytes;
   constexpr int kBytes = block_bytes(kBits);
   constexpr int kRt = kRotatedInput ? 1 : kD * kD;
   __shared__ __bf16 rt_hi[2][kRt];            // [K|V] R^T hi terms
   __shared__ __bf16 rt_lo[2][kRt];
   __shared__ float tau_s[2][kD];
-  __shared__ __attribute__((aligned(16))) uint8_t img_all[8][kPages * kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t img_all[8][kPages * kPart];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 15, g = lane >> 4;
@@ -372,16 +361,21 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     tau_s[tid >> 7][tid & 127] = ((tid >> 7) ? a.clip_v : a.clip_k)[(size_t)hk_base * a.clip_kv_stride + (tid & 127)];
   __syncthreads();
 
+  // waves 0..3 demote K, waves 4..7 V (one of each per SIMD); the loop is
+  // compiled once per tensor
+  auto run = [&](auto tensor) {
+  constexpr int is_v = decltype(tensor)::value;
   uint8_t* img = img_all[wave];
   const int ups = a.unit_tiles;                       // units per (sequence, KV head)
   const int n_units = a.batch * heads_here * ups;
-  const int stride = gridDim.x * 8;
-  const int u_first = blockIdx.x * 8 + wave;          // this wave's units: u_first + stride * j
+  const int stride = gridDim.x * 4;
+  const int u_first = blockIdx.x * 4 + (wave & 3);    // this wave's units: u_first + stride * j
   // A work unit: kPages history pages of one (sequence, KV head), starting at
-  // the page that holds the sequence's first demoted token.  Its metadata
-  // (demoted count, first demoted position, physical pages) is loaded for
-  // kMeta units at a time into lanes: lane kPages * jj + p holds page p of
-  // unit jj of the batch, so the loop body issues no dependent loads.
+  // the page that holds the sequence's first demoted token; one K wave and
+  // one V wave take it.  Its metadata (demoted count, first demoted
+  // position, physical pages) is loaded for kMeta units at a time into
+  // lanes: lane kPages * jj + p holds page p of unit jj of the batch, so the
+  // loop body issues no dependent loads.
   constexpr int kMeta = 64 / kPages;
   int m_pg = 0, m_cnt = 0, m_h0 = 0;
   auto fill_meta = [&](int j0) {
@@ -390,7 +384,7 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     m_pg = 0;
     m_cnt = 0;
     m_h0 = 0;
-    if (uu < n_units) {
+    if (jj < kMeta && uu < n_units) {
       const int b = uu / (heads_here * ups), ui = (uu % (heads_here * ups)) % ups;
       const int cnt = a.length ? max(0, a.length[b] - kSink - kRecent) : a.n_tokens;
       const int h0 = a.hist_start ? a.hist_start[b] : 0;
@@ -439,29 +433,32 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     const int idx = w.live ? min(max(16 * (w.page0 + p) + t - w.h0, 0), w.count - 1) : 0;
     return (((size_t)w.b * a.src_tokens + a.src_tok0 + idx) * a.hkv + w.hk) * kD;
   };
-  // the inputs of one tensor of a unit, as the B operands of the rotation
+  // this wave's tensor inputs of a unit, as the B operands of the rotation
   // (lane (t, g): token t of each page, input channels 32 kk + 8 g .. + 7)
   typedef bf16x8_t UnitX[kPages][4];
-  auto load_x = [&](const Unit& w, int is_v, UnitX& x) {
+  const uint16_t* src_x = is_v ? a.src_v : a.src_k;
+  auto load_x = [&](const Unit& w, UnitX& x) {
     if constexpr (!kRotatedInput) {
 #pragma unroll
       for (int p = 0; p < kPages; ++p) {
-        const uint16_t* src = (is_v ? a.src_v : a.src_k) + src_row(w, p);
+        const uint16_t* src = src_x + src_row(w, p);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) x[p][kk] = *reinterpret_cast<const bf16x8_t*>(src + 32 * kk + 8 * g);
       }
     }
   };
+  const __bf16* rth = rt_hi[is_v];
+  const __bf16* rtl = rt_lo[is_v];
   // acc[p][m] = rotated channels 32 g + 4 m + i of token t of page p
-  auto rotate = [&](int is_v, const UnitX& x, float4_t (&acc)[kPages][8]) {
+  auto rotate = [&](const UnitX& x, float4_t (&acc)[kPages][8]) {
     // R^T fragments f = 8 kk + m stream from LDS kAhead steps ahead of the
     // products that use them (a ring of kAhead + 1)
     constexpr int kAhead = 3;
     bf16x8_t fh[kAhead + 1], fl[kAhead + 1];
     auto frag = [&](int f, bf16x8_t& h, bf16x8_t& l) {
       const int row = rt_index(out_channel(f & 7, t), 32 * (f >> 3) + 8 * g);
-      h = *reinterpret_cast<const bf16x8_t*>(&rt_hi[is_v][row]);
-      l = *reinterpret_cast<const bf16x8_t*>(&rt_lo[is_v][row]);
+      h = *reinterpret_cast<const bf16x8_t*>(&rth[row]);
+      l = *reinterpret_cast<const bf16x8_t*>(&rtl[row]);
     };
 #pragma unroll
     for (int f = 0; f < kAhead; ++f) frag(f, fh[f], fl[f]);
@@ -484,12 +481,40 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
       for (int p = 0; p < kPages; ++p) acc[p][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, x[p][kk], acc[p][m], 0, 0, 0);
     }
   };
+  // this wave's bytes of a block <-> its image of the page: the code bytes
+  // (INT2: 8 bytes of each 16-byte row, INT4: 16 contiguous bytes per lane)
+  // and 4 bytes per lane of the tensor's 256 metadata bytes
+  constexpr int kCodeOff = kBits == 4 ? 1024 * is_v : 8 * is_v;   // first code byte of lane 0 in the block
+  constexpr int kCodeStride = kBits == 4 ? 16 : 16;                // block bytes between lanes' code bytes
+  constexpr int kMetaOff = DemCfg<kBits>::kMetaBase + 256 * is_v;
+  auto part_read = [&](const uint8_t* blk, uint8_t* im) {
+    if constexpr (kBits == 4)
+      *reinterpret_cast<u32x4_t*>(im + 16 * lane) = *reinterpret_cast<const u32x4_t*>(blk + kCodeOff + kCodeStride * lane);
+    else
+      *reinterpret_cast<uint64_t*>(im + 8 * lane) = *reinterpret_cast<const uint64_t*>(blk + kCodeOff + kCodeStride * lane);
+    *reinterpret_cast<uint32_t*>(im + kCodeBytes + 4 * lane) = *reinterpret_cast<const uint32_t*>(blk + kMetaOff + 4 * lane);
+  };
+  // stores through a buffer resource: a page with nothing to store gets an
+  // empty range, which the hardware drops, so every path issues the same
+  // stores (and the waits before the next products need not cover them)
+  auto part_store = [&](uint8_t* blk, bool store, const uint8_t* im) {
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(blk, (short)0, store ? kBytes : 0, 0x00020000);
+    if constexpr (kBits == 4)
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(im + 16 * lane), r, kCodeOff + kCodeStride * lane, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2_t*>(im + 8 * lane), r, kCodeOff + kCodeStride * lane, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(*reinterpret_cast<const uint32_t*>(im + kCodeBytes + 4 * lane), r, kMetaOff + 4 * lane, 0, 0);
+  };
+
   int jb = 0;                                          // first unit of the loaded metadata
   fill_meta(0);
   Unit cur = unit_at(0, 0);
-  UnitX xk, xv;
-  load_x(cur, 0, xk);
-  load_x(cur, 1, xv);
+  UnitX x;
+  load_x(cur, x);
+  // the stores that follow the loads in every round, here with empty ranges,
+  // so that the loop is entered with the memory counter it keeps
+#pragma unroll
+  for (int p = 0; p < kPages; ++p) part_store(a.hist, false, img + p * kPart);
   for (int j = 0; u_first + stride * j < n_units; ++j) {
     if (j + 1 - jb == kMeta) {                           // wave-uniform
       jb += kMeta;
@@ -497,7 +522,7 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     }
     const Unit nxt = unit_at(j + 1, j + 1 - jb);
     // (the branches below are wave-uniform; the next unit's loads sit at the
-    // same points whether or not this unit has work, into the same registers)
+    // same point whether or not this unit has work, into the same registers)
     uint8_t* blk[kPages];
 #pragma unroll
     for (int p = 0; p < kPages; ++p) blk[p] = a.hist + ((size_t)cur.pg[p] * a.hkv + cur.hk) * kBytes;
@@ -506,79 +531,68 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
 #pragma unroll
       for (int p = 0; p < kPages; ++p) {
         const int first = 16 * (cur.page0 + p);
-        if (p < cur.n_pg && (first < cur.h0 || first + 16 > cur.h0 + cur.count)) {
-#pragma unroll
-          for (int o = 0; o < kBytes; o += 512)
-            *reinterpret_cast<uint64_t*>(img + p * kBytes + o + 8 * lane) =
-                *reinterpret_cast<const uint64_t*>(blk[p] + o + 8 * lane);
-        }
+        if (p < cur.n_pg && (first < cur.h0 || first + 16 > cur.h0 + cur.count)) part_read(blk[p], img + p * kPart);
       }
     }
     auto valid_tok = [&](int p) {
       const int h = 16 * (cur.page0 + p) + t;
       return p < cur.n_pg && h >= cur.h0 && h < cur.h0 + cur.count;
     };
-#pragma unroll
-    for (int is_v = 0; is_v < 2; ++is_v) {
-      float4_t acc[kPages][8];
-      if constexpr (kRotatedInput) {
-        if (cur.live) {
-#pragma unroll
-          for (int p = 0; p < kPages; ++p) {
-            const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) + src_row(cur, p) + 32 * g;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-              const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * m);
-              acc[p][m] = (float4_t){v4.x, v4.y, v4.z, v4.w};
-            }
-          }
-        }
-      } else {
-        if (cur.live) rotate(is_v, is_v ? xv : xk, acc);
-        // this tensor's inputs of the next unit go out as soon as the
-        // products have consumed the current ones; they are issued on every
-        // path (a dead unit reads a valid row), so the waits before the next
-        // products count exactly the loads and stores issued since
-        load_x(nxt, is_v, is_v ? xv : xk);
-      }
+    float4_t acc[kPages][8];
+    if constexpr (kRotatedInput) {
       if (cur.live) {
 #pragma unroll
         for (int p = 0; p < kPages; ++p) {
-          if (p < cur.n_pg) {
-            float y[8][4];
+          const float* src = (is_v ? a.src_v_f32 : a.src_k_f32) + src_row(cur, p) + 32 * g;
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) y[m][i] = acc[p][m][i];
-            if constexpr (kBits == 2) {
-              quant_pack_int2(y, &tau_s[is_v][32 * g], is_v != 0, t, g, valid_tok(p), img + p * kBytes);
-            } else {
-              uint32_t code[8][4];
-              __half sc, zr;
-              quant_lane_group<kBits>(y, &tau_s[is_v][32 * g], code, sc, zr);
-              pack_lane_group<kBits>(code, sc, zr, is_v != 0, t, g, valid_tok(p), img + p * kBytes);
-            }
+          for (int m = 0; m < 8; ++m) {
+            const float4 v4 = *reinterpret_cast<const float4*>(src + 4 * m);
+            acc[p][m] = (float4_t){v4.x, v4.y, v4.z, v4.w};
           }
         }
       }
+    } else {
+      // (on every path: a dead unit rotates the valid rows it loaded, so the
+      // loads are always consumed here)
+      rotate(x, acc);
     }
-    if (cur.live) {
-      __builtin_amdgcn_wave_barrier();
-      // whole blocks out, 512 contiguous bytes per store over all lanes (the
-      // same stores on every lane, so waits on later loads need not drain them)
+    auto quant_page = [&](int p) {
+      float y[8][4];
 #pragma unroll
-      for (int p = 0; p < kPages; ++p) {
-        if (p < cur.n_pg) {
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-          for (int o = 0; o < kBytes; o += 512)
-            *reinterpret_cast<uint64_t*>(blk[p] + o + 8 * lane) =
-                *reinterpret_cast<const uint64_t*>(img + p * kBytes + o + 8 * lane);
-        }
+        for (int i = 0; i < 4; ++i) y[m][i] = acc[p][m][i];
+      if constexpr (kBits == 2) {
+        quant_pack_int2(y, &tau_s[is_v][32 * g], is_v != 0, t, g, valid_tok(p), img + p * kPart);
+      } else {
+        uint32_t code[8][4];
+        __half sc, zr;
+        quant_lane_group<kBits>(y, &tau_s[is_v][32 * g], code, sc, zr);
+        pack_lane_group4(code, sc, zr, is_v != 0, t, g, valid_tok(p), img + p * kPart);
       }
-      __builtin_amdgcn_wave_barrier();
+    };
+    if (cur.live) quant_page(0);                       // a live unit has its first page
+    // the next unit's inputs go out once the products have consumed the
+    // current ones and the first page's accumulators are free; they are
+    // issued on every path (a dead unit reads a valid row), so the waits
+    // before the next products count exactly the loads and stores issued since
+    load_x(nxt, x);
+    if (cur.live) {
+#pragma unroll
+      for (int p = 1; p < kPages; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (p < cur.n_pg) quant_page(p);
+      }
     }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int p = 0; p < kPages; ++p) part_store(blk[p], cur.live && p < cur.n_pg, img + p * kPart);
+    __builtin_amdgcn_wave_barrier();
     cur = nxt;
   }
+  };
+  if (wave < 4) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -623,7 +637,7 @@ hipError_t launch_demote(const DemoteArgs& a_in, int batch, int max_count, bool 
   const bool per_head = a.clip_kv_stride != 0;
   const int heads = per_head ? a.hkv : 1;
   const long units = (long)batch * (per_head ? 1 : a.hkv) * a.unit_tiles;
-  const int nwg = (int)std::min<long>((units + 7) / 8, std::max(1, 256 / heads));
+  const int nwg = (int)std::min<long>((units + 3) / 4, std::max(1, 256 / heads));   // 4 units per round
   const dim3 grid(nwg, 1, heads);
   if (a.code_bits == 4) {
     if (rotated)
