@@ -609,14 +609,16 @@ def run_demote(torch, reps, seed, code_bits=2):
     kd, vd = bf16_tensor(k), bf16_tensor(v)
     pool.demote(starts, kd, vd)
     torch.cuda.synchronize()
-    t = Timer(torch)
+    # back-to-back launches between two events (events around every call
+    # would add their own microseconds to each)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     gpu_hold(torch, 20)
+    e0.record()
     for _ in range(reps):
-        s = t.start()
         pool.demote(starts, kd, vd)
-        t.stop(s)
+    e1.record()
     torch.cuda.synchronize()
-    us = t.mean_us()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
     tokens = batch * chunk
     nbytes = tokens * hkv * (2 * 256 + hist_token_bytes(code_bits))
     return dict(us=us, tok_per_s=tokens / (us * 1e-6), gbps=nbytes / (us * 1e3), tokens=tokens, bytes=nbytes)
@@ -667,6 +669,30 @@ def measured_traffic():
     if rec.get("source_digest") != kernel_source_digest():
         return None
     return rec.get("bytes_per_launch")
+
+
+DEMOTE_COUNTERS_FILE = os.path.join(ROOT, "profiles", "demote_bulk_int2_16x4096x8_counters.md")
+
+
+def demote_counters():
+    """Counter figures of the bulk demotion kernel (HBM traffic, matrix-core
+    use) from the committed summary, or None when it is missing or was taken
+    on other kernel sources."""
+    try:
+        with open(DEMOTE_COUNTERS_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    block = text.split("```json", 1)[-1].split("```", 1)[0] if "```json" in text else ""
+    try:
+        rec = json.loads(block)
+    except ValueError:
+        return None
+    if rec.get("source_digest") != kernel_source_digest():
+        return None
+    return {k: rec[k] for k in ("traffic_MB_per_launch", "traffic_vs_algorithmic", "mfma_busy_frac",
+                                "mfma_tflops_at_trace_time", "mfma_frac_of_bf16_dense", "valu_issue_frac",
+                                "trace_us") if k in rec}
 
 
 def _oracle_pool(hkv, n0, k, v, rot_k, rot_v, tau_k, tau_v):
@@ -766,6 +792,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="append one plain device copy of this many MB (counter calibration runs)")
+    ap.add_argument("--workload", choices=("step", "demote", "bf16"), default="step",
+                    help="step: the timed decode step (the metric, default); demote: only the bulk demotion "
+                         "(16 x 4096 tokens x 8 KV heads), --steps launches; bf16: only the BF16 baseline "
+                         "decode at --ctx tokens, --steps calls (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -776,6 +806,32 @@ def main():
     binding.load()
 
     hq, hkv, n0 = 32, 8, args.ctx
+
+    def copy_probe():
+        # a plain streaming kernel of known size (reads and writes n bytes once):
+        # the counter calibration for the traffic figures
+        if args.copy_probe_mb:
+            src = torch.ones((args.copy_probe_mb << 20) // 4, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+
+    if args.workload != "step":
+        if args.workload == "demote":
+            d = run_demote(torch, args.steps, 1004)
+            rec = {"workload": "bulk demotion, 16 sequences x 4096 tokens x 8 KV heads, K+V",
+                   "us_per_launch": round(d["us"], 3), "tok_per_s": round(d["tok_per_s"], 0),
+                   "algorithmic_bytes": d["bytes"], "GBps": round(d["gbps"], 1)}
+        else:
+            k1, v1 = _seq_kv(hkv, n0, 1001)
+            b = run_bf16(torch, hq, hkv, n0, args.layers, args.steps, 1001, k1, v1)
+            rec = {"workload": f"BF16 paged decode, {hq} q / {hkv} KV heads, batch 1, {n0} tokens",
+                   "us_per_call": round(b["decode_us"], 3), "algorithmic_bytes": b["decode_bytes"],
+                   "GBps": round(b["decode_bytes"] / (b["decode_us"] * 1e3), 1)}
+        copy_probe()
+        print(json.dumps(rec))
+        return
     host128 = None
     res = run_tiered(torch, hq, hkv, n0, args.layers, args.steps, args.warmup, seed=1001 if n0 == 32768 else 1002)
     dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
@@ -786,6 +842,8 @@ def main():
              "step_call_us": round(res["step_call_us"], 3),
              "decode_call_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),
              "decode_algorithmic_bytes": res["decode_bytes"], "decode_GBps": round(dec_gbps, 1),
+             "step_GBps": round(res["decode_bytes"] / (res["us_per_step"] * 1e3), 1),
+             "step_frac_of_8TBps": round(res["decode_bytes"] / (res["us_per_step"] * 1e3) / HBM_PEAK_GBPS, 4),
              "roofline_kernel": "decode_int2_kernel<4, false>: the decode's split kernel alone "
                                  "(oscar_decode_partials, back-to-back launches between two events)",
              "split_kernel_us": round(res["split_us"], 3), "split_kernel_bytes": round(res["split_bytes"]),
@@ -828,6 +886,7 @@ def main():
         extra["demote_us_per_chunk"] = round(d["us"], 2)
         extra["demote_GBps"] = round(d["gbps"], 1)
         extra["demote_workload"] = "16 sequences x 4096-token chunk, 8 KV heads, K+V, bf16 in, MFMA rotation"
+        extra["demote_counters"] = demote_counters()
         # INT4 variant of the pool: the same step, the 128K decode and bulk demotion
         r4 = run_tiered(torch, hq, hkv, n0, args.layers, min(args.steps, 200), args.warmup, seed=1001,
                         calib=res["host"][2:], code_bits=4)
@@ -845,14 +904,7 @@ def main():
                          "ctx128k_decode_GBps": round(r4_128["decode_bytes"] / (r4_128["decode_us"] * 1e3), 1),
                          "demote_tok_per_s": round(d4["tok_per_s"], 0), "demote_us_per_chunk": round(d4["us"], 2)}
         del r4, r4_128
-    if args.copy_probe_mb:
-        # a plain streaming kernel of known size (reads and writes n bytes once):
-        # the counter calibration for the traffic figure
-        src = torch.ones((args.copy_probe_mb << 20) // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
+    copy_probe()
     cpu = None
     if not args.no_cpu:
         cpu, extra["cpu_oracle"] = cpu_baseline(hq, hkv, n0, res["host"], 1001, host128=host128)
