@@ -628,8 +628,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_int2_qwen3-4b_32k_traffic.
 
 
 def kernel_source_digest():
-    """Digest of the device sources and build flags of the library; a counter
-    summary taken on other sources no longer describes the kernel."""
+    """Digest of the device code (comments and blank lines dropped) and build
+    flags of the library; a counter summary taken on other code no longer
+    describes the kernel."""
     import hashlib
     from bit_rotated_kv_demote_amd import build
     import re
@@ -648,7 +649,11 @@ def kernel_source_digest():
         todo += re.findall(r'#include "([^"/]+)"', text.decode())
     for name in sorted(seen):
         with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+            text = f.read().decode()
+        # comments and layout do not change the kernels: hash the code alone
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        code = [ln.split("//", 1)[0].strip() for ln in text.splitlines()]
+        h.update(name.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,10 +13,11 @@
 //   append_kernel      one decode step: demote the ring slot about to be
 //                      reused (fp32 VALU rotation, latency-bound), then write
 //                      the new token into sink or ring.
-//   demote_bulk_kernel many tokens: 64-token units per wave; the rotation is
-//                      a 128x128x64 product on the matrix cores with R split
-//                      into bf16 hi + lo terms (fp32 accumulation), or the
-//                      input is already-rotated fp32.
+//   demote_bulk_kernel many tokens: units of three pages (INT2) per wave,
+//                      one tensor per wave; the rotation is a 128x128x48
+//                      product on the matrix cores with R split into bf16
+//                      hi + lo terms (fp32 accumulation), or the input is
+//                      already-rotated fp32.
 //   prefill_route_kernel  copies of the sink and recent tiers of a prefill.
 #include <algorithm>
 #include <type_traits>
@@ -82,13 +83,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // ---------------------------------------------------------------------------
 // Bulk demotion.  grid (nwg, 1, heads), 512 threads (8 waves), one
 // workgroup per compute unit.  The workgroup stages R_K^T and R_V^T as bf16
-// hi + lo terms in LDS once; each wave then takes work units of kDemPages
-// history pages of one (sequence, KV head) in turn (unit u goes to wave
-// u mod (8 nwg)) and demotes both K and V of their tokens.  K and V codes
-// share every 16-byte chunk of a page block, so a wave assembles whole
-// blocks in a wave-private LDS image and writes them with 16-byte stores.
-// A page only partly covered by the demoted tokens is read into the image
-// first, so its other slots keep their bytes.
+// hi + lo terms in LDS once.  Waves 0..3 demote K and waves 4..7 V (one of
+// each per SIMD); each takes work units of kPages history pages of one
+// (sequence, KV head) in turn (unit u goes to the u mod (4 nwg)-th wave of
+// its tensor).  A wave builds its tensor's bytes of each page block in a
+// wave-private LDS image (codes, then scales and zeros) and stores them with
+// one store per lane for the codes and one for the metadata; the K and V
+// halves of a block meet in L2.  A page only partly covered by the demoted
+// tokens is read into the image first, so its other slots keep their bytes.
 //
 // Rotation: D[c][t] = sum_i R[i][c] x[t][i] on 16x16x32 bf16 matrix-core
 // products, x . R_hi + x . R_lo with fp32 accumulation, one page of tokens
