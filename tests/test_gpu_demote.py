@@ -175,3 +175,51 @@ def test_bulk_demotion_full_size_sampled(code_bits):
     for b in range(batch):
         used[pt[b, (starts[b] + np.arange(chunk)) // 16]] = True
     assert not got[~used].any()
+
+
+@pytest.mark.parametrize("code_bits", [2, 4])
+def test_bulk_demotion_reloads_unit_metadata(code_bits):
+    # Long enough that the first waves of the launch take more work units than
+    # one batch of lane-resident unit metadata covers (64 lanes / pages per
+    # unit: 21 units of three pages for INT2, 64 one-page units for INT4), so
+    # the kernel reloads it mid-loop: 16 sequences x 8192 tokens x 8 KV heads,
+    # 256 workgroups of 4 waves per tensor.  The units past the reload are the
+    # last ones of the index space, all in sequence 15; it is compared with the
+    # oracle in full (all heads, K and V), with sequence 0 beside it.
+    import math
+    from bit_rotated_kv_demote_amd.pool import TieredKV
+    batch, chunk, hkv, hq = 16, 8192, 8, 64
+    pages_per_unit, meta_units = (3, 21) if code_bits == 2 else (1, 64)
+    ups = math.ceil((15 + chunk) / (16 * pages_per_unit))
+    units, waves = batch * hkv * ups, 256 * 4
+    assert units > meta_units * waves                 # some waves run past one metadata batch
+    first_reloaded = meta_units * waves               # lowest unit index taken after a reload
+    assert first_reloaded // (hkv * ups) == batch - 1
+    st = synth.streams(1005)
+    out_ch = synth.outlier_channels(st["outliers"])
+    k = synth.kv_tokens(st["k"], st["lognormal"], batch * chunk, hkv, out_ch).reshape(batch, chunk, hkv, 128)
+    v = synth.kv_tokens(st["v"], st["lognormal"], batch * chunk, hkv, out_ch).reshape(batch, chunk, hkv, 128)
+    rot = synth.random_rotation(st["rot"])
+    tau_k = orc.clip_thresholds(synth.bf16_bits_to_f32(k[0, :2048]), rot)
+    tau_v = orc.clip_thresholds(synth.bf16_bits_to_f32(v[0, :2048]), rot)
+    max_pages = chunk // 16 + 2
+    pt = synth.page_permutation(st["perm"], batch * max_pages).reshape(batch, max_pages).astype(np.int32)
+    starts = [int(x) for x in synth.ragged_lengths(st["lengths"], batch, 0, 15)]
+    dev = TieredKV(hq, hkv, batch, max_pages, batch * max_pages, rot, rot, tau_k, tau_v, page_table=pt,
+                   code_bits=code_bits)
+    dev.demote(i32(starts), bf16_tensor(k), bf16_tensor(v))
+    torch.cuda.synchronize()
+    got = dev.hist.cpu().numpy()
+    ref = orc.Pool(batch, hkv, batch * max_pages, pt, bits=code_bits)
+    pages, slots = [], []
+    for b in (0, batch - 1):
+        h = starts[b] + np.arange(chunk)
+        ref.demote_many(b, h, k[b], v[b], rot, rot, tau_k, tau_v)
+        pages.append(pt[b, h // 16])
+        slots.append(h % 16)
+    rate, maxd, meta_ulp = code_diff_stats(got, ref.hist, np.concatenate(pages), np.concatenate(slots))
+    assert rate <= FLIP_RATE and maxd <= 1 and meta_ulp <= 2, (rate, maxd, meta_ulp)
+    used = np.zeros(got.shape[0], bool)
+    for b in range(batch):
+        used[pt[b, (starts[b] + np.arange(chunk)) // 16]] = True
+    assert not got[~used].any()
