@@ -572,6 +572,20 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
                       [&](int uu) { const int u = u0 + uu; return u < n_sink_used ? u : recent_first + (u - n_sink_used); },
                       [&](int x) { return n - a.q_tokens + (cg * G + x) / a.g_model; }, n - a.q_tokens, sm, wave,
                       lane);
+    if (split == 0 && cg == 0 && act_hist > 0) {
+      // The merge kernel that follows applies R_V^T to the history part and
+      // waits on its rows first thing.  Tile splits end well before the
+      // history splits, so tile split 0 of each (sequence, KV head) reads
+      // that R_V once (64 KiB) and leaves it in the caches for the merge.
+      const float4* rv = reinterpret_cast<const float4*>(a.rot_v + (size_t)hk * a.rot_kv_stride);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float4 r = rv[tid + 256 * e];
+        acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+      }
+      asm volatile("" :: "v"(acc.x), "v"(acc.y), "v"(acc.z), "v"(acc.w));   // keeps the loads
+    }
   } else {
     const int pg_begin = hs * a.pages_per_split;
     // (empty for a demoting split whose only page holds just the new token)
