@@ -5,14 +5,14 @@
 // column group, page range), per-split partials, then the same log-sum-exp
 // merge kernel.
 //
-// A wave walks its share of a split in steps of two pages (32 tokens, 16 KiB
-// of K and V) with a two-stage register ring: while one step is processed
-// the next is in flight.  Scores: each lane loads exactly its K operands of
-// the 16x16x32 bf16 products (16 B per token row per k-slice), q in the
-// columns.  Values on the vector unit: lane l loads 16 B of V rows (channels
-// 8 (l & 15) .. + 8 of tokens 4 i + (l >> 4)), reads its tokens' weights from
-// LDS once per step, and accumulates G x 8 outputs; the four lane groups
-// that share channels are summed once at the end of the split.
+// A wave walks its share of a split in steps of one page (16 tokens, 8 KiB
+// of K and V) with a four-stage register ring: while one step is processed
+// the wave's next three are in flight.  Scores: each lane loads exactly its K
+// operands of the 16x16x32 bf16 products (16 B per token row per k-slice), q
+// in the columns.  Values on the vector unit: lane l loads 16 B of V rows
+// (channels 8 (l & 15) .. + 8 of tokens 4 i + (l >> 4)), reads its tokens'
+// weights from LDS once per step, and accumulates G x 8 outputs; the four
+// lane groups that share channels are summed once at the end of the split.
 #include "attn_common.h"
 #include "launchers.h"
 
@@ -20,23 +20,24 @@ namespace oscar {
 
 namespace {
 
-constexpr int kBfStepPages = 2;
-constexpr int kBfMaxPagesPerSplit = 4 * 32 * kBfStepPages;   // 32 steps per wave (one page id per lane)
+constexpr int kBfStepPages = 1;
+constexpr int kBfRing = 4;                                   // steps in registers per wave
+constexpr int kBfMaxPagesPerSplit = 4 * 64 * kBfStepPages;   // 64 steps per wave (one page id per lane)
 
 template <int G>
 struct alignas(16) Bf16Smem {
-  float pt[4][32][G];        // per wave: one step's weights [token][column]
+  float pt[4][16 * kBfStepPages][G];   // per wave: one step's weights [token][column]
   float am[4][16];           // per wave: rescale factor of each column's sums when its max grew
   float wm[4][16];           // per-wave records (max, sum, output) for store
   float wl[4][16];
   float wo[4][G][kD];
 };
 
-// One step's operands in registers: K as 2 pages x 4 k-slices of 8 bf16, V
-// as 2 pages x 4 row groups of 16 B.
+// One step's operands in registers: K as 4 k-slices of 8 bf16 per page, V as
+// 4 row groups of 16 B per page.
 struct Bf16Step {
-  bf16x8_t k[2][4];
-  u32x4_t v[2][4];
+  bf16x8_t k[kBfStepPages][4];
+  u32x4_t v[kBfStepPages][4];
 };
 
 __device__ __forceinline__ void issue_bf16_step(const DecodeBf16Args& a, int32_t ids, int hk, int k, int lane,
@@ -67,15 +68,15 @@ __device__ void bf16_split_wave(const DecodeBf16Args& a, Bf16Smem<G>& sm, const 
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
-  const int nsteps = (count + 32 * 1 - 1) / 32;
-  Bf16Step sA, sB;
+  constexpr int kTok = 16 * kBfStepPages;          // tokens per step
+  const int nsteps = (count + kTok - 1) / kTok;
   auto body = [&](const Bf16Step& cur, int st) __attribute__((always_inline)) {
-    const int base = 32 * st;                       // first token of the step within the split
-    const int cn = min(32, count - base);
-    const bool partial = t0 + base + 31 > lim_min;  // some token may be past a query's position
-    float sc[2][4];
+    const int base = kTok * st;                     // first token of the step within the split
+    const int cn = min(kTok, count - base);
+    const bool partial = t0 + base + kTok - 1 > lim_min;  // some token may be past a query's position
+    float sc[kBfStepPages][4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < kBfStepPages; ++p) {
       float4_t d = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[p][kk], bq[kk], d, 0, 0, 0);
@@ -87,13 +88,16 @@ __device__ void bf16_split_wave(const DecodeBf16Args& a, Bf16Smem<G>& sm, const 
     }
     if (partial) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < kBfStepPages; ++p)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (t0 + base + 16 * p + 4 * qa + r > lim_x) sc[p][r] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    float mx = sc[0][0];
+#pragma unroll
+    for (int p = 0; p < kBfStepPages; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[p][r]);
     mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const bool grew = __builtin_amdgcn_ballot_w64(m_new > m_run) != 0ull;
@@ -105,7 +109,7 @@ __device__ void bf16_split_wave(const DecodeBf16Args& a, Bf16Smem<G>& sm, const 
       m_run = m_new;
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < kBfStepPages; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pv = __builtin_amdgcn_exp2f(sc[p][r] - m_run);
@@ -123,7 +127,7 @@ __device__ void bf16_split_wave(const DecodeBf16Args& a, Bf16Smem<G>& sm, const 
     }
     // this lane's tokens: 16 p + 4 i + qa, channels 8 x .. 8 x + 7
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < kBfStepPages; ++p)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * p + 4 * i + qa;
@@ -141,7 +145,7 @@ __device__ void bf16_split_wave(const DecodeBf16Args& a, Bf16Smem<G>& sm, const 
         u32x4_t vv = cur.v[p][i];
         // rows past the split's tokens (a partly filled last page) may hold
         // anything: they enter with weight 0 and value 0
-        if (cn < 32 && t >= cn) vv = (u32x4_t){0u, 0u, 0u, 0u};
+        if (cn < kTok && t >= cn) vv = (u32x4_t){0u, 0u, 0u, 0u};
         float vf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -155,17 +159,23 @@ __device__ void bf16_split_wave(const DecodeBf16Args& a, Bf16Smem<G>& sm, const 
       }
     __builtin_amdgcn_wave_barrier();
   };
-  // two-stage ring: while step st is processed, the wave's next step is in flight
-  int st = wave;
-  if (st < nsteps) issue_bf16_step(a, ids, hk, 0, lane, sA);
-  while (st < nsteps) {
-    if (st + 4 < nsteps) issue_bf16_step(a, ids, hk, (st + 4 - wave) >> 2, lane, sB);
-    body(sA, st);
-    st += 4;
-    if (st >= nsteps) break;
-    if (st + 4 < nsteps) issue_bf16_step(a, ids, hk, (st + 4 - wave) >> 2, lane, sA);
-    body(sB, st);
-    st += 4;
+  // kBfRing-stage ring: while step st is processed, the wave's next
+  // kBfRing - 1 steps are in flight.  Every slot is refilled on every round
+  // (past the wave's last step it re-reads that step, an L2 hit), so each
+  // body waits only for its own step's loads.
+  Bf16Step ring[kBfRing];
+  const int last_st = nsteps > wave ? wave + ((nsteps - 1 - wave) / 4) * 4 : wave;
+  auto issue = [&](int st_, Bf16Step& s_) { issue_bf16_step(a, ids, hk, (min(st_, last_st) - wave) >> 2, lane, s_); };
+#pragma unroll
+  for (int r = 0; r < kBfRing - 1; ++r) issue(wave + 4 * r, ring[r]);
+  for (int st = wave; st < nsteps; st += 4 * kBfRing) {
+#pragma unroll
+    for (int r = 0; r < kBfRing; ++r) {
+      const int s_r = st + 4 * r;
+      if (s_r >= nsteps) break;                        // wave-uniform
+      issue(s_r + 4 * (kBfRing - 1), ring[(r + kBfRing - 1) % kBfRing]);
+      body(ring[r], s_r);
+    }
   }
   // the four lane groups (l >> 4) hold the same channels for different tokens
 #pragma unroll
