@@ -129,11 +129,10 @@ __device__ __forceinline__ int rt_swz(int c) { return (c & 3) | (((c >> 5) & 3) 
 __device__ __forceinline__ int rt_index(int c, int i) { return c * kD + ((((i >> 3) ^ rt_swz(c))) << 3) + (i & 7); }
 __device__ __forceinline__ int out_channel(int m, int r) { return 32 * (r >> 2) + 4 * m + (r & 3); }
 
-// Clip, group parameters and codes of one lane's group (32 values, channel
-// 32 g + 4 m + i in y[m][i]); tau_g: LDS, the group's 32 thresholds.
-template <int kBits>
-__device__ __forceinline__ void quant_lane_group(float (&y)[8][4], const float* tau_g, uint32_t (&code)[8][4],
-                                                 __half& sc, __half& zr) {
+// Clip one lane's group in place (32 values, channel 32 g + 4 m + i in
+// y[m][i]; tau_g: LDS, the group's 32 thresholds) and take its minimum and
+// maximum.
+__device__ __forceinline__ void clip_group(float (&y)[8][4], const float* tau_g, float& mn, float& mx) {
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const float4 t4 = *reinterpret_cast<const float4*>(&tau_g[4 * m]);
@@ -142,7 +141,8 @@ __device__ __forceinline__ void quant_lane_group(float (&y)[8][4], const float* 
     y[m][2] = clip_med3(y[m][2], t4.z);
     y[m][3] = clip_med3(y[m][3], t4.w);
   }
-  float mn = y[0][0], mx = y[0][0];
+  mn = y[0][0];
+  mx = y[0][0];
 #pragma unroll
   for (int e = 1; e < 31; e += 2) {
     const float v0 = y[e >> 2][e & 3], v1 = y[(e + 1) >> 2][(e + 1) & 3];
@@ -151,14 +151,20 @@ __device__ __forceinline__ void quant_lane_group(float (&y)[8][4], const float* 
   }
   mn = fminf(mn, y[7][3]);
   mx = fmaxf(mx, y[7][3]);
-  group_scale_zero(mn, mx, &sc, &zr, kBits == 4 ? 15.0f : 3.0f);
+}
+
+// INT4: clip, group parameters and codes (correctly rounded division) of
+// one lane's group.
+__device__ __forceinline__ void quant_lane_group4(float (&y)[8][4], const float* tau_g, uint32_t (&code)[8][4],
+                                                  __half& sc, __half& zr) {
+  float mn, mx;
+  clip_group(y, tau_g, mn, mx);
+  group_scale_zero(mn, mx, &sc, &zr, 15.0f);
   const float zf = __half2float(zr), sf = __half2float(sc);
-  const CodeCut cut = code_cut(sf);
 #pragma unroll
   for (int m = 0; m < 8; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      code[m][i] = kBits == 4 ? quant_code(y[m][i], zf, sf, 15.0f) : quant_code_cut(y[m][i] - zf, cut);
+    for (int i = 0; i < 4; ++i) code[m][i] = quant_code(y[m][i], zf, sf, 15.0f);
 }
 
 // INT2 fast path of one lane's group: clip, group parameters, then each
@@ -171,23 +177,8 @@ __device__ __forceinline__ void quant_lane_group(float (&y)[8][4], const float* 
 // alignbit(w, z, 31) = (w << 1) | (z >> 31) shifts a sign bit into w.
 __device__ __forceinline__ void quant_pack_int2(float (&y)[8][4], const float* tau_g, bool is_v, int t, int g,
                                                 bool valid, uint8_t* img) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const float4 t4 = *reinterpret_cast<const float4*>(&tau_g[4 * m]);
-    y[m][0] = clip_med3(y[m][0], t4.x);
-    y[m][1] = clip_med3(y[m][1], t4.y);
-    y[m][2] = clip_med3(y[m][2], t4.z);
-    y[m][3] = clip_med3(y[m][3], t4.w);
-  }
-  float mn = y[0][0], mx = y[0][0];
-#pragma unroll
-  for (int e = 1; e < 31; e += 2) {
-    const float v0 = y[e >> 2][e & 3], v1 = y[(e + 1) >> 2][(e + 1) & 3];
-    mn = fminf(fminf(mn, v0), v1);
-    mx = fmaxf(fmaxf(mx, v0), v1);
-  }
-  mn = fminf(mn, y[7][3]);
-  mx = fmaxf(mx, y[7][3]);
+  float mn, mx;
+  clip_group(y, tau_g, mn, mx);
   __half sc, zr;
   group_scale_zero(mn, mx, &sc, &zr, 3.0f);
   const float zf = __half2float(zr);
@@ -569,7 +560,7 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
       } else {
         uint32_t code[8][4];
         __half sc, zr;
-        quant_lane_group<kBits>(y, &tau_s[is_v][32 * g], code, sc, zr);
+        quant_lane_group4(y, &tau_s[is_v][32 * g], code, sc, zr);
         pack_lane_group4(code, sc, zr, is_v != 0, t, g, valid_tok(p), img + p * kPart);
       }
     };
