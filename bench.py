@@ -2,8 +2,9 @@
 
 A step is one pass of the whole hot path over one batch: the append of the
 new token (route it; demote the ring slot it reuses: rotate, clip, quantise,
-pack) followed by tiered decode attention, as one oscar_step call (the
-append launch also computes q . R_K for the decode).  The same steps as
+pack) followed by tiered decode attention, as one oscar_step call: two
+launches, the split kernel (which also writes the new token, demotes the
+leaving one and computes q . R_K) and the merge.  The same steps as
 separate oscar_append + oscar_decode calls are timed beside it.  The default workload is
 the Qwen3-4B-shaped layer: 32 q / 8 KV heads, head_dim 128, batch 1, 32768
 cached tokens (64 BF16 sink + INT2 history + 256 BF16 recent, 16-token pages),
@@ -842,7 +843,8 @@ def main():
     dec_gbps = res["decode_bytes"] / (res["decode_us"] * 1e3)
     # the roofline kernel: the decode's split kernel (oscar_decode_partials)
     split_gbps = res["split_bytes"] / (res["split_us"] * 1e3)
-    extra = {"step_mode": "oscar_step (append + decode in one call; the append launch also computes q . R_K)",
+    extra = {"step_mode": "oscar_step (append + decode in one call, two launches: the split kernel writes the new "
+                          "token, demotes the leaving one and computes q . R_K; then the merge)",
              "us_per_step_separate_calls": round(res["us_per_step_separate"], 3),
              "step_call_us": round(res["step_call_us"], 3),
              "decode_call_us": round(res["decode_us"], 3), "append_kernel_us": round(res["append_us"], 3),

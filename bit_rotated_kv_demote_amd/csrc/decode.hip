@@ -190,6 +190,7 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
 
     // ---------------- scores
     float sc[kStepPages][4];
+    float4_t cacc_all[kStepPages][kTiles];
 #pragma unroll
     for (int p = 0; p < kStepPages; ++p) {
       const uint8_t* mp = mbuf + 512 * p;
@@ -224,7 +225,7 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
       const u32x4_t s23 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa + 16);
       const _Float16* sh0 = reinterpret_cast<const _Float16*>(&s01);
       const _Float16* sh1 = reinterpret_cast<const _Float16*>(&s23);
-      float4_t cacc[kTiles];
+      float4_t (&cacc)[kTiles] = cacc_all[p];
 #pragma unroll
       for (int tl = 0; tl < kTiles; ++tl) {
         // sum_g zero[t][g] * (scaled group sums of q'), t = lane's row token
@@ -240,6 +241,12 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
           for (int g = 0; g < 4; ++g) cacc[tl][r] = fmaf((float)sr[g], d[g][r], cacc[tl][r]);
         }
       }
+    }
+    // hi + lo columns, once every page's products are in (the lane moves
+    // then read registers written well before)
+#pragma unroll
+    for (int p = 0; p < kStepPages; ++p) {
+      const float4_t (&cacc)[kTiles] = cacc_all[p];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         // hi + lo halves of the same head (tile 1: the halves sit the other way round)
@@ -263,9 +270,11 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
     for (int p = 0; p < kStepPages; ++p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[p][r]);
-    mx = rows_max(mx);
-    const float m_new = fmaxf(m_run, mx * mult);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0ull) {
+    // A column's maximum needs its four lane quarters only when one of them
+    // passes the running maximum (mult >= 0); otherwise the step leaves the
+    // maximum where it was and nothing is rescaled.
+    if (__builtin_amdgcn_ballot_w64(mx * mult > m_run) != 0ull) {
+      const float m_new = fmaxf(m_run, rows_max(mx) * mult);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int m = 0; m < 8; ++m) acc_o[m] *= alpha;
