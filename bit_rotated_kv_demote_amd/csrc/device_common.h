@@ -66,7 +66,7 @@ __device__ __forceinline__ int v4_halfword_byte(int t, int b, int hi_m) {
 // ---- INT2 quantiser of one 32-channel group (asymmetric min-max, four levels).
 // zero = fp16 rounded toward -inf of the group minimum, scale = fp16 rounded
 // toward +inf of (max - zero) / 3, code = clamp(rint((y - zero) / scale), 0, 3)
-// in IEEE fp32 with a correctly rounded division; code 0 when scale == 0.
+// in IEEE fp32 with the correctly rounded quotient; code 0 when scale == 0.
 // The INT4 quantiser is the same with 16 levels: (max - zero) / 15 and codes
 // clamped to [0, 15].
 __device__ __forceinline__ void group_scale_zero(float mn, float mx, __half* scale, __half* zero,
@@ -77,9 +77,25 @@ __device__ __forceinline__ void group_scale_zero(float mn, float mx, __half* sca
   *scale = __float2half_ru(span / n_steps);
 }
 
+// The quotient fl(x / s) without a division, for an fp16 value s > 0 and
+// x >= 0 in the quantiser's range (Markstein's correction step): y = fl(1/s)
+// from the hardware reciprocal (within one ulp) and one residual step, then
+// q0 = fl(x y), r = x - s q0 (exact in fp32 by an fma) and q = fl(q0 + r y).
+// With y the correctly rounded reciprocal and q0 within one ulp of x / s,
+// q is the correctly rounded quotient.  Checked exhaustively in exact
+// arithmetic for every fp16 significand of s (the steps scale with powers
+// of two): y = fl(1/s) from any start within two ulps, and q = fl(x / s) for
+// x within four ulps of every midpoint (k + 1/2) s, k = 0..15.
+__device__ __forceinline__ float recip_of_half(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  return fmaf(fmaf(-s, y0, 1.0f), y0, y0);
+}
 __device__ __forceinline__ uint32_t quant_code(float yc, float zf, float sf, float max_code = 3.0f) {
   if (!(sf > 0.0f)) return 0u;
-  const float q = (yc - zf) / sf;
+  const float x = yc - zf;
+  const float y = recip_of_half(sf);
+  const float q0 = __fmul_rn(x, y);
+  const float q = fmaf(fmaf(-q0, sf, x), y, q0);     // fl(x / s)
   const float c = fminf(fmaxf(rintf(q), 0.0f), max_code);
   return (uint32_t)c;
 }
