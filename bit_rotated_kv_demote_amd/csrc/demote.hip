@@ -81,12 +81,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Bulk demotion.  grid (nwg, 1, heads), 512 threads (8 waves), one
-// workgroup per compute unit.  The workgroup stages R_K^T and R_V^T as bf16
-// hi + lo terms in LDS once.  Waves 0..3 demote K and waves 4..7 V (one of
-// each per SIMD); each takes work units of kPages history pages of one
-// (sequence, KV head) in turn (unit u goes to the u mod (4 nwg)-th wave of
-// its tensor).  A wave builds its tensor's bytes of each page block in a
+// Bulk demotion.  grid (nwg, 1, heads), one workgroup per compute unit of
+// 2 W waves (INT2: W = 6, three waves per SIMD; INT4: W = 8, four).  The
+// workgroup stages R_K^T and R_V^T as bf16 hi + lo terms in LDS once.  Waves
+// 0..W-1 demote K and waves W..2W-1 V; each takes work units of kPages
+// history pages of one (sequence, KV head) in turn (unit u goes to the
+// u mod (W nwg)-th wave of its tensor).  A wave builds its tensor's bytes of each page block in a
 // wave-private LDS image (codes, then scales and zeros) and stores them with
 // one store per lane for the codes and one for the metadata; the K and V
 // halves of a block meet in L2.  A page only partly covered by the demoted
@@ -102,7 +102,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 // ---------------------------------------------------------------------------
 template <int kBits>
 struct DemCfg {
-  static constexpr int kPages = kBits == 4 ? 1 : 3;        // pages per work unit
+  static constexpr int kPages = kBits == 4 ? 1 : 2;        // pages per work unit
+  // waves per tensor: the unit's accumulators (32 VGPRs per page) set the
+  // waves a SIMD can hold, and more waves hide the LDS and memory waits
+  static constexpr int kTensorWaves = kBits == 4 ? 8 : 6;
+  static constexpr int kThreads = 2 * 64 * kTensorWaves;
   static constexpr int kCodeBytes = kBits == 4 ? 1024 : 512;   // one tensor's code bytes in a block
   static constexpr int kPart = kCodeBytes + 256;            // one tensor's bytes in a block (codes + meta)
   static constexpr int kMetaBase = kBits == 4 ? 2048 : 1024;   // block offset of the K metadata
@@ -312,8 +316,9 @@ __device__ __forceinline__ void pack_lane_group4(const uint32_t (&c)[8][4], __ha
 }
 
 template <bool kRotatedInput, int kBits>
-__global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
+__global__ __launch_bounds__(DemCfg<kBits>::kThreads, 1) void demote_bulk_kernel(DemoteArgs a) {
   constexpr int kPages = DemCfg<kBits>::kPages;
+  constexpr int kTW = DemCfg<kBits>::kTensorWaves;
   constexpr int kPart = DemCfg<kBits>::kPart;
   constexpr int kCodeBytes = DemCfg<kBits>::kCodeBytes;
   constexpr int kBytes = block_bytes(kBits);
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
   __shared__ __bf16 rt_hi[2][kRt];            // [K|V] R^T hi terms
   __shared__ __bf16 rt_lo[2][kRt];
   __shared__ float tau_s[2][kD];
-  __shared__ __attribute__((aligned(16))) uint8_t img_all[8][kPages * kPart];
+  __shared__ __attribute__((aligned(16))) uint8_t img_all[2 * kTW][kPages * kPart];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane & 15, g = lane >> 4;
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     // R (row-major fp32) -> LDS R^T split into bf16 hi + lo, for K and V, in
     // chunks of 8 input rows of one column: lanes take consecutive columns
     // (coalesced reads), each chunk leaves as one 16-byte store per term
-    for (int c = tid; c < 2 * kD * (kD / 8); c += 512) {
+    for (int c = tid; c < 2 * kD * (kD / 8); c += DemCfg<kBits>::kThreads) {
       const int which = c / (kD * (kD / 8)), rem = c % (kD * (kD / 8));
       const int j = rem % kD, i0 = 8 * (rem / kD);
       const float* R = (which ? a.rot_v : a.rot_k) + (size_t)hk_base * a.rot_kv_stride;
@@ -354,15 +359,15 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     tau_s[tid >> 7][tid & 127] = ((tid >> 7) ? a.clip_v : a.clip_k)[(size_t)hk_base * a.clip_kv_stride + (tid & 127)];
   __syncthreads();
 
-  // waves 0..3 demote K, waves 4..7 V (one of each per SIMD); the loop is
-  // compiled once per tensor
+  // waves 0..kTW-1 demote K, the others V; the loop is compiled once per
+  // tensor
   auto run = [&](auto tensor) {
   constexpr int is_v = decltype(tensor)::value;
   uint8_t* img = img_all[wave];
   const int ups = a.unit_tiles;                       // units per (sequence, KV head)
   const int n_units = a.batch * heads_here * ups;
-  const int stride = gridDim.x * 4;
-  const int u_first = blockIdx.x * 4 + (wave & 3);    // this wave's units: u_first + stride * j
+  const int stride = gridDim.x * kTW;
+  const int u_first = blockIdx.x * kTW + wave % kTW;  // this wave's units: u_first + stride * j
   // A work unit: kPages history pages of one (sequence, KV head), starting at
   // the page that holds the sequence's first demoted token; one K wave and
   // one V wave take it.  Its metadata (demoted count, first demoted
@@ -584,7 +589,7 @@ __global__ __launch_bounds__(512, 1) void demote_bulk_kernel(DemoteArgs a) {
     cur = nxt;
   }
   };
-  if (wave < 4) run(std::integral_constant<int, 0>{});
+  if (wave < kTW) run(std::integral_constant<int, 0>{});
   else run(std::integral_constant<int, 1>{});
 }
 
@@ -630,18 +635,21 @@ hipError_t launch_demote(const DemoteArgs& a_in, int batch, int max_count, bool 
   const bool per_head = a.clip_kv_stride != 0;
   const int heads = per_head ? a.hkv : 1;
   const long units = (long)batch * (per_head ? 1 : a.hkv) * a.unit_tiles;
-  const int nwg = (int)std::min<long>((units + 3) / 4, std::max(1, 256 / heads));   // 4 units per round
+  const int tw = a.code_bits == 4 ? DemCfg<4>::kTensorWaves : DemCfg<2>::kTensorWaves;   // units per round
+  const int nwg = (int)std::min<long>((units + tw - 1) / tw, std::max(1, 256 / heads));
   const dim3 grid(nwg, 1, heads);
   if (a.code_bits == 4) {
+    constexpr int kT = DemCfg<4>::kThreads;
     if (rotated)
-      hipLaunchKernelGGL((demote_bulk_kernel<true, 4>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<true, 4>), grid, dim3(kT), 0, st, a);
     else
-      hipLaunchKernelGGL((demote_bulk_kernel<false, 4>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<false, 4>), grid, dim3(kT), 0, st, a);
   } else {
+    constexpr int kT = DemCfg<2>::kThreads;
     if (rotated)
-      hipLaunchKernelGGL((demote_bulk_kernel<true, 2>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<true, 2>), grid, dim3(kT), 0, st, a);
     else
-      hipLaunchKernelGGL((demote_bulk_kernel<false, 2>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((demote_bulk_kernel<false, 2>), grid, dim3(kT), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -177,44 +177,49 @@ def test_bulk_demotion_full_size_sampled(code_bits):
     assert not got[~used].any()
 
 
-@pytest.mark.parametrize("code_bits", [2, 4])
-def test_bulk_demotion_reloads_unit_metadata(code_bits):
+@pytest.mark.parametrize("code_bits,batch", [(2, 16), (4, 32)])
+def test_bulk_demotion_reloads_unit_metadata(code_bits, batch):
     # Long enough that the first waves of the launch take more work units than
     # one batch of lane-resident unit metadata covers (64 lanes / pages per
-    # unit: 21 units of three pages for INT2, 64 one-page units for INT4), so
-    # the kernel reloads it mid-loop: 16 sequences x 8192 tokens x 8 KV heads,
-    # 256 workgroups of 4 waves per tensor.  The units past the reload are the
-    # last ones of the index space, all in sequence 15; it is compared with the
-    # oracle in full (all heads, K and V), with sequence 0 beside it.
+    # unit: 32 units of two pages for INT2, 64 one-page units for INT4), so the
+    # kernel reloads it mid-loop: 16 (INT2) or 32 (INT4) sequences x 16384
+    # tokens x 8 KV heads, 256 workgroups of 6 (INT2) or 8 (INT4) waves per
+    # tensor.  The units past the reload are the last ones of the index space;
+    # the last sequence holds some of them and is compared with the oracle in
+    # full (all heads, K and V), with sequence 0 beside it.  Every sequence
+    # demotes the same tokens (with its own start slot and pages).
     import math
     from bit_rotated_kv_demote_amd.pool import TieredKV
-    batch, chunk, hkv, hq = 16, 8192, 8, 64
-    pages_per_unit, meta_units = (3, 21) if code_bits == 2 else (1, 64)
+    chunk, hkv, hq = 16384, 8, 64
+    pages_per_unit, meta_units, tensor_waves = (2, 32, 6) if code_bits == 2 else (1, 64, 8)
     ups = math.ceil((15 + chunk) / (16 * pages_per_unit))
-    units, waves = batch * hkv * ups, 256 * 4
-    assert units > meta_units * waves                 # some waves run past one metadata batch
+    units, waves = batch * hkv * ups, 256 * tensor_waves
     first_reloaded = meta_units * waves               # lowest unit index taken after a reload
-    assert first_reloaded // (hkv * ups) == batch - 1
+    assert first_reloaded < units                     # some waves run past one metadata batch
+    assert first_reloaded // (hkv * ups) <= batch - 1 < units // (hkv * ups)
     st = synth.streams(1005)
     out_ch = synth.outlier_channels(st["outliers"])
-    k = synth.kv_tokens(st["k"], st["lognormal"], batch * chunk, hkv, out_ch).reshape(batch, chunk, hkv, 128)
-    v = synth.kv_tokens(st["v"], st["lognormal"], batch * chunk, hkv, out_ch).reshape(batch, chunk, hkv, 128)
+    k1 = synth.kv_tokens(st["k"], st["lognormal"], chunk, hkv, out_ch)
+    v1 = synth.kv_tokens(st["v"], st["lognormal"], chunk, hkv, out_ch)
     rot = synth.random_rotation(st["rot"])
-    tau_k = orc.clip_thresholds(synth.bf16_bits_to_f32(k[0, :2048]), rot)
-    tau_v = orc.clip_thresholds(synth.bf16_bits_to_f32(v[0, :2048]), rot)
+    tau_k = orc.clip_thresholds(synth.bf16_bits_to_f32(k1[:2048]), rot)
+    tau_v = orc.clip_thresholds(synth.bf16_bits_to_f32(v1[:2048]), rot)
     max_pages = chunk // 16 + 2
     pt = synth.page_permutation(st["perm"], batch * max_pages).reshape(batch, max_pages).astype(np.int32)
     starts = [int(x) for x in synth.ragged_lengths(st["lengths"], batch, 0, 15)]
     dev = TieredKV(hq, hkv, batch, max_pages, batch * max_pages, rot, rot, tau_k, tau_v, page_table=pt,
                    code_bits=code_bits)
-    dev.demote(i32(starts), bf16_tensor(k), bf16_tensor(v))
+    kd = bf16_tensor(k1)[None].expand(batch, -1, -1, -1).contiguous()
+    vd = bf16_tensor(v1)[None].expand(batch, -1, -1, -1).contiguous()
+    dev.demote(i32(starts), kd, vd)
     torch.cuda.synchronize()
+    del kd, vd
     got = dev.hist.cpu().numpy()
     ref = orc.Pool(batch, hkv, batch * max_pages, pt, bits=code_bits)
     pages, slots = [], []
     for b in (0, batch - 1):
         h = starts[b] + np.arange(chunk)
-        ref.demote_many(b, h, k[b], v[b], rot, rot, tau_k, tau_v)
+        ref.demote_many(b, h, k1, v1, rot, rot, tau_k, tau_v)
         pages.append(pt[b, h // 16])
         slots.append(h % 16)
     rate, maxd, meta_ulp = code_diff_stats(got, ref.hist, np.concatenate(pages), np.concatenate(slots))
