@@ -13,9 +13,10 @@
 //   append_kernel      one decode step: demote the ring slot about to be
 //                      reused (fp32 VALU rotation, latency-bound), then write
 //                      the new token into sink or ring.
-//   demote_bulk_kernel many tokens: units of three pages (INT2) per wave,
-//                      one tensor per wave; the rotation is a 128x128x48
-//                      product on the matrix cores with R split into bf16
+//   demote_bulk_kernel many tokens: units of two pages (INT2) or one
+//                      (INT4) per wave, one tensor per wave; the rotation is
+//                      a 128x128x32 (INT2) product on the matrix cores with
+//                      R split into bf16
 //                      hi + lo terms (fp32 accumulation), or the input is
 //                      already-rotated fp32.
 //   prefill_route_kernel  copies of the sink and recent tiers of a prefill.
