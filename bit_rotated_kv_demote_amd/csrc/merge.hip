@@ -30,11 +30,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int kRows = kD / kRB;          // output rows of this workgroup
   constexpr int kColParts = 256 / kRows;   // threads sharing one row of R
   constexpr int kCols = kD / kColParts;    // columns of R per thread
-  __shared__ float w[kMaxSplits];
+  __shared__ float w[4][kMaxSplits];       // per wave: the weight of every slot
   __shared__ float4 red[kParts][2][kD / 4];
   __shared__ float oh[2][kD];      // weighted sums: plain part, rotated part
   __shared__ float rr[kColParts][kRows];   // partial sums of (rotated part . R^T)
-  __shared__ float wred[2][4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
   // output row head = (b * q_tokens + t) * Hq + hq; its records: work-item
@@ -53,12 +52,14 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
   const int row0 = kRows * blockIdx.y;     // first output row of this workgroup
   // Every load first, before the sequence length is known: (m, l) of every
-  // slot, the first round of record columns and this thread's slice of R
-  // (row row0 + ri, columns [kCols jh, kCols jh + kCols)).  Slots the first
-  // kernel left untouched for this length are masked below, never
-  // multiplied in.
-  const float2 ml0 = *reinterpret_cast<const float2*>(rec(tid) + kD);
-  const float2 ml1 = *reinterpret_cast<const float2*>(rec(tid + 256) + kD);
+  // slot (each wave loads all of them, lane s taking slots s + 64 k), the
+  // first round of record columns and this thread's slice of R (row
+  // row0 + ri, columns [kCols jh, kCols jh + kCols)).  Slots the first kernel
+  // left untouched for this length are masked below, never multiplied in.
+  constexpr int kMlRounds = (kMaxSplits + 63) / 64;
+  float2 ml[kMlRounds];
+#pragma unroll
+  for (int k = 0; k < kMlRounds; ++k) ml[k] = *reinterpret_cast<const float2*>(rec(lane + 64 * k) + kD);
   const int c4 = tid & 31, part = tid >> 5;
   float4 v[kMergeBatch];
 #pragma unroll
@@ -93,34 +94,33 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
   auto active = [&](int s) { return s < a.n_plain_slots ? s < n_plain : s - a.n_plain_slots < n_rot; };
 
-  // global max over the head's active splits, weights, total sum
-  const bool act0 = tid < n_slots && active(tid), act1 = tid + 256 < n_slots && active(tid + 256);
-  float mm = fmaxf(act0 ? ml0.x : kMInit, act1 ? ml1.x : kMInit);
-  mm = wave_max(mm);
-  if (lane == 0) wred[0][wave] = mm;
-  __syncthreads();
-  const float m_all = fmaxf(fmaxf(wred[0][0], wred[0][1]), fmaxf(wred[0][2], wred[0][3]));
+  // maximum over the head's active splits, weights and total sum: every wave
+  // computes them itself, so no workgroup barrier is needed before the sums
+  float mm = kMInit;
+#pragma unroll
+  for (int k = 0; k < kMlRounds; ++k) {
+    const int s = lane + 64 * k;
+    if (s < n_slots && active(s)) mm = fmaxf(mm, ml[k].x);
+  }
+  const float m_all = wave_max(mm);
   float ll = 0.0f;
-  if (act0) {
-    const float wk = __builtin_amdgcn_exp2f(ml0.x - m_all);
-    w[tid] = wk;
-    ll = wk * ml0.y;
+#pragma unroll
+  for (int k = 0; k < kMlRounds; ++k) {
+    const int s = lane + 64 * k;
+    if (s < n_slots && active(s)) {
+      const float wk = __builtin_amdgcn_exp2f(ml[k].x - m_all);
+      w[wave][s] = wk;
+      ll = fmaf(wk, ml[k].y, ll);
+    }
   }
-  if (act1) {
-    const float wk = __builtin_amdgcn_exp2f(ml1.x - m_all);
-    w[tid + 256] = wk;
-    ll = fmaf(wk, ml1.y, ll);
-  }
-  ll = wave_sum(ll);
-  if (lane == 0) wred[1][wave] = ll;
-  __syncthreads();
-  const float l_all = (wred[1][0] + wred[1][1]) + (wred[1][2] + wred[1][3]);
+  const float l_all = wave_sum(ll);
+  __builtin_amdgcn_wave_barrier();
 
   // weighted sums of the record columns, plain and rotated kept apart
   float4 ap = make_float4(0.f, 0.f, 0.f, 0.f), ar = ap;
   auto acc_into = [&](int s, const float4& x) {
     if (s >= n_slots || !active(s)) return;
-    const float wk = w[s];
+    const float wk = w[wave][s];
     float4& acc = s < a.n_plain_slots ? ap : ar;
     acc.x = fmaf(wk, x.x, acc.x); acc.y = fmaf(wk, x.y, acc.y);
     acc.z = fmaf(wk, x.z, acc.z); acc.w = fmaf(wk, x.w, acc.w);
