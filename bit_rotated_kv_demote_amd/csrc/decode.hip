@@ -659,8 +659,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
       frexpf(amax, &e2);
       const int s_exp = amax > 0.0f ? min(15 - e2, 100) : 0;
       // group sums: lanes 0..31 hold groups 0 (v0) and 2 (v1), lanes 32..63 groups 1 and 3
-      float g0 = v0, g1 = v1;
-      for (int m = 16; m >= 1; m >>= 1) { g0 += __shfl_xor(g0, m); g1 += __shfl_xor(g1, m); }
+      const float g0 = half_wave_sum(v0), g1 = half_wave_sum(v1);
       if (lane == 0) { sm.sexp[h] = (float)s_exp; sm.qs[h][0] = g0; sm.qs[h][2] = g1; }
       if (lane == 32) { sm.qs[h][1] = g0; sm.qs[h][3] = g1; }
     }

@@ -63,6 +63,74 @@ __device__ __forceinline__ int v4_halfword_byte(int t, int b, int hi_m) {
   return kVCodeOff4 + 16 * (16 * (t >> 2) + b) + 4 * (2 * hi_m + ((t & 3) >> 1)) + 2 * (t & 1);
 }
 
+// ---- cross-lane reductions (DPP within 16-lane rows, lane swaps across rows)
+// max / sum over the four 16-lane rows of a wave (lanes x, x+16, x+32, x+48)
+__device__ __forceinline__ float rows_max(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+// v(lane) + v(lane ^ 32)
+__device__ __forceinline__ float half_swap_sum(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+// v from another lane of the same 16-lane row (DPP control kCtrl)
+template <int kCtrl>
+__device__ __forceinline__ float dpp_from(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+// max / sum over the whole wave, the result in every lane: lane pairs, quad
+// pairs (quad_perm), the two quads of each half row (row_half_mirror), the
+// two halves of each row (row_mirror), then the four rows
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_from<0xB1>(v));      // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_from<0x4E>(v));      // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_from<0x141>(v));     // row_half_mirror
+  v = fmaxf(v, dpp_from<0x140>(v));     // row_mirror
+  return rows_max(v);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_from<0xB1>(v);
+  v += dpp_from<0x4E>(v);
+  v += dpp_from<0x141>(v);
+  v += dpp_from<0x140>(v);
+  return rows_sum(v);
+}
+// min / max / sum within each 32-lane half of a wave (lanes [0, 32) and
+// [32, 64) separately), the result in every lane of the half
+__device__ __forceinline__ float half_wave_min(float v) {
+  v = fminf(v, dpp_from<0xB1>(v));
+  v = fminf(v, dpp_from<0x4E>(v));
+  v = fminf(v, dpp_from<0x141>(v));
+  v = fminf(v, dpp_from<0x140>(v));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = fmaxf(v, dpp_from<0xB1>(v));
+  v = fmaxf(v, dpp_from<0x4E>(v));
+  v = fmaxf(v, dpp_from<0x141>(v));
+  v = fmaxf(v, dpp_from<0x140>(v));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += dpp_from<0xB1>(v);
+  v += dpp_from<0x4E>(v);
+  v += dpp_from<0x141>(v);
+  v += dpp_from<0x140>(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // ---- INT2 quantiser of one 32-channel group (asymmetric min-max, four levels).
 // zero = fp16 rounded toward -inf of the group minimum, scale = fp16 rounded
 // toward +inf of (max - zero) / 3, code = clamp(rint((y - zero) / scale), 0, 3)

@@ -45,10 +45,10 @@ __device__ __forceinline__ void rotate_partial(const float* x, const float4 (&rq
   acc.y += acc2.y;
   acc.z += acc2.z;
   acc.w += acc2.w;
-  acc.x += __shfl_xor(acc.x, 32);
-  acc.y += __shfl_xor(acc.y, 32);
-  acc.z += __shfl_xor(acc.z, 32);
-  acc.w += __shfl_xor(acc.w, 32);
+  acc.x = half_swap_sum(acc.x);
+  acc.y = half_swap_sum(acc.y);
+  acc.z = half_swap_sum(acc.z);
+  acc.w = half_swap_sum(acc.w);
   if ((tid & 32) == 0) *reinterpret_cast<float4*>(&part[(tid >> 6) * kD + 4 * c4]) = acc;
 }
 
@@ -65,12 +65,7 @@ __device__ float quantize_pack_channel_per_thread(float yc, bool is_v, uint8_t* 
                                                   int bits) {
   const int c = threadIdx.x;
   const bool act = c < kD;
-  float mn = yc, mx = yc;
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, m));
-    mx = fmaxf(mx, __shfl_xor(mx, m));
-  }
+  const float mn = half_wave_min(yc), mx = half_wave_max(yc);   // the thread's 32-channel group
   __half s, z;
   const bool int4 = bits == 4;
   group_scale_zero(mn, mx, &s, &z, int4 ? 15.0f : 3.0f);
