@@ -647,13 +647,15 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
       if (lane < 32) *reinterpret_cast<float4*>(&sm.wo[wave][h][4 * c4]) = acc;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * kD; idx += 256) {
-      const int h = idx / kD, jj = idx % kD;
-      sm.qr[h][jj] = (sm.wo[0][h][jj] + sm.wo[1][h][jj]) + (sm.wo[2][h][jj] + sm.wo[3][h][jj]);
-    }
-    __syncthreads();
+    // wave w finishes heads w, w + 4, ...: the four waves' partials, then the
+    // head's scale exponent and group sums
     for (int h = wave; h < G; h += 4) {
-      const float v0 = sm.qr[h][lane], v1 = sm.qr[h][lane + 64];
+      auto wsum = [&](int jj) {
+        return (sm.wo[0][h][jj] + sm.wo[1][h][jj]) + (sm.wo[2][h][jj] + sm.wo[3][h][jj]);
+      };
+      const float v0 = wsum(lane), v1 = wsum(lane + 64);
+      sm.qr[h][lane] = v0;
+      sm.qr[h][lane + 64] = v1;
       const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1))) * kC0;
       int e2 = 0;
       frexpf(amax, &e2);
