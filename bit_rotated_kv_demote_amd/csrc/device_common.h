@@ -168,10 +168,10 @@ __device__ __forceinline__ uint32_t quant_code(float yc, float zf, float sf, flo
   return (uint32_t)c;
 }
 
-// The same code without a division, for x = fl(y - zero) >= 0 and an fp16
-// group scale s > 0.  With q = fl(x / s) correctly rounded: rint(q) >= 1 iff
-// q > 0.5, >= 2 iff q >= 1.5 and 3 iff q > 2.5 (ties to even send 0.5 and 2.5
-// down and 1.5 up); over the exact quotient these are x/s > 0.5 + 2^-25,
+// Cuts that give the INT2 code without forming the quotient, for
+// x = fl(y - zero) >= 0 and an fp16 group scale s > 0.  With q = fl(x / s)
+// correctly rounded: rint(q) >= 1 iff q > 0.5, >= 2 iff q >= 1.5 and 3 iff
+// q > 2.5 (ties to even send 0.5 and 2.5 down and 1.5 up); over the exact quotient these are x/s > 0.5 + 2^-25,
 // x/s >= 1.5 - 2^-24 and x/s > 2.5 + 2^-23 (half an fp32 spacing past each
 // midpoint).  k s is exact in fp32 for k = 0.5, 1.5, 2.5 (s has 11
 // significant bits), and the fp32 spacing next to k s exceeds s 2^-25,
@@ -183,9 +183,6 @@ struct CodeCut {
 };
 __device__ __forceinline__ CodeCut code_cut(float sf) {
   return {0.5f * sf, sf > 0.0f ? 1.5f * sf : 1.0f, 2.5f * sf};
-}
-__device__ __forceinline__ uint32_t quant_code_cut(float x, const CodeCut& c) {
-  return (uint32_t)(x > c.c0) + (uint32_t)(x >= c.c1) + (uint32_t)(x > c.c2);
 }
 
 __device__ __forceinline__ float clip_value(float y, float tau) { return fminf(fmaxf(y, -tau), tau); }
