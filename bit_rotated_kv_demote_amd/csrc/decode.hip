@@ -112,21 +112,20 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
                           int pg_begin, int pg_end, int wave, int lane, const PageCodes<kBits>* c_first,
                           const u32x2_t* m_first) {
   const int x = lane & 15, qa = lane >> 4;
-  // ---- score operands: q' in fp16 hi (columns 0..G-1) and lo (G..2G-1)
-  // Up to 8 heads per 16-column score tile (hi and lo halves in two columns).
-  // Tile 0 holds heads 0..kGT-1: hi in columns [0, kGT), lo in [kGT, 2 kGT).
-  // With 16 heads, tile 1 holds heads 8..15 the other way round: hi in
-  // columns 8..15 (head = column), lo in columns 0..7, so that one rotate by
-  // 8 lanes pairs the halves of every head of either tile.
-  constexpr int kTiles = G > 8 ? 2 : 1;
-  constexpr int kGT = G > 8 ? 8 : G;
-  half8_t bq[kTiles][4];
-  float be[kTiles];
+  // ---- score operands: q' in fp16 hi and lo halves
+  // Up to 8 heads: one operand set, hi halves in columns [0, G) and lo halves
+  // in [G, 2G); one rotate by 8 lanes then pairs the halves of every head.
+  // 16 heads: head = column, and two operand sets (hi, then lo) whose
+  // products accumulate into one tile, so that the scale and the scores are
+  // applied once per head.
+  constexpr int kSets = G > 8 ? 2 : 1;
+  half8_t bq[kSets][4];
+  float be;
 #pragma unroll
-  for (int tl = 0; tl < kTiles; ++tl) {
-    const bool hi_col = tl == 0 ? x < kGT : x >= 8;
-    const bool col_used = tl == 0 ? x < 2 * kGT : true;
-    const int col_head = !col_used ? 0 : (tl == 0 ? (x < kGT ? x : x - kGT) : 8 + (x & 7));
+  for (int st = 0; st < kSets; ++st) {
+    const bool hi_col = kSets == 2 ? st == 0 : x < G;
+    const bool col_used = kSets == 2 ? true : x < 2 * G;
+    const int col_head = kSets == 2 ? x : (!col_used ? 0 : (x < G ? x : x - G));
     const float col_scale = ldexpf(kC0, (int)sm.sexp[col_head]);
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -141,10 +140,11 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
           const float v = ldexpf(sm.qr[col_head][j] * col_scale, -lsh);
           const _Float16 hi = (_Float16)v;
           const _Float16 e = hi_col ? hi : (_Float16)(v - (float)hi);
-          bq[tl][g][2 * i + hf] = col_used ? e : (_Float16)0.0f;
+          bq[st][g][2 * i + hf] = col_used ? e : (_Float16)0.0f;
         }
     // zero-point term operand (fp32 product, 4 groups = K of 4), hi columns only
-    be[tl] = (hi_col && col_used) ? ldexpf(sm.qs[col_head][qa] * kC0, (int)sm.sexp[col_head] - 24) : 0.0f;
+    if (st == 0)
+      be = (hi_col && col_used) ? ldexpf(sm.qs[col_head][qa] * kC0, (int)sm.sexp[col_head] - 24) : 0.0f;
   }
   // matrix-core units -> log2 units; 0 for the columns that hold no head, so
   // that their (unused) scores stay at 0 and never move the running maximum
@@ -190,7 +190,7 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
 
     // ---------------- scores
     float sc[kStepPages][4];
-    float4_t cacc_all[kStepPages][kTiles];
+    float4_t cacc_all[kStepPages];
 #pragma unroll
     for (int p = 0; p < kStepPages; ++p) {
       const uint8_t* mp = mbuf + 512 * p;
@@ -225,38 +225,35 @@ __device__ void hist_wave(const DecodeArgs& a, DecodeSmem<G>& sm, int32_t ids, i
       const u32x4_t s23 = *reinterpret_cast<const u32x4_t*>(mp + 32 * qa + 16);
       const _Float16* sh0 = reinterpret_cast<const _Float16*>(&s01);
       const _Float16* sh1 = reinterpret_cast<const _Float16*>(&s23);
-      float4_t (&cacc)[kTiles] = cacc_all[p];
+      float4_t& cacc = cacc_all[p];
+      cacc = __builtin_amdgcn_mfma_f32_16x16x4f32((float)zk, be, (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      float4_t d[4];
 #pragma unroll
-      for (int tl = 0; tl < kTiles; ++tl) {
-        // sum_g zero[t][g] * (scaled group sums of q'), t = lane's row token
-        cacc[tl] = __builtin_amdgcn_mfma_f32_16x16x4f32((float)zk, be[tl], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        float4_t d[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          d[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[g], bq[tl][g], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const _Float16* sr = (r < 2) ? sh0 + 4 * r : sh1 + 4 * (r - 2);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) cacc[tl][r] = fmaf((float)sr[g], d[g][r], cacc[tl][r]);
-        }
+      for (int g = 0; g < 4; ++g) {
+        d[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[g], bq[0][g], (float4_t){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        if constexpr (kSets == 2) d[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak[g], bq[1][g], d[g], 0, 0, 0);
       }
-    }
-    // hi + lo columns, once every page's products are in (the lane moves
-    // then read registers written well before)
-#pragma unroll
-    for (int p = 0; p < kStepPages; ++p) {
-      const float4_t (&cacc)[kTiles] = cacc_all[p];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // hi + lo halves of the same head (tile 1: the halves sit the other way round)
-        const float mine = kTiles == 1 ? cacc[0][r] : (x < 8 ? cacc[0][r] : cacc[kTiles - 1][r]);
-        const float peer = kTiles == 1 ? cacc[0][r] : (x < 8 ? cacc[kTiles - 1][r] : cacc[0][r]);
-        const float other = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-            0u, __float_as_uint(peer), 0x120 + (16 - kGT), 0xF, 0xF, false));
-        sc[p][r] = mine + other;
+        const _Float16* sr = (r < 2) ? sh0 + 4 * r : sh1 + 4 * (r - 2);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) cacc[r] = fmaf((float)sr[g], d[g][r], cacc[r]);
       }
     }
+    // hi + lo columns (up to 8 heads), once every page's products are in
+    // (the lane moves then read registers written well before)
+#pragma unroll
+    for (int p = 0; p < kStepPages; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (kSets == 2) {
+          sc[p][r] = cacc_all[p][r];
+        } else {
+          const float other = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+              0u, __float_as_uint(cacc_all[p][r]), 0x120 + (16 - G), 0xF, 0xF, false));
+          sc[p][r] = cacc_all[p][r] + other;
+        }
+      }
     if (partial) {
 #pragma unroll
       for (int p = 0; p < kStepPages; ++p)

@@ -54,7 +54,7 @@ namespace {
 // Several query tokens per sequence: the query heads' virtual heads (t, h)
 // of one KV head are split into work-item column groups of `group` columns,
 // the largest power of two (at most max_group) that divides n_query * G.
-// The INT2 kernel takes 16 columns (two score tiles) only when that still
+// The INT2 kernel takes 16 columns (one head per column) only when that still
 // leaves two or more groups: at 16 virtual heads, two 8-column groups keep
 // twice the workgroups busy and are faster on one long sequence.
 constexpr int kMaxQueryTokens = 256;
