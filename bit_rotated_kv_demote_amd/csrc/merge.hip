@@ -170,18 +170,21 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   }
 }
 
-// Large grids: one workgroup per record group (sequence, KV head, column
-// group) of G columns.  Wave w merges columns w, w + 4, ...; the workgroup
-// then applies R^T to every column with one load of its slice of R, so the
-// R traffic (the bound when thousands of heads are merged) falls G-fold.
-__global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
+// Large grids: `parts` workgroups per record group (sequence, KV head,
+// column group) of G columns, each taking G / parts >= 4 consecutive
+// columns.  Wave w merges the part's columns w, w + 4, ...; the workgroup
+// then applies R^T to each of them with one load of its slice of R, so the
+// R traffic (the bound when thousands of heads are merged) falls
+// (G / parts)-fold.
+__global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a, int parts) {
   __shared__ float w[4][kMaxSplits];
   __shared__ float oh[16][2][kD];
   __shared__ float rr[16][2][kD];
   __shared__ float lsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
-  const int grp = blockIdx.x;
+  const int grp = blockIdx.x / parts;
+  const int h0 = (blockIdx.x % parts) * (G / parts), h1 = h0 + G / parts;
   const int b = grp / (a.hkv * a.n_colgroups), hk = (grp / a.n_colgroups) % a.hkv, cg = grp % a.n_colgroups;
   const int n_slots = a.n_splits_total;
   const float* gbase = a.partials + (size_t)grp * n_slots * G * kPartStride;
@@ -212,13 +215,13 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
     n_rot = 0;
   }
   if (n_plain + n_rot <= 0) {       // no tokens: nothing to attend
-    for (int idx = tid; idx < G * kD; idx += 256) out_row(idx / kD)[idx % kD] = 0.0f;
+    for (int idx = tid; idx < (h1 - h0) * kD; idx += 256) out_row(h0 + idx / kD)[idx % kD] = 0.0f;
     return;
   }
   auto active = [&](int s) { return s < a.n_plain_slots ? s < n_plain : s - a.n_plain_slots < n_rot; };
 
   const int c4 = lane & 31, part = lane >> 5;
-  for (int h = wave; h < G; h += 4) {
+  for (int h = h0 + wave; h < h1; h += 4) {
     const float* hb = gbase + (size_t)h * kPartStride;
     auto rec = [&](int s) { return hb + (size_t)min(s, n_slots - 1) * G * kPartStride; };
     // max, weights and total over the column's active splits (lanes stride 64)
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
   }
   __syncthreads();
   // inverse rotation of every column's history part: (y R^T)_i = sum_j y_j R[i][j]
-  for (int h = 0; h < G; ++h) {
+  for (int h = h0; h < h1; ++h) {
     float acc = 0.0f;
     if (n_rot > 0) {
 #pragma unroll
@@ -277,8 +280,8 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a) {
     rr[h][jh][ri] = acc;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += 256) {
-    const int h = idx / kD, i = idx % kD;
+  for (int idx = tid; idx < (h1 - h0) * kD; idx += 256) {
+    const int h = h0 + idx / kD, i = idx % kD;
     const float l = lsum[h];
     out_row(h)[i] = l > 0.0f ? (oh[h][0][i] + (rr[h][0][i] + rr[h][1][i])) / l : 0.0f;
   }
@@ -290,13 +293,18 @@ hipError_t launch_merge(const MergeArgs& a, int n_heads, hipStream_t st) {
   if (n_heads <= 0) return hipSuccess;
   // few heads: four workgroups per head (a quarter of R each); up to about
   // three workgroups per compute unit: one workgroup per head spreads the
-  // latency; beyond that, one per record group shares R
-  if (n_heads <= 64)
+  // latency; beyond that, record groups share R, split over up to four
+  // workgroups (at least four columns each) while fewer than 512 run
+  if (n_heads <= 64) {
     hipLaunchKernelGGL(merge_kernel<4>, dim3(n_heads, 4), dim3(256), 0, st, a);
-  else if (n_heads <= 768 || a.group < 2)
+  } else if (n_heads <= 768 || a.group < 2) {
     hipLaunchKernelGGL(merge_kernel<1>, dim3(n_heads), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(merge_group_kernel, dim3(n_heads / a.group), dim3(256), 0, st, a);
+  } else {
+    const int n_groups = n_heads / a.group;
+    int parts = 1;
+    while (4 * parts < a.group && n_groups * parts < 512) parts *= 2;
+    hipLaunchKernelGGL(merge_group_kernel, dim3(n_groups * parts), dim3(256), 0, st, a, parts);
+  }
   return hipGetLastError();
 }
 

@@ -139,9 +139,20 @@ def test_large_grid_merge_per_record_group():
 
 
 def test_large_grid_merge_multi_query_16_columns():
-    # 4 sequences x 8 queries x 32 heads = 1024 merged heads in 16-column groups
+    # 4 sequences x 8 queries x 32 heads = 1024 merged heads in 64 groups of
+    # 16 columns: four merge workgroups per group, four columns each
     lengths = [900, 410, 1300, 333]
     layer = Layer(seed=1171, batch=4, hq=32, hkv=8, max_len=max(lengths))
     out, ref = _multi_vs_oracle(layer, lengths, 8, 14)
     for b in range(4):
+        assert rel_l2(out[b], ref[b]) <= TOL, b
+
+
+def test_large_grid_merge_two_parts_per_record_group():
+    # 20 sequences x 8 queries x 32 heads = 5120 merged heads in 320 groups of
+    # 16 columns: two merge workgroups per group, eight columns each
+    lengths = [330 + 17 * b for b in range(20)]
+    layer = Layer(seed=1172, batch=20, hq=32, hkv=8, max_len=max(lengths))
+    out, ref = _multi_vs_oracle(layer, lengths, 8, 15)
+    for b in range(20):
         assert rel_l2(out[b], ref[b]) <= TOL, b
