@@ -123,12 +123,11 @@ def test_int4_large_grid_merge_per_record_group():
     assert rel_l2(out, ref) <= TOL
 
 
-def test_int4_qwen3_4b_32k_sampled_heads():
-    # the 32K workload's shape: device prefill for every KV head, the
-    # oracle's bytes for the two compared KV heads
-    n = 32768
-    layer = Layer(seed=1430, batch=1, hq=32, hkv=8, max_len=n, code_bits=4)
-    kv_heads = [1, 6]
+@pytest.mark.parametrize("n,kv_heads,seed", [(32768, [1, 6], 1430), (131072, [4], 1431)])
+def test_int4_full_size_sampled_heads(n, kv_heads, seed):
+    # the 32K and 128K workloads' shape (32 q / 8 KV heads): device prefill
+    # for every KV head, the oracle's bytes for the compared KV heads
+    layer = Layer(seed=seed, batch=1, hq=32, hkv=8, max_len=n, code_bits=4)
     opool = layer.oracle_pool([n], kv_heads)
     dev = layer.device_pool()
     dev.prefill(i32([n]), bf16_tensor(layer.k), bf16_tensor(layer.v))
