@@ -18,7 +18,8 @@
 //   q . k~_t = sum_g s_{t,g} sum_{j in g} q'_j c_{t,j} + sum_g z_{t,g} sum_{j in g} q'_j.
 // The per-group code sums run on the matrix cores: 2-bit codes are placed in
 // fp16 operands as exact subnormals (one AND per two codes, c * 4^f * 2^-24)
-// and q' is split into fp16 hi + lo halves occupying two operand columns.
+// and q' is split into fp16 hi + lo halves: two operand columns per head (up
+// to 8 heads), or two products into one tile with a head per column (16).
 // The value side accumulates p_t s_{t,g} c_{t,j} on the matrix cores and
 // p_t z_{t,g} with one more small product, all in the rotated space.
 #include "attn_common.h"
