@@ -10,7 +10,13 @@ namespace oscar {
 constexpr float kC0 = 0.12751743082459868f;     // log2(e) / sqrt(128)
 constexpr float kMInit = -1.0e30f;
 constexpr int kPartStride = 132;                // floats per (split, head) record: acc[128], m, l
-constexpr int kTileTokens = 128;                // BF16 tokens per tile split
+// BF16 tokens per tile split: 128 for work items of up to 8 columns; one
+// split of all 320 sink and recent tokens for 16-column work items (several
+// query tokens), whose groups are many, so that tile splits take fewer
+// workgroup slots from the history splits
+constexpr int kTileTokens = 128;
+constexpr int kTileTokensWide = 320;
+__host__ __device__ constexpr int tile_tokens_for(int columns) { return columns == 16 ? kTileTokensWide : kTileTokens; }
 constexpr int kMaxSplits = 320;                 // per (sequence, KV head)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));

@@ -539,13 +539,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
   const int n_sink_used = min(n, kSink);
   const int n_recent_used = min(max(n - kSink, 0), kRecent);
   const int n_tile = n_sink_used + n_recent_used;
-  const int act_tile = (n_tile + kTileTokens - 1) / kTileTokens;
+  const int act_tile = (n_tile + a.tile_tokens - 1) / a.tile_tokens;
   const int hs = split - a.n_tile_splits;
   if (is_tile ? (split >= act_tile) : (hs >= act_hist)) return;
 
   float* part_base = a.partials + (size_t)grp * n_split_total * G * kPartStride;
   if (is_tile) {
-    const int u0 = split * kTileTokens;
+    const int u0 = split * a.tile_tokens;
     const int recent_first = max(kSink, n - kRecent);
     const size_t sink_base = ((size_t)slot * a.hkv + hk) * kSink;
     const size_t ring_base = ((size_t)slot * a.hkv + hk) * kRecent;
@@ -573,7 +573,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
       return ring + (ring_base + ((pos - kSink) & (kRecent - 1))) * kD;
     };
     // causal limit of column x: its query's position n - q_tokens + t
-    bf16_span_wave<G>(q_row, min(kTileTokens, n_tile - u0),
+    bf16_span_wave<G>(q_row, min(a.tile_tokens, n_tile - u0),
                       [&](int uu) { return row(a.sink_k, a.recent_k, a.k_new, uu); },
                       [&](int uu) { return row(a.sink_v, a.recent_v, a.v_new, uu); },
                       [&](int uu) { const int u = u0 + uu; return u < n_sink_used ? u : recent_first + (u - n_sink_used); },
@@ -694,7 +694,8 @@ DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_s
   const int max_pages = (max_hist + kPage - 1) / kPage;
   const long n_groups = (long)batch * hkv * n_colgroups;
   const int max_tile = min(max_seq_len, kSink + kRecent);
-  const int n_tile = (max_tile + kTileTokens - 1) / kTileTokens;
+  p.tile_tokens = tile_tokens_for(group);
+  const int n_tile = (max_tile + p.tile_tokens - 1) / p.tile_tokens;
   // The most history splits per group that keep the grid within `target`
   // workgroups; each split then gets the smallest multiple of kStepPages
   // pages (one wave step) that covers the history with that many.

@@ -78,6 +78,7 @@ struct DecodeArgs {
   int n_hist_splits;          // history splits per (sequence, KV head)
   int pages_per_split;        // a multiple of the wave step (4 pages)
   int n_tile_splits;          // BF16 sink/recent splits per (sequence, KV head)
+  int tile_tokens;            // BF16 tokens per tile split (tile_tokens_for(G))
   int n_groups_total;         // batch * Hkv * n_colgroups
   int grid_per_xcd;
   // Query columns.  A sequence has q_tokens queries (its last q_tokens
@@ -132,6 +133,7 @@ struct MergeArgs {
   int n_plain_slots;          // slots before the first rotated record (INT2: tile splits; BF16: all)
   int pages_per_split;
   int tiered;                 // 1: INT2 tiers (plain tile splits + rotated history); 0: BF16 pages
+  int tile_tokens;            // INT2 tiers: BF16 tokens per tile split
 };
 
 // Decode split geometry, shared by the workspace-size query and the launch.
@@ -139,6 +141,7 @@ struct DecodePlan {
   int n_hist_splits;
   int pages_per_split;
   int n_tile_splits;
+  int tile_tokens;            // BF16 tokens per tile split
   int n_splits_total;         // hist + tile
   int n_work;                 // batch * Hkv * n_splits_total
   int grid;                   // padded to a multiple of 8 (one slice per XCD)

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int hist_len = max(0, n - kSink - kRecent);
     const int n_hist_pages = (hist_len + kPage - 1) / kPage;
     const int n_tile = min(n, kSink) + min(max(n - kSink, 0), kRecent);
-    n_plain = min((n_tile + kTileTokens - 1) / kTileTokens, a.n_plain_slots);
+    n_plain = min((n_tile + a.tile_tokens - 1) / a.tile_tokens, a.n_plain_slots);
     n_rot = min((n_hist_pages + a.pages_per_split - 1) / a.pages_per_split, n_slots - a.n_plain_slots);
   } else {
     const int npages = (max(n, 0) + kPage - 1) / kPage;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void merge_group_kernel(MergeArgs a, int parts
     const int hist_len = max(0, n - kSink - kRecent);
     const int n_hist_pages = (hist_len + kPage - 1) / kPage;
     const int n_tile = min(n, kSink) + min(max(n - kSink, 0), kRecent);
-    n_plain = min((n_tile + kTileTokens - 1) / kTileTokens, a.n_plain_slots);
+    n_plain = min((n_tile + a.tile_tokens - 1) / a.tile_tokens, a.n_plain_slots);
     n_rot = min((n_hist_pages + a.pages_per_split - 1) / a.pages_per_split, n_slots - a.n_plain_slots);
   } else {
     const int npages = (max(n, 0) + kPage - 1) / kPage;

@@ -329,6 +329,7 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   a.n_hist_splits = plan.n_hist_splits;
   a.pages_per_split = plan.pages_per_split;
   a.n_tile_splits = plan.n_tile_splits;
+  a.tile_tokens = plan.tile_tokens;
   a.n_groups_total = batch * hkv * c.n_colgroups;
   a.grid_per_xcd = plan.grid / 8;
   a.q_tokens = n_query;
@@ -353,6 +354,7 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   m.n_plain_slots = plan.n_tile_splits;
   m.pages_per_split = plan.pages_per_split;
   m.tiered = 1;
+  m.tile_tokens = plan.tile_tokens;
   return hip_status(launch_merge(m, batch * n_query * desc->num_q_heads, hs));
 }
 
