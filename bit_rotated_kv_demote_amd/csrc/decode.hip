@@ -480,10 +480,31 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, DecodeSmem<G>& 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // XCD-aware order: consecutive workgroup ids go to different XCDs, so work
   // item = xcd * grid_per_xcd + local keeps a group's splits on one XCD.
-  const int item = (blockIdx.x & 7) * a.grid_per_xcd + (blockIdx.x >> 3);
+  // When the grid takes more than one round of workgroup slots (tiles_last:
+  // then the groups divide evenly over the XCDs), each XCD takes whole
+  // groups and dispatches their history splits first and their tile splits
+  // last, so that the short tile workgroups fill the slots the history
+  // splits leave at the end.
   const int n_split_total = a.n_tile_splits + a.n_hist_splits;
-  if (item >= a.n_groups_total * n_split_total) return;
-  const int grp = item / n_split_total, split = item % n_split_total;
+  const int local = blockIdx.x >> 3;
+  int grp, split;
+  if (a.tiles_last) {
+    const int gx = a.grid_per_xcd / n_split_total;     // groups per XCD
+    const int n_hist_x = gx * a.n_hist_splits;
+    const int g0 = (blockIdx.x & 7) * gx;
+    if (local < n_hist_x) {
+      grp = g0 + local / a.n_hist_splits;
+      split = a.n_tile_splits + local % a.n_hist_splits;
+    } else {
+      grp = g0 + (local - n_hist_x) / a.n_tile_splits;
+      split = (local - n_hist_x) % a.n_tile_splits;
+    }
+  } else {
+    const int item = (blockIdx.x & 7) * a.grid_per_xcd + local;
+    grp = item / n_split_total;
+    split = item % n_split_total;
+  }
+  if (grp >= a.n_groups_total) return;
   // group = (sequence b, KV head hk, column group cg); column x of the group
   // is virtual head cg * G + x = (query token t, head h of the KV head)
   const int cg = grp % a.n_colgroups;
@@ -711,6 +732,9 @@ DecodePlan plan_decode(int batch, int hkv, int group, int n_colgroups, int max_s
   p.n_tile_splits = n_tile;
   p.n_splits_total = p.n_hist_splits + p.n_tile_splits;
   p.n_work = (int)(n_groups * p.n_splits_total);
+  // more than one round of workgroups with groups that divide over the 8
+  // XCDs: whole groups per XCD, tile splits last; else contiguous items
+  p.tiles_last = p.n_work > target && n_groups % 8 == 0 && p.n_hist_splits > 0;
   p.grid = ((p.n_work + 7) / 8) * 8;
   p.partial_floats = (size_t)n_groups * p.n_splits_total * group * kPartStride;
   p.workspace_bytes = p.partial_floats * sizeof(float);

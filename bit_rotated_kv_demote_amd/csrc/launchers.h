@@ -79,6 +79,7 @@ struct DecodeArgs {
   int pages_per_split;        // a multiple of the wave step (4 pages)
   int n_tile_splits;          // BF16 sink/recent splits per (sequence, KV head)
   int tile_tokens;            // BF16 tokens per tile split (tile_tokens_for(G))
+  int tiles_last;             // 1: on each XCD the tile splits after the history splits
   int n_groups_total;         // batch * Hkv * n_colgroups
   int grid_per_xcd;
   // Query columns.  A sequence has q_tokens queries (its last q_tokens
@@ -142,6 +143,7 @@ struct DecodePlan {
   int pages_per_split;
   int n_tile_splits;
   int tile_tokens;            // BF16 tokens per tile split
+  bool tiles_last;            // more than one round of workgroups: tile splits dispatched last
   int n_splits_total;         // hist + tile
   int n_work;                 // batch * Hkv * n_splits_total
   int grid;                   // padded to a multiple of 8 (one slice per XCD)

@@ -330,6 +330,7 @@ static oscar_status decode_tiered(const oscar_layer_desc* desc, const oscar_pool
   a.pages_per_split = plan.pages_per_split;
   a.n_tile_splits = plan.n_tile_splits;
   a.tile_tokens = plan.tile_tokens;
+  a.tiles_last = plan.tiles_last ? 1 : 0;
   a.n_groups_total = batch * hkv * c.n_colgroups;
   a.grid_per_xcd = plan.grid / 8;
   a.q_tokens = n_query;
