@@ -115,7 +115,7 @@ def code_diff_stats(hist_a, hist_b, pages, slots):
     return float(np.mean(diffs != 0)), int(np.abs(diffs).max()) if diffs.size else 0, max(meta)
 
 
-# Bounds of the fused path (the spec contract): at most 0.1 % of the
+# Bounds of the fused path (the accuracy contract): at most 0.1 % of the
 # codes of demoted tokens differ from the oracle's, each by at most one level,
 # and scale / zero lie within 2 fp16 ulp; decode outputs over identical pool
 # bytes match within 2e-3 relative L2.
